@@ -1,0 +1,282 @@
+"""CPU oracle of the LSTM and GRU layer equations (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY. Only the test-suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module; the product path (the
+HIP library and its binding) never does, and shares no code with it.
+
+Every function evaluates the recurrence step by step, in plain fp64, in the
+order and notation of the pages it follows:
+
+* LSTM forward: popnn Lstm.cpp page, "basicLstmCellForwardPass" and
+  "applyGateNonlinearities" (sigmoid on input/forget/output gates, tanh on the
+  candidate; c = f*c_prev + i*g; h = o*tanh(c)).
+* LSTM backward: popnn Lstm.cpp page, "backwardStepImpl" (one step of BPTT
+  with the carried cell-state gradient), "basicLstmParamUpdate" (weight
+  gradients dW += dG^T [x; h_prev]); cross-checked by the LSTM branch of the
+  persistent backward kernel on the CUDA fragment page.
+* GRU forward: popnn Gru.cpp page, "basicGruCellForwardPass" (reset, update,
+  candidate; h = u*h_prev + (1-u)*c) and, for the reset-after variant,
+  "gruCellForwardPassCalcUnitsResetAfter" (reset applied to the recurrent
+  candidate term h_prev W_hc^T + b_hc).
+* GRU backward: popnn Gru.cpp page, "backwardStepImpl" (basic) and
+  "backwardStepImplResetAfter"; weight gradients "basicGruParamUpdate";
+  cross-checked by the GRU (linear-before-reset) branch of the CUDA fragment.
+
+Conventions (readings where the pages leave a point open):
+* Gate storage order: order[k] is the gate id stored in row block k of W_ih,
+  W_hh, b_ih, b_hh (LSTM ids i=0, f=1, g=2, o=3; GRU r=0, u=1, c=2).
+* Two bias vectors b_ih and b_hh; LSTM and basic GRU use their sum, the
+  reset-after GRU keeps the recurrent candidate bias inside r*(.).
+* reverse=True processes t = T-1 .. 0 but stores every per-step tensor at its
+  own t; the final state is the one after t = 0.
+* dh carry is seeded from dhT (and dcT for LSTM); None means zero.
+* Weight gradients are sums over (t, b); db_ih and db_hh are reported
+  separately (they differ only for the reset-after candidate row block).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LSTM_I, LSTM_F, LSTM_G, LSTM_O = 0, 1, 2, 3
+GRU_R, GRU_U, GRU_C = 0, 1, 2
+
+
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def _slot(order, gate, H):
+    """Row range of gate `gate` in storage order `order`."""
+    k = list(order).index(gate)
+    return slice(k * H, (k + 1) * H)
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def _steps(T, reverse):
+    return range(T - 1, -1, -1) if reverse else range(T)
+
+
+# ---------------------------------------------------------------- LSTM ----
+
+def lstm_forward(x, h0, c0, W_ih, W_hh, b_ih, b_hh, order=(0, 1, 2, 3), reverse=False):
+    """LSTM layer forward over a sequence x [T, B, I].
+
+    Returns a dict with y [T,B,H], hT, cT and the per-step activations the
+    backward pass reads (i, f, g, o, c each [T,B,H]) plus the inputs."""
+    x, W_ih, W_hh, b_ih, b_hh = map(_f64, (x, W_ih, W_hh, b_ih, b_hh))
+    T, B, _ = x.shape
+    H = W_hh.shape[1]
+    h = np.zeros((B, H)) if h0 is None else _f64(h0).copy()
+    c = np.zeros((B, H)) if c0 is None else _f64(c0).copy()
+    s = {k: _slot(order, k, H) for k in (LSTM_I, LSTM_F, LSTM_G, LSTM_O)}
+    st = {k: np.zeros((T, B, H)) for k in ("i", "f", "g", "o", "c", "y")}
+    for t in _steps(T, reverse):
+        z = x[t] @ W_ih.T + b_ih + h @ W_hh.T + b_hh        # [B, 4H], storage order
+        i = sigmoid(z[:, s[LSTM_I]])
+        f = sigmoid(z[:, s[LSTM_F]])
+        g = np.tanh(z[:, s[LSTM_G]])
+        o = sigmoid(z[:, s[LSTM_O]])
+        c = f * c + i * g
+        h = o * np.tanh(c)
+        for k, v in (("i", i), ("f", f), ("g", g), ("o", o), ("c", c), ("y", h)):
+            st[k][t] = v
+    st.update(hT=h, cT=c, x=x, h0=h0, c0=c0, W_ih=W_ih, W_hh=W_hh,
+              order=tuple(order), reverse=reverse)
+    return st
+
+
+def lstm_backward(fw, dy, dhT=None, dcT=None):
+    """BPTT through an LSTM layer given the forward record `fw`.
+
+    dy [T,B,H] is the gradient arriving at every output; dhT/dcT seed the
+    carries at the last processed step. Returns dx, dh0, dc0, dW_ih, dW_hh,
+    db_ih, db_hh and the per-step gate gradients dG [T,B,4H] (storage order,
+    gradients with respect to the gate pre-activations)."""
+    x, W_ih, W_hh, order, reverse = fw["x"], fw["W_ih"], fw["W_hh"], fw["order"], fw["reverse"]
+    T, B, _ = x.shape
+    H = W_hh.shape[1]
+    dy = _f64(dy)
+    s = {k: _slot(order, k, H) for k in (LSTM_I, LSTM_F, LSTM_G, LSTM_O)}
+    h0 = np.zeros((B, H)) if fw["h0"] is None else _f64(fw["h0"])
+    c0 = np.zeros((B, H)) if fw["c0"] is None else _f64(fw["c0"])
+    dh_carry = np.zeros((B, H)) if dhT is None else _f64(dhT).copy()
+    dc_carry = np.zeros((B, H)) if dcT is None else _f64(dcT).copy()
+    dx = np.zeros_like(x)
+    dW_ih = np.zeros_like(W_ih)
+    dW_hh = np.zeros_like(W_hh)
+    db = np.zeros(W_hh.shape[0])
+    dG_all = np.zeros((T, B, 4 * H))
+    for t in reversed(list(_steps(T, reverse))):
+        tp = (t + 1) if reverse else (t - 1)          # the step processed before t
+        first = (t == T - 1) if reverse else (t == 0)
+        c_prev = c0 if first else fw["c"][tp]
+        h_prev = h0 if first else fw["y"][tp]
+        i, f, g, o, c = (fw[k][t] for k in ("i", "f", "g", "o", "c"))
+        dh = dy[t] + dh_carry
+        tc = np.tanh(c)
+        d_o = dh * tc * o * (1 - o)
+        dc = dh * o * (1 - tc * tc) + dc_carry
+        d_i = dc * g * i * (1 - i)
+        d_f = dc * c_prev * f * (1 - f)
+        d_g = dc * i * (1 - g * g)
+        dG = np.zeros((B, 4 * H))
+        dG[:, s[LSTM_I]], dG[:, s[LSTM_F]] = d_i, d_f
+        dG[:, s[LSTM_G]], dG[:, s[LSTM_O]] = d_g, d_o
+        dG_all[t] = dG
+        dh_carry = dG @ W_hh
+        dc_carry = dc * f
+        dx[t] = dG @ W_ih
+        dW_ih += dG.T @ x[t]
+        dW_hh += dG.T @ h_prev
+        db += dG.sum(axis=0)
+    return dict(dx=dx, dh0=dh_carry, dc0=dc_carry, dW_ih=dW_ih, dW_hh=dW_hh,
+                db_ih=db.copy(), db_hh=db.copy(), dG=dG_all)
+
+
+# ----------------------------------------------------------------- GRU ----
+
+def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), reverse=False):
+    """GRU layer forward over x [T, B, I] (basic or reset-after variant).
+
+    Returns y, hT and the per-step r, u, c (activated), n_h (reset-after:
+    h_prev W_hc^T + b_hc, saved before the reset gate is applied) and
+    rh = r*h_prev (basic: the activation the candidate weights see)."""
+    x, W_ih, W_hh, b_ih, b_hh = map(_f64, (x, W_ih, W_hh, b_ih, b_hh))
+    T, B, _ = x.shape
+    H = W_hh.shape[1]
+    h = np.zeros((B, H)) if h0 is None else _f64(h0).copy()
+    sr, su, sc = (_slot(order, k, H) for k in (GRU_R, GRU_U, GRU_C))
+    st = {k: np.zeros((T, B, H)) for k in ("r", "u", "c", "nh", "rh", "y")}
+    for t in _steps(T, reverse):
+        xi = x[t] @ W_ih.T + b_ih                 # input parts, storage order
+        hr = h @ W_hh.T + b_hh                    # recurrent parts, storage order
+        r = sigmoid(xi[:, sr] + hr[:, sr])
+        u = sigmoid(xi[:, su] + hr[:, su])
+        if reset_after:
+            nh = hr[:, sc]
+            c = np.tanh(xi[:, sc] + r * nh)
+            st["nh"][t] = nh
+        else:
+            rh = r * h
+            c = np.tanh(xi[:, sc] + rh @ W_hh[sc].T + b_hh[sc])
+            st["rh"][t] = rh
+        h = u * h + (1 - u) * c
+        st["r"][t], st["u"][t], st["c"][t], st["y"][t] = r, u, c, h
+    st.update(hT=h, x=x, h0=h0, W_ih=W_ih, W_hh=W_hh, order=tuple(order),
+              reverse=reverse, reset_after=reset_after)
+    return st
+
+
+def gru_backward(fw, dy, dhT=None):
+    """BPTT through a GRU layer given the forward record `fw`.
+
+    Returns dx, dh0, dW_ih, dW_hh, db_ih, db_hh and the per-step
+    pre-activation gradients dGi (input side: [d_r, d_u, d_c]) and dGh
+    (recurrent side), both [T,B,3H] in storage order."""
+    x, W_ih, W_hh, order, reverse = fw["x"], fw["W_ih"], fw["W_hh"], fw["order"], fw["reverse"]
+    ra = fw["reset_after"]
+    T, B, _ = x.shape
+    H = W_hh.shape[1]
+    dy = _f64(dy)
+    sr, su, sc = (_slot(order, k, H) for k in (GRU_R, GRU_U, GRU_C))
+    h0 = np.zeros((B, H)) if fw["h0"] is None else _f64(fw["h0"])
+    carry = np.zeros((B, H)) if dhT is None else _f64(dhT).copy()
+    dx = np.zeros_like(x)
+    dW_ih = np.zeros_like(W_ih)
+    dW_hh = np.zeros_like(W_hh)
+    db_ih = np.zeros(W_ih.shape[0])
+    db_hh = np.zeros(W_hh.shape[0])
+    dGi_all = np.zeros((T, B, 3 * H))
+    dGh_all = np.zeros((T, B, 3 * H))
+    for t in reversed(list(_steps(T, reverse))):
+        tp = (t + 1) if reverse else (t - 1)
+        first = (t == T - 1) if reverse else (t == 0)
+        h_prev = h0 if first else fw["y"][tp]
+        r, u, c = fw["r"][t], fw["u"][t], fw["c"][t]
+        dh = dy[t] + carry
+        d_c = dh * (1 - u) * (1 - c * c)
+        d_u = dh * (h_prev - c) * u * (1 - u)
+        dGi = np.zeros((B, 3 * H))
+        dGh = np.zeros((B, 3 * H))
+        if ra:
+            d_r = d_c * fw["nh"][t] * r * (1 - r)
+            dGi[:, sr], dGi[:, su], dGi[:, sc] = d_r, d_u, d_c
+            dGh[:, sr], dGh[:, su], dGh[:, sc] = d_r, d_u, d_c * r
+            carry = dGh @ W_hh + dh * u
+            dW_hh += dGh.T @ h_prev
+        else:
+            d_rh = d_c @ W_hh[sc]                 # gradient wrt r*h_prev
+            d_r = d_rh * h_prev * r * (1 - r)
+            dGi[:, sr], dGi[:, su], dGi[:, sc] = d_r, d_u, d_c
+            dGh[:] = dGi
+            carry = d_rh * r + dh * u + dGh[:, sr] @ W_hh[sr] + dGh[:, su] @ W_hh[su]
+            dW_hh[sr] += d_r.T @ h_prev
+            dW_hh[su] += d_u.T @ h_prev
+            dW_hh[sc] += d_c.T @ fw["rh"][t]
+        dGi_all[t], dGh_all[t] = dGi, dGh
+        dx[t] = dGi @ W_ih
+        dW_ih += dGi.T @ x[t]
+        db_ih += dGi.sum(axis=0)
+        db_hh += dGh.sum(axis=0)
+    return dict(dx=dx, dh0=carry, dW_ih=dW_ih, dW_hh=dW_hh, db_ih=db_ih,
+                db_hh=db_hh, dGi=dGi_all, dGh=dGh_all)
+
+
+# ------------------------------------------------------ layer wrappers ----
+
+def layer_forward(mode, x, h0, c0, p, order, reverse=False, reset_after=True):
+    """One layer and direction; p has W_ih, W_hh, b_ih, b_hh."""
+    if mode == "lstm":
+        return lstm_forward(x, h0, c0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, order, reverse)
+    return gru_forward(x, h0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, reset_after, order, reverse)
+
+
+def layer_backward(mode, fw, dy, dhT=None, dcT=None):
+    if mode == "lstm":
+        return lstm_backward(fw, dy, dhT, dcT)
+    return gru_backward(fw, dy, dhT)
+
+
+def stack_forward(mode, x, params, order, bidir, reset_after=True, h0=None, c0=None):
+    """Stacked (optionally bidirectional) layers: layer l+1 reads the
+    concatenation [y_fwd, y_rev] of layer l along the feature axis (the
+    strided-output layout of the CUDA fragment's OUTPUT_STRIDE rows).
+    h0/c0 apply to every layer and direction (None = zero)."""
+    recs = []
+    inp = _f64(x)
+    for layer_params in params:
+        fws = [layer_forward(mode, inp, h0, c0, p, order, reverse=(d == 1), reset_after=reset_after)
+               for d, p in enumerate(layer_params)]
+        recs.append(fws)
+        inp = np.concatenate([fw["y"] for fw in fws], axis=2)
+        if not bidir:
+            assert len(fws) == 1
+    return recs, inp
+
+
+def stack_backward(mode, recs, dy):
+    """BPTT through the stack built by stack_forward; returns per layer and
+    direction the gradient dicts, and dx of the first layer."""
+    grads = [None] * len(recs)
+    d_out = _f64(dy)
+    for li in range(len(recs) - 1, -1, -1):
+        fws = recs[li]
+        H = fws[0]["W_hh"].shape[1]
+        gl = [layer_backward(mode, fw, d_out[:, :, d * H:(d + 1) * H]) for d, fw in enumerate(fws)]
+        grads[li] = gl
+        d_out = sum(g["dx"] for g in gl)
+    return grads, d_out
+
+
+def rel_err(got, ref):
+    """max_i |got_i - ref_i| / max_i |ref_i| (0 when both are all-zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    den = np.max(np.abs(ref)) if ref.size else 0.0
+    num = np.max(np.abs(got - ref)) if ref.size else 0.0
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
