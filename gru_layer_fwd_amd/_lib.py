@@ -1,0 +1,119 @@
+"""ctypes binding of librnn.so (include/rnn.h). Argument marshalling only.
+
+The functions keep the C names and arguments; tensor arguments are passed as
+integer device addresses (0 = NULL) and `stream` as an integer hipStream_t.
+Loading fails loudly when the library has not been built: there is no other
+implementation behind these names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librnn.so")
+
+RNN_LSTM, RNN_GRU = 0, 1
+RNN_F32, RNN_BF16 = 0, 1
+
+RNN_OK = 0
+RNN_ERR_INVALID_ARG = -1
+RNN_ERR_WORKSPACE_TOO_SMALL = -2
+RNN_ERR_UNSUPPORTED = -3
+RNN_ERR_DEVICE = -4
+RNN_ERR_TIMEOUT = -5
+
+# every function the header declares, with its C signature
+_c = ctypes
+_P = _c.c_void_p
+_SIGS = {
+    "rnn_workspace_bytes": (_c.c_size_t, [_P]),
+    "rnn_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "rnn_bwd_data": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
+    "rnn_bwd_weights": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
+    "rnn_last_device_status": (_c.c_int, [_P]),
+    "rnn_status_string": (_c.c_char_p, [_c.c_int]),
+}
+
+
+class RnnDesc(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int),
+        ("direction", ctypes.c_int),
+        ("reset_after", ctypes.c_int),
+        ("gate_order", ctypes.c_int * 4),
+        ("dtype", ctypes.c_int),
+        ("T", ctypes.c_int),
+        ("B", ctypes.c_int),
+        ("I", ctypes.c_int),
+        ("H", ctypes.c_int),
+        ("ldx", ctypes.c_longlong),
+        ("ldy", ctypes.c_longlong),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded librnn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gru_layer_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+class RnnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = lib().rnn_status_string(status).decode()
+        super().__init__(f"{where}: {msg} ({status})")
+        self.status = status
+
+
+def make_desc(mode: int, T: int, B: int, I: int, H: int, dtype: int, direction: int = 0,
+              reset_after: int = 1, gate_order=None, ldx: int = 0, ldy: int = 0) -> RnnDesc:
+    d = RnnDesc()
+    d.mode, d.direction, d.reset_after, d.dtype = mode, direction, reset_after, dtype
+    d.T, d.B, d.I, d.H, d.ldx, d.ldy = T, B, I, H, ldx, ldy
+    if gate_order is None:
+        gate_order = (0, 1, 2, 3) if mode == RNN_LSTM else (0, 1, 2)
+    order = list(gate_order) + [0] * (4 - len(gate_order))
+    for k in range(4):
+        d.gate_order[k] = order[k]
+    return d
+
+
+def rnn_workspace_bytes(desc: RnnDesc) -> int:
+    return int(lib().rnn_workspace_bytes(ctypes.byref(desc)))
+
+
+def rnn_fwd(desc, x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, workspace, ws_bytes, stream) -> int:
+    return lib().rnn_fwd(ctypes.byref(desc), x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT,
+                         workspace, ws_bytes, stream)
+
+
+def rnn_bwd_data(desc, W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, accumulate,
+                 workspace, ws_bytes, stream) -> int:
+    return lib().rnn_bwd_data(ctypes.byref(desc), W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0,
+                              accumulate, workspace, ws_bytes, stream)
+
+
+def rnn_bwd_weights(desc, x, h0, y, dW_ih, dW_hh, db_ih, db_hh, accumulate, workspace, ws_bytes,
+                    stream) -> int:
+    return lib().rnn_bwd_weights(ctypes.byref(desc), x, h0, y, dW_ih, dW_hh, db_ih, db_hh, accumulate,
+                                 workspace, ws_bytes, stream)
+
+
+def rnn_last_device_status(workspace) -> int:
+    return lib().rnn_last_device_status(workspace)
+
+
+def rnn_status_string(status: int) -> str:
+    return lib().rnn_status_string(status).decode()

@@ -1,0 +1,122 @@
+"""Torch-facing marshalling over the C ABI: tensors in, device addresses out.
+
+PyTorch provides device memory and the stream; every step of the layer runs
+in the HIP kernels of librnn.so. Nothing here computes.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib as L
+
+TORCH_DT = {L.RNN_F32: torch.float32, L.RNN_BF16: torch.bfloat16}
+DT_OF = {"f32": L.RNN_F32, "bf16": L.RNN_BF16}
+MODE_OF = {"lstm": L.RNN_LSTM, "gru": L.RNN_GRU}
+
+
+def _p(t) -> int:
+    return 0 if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(st: int, where: str):
+    if st != L.RNN_OK:
+        raise L.RnnError(st, where)
+
+
+class RnnLayer:
+    """One layer and direction: descriptor plus its workspace."""
+
+    def __init__(self, mode: str, T: int, B: int, I: int, H: int, dtype: str, direction: int = 0,
+                 reset_after: bool = True, gate_order=None, ldx: int = 0, ldy: int = 0, device="cuda"):
+        self.mode, self.dtype = mode, dtype
+        self.T, self.B, self.I, self.H = T, B, I, H
+        self.desc = L.make_desc(MODE_OF[mode], T, B, I, H, DT_OF[dtype], direction,
+                                int(bool(reset_after)), gate_order, ldx, ldy)
+        self.ws_bytes = L.rnn_workspace_bytes(self.desc)
+        if self.ws_bytes == 0:
+            raise L.RnnError(L.RNN_ERR_INVALID_ARG, "rnn_workspace_bytes")
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+
+    @property
+    def torch_dtype(self):
+        return TORCH_DT[DT_OF[self.dtype]]
+
+    def fwd(self, x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT=None, cT=None, stream=None):
+        _check(L.rnn_fwd(self.desc, _p(x), _p(h0), _p(c0), _p(W_ih), _p(W_hh), _p(b_ih), _p(b_hh),
+                         _p(y), _p(hT), _p(cT), _p(self.workspace), self.ws_bytes, _stream(stream)),
+               "rnn_fwd")
+
+    def bwd_data(self, W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0=None, dc0=None, accumulate=False,
+                 stream=None):
+        _check(L.rnn_bwd_data(self.desc, _p(W_ih), _p(W_hh), _p(h0), _p(c0), _p(y), _p(dy), _p(dhT),
+                              _p(dcT), _p(dx), _p(dh0), _p(dc0), int(bool(accumulate)),
+                              _p(self.workspace), self.ws_bytes, _stream(stream)),
+               "rnn_bwd_data")
+
+    def bwd_weights(self, x, h0, y, dW_ih, dW_hh, db_ih, db_hh, accumulate=False, stream=None):
+        _check(L.rnn_bwd_weights(self.desc, _p(x), _p(h0), _p(y), _p(dW_ih), _p(dW_hh), _p(db_ih),
+                                 _p(db_hh), int(bool(accumulate)), _p(self.workspace), self.ws_bytes,
+                                 _stream(stream)),
+               "rnn_bwd_weights")
+
+    def device_status(self) -> int:
+        return L.rnn_last_device_status(_p(self.workspace))
+
+
+class RnnStack:
+    """Stacked, optionally bidirectional layers over one [T, B, I] input.
+
+    Layer l writes [T, B, dirs*H]: the forward direction in columns [0, H),
+    the reverse one in [H, 2H) (row stride dirs*H), and layer l+1 reads that
+    tensor as its input. Backward: the input gradient of layer l+1 (both
+    directions accumulated into one buffer) is the output gradient of layer l.
+    Parameters: params[l][d] = (W_ih, W_hh, b_ih, b_hh) device tensors.
+    """
+
+    def __init__(self, mode, T, B, I, H, dtype, layers, bidir, reset_after=True, gate_order=None,
+                 device="cuda"):
+        self.dirs = 2 if bidir else 1
+        self.T, self.B, self.I, self.H = T, B, I, H
+        self.layers = []
+        for layer in range(layers):
+            Il = I if layer == 0 else H * self.dirs
+            self.layers.append([
+                RnnLayer(mode, T, B, Il, H, dtype, direction=d, reset_after=reset_after,
+                         gate_order=gate_order, ldx=Il, ldy=H * self.dirs, device=device)
+                for d in range(self.dirs)])
+        dt = self.layers[0][0].torch_dtype
+        self.ys = [torch.empty(T, B, H * self.dirs, dtype=dt, device=device) for _ in range(layers)]
+        # input gradients of layers 1.. (the output gradients of the layer below)
+        self.dxs = [None] + [torch.empty(T, B, H * self.dirs, dtype=dt, device=device)
+                             for _ in range(layers - 1)]
+
+    def fwd(self, x, params, h0=None, c0=None, stream=None):
+        inp = x
+        for li, per in enumerate(self.layers):
+            for d, lay in enumerate(per):
+                W_ih, W_hh, b_ih, b_hh = params[li][d]
+                lay.fwd(inp, h0, c0, W_ih, W_hh, b_ih, b_hh, self.ys[li][:, :, d * self.H:], stream=stream)
+            inp = self.ys[li]
+        return self.ys[-1]
+
+    def bwd(self, x, params, dy, dx=None, grads=None, h0=None, c0=None, stream=None):
+        """dy: gradient of the last layer's output. grads[l][d] = (dW_ih, dW_hh, db_ih, db_hh)
+        (or None to skip the weight gradients)."""
+        d_out = dy
+        for li in range(len(self.layers) - 1, -1, -1):
+            d_in = dx if li == 0 else self.dxs[li]
+            for d, lay in enumerate(self.layers[li]):
+                W_ih, W_hh, _, _ = params[li][d]
+                lay.bwd_data(W_ih, W_hh, h0, c0, self.ys[li][:, :, d * self.H:],
+                             d_out[:, :, d * self.H:], None, None, d_in, accumulate=(d > 0), stream=stream)
+                if grads is not None:
+                    inp = x if li == 0 else self.ys[li - 1]
+                    lay.bwd_weights(inp, h0, self.ys[li][:, :, d * self.H:], *grads[li][d], stream=stream)
+            d_out = d_in
+        return dx

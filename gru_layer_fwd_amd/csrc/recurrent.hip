@@ -1,0 +1,707 @@
+// Persistent recurrent kernels: one launch walks all T steps.
+//
+// Partition. The batch is cut into groups of BG = 16*MB rows and the hidden
+// units into slices of HS units; workgroup (group, slice) owns the hidden
+// units of its slice for every gate, so the cell update needs no exchange.
+// Its slice of W_hh (all gate rows of its units in the forward pass, all
+// gate-row columns of its units in the backward pass) is loaded once into
+// VGPRs as MFMA B operands and stays there for the whole sequence: the
+// weight-stationary scheme of the persistent backward kernel on the CUDA
+// fragment page (the recurrent tile lives in registers across steps), here
+// with the contraction split over the waves of the workgroup and the partial
+// products summed through LDS.
+//
+// Exchange. The only data that crosses workgroups is the recurrent vector of
+// a step (forward: h_t, backward: the gate gradients dG_t), which every
+// workgroup of the batch group reads in full at the next step. Producers
+// store it to HBM, release it at agent scope and publish a per-workgroup step
+// counter; consumers poll the counters of their group (one coalesced load per
+// wave), acquire, and then read the vector. The CUDA fragment's kernel waits
+// on the data itself (a -0.0 sentinel) with no bound; here every wait is
+// bounded by a wall-clock time-out that sets a status word, after which all
+// waits are skipped so that every wave still runs to the end of the grid.
+//
+// Equations (canonical gate order, fp32 arithmetic, storage rounding on
+// store): LSTM popnn Lstm.cpp "basicLstmCellForwardPass" and
+// "backwardStepImpl"; GRU popnn Gru.cpp "basicGruCellForwardPass",
+// "gruCellForwardPassCalcUnitsResetAfter", "backwardStepImpl" and
+// "backwardStepImplResetAfter".
+#include "rnn_internal.hpp"
+
+namespace rnn {
+
+namespace {
+
+constexpr int ST_TIMEOUT = -5;
+
+__device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout) {
+  const int lane = threadIdx.x & 63;
+  long long t0 = 0;
+  bool started = false;
+  while (true) {
+    bool ok = true;
+    for (int i = lane; i < n; i += 64)
+      ok = ok && (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
+    if (__all(ok)) break;
+    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+    const long long now = (long long)wall_clock64();
+    if (!started) {
+      t0 = now;
+      started = true;
+    } else if (now - t0 > timeout) {
+      if (lane == 0) __hip_atomic_store(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+// Every thread makes its own stores visible at agent scope, the workgroup
+// meets, then one thread publishes the step counter.
+__device__ __forceinline__ void release_flag(int* f, int v) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Workgroup -> (group, slice). Workgroups are dispatched round-robin over the
+// 8 XCDs; consecutive workgroups of one batch group are placed on the same
+// XCD where the counts allow, so that the vector they exchange stays in few
+// L2s. Correctness does not depend on the placement.
+__device__ __forceinline__ void wg_coords(int nGroups, int nSlices, int& grp, int& sl) {
+  const int n = nGroups * nSlices;
+  int L = blockIdx.x;
+  if ((n & 7) == 0) L = (blockIdx.x & 7) * (n >> 3) + (blockIdx.x >> 3);
+  grp = L / nSlices;
+  sl = L - grp * nSlices;
+}
+
+// acc[mb][nt] += A[b0+mb*16.., k] . Wr[nt][k] over this wave's k-steps, with
+// A(b, k) = src[b*ld + k + (k >= kshift ? kskip : 0)] (zero when b >= B or
+// src is NULL). The wave owns k-steps [w*KI, w*KI+KI) of the contraction.
+template <typename TS, int MB, int NT, int KI>
+__device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const TS* src,
+                                         long long ld, int b0, int B, int K, int kshift, int kskip) {
+  constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int ks = 0; ks < KI; ++ks) {
+    const int kb = (w * KI + ks) * KSTEP;
+    if (kb >= K) break;  // wave-uniform
+    const int k = kb + q * KQ;
+    const int kc = k + (k >= kshift ? kskip : 0);
+    uint4 av[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int b = b0 + mb * 16 + r16;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (src != nullptr && b < B && k < K) v = *(const uint4*)(src + (long long)b * ld + kc);
+      av[mb] = v;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[mb][nt], av[mb], Wr[nt][ks]);
+  }
+}
+
+template <int MB, int NT>
+__device__ __forceinline__ void zero_acc(f4 (&acc)[MB][NT]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = f4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Partial products of every wave to LDS: red[w][row][col], row < BG, col < NCOL.
+template <int MB, int NT>
+__device__ __forceinline__ void spill_acc(float* red, const f4 (&acc)[MB][NT]) {
+  constexpr int BG = MB * 16, NCOL = NT * 16;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[(w * BG + mb * 16 + q * 4 + e) * NCOL + nt * 16 + r16] = acc[mb][nt][e];
+}
+
+template <int NW, int BG, int NCOL>
+__device__ __forceinline__ float red_sum(const float* red, int row, int col) {
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) s += red[(w * BG + row) * NCOL + col];
+  return s;
+}
+
+// Load the B-operand tiles of W_hh rows (forward: output column col of the
+// tile is W_hh row rowof(col); contraction over the H columns of W_hh).
+template <typename TS, int NT, int KI, typename RowOf>
+__device__ __forceinline__ void load_w_rows(uint4 (&Wr)[NT][KI], const TS* W, int H, RowOf rowof) {
+  constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const long long row = rowof(nt * 16 + r16);
+#pragma unroll
+    for (int ks = 0; ks < KI; ++ks) {
+      const int k = (w * KI + ks) * KSTEP + q * KQ;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (k < H && row >= 0) v = *(const uint4*)(W + row * H + k);
+      Wr[nt][ks] = v;
+    }
+  }
+}
+
+// Load the B-operand tiles of W_hh columns (backward: output column col is
+// hidden unit J0+col, contraction index k runs over canonical gate rows
+// kb + [0, K): W_hh[perm[g]*H + k%H][J0+col] with g = k/H).
+template <typename TS, int NT, int KI>
+__device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, int H, const int* perm, int J0,
+                                            int gate0, int K) {
+  constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int r16 = lane & 15, q = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int col = J0 + nt * 16 + r16;
+#pragma unroll
+    for (int ks = 0; ks < KI; ++ks) {
+      const int k = (w * KI + ks) * KSTEP + q * KQ;
+      TS e[KQ];
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) e[i] = from_f<TS>(0.f);
+      if (k < K) {
+        const int g = gate0 + k / H;
+        const int kk = k % H;
+#pragma unroll
+        for (int i = 0; i < KQ; ++i) e[i] = W[((long long)perm[g] * H + kk + i) * H + col];
+      }
+      Wr[nt][ks] = *(const uint4*)e;
+    }
+  }
+}
+
+// ------------------------------------------------------ forward kernels --
+// LSTM (GL = 4 gate lanes) and reset-after GRU (GL = 3: r, u and the
+// recurrent candidate term n_h = h W_hc^T + b_hc, kept apart).
+template <int CELL, typename TS, int NW, int MB, int NT, int KI>
+__global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
+  constexpr int NTH = NW * 64, BG = MB * 16, NCOL = NT * 16;
+  constexpr int GL = (CELL == CELL_LSTM) ? 4 : 3;
+  constexpr int HS = NCOL / GL;
+  static_assert(HS * GL == NCOL, "columns must hold whole units");
+  constexpr int UNITS = BG * HS;
+  constexpr int UPT = (UNITS + NTH - 1) / NTH;
+  extern __shared__ float red[];
+
+  int grp, sl;
+  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
+  const int tid = threadIdx.x;
+  const int H = a.H, B = a.B, T = a.T;
+  const int J0 = sl * HS, b0 = grp * BG;
+  const long long GZH = (long long)a.GZ * H;
+
+  uint4 Wr[NT][KI];
+  load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, [&](int col) -> long long {
+    const int g = col / HS;
+    return (long long)a.perm[g] * H + J0 + (col - g * HS);
+  });
+
+  float cst[UPT], hst[UPT], bhc[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    cst[u] = 0.f;
+    hst[u] = 0.f;
+    bhc[u] = 0.f;
+    const int unit = tid + u * NTH;
+    const int bl = unit / HS, j = unit - (unit / HS) * HS, b = b0 + bl;
+    if (unit < UNITS && b < B) {
+      if (a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
+      if (CELL == CELL_LSTM && a.c0) cst[u] = to_f(((const TS*)a.c0)[(long long)b * H + J0 + j]);
+      if (CELL == CELL_GRU_RA) bhc[u] = to_f(((const TS*)a.b_hh)[(long long)a.perm[2] * H + J0 + j]);
+    }
+  }
+
+  for (int s = 0; s < T; ++s) {
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+    if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
+    f4 acc[MB][NT];
+    zero_acc(acc);
+    const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
+    const long long ld = (s == 0) ? H : a.ldy;
+    contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, B, H, 1 << 30, 0);
+    spill_acc(red, acc);
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      const int bl = unit / HS, j = unit - (unit / HS) * HS, b = b0 + bl;
+      if (unit >= UNITS || b >= B) continue;
+      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
+      TS* yr = (TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j;
+      float h;
+      if constexpr (CELL == CELL_LSTM) {
+        const float zi = red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(zr[0]);
+        const float zf = red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(zr[H]);
+        const float zg = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + to_f(zr[2 * H]);
+        const float zo = red_sum<NW, BG, NCOL>(red, bl, 3 * HS + j) + to_f(zr[3 * H]);
+        const float ig = sigmoidf_(zi), fg = sigmoidf_(zf), gg = tanhf_(zg), og = sigmoidf_(zo);
+        const float c = fg * cst[u] + ig * gg;
+        cst[u] = c;
+        h = og * tanhf_(c);
+        zr[0] = from_f<TS>(ig);
+        zr[H] = from_f<TS>(fg);
+        zr[2 * H] = from_f<TS>(gg);
+        zr[3 * H] = from_f<TS>(og);
+        ((TS*)a.cbuf)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(c);
+        if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(c);
+      } else {
+        const float r = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(zr[0]));
+        const float uu = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(zr[H]));
+        const float nh = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + bhc[u];
+        const float c = tanhf_(to_f(zr[2 * H]) + r * nh);
+        h = uu * hst[u] + (1.f - uu) * c;
+        hst[u] = h;
+        zr[0] = from_f<TS>(r);
+        zr[H] = from_f<TS>(uu);
+        zr[2 * H] = from_f<TS>(c);
+        zr[3 * H] = from_f<TS>(nh);
+      }
+      *yr = from_f<TS>(h);
+      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
+    }
+    release_flag(myflag, s + 1);
+  }
+}
+
+// Basic GRU: the candidate contracts r*h_{t-1} over all hidden units, so a
+// step has two exchanges (h_{t-1}, then r*h_{t-1}); phase counters advance by
+// two per step. Workgroup columns: phase A r,u (2*HS), phase B candidate (HS).
+template <typename TS, int NW, int MB, int NTB, int KI>
+__global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
+  constexpr int NTH = NW * 64, BG = MB * 16, HS = NTB * 16;
+  constexpr int NTA = 2 * NTB;
+  constexpr int UNITS = BG * HS;
+  constexpr int UPT = (UNITS + NTH - 1) / NTH;
+  extern __shared__ float red[];
+
+  int grp, sl;
+  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
+  const int tid = threadIdx.x;
+  const int H = a.H, B = a.B, T = a.T;
+  const int J0 = sl * HS, b0 = grp * BG;
+  const long long GZH = (long long)a.GZ * H;
+
+  uint4 WA[NTA][KI], WB[NTB][KI];
+  load_w_rows<TS, NTA, KI>(WA, (const TS*)a.W_hh, H, [&](int col) -> long long {
+    const int g = col / HS;
+    return (long long)a.perm[g] * H + J0 + (col - g * HS);
+  });
+  load_w_rows<TS, NTB, KI>(WB, (const TS*)a.W_hh, H,
+                           [&](int col) -> long long { return (long long)a.perm[2] * H + J0 + col; });
+
+  float hst[UPT], ust[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    hst[u] = 0.f;
+    ust[u] = 0.f;
+    const int unit = tid + u * NTH;
+    const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+    if (unit < UNITS && b < B && a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
+  }
+
+  for (int s = 0; s < T; ++s) {
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+    // phase A: r, u
+    if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks);
+    {
+      f4 acc[MB][NTA];
+      zero_acc(acc);
+      const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
+      const long long ld = (s == 0) ? H : a.ldy;
+      contract<TS, MB, NTA, KI>(acc, WA, src, ld, b0, B, H, 1 << 30, 0);
+      spill_acc(red, acc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+      if (unit >= UNITS || b >= B) continue;
+      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
+      const float r = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, j) + to_f(zr[0]));
+      const float uu = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, HS + j) + to_f(zr[H]));
+      ust[u] = uu;
+      zr[0] = from_f<TS>(r);
+      zr[H] = from_f<TS>(uu);
+      ((TS*)a.rh)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(r * hst[u]);
+    }
+    release_flag(myflag, 2 * s + 1);
+    // phase B: candidate and new state
+    wait_flags(gflags, a.nSlices, 2 * s + 1, a.status, a.timeout_ticks);
+    {
+      f4 acc[MB][NTB];
+      zero_acc(acc);
+      contract<TS, MB, NTB, KI>(acc, WB, (const TS*)a.rh + (long long)t * B * H, H, b0, B, H, 1 << 30, 0);
+      spill_acc(red, acc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+      if (unit >= UNITS || b >= B) continue;
+      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
+      const float c = tanhf_(red_sum<NW, BG, HS>(red, bl, j) + to_f(zr[2 * H]));
+      const float h = ust[u] * hst[u] + (1.f - ust[u]) * c;
+      hst[u] = h;
+      zr[2 * H] = from_f<TS>(c);
+      ((TS*)a.y)[((long long)t * B + b) * a.ldy + J0 + j] = from_f<TS>(h);
+      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
+    }
+    release_flag(myflag, 2 * s + 2);
+  }
+}
+
+// ----------------------------------------------------- backward kernels --
+// LSTM and reset-after GRU: the carried hidden gradient of step t is
+// dG'_{t+1} W_hh (dG' = [di,df,dg,do], or [d_r, d_u, d_c*r] for the GRU),
+// contracted over all gate rows; the workgroup holds the W_hh columns of its
+// HS units. Steps are processed in the reverse of the forward order.
+template <int CELL, typename TS, int NW, int MB, int NT, int KI>
+__global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
+  constexpr int NTH = NW * 64, BG = MB * 16, HS = NT * 16;
+  constexpr int GK = (CELL == CELL_LSTM) ? 4 : 3;
+  constexpr int UNITS = BG * HS;
+  constexpr int UPT = (UNITS + NTH - 1) / NTH;
+  extern __shared__ float red[];
+
+  int grp, sl;
+  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
+  const int tid = threadIdx.x;
+  const int H = a.H, B = a.B, T = a.T;
+  const int J0 = sl * HS, b0 = grp * BG;
+  const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
+  const int K = GK * H;
+  // GRU: lanes r, u, then the recurrent candidate lane d_c*r stored in lane 3
+  const int kshift = (CELL == CELL_LSTM) ? (1 << 30) : 2 * H;
+  const int kskip = (CELL == CELL_LSTM) ? 0 : H;
+
+  uint4 Wr[NT][KI];
+  load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K);
+
+  float dcar[UPT], hcar[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) {
+    dcar[u] = 0.f;
+    hcar[u] = 0.f;
+    const int unit = tid + u * NTH;
+    const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+    if (CELL == CELL_LSTM && unit < UNITS && b < B && a.dcT)
+      dcar[u] = to_f(((const TS*)a.dcT)[(long long)b * H + J0 + j]);
+  }
+
+  for (int n = 0; n <= T; ++n) {
+    const int s = T - 1 - n;  // processing index of this step (-1: the final dh0 contraction)
+    f4 acc[MB][1 * NT];
+    zero_acc(acc);
+    if (n > 0) {
+      wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks);
+      const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
+      contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, B, K, kshift,
+                               kskip);
+    }
+    spill_acc(red, acc);
+    __syncthreads();
+    if (n == T) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int unit = tid + u * NTH;
+        const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+        if (unit >= UNITS || b >= B) continue;
+        const float dh0 = red_sum<NW, BG, HS>(red, bl, j) + hcar[u];
+        if (a.dh0) ((TS*)a.dh0)[(long long)b * H + J0 + j] = from_f<TS>(dh0);
+        if (CELL == CELL_LSTM && a.dc0) ((TS*)a.dc0)[(long long)b * H + J0 + j] = from_f<TS>(dcar[u]);
+      }
+      break;
+    }
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+      if (unit >= UNITS || b >= B) continue;
+      const long long row = (long long)t * B + b;
+      float dh = red_sum<NW, BG, HS>(red, bl, j) + to_f(((const TS*)a.dy)[row * a.ldy + J0 + j]) + hcar[u];
+      if (n == 0 && a.dhT) dh += to_f(((const TS*)a.dhT)[(long long)b * H + J0 + j]);
+      const TS* zr = (const TS*)a.z + row * GZH + J0 + j;
+      TS* gr = (TS*)a.dg + row * GDH + J0 + j;
+      if constexpr (CELL == CELL_LSTM) {
+        const float ig = to_f(zr[0]), fg = to_f(zr[H]), gg = to_f(zr[2 * H]), og = to_f(zr[3 * H]);
+        const float c = to_f(((const TS*)a.cbuf)[row * H + J0 + j]);
+        float cp = 0.f;
+        if (s == 0) {
+          if (a.c0) cp = to_f(((const TS*)a.c0)[(long long)b * H + J0 + j]);
+        } else {
+          cp = to_f(((const TS*)a.cbuf)[((long long)tp * B + b) * H + J0 + j]);
+        }
+        const float tc = tanhf_(c);
+        const float d_o = dh * tc * og * (1.f - og);
+        const float dc = dh * og * (1.f - tc * tc) + dcar[u];
+        const float d_i = dc * gg * ig * (1.f - ig);
+        const float d_f = dc * cp * fg * (1.f - fg);
+        const float d_g = dc * ig * (1.f - gg * gg);
+        dcar[u] = dc * fg;
+        gr[0] = from_f<TS>(d_i);
+        gr[H] = from_f<TS>(d_f);
+        gr[2 * H] = from_f<TS>(d_g);
+        gr[3 * H] = from_f<TS>(d_o);
+      } else {
+        const float r = to_f(zr[0]), uu = to_f(zr[H]), c = to_f(zr[2 * H]), nh = to_f(zr[3 * H]);
+        float hp = 0.f;
+        if (s == 0) {
+          if (a.h0) hp = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
+        } else {
+          hp = to_f(((const TS*)a.y)[((long long)tp * B + b) * a.ldy + J0 + j]);
+        }
+        const float d_c = dh * (1.f - uu) * (1.f - c * c);
+        const float d_u = dh * (hp - c) * uu * (1.f - uu);
+        const float d_r = d_c * nh * r * (1.f - r);
+        hcar[u] = dh * uu;
+        gr[0] = from_f<TS>(d_r);
+        gr[H] = from_f<TS>(d_u);
+        gr[2 * H] = from_f<TS>(d_c);
+        gr[3 * H] = from_f<TS>(d_c * r);
+      }
+    }
+    release_flag(myflag, n + 1);
+  }
+}
+
+// Basic GRU backward: phase A contracts [d_r, d_u]_{t+1} with W_h{r,u} and
+// forms d_c, d_u; phase B contracts d_c_t with W_hc (gradient of r*h_{t-1})
+// and forms d_r. Counters advance by two per step.
+template <typename TS, int NW, int MB, int NT, int KIA, int KIB>
+__global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
+  constexpr int NTH = NW * 64, BG = MB * 16, HS = NT * 16;
+  constexpr int UNITS = BG * HS;
+  constexpr int UPT = (UNITS + NTH - 1) / NTH;
+  extern __shared__ float red[];
+
+  int grp, sl;
+  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
+  const int tid = threadIdx.x;
+  const int H = a.H, B = a.B, T = a.T;
+  const int J0 = sl * HS, b0 = grp * BG;
+  const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
+
+  uint4 WA[NT][KIA], WB[NT][KIB];
+  load_w_cols<TS, NT, KIA>(WA, (const TS*)a.W_hh, H, a.perm, J0, 0, 2 * H);
+  load_w_cols<TS, NT, KIB>(WB, (const TS*)a.W_hh, H, a.perm, J0, 2, H);
+
+  float hcar[UPT], dhs[UPT], rs[UPT], us[UPT], hps[UPT];
+#pragma unroll
+  for (int u = 0; u < UPT; ++u) hcar[u] = dhs[u] = rs[u] = us[u] = hps[u] = 0.f;
+
+  for (int n = 0; n <= T; ++n) {
+    const int s = T - 1 - n;
+    {
+      f4 acc[MB][NT];
+      zero_acc(acc);
+      if (n > 0) {
+        wait_flags(gflags, a.nSlices, 2 * n, a.status, a.timeout_ticks);
+        const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);
+        contract<TS, MB, NT, KIA>(acc, WA, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, B, 2 * H, 1 << 30,
+                                  0);
+      }
+      spill_acc(red, acc);
+    }
+    __syncthreads();
+    if (n == T) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const int unit = tid + u * NTH;
+        const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+        if (unit >= UNITS || b >= B) continue;
+        if (a.dh0) ((TS*)a.dh0)[(long long)b * H + J0 + j] = from_f<TS>(red_sum<NW, BG, HS>(red, bl, j) + hcar[u]);
+      }
+      break;
+    }
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+      if (unit >= UNITS || b >= B) continue;
+      const long long row = (long long)t * B + b;
+      float dh = red_sum<NW, BG, HS>(red, bl, j) + to_f(((const TS*)a.dy)[row * a.ldy + J0 + j]) + hcar[u];
+      if (n == 0 && a.dhT) dh += to_f(((const TS*)a.dhT)[(long long)b * H + J0 + j]);
+      const TS* zr = (const TS*)a.z + row * GZH + J0 + j;
+      const float r = to_f(zr[0]), uu = to_f(zr[H]), c = to_f(zr[2 * H]);
+      float hp = 0.f;
+      if (s == 0) {
+        if (a.h0) hp = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
+      } else {
+        hp = to_f(((const TS*)a.y)[((long long)tp * B + b) * a.ldy + J0 + j]);
+      }
+      const float d_c = dh * (1.f - uu) * (1.f - c * c);
+      const float d_u = dh * (hp - c) * uu * (1.f - uu);
+      TS* gr = (TS*)a.dg + row * GDH + J0 + j;
+      gr[H] = from_f<TS>(d_u);
+      gr[2 * H] = from_f<TS>(d_c);
+      dhs[u] = dh;
+      rs[u] = r;
+      us[u] = uu;
+      hps[u] = hp;
+    }
+    release_flag(myflag, 2 * n + 1);
+    wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks);
+    {
+      f4 acc[MB][NT];
+      zero_acc(acc);
+      const int t2 = a.dir ? T - 1 - s : s;
+      contract<TS, MB, NT, KIB>(acc, WB, (const TS*)a.dg + (long long)t2 * B * GDH + 2 * H, GDH, b0, B, H,
+                                1 << 30, 0);
+      spill_acc(red, acc);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
+      if (unit >= UNITS || b >= B) continue;
+      const long long row = (long long)t * B + b;
+      const float d_rh = red_sum<NW, BG, HS>(red, bl, j);
+      const float d_r = d_rh * hps[u] * rs[u] * (1.f - rs[u]);
+      ((TS*)a.dg)[row * GDH + J0 + j] = from_f<TS>(d_r);
+      hcar[u] = d_rh * rs[u] + dhs[u] * us[u];
+    }
+    release_flag(myflag, 2 * n + 2);
+  }
+}
+
+// ------------------------------------------------------------ plans ------
+struct Entry {
+  int cell, dtype, fwd, nw, mb, nt, ki, kib;
+  const void* func;
+};
+
+#define F_LSTM(TS, NW, MB, NT, KI) (const void*)rec_fwd<CELL_LSTM, TS, NW, MB, NT, KI>
+#define F_GRA(TS, NW, MB, NT, KI) (const void*)rec_fwd<CELL_GRU_RA, TS, NW, MB, NT, KI>
+#define B_LSTM(TS, NW, MB, NT, KI) (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI>
+#define B_GRA(TS, NW, MB, NT, KI) (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI>
+
+// dtype 0 = fp32, 1 = bf16
+const Entry kTable[] = {
+    // forward LSTM
+    {CELL_LSTM, 1, 1, 4, 1, 4, 8, 0, F_LSTM(bf16, 4, 1, 4, 8)},
+    {CELL_LSTM, 1, 1, 4, 1, 1, 8, 0, F_LSTM(bf16, 4, 1, 1, 8)},
+    {CELL_LSTM, 1, 1, 4, 8, 2, 16, 0, F_LSTM(bf16, 4, 8, 2, 16)},
+    {CELL_LSTM, 0, 1, 4, 1, 4, 8, 0, F_LSTM(float, 4, 1, 4, 8)},
+    {CELL_LSTM, 0, 1, 4, 1, 1, 8, 0, F_LSTM(float, 4, 1, 1, 8)},
+    // forward reset-after GRU
+    {CELL_GRU_RA, 1, 1, 4, 1, 3, 8, 0, F_GRA(bf16, 4, 1, 3, 8)},
+    {CELL_GRU_RA, 1, 1, 8, 4, 3, 8, 0, F_GRA(bf16, 8, 4, 3, 8)},
+    {CELL_GRU_RA, 0, 1, 4, 1, 3, 8, 0, F_GRA(float, 4, 1, 3, 8)},
+    // forward basic GRU (nt = candidate tiles)
+    {CELL_GRU_BASIC, 1, 1, 4, 1, 1, 8, 0, (const void*)rec_fwd_grub<bf16, 4, 1, 1, 8>},
+    {CELL_GRU_BASIC, 0, 1, 4, 1, 1, 8, 0, (const void*)rec_fwd_grub<float, 4, 1, 1, 8>},
+    // backward LSTM
+    {CELL_LSTM, 1, 0, 4, 1, 1, 32, 0, B_LSTM(bf16, 4, 1, 1, 32)},
+    {CELL_LSTM, 1, 0, 8, 4, 1, 32, 0, B_LSTM(bf16, 8, 4, 1, 32)},
+    {CELL_LSTM, 0, 0, 4, 1, 1, 32, 0, B_LSTM(float, 4, 1, 1, 32)},
+    // backward reset-after GRU
+    {CELL_GRU_RA, 1, 0, 4, 1, 1, 32, 0, B_GRA(bf16, 4, 1, 1, 32)},
+    {CELL_GRU_RA, 1, 0, 8, 4, 1, 32, 0, B_GRA(bf16, 8, 4, 1, 32)},
+    {CELL_GRU_RA, 0, 0, 4, 1, 1, 32, 0, B_GRA(float, 4, 1, 1, 32)},
+    // backward basic GRU (ki = phase A k-steps, kib = phase B)
+    {CELL_GRU_BASIC, 1, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<bf16, 4, 1, 1, 16, 8>},
+    {CELL_GRU_BASIC, 0, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<float, 4, 1, 1, 16, 8>},
+};
+
+int units_per_wg(const Entry& e) {
+  if (!e.fwd) return e.nt * 16;
+  if (e.cell == CELL_LSTM) return e.nt * 16 / 4;
+  if (e.cell == CELL_GRU_RA) return e.nt * 16 / 3;
+  return e.nt * 16;
+}
+
+size_t lds_of(const Entry& e) {
+  int ncol;
+  if (e.fwd) ncol = (e.cell == CELL_GRU_BASIC) ? 2 * e.nt * 16 : e.nt * 16;
+  else ncol = e.nt * 16;
+  return (size_t)e.nw * e.mb * 16 * ncol * sizeof(float);
+}
+
+bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p) {
+  const int kstep = dtype ? 32 : 16;
+  double best = 1e300;
+  bool found = false;
+  for (const Entry& e : kTable) {
+    if (e.cell != cell || e.dtype != dtype || e.fwd != fwd) continue;
+    const int hs = units_per_wg(e);
+    if (H % hs) continue;
+    // contraction length of the (first) recurrent product
+    int K = H;
+    if (!fwd) K = (cell == CELL_LSTM) ? 4 * H : (cell == CELL_GRU_RA ? 3 * H : 2 * H);
+    if ((long long)e.nw * e.ki * kstep < K) continue;
+    if (cell == CELL_GRU_BASIC && !fwd && (long long)e.nw * e.kib * kstep < H) continue;
+    const int bg = e.mb * 16;
+    const int groups = (B + bg - 1) / bg;
+    const long long nwg = (long long)groups * (H / hs);
+    RecPlan cand{e.nw, e.mb, e.nt, e.ki, hs, groups, H / hs, e.func, lds_of(e)};
+    if (nwg > cu_count) continue;  // at most one persistent workgroup per CU
+    // cost: MFMA issue per SIMD per step, waves sharing a SIMD serialise
+    const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
+    const double cost = (double)e.mb * e.nt * kused * (e.nw > 4 ? e.nw / 4.0 : 1.0) + 1e-3 * nwg;
+    if (cost < best) {
+      best = cost;
+      *p = cand;
+      found = true;
+    }
+  }
+  return found;
+}
+
+}  // namespace
+
+bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p) {
+  return choose(cell, dtype, 1, B, H, cu_count, p);
+}
+bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p) {
+  return choose(cell, dtype, 0, B, H, cu_count, p);
+}
+
+int max_coresident(const RecPlan& p) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, p.func, p.nw * 64, p.lds_bytes) != hipSuccess) return 0;
+  return n;
+}
+
+hipError_t launch_rec(const RecPlan& p, const RecArgs& a, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(p.func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
+  if (e != hipSuccess) return e;
+  RecArgs args = a;
+  void* kargs[] = {&args};
+  return hipLaunchCooperativeKernel(p.func, dim3(p.nGroups * p.nSlices), dim3(p.nw * 64), kargs,
+                                    (unsigned)p.lds_bytes, s);
+}
+
+}  // namespace rnn

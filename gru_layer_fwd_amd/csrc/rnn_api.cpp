@@ -1,0 +1,431 @@
+// C ABI of the layer engine: argument checks, workspace layout, launches.
+// Every check happens on the host before anything is queued on the stream.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "../../include/rnn.h"
+#include "rnn_internal.hpp"
+
+#define RNN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using rnn::bf16;
+
+constexpr size_t ALIGN = 256;
+constexpr int FLAG_SLOTS = 4096;   // per region; >= persistent workgroups
+constexpr int MAX_CHUNKS = 64;     // bias-gradient partial sums
+constexpr double TIMEOUT_S = 10.0;
+
+size_t up(size_t v) { return (v + ALIGN - 1) / ALIGN * ALIGN; }
+
+int gates(const rnn_desc_t* d) { return d->mode == RNN_LSTM ? 4 : 3; }
+int cell_of(const rnn_desc_t* d) {
+  if (d->mode == RNN_LSTM) return rnn::CELL_LSTM;
+  return d->reset_after ? rnn::CELL_GRU_RA : rnn::CELL_GRU_BASIC;
+}
+long long ldx_of(const rnn_desc_t* d) { return d->ldx ? d->ldx : d->I; }
+long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : d->H; }
+size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
+
+struct Layout {
+  size_t status, flags, partial, z, c, rh, dg, total;
+  int GZ, GD;
+};
+
+bool desc_ok(const rnn_desc_t* d) {
+  if (!d) return false;
+  if (d->mode != RNN_LSTM && d->mode != RNN_GRU) return false;
+  if (d->dtype != RNN_F32 && d->dtype != RNN_BF16) return false;
+  if (d->direction != 0 && d->direction != 1) return false;
+  if (d->mode == RNN_GRU && d->reset_after != 0 && d->reset_after != 1) return false;
+  if (d->T < 1 || d->B < 1 || d->I < 1 || d->H < 1) return false;
+  const int G = gates(d);
+  int seen = 0;
+  for (int k = 0; k < G; ++k) {
+    const int g = d->gate_order[k];
+    if (g < 0 || g >= G || (seen & (1 << g))) return false;
+    seen |= 1 << g;
+  }
+  if (d->ldx != 0 && d->ldx < d->I) return false;
+  if (d->ldy != 0 && d->ldy < d->H) return false;
+  return true;
+}
+
+// granularity the kernels need (16-byte chunks along I and H)
+bool shape_supported(const rnn_desc_t* d) {
+  if (d->I % 8 || d->H % 16) return false;
+  if (ldx_of(d) % 8 || ldy_of(d) % 8) return false;
+  if ((long long)d->T * d->B > (1LL << 31) / 2) return false;
+  return true;
+}
+
+Layout layout(const rnn_desc_t* d) {
+  Layout L{};
+  const size_t s = esz(d);
+  const size_t TB = (size_t)d->T * d->B, H = d->H;
+  const int cell = cell_of(d);
+  L.GZ = (cell == rnn::CELL_GRU_RA) ? 4 : gates(d);
+  L.GD = (cell == rnn::CELL_GRU_RA) ? 4 : gates(d);
+  size_t off = 0;
+  L.status = off;
+  off += ALIGN;
+  L.flags = off;
+  off += up(2 * FLAG_SLOTS * sizeof(int));
+  L.partial = off;
+  off += up((size_t)MAX_CHUNKS * 4 * H * sizeof(float));
+  L.z = off;
+  off += up(TB * L.GZ * H * s);
+  L.c = off;
+  if (cell == rnn::CELL_LSTM) off += up(TB * H * s);
+  L.rh = off;
+  if (cell == rnn::CELL_GRU_BASIC) off += up(TB * H * s);
+  L.dg = off;
+  off += up(TB * L.GD * H * s);
+  L.total = off;
+  return L;
+}
+
+bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+struct DevInfo {
+  int cu = 0;
+  long long ticks = 0;
+};
+
+int dev_info(DevInfo* out) {
+  static DevInfo cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RNN_ERR_DEVICE;
+  if (cache[dev].cu == 0) {
+    int cu = 0, rate_khz = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return RNN_ERR_DEVICE;
+    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate_khz <= 0)
+      rate_khz = 100000;
+    cache[dev].ticks = (long long)(TIMEOUT_S * rate_khz * 1000.0);
+    cache[dev].cu = cu;
+  }
+  *out = cache[dev];
+  return RNN_OK;
+}
+
+bool log_on() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("RNN_LOG");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+void inv_perm(const rnn_desc_t* d, int perm[4]) {
+  for (int k = 0; k < 4; ++k) perm[k] = 0;
+  for (int k = 0; k < gates(d); ++k) perm[d->gate_order[k]] = k;
+}
+
+int check_common(const rnn_desc_t* d, const void* ws, size_t ws_bytes) {
+  if (!desc_ok(d)) return RNN_ERR_INVALID_ARG;
+  if (!shape_supported(d)) return RNN_ERR_UNSUPPORTED;
+  if (!ws || !aligned(ws)) return RNN_ERR_INVALID_ARG;
+  if (ws_bytes < layout(d).total) return RNN_ERR_WORKSPACE_TOO_SMALL;
+  return RNN_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_ERR_DEVICE; }
+
+rnn::RowMap rows(const void* p, long long ld) {
+  rnn::RowMap m{};
+  m.ptr = p;
+  m.ld = ld;
+  m.kind = 0;
+  return m;
+}
+rnn::RowMap perm_rows(const void* p, long long ld, int H, const int perm[4]) {
+  rnn::RowMap m = rows(p, ld);
+  m.kind = 1;
+  m.H = H;
+  for (int i = 0; i < 4; ++i) m.perm[i] = perm[i];
+  return m;
+}
+
+template <typename TS>
+hipError_t gemm(const rnn::GemmArgs& g, bool ak, bool bk, hipStream_t s) {
+  return rnn::launch_gemm<TS>(g, ak, bk, s);
+}
+hipError_t gemm_dt(int dtype, const rnn::GemmArgs& g, bool ak, bool bk, hipStream_t s) {
+  return dtype == RNN_BF16 ? gemm<bf16>(g, ak, bk, s) : gemm<float>(g, ak, bk, s);
+}
+hipError_t colsum_dt(int dtype, const void* src, long long lds, long long M, int col0, int ncols, void* out,
+                     int out_row0, int H, const int perm[4], int acc, float* partial, hipStream_t s) {
+  if (dtype == RNN_BF16)
+    return rnn::launch_colsum<bf16>(src, lds, M, col0, ncols, out, out_row0, H, perm, acc, partial, MAX_CHUNKS, s);
+  return rnn::launch_colsum<float>(src, lds, M, col0, ncols, out, out_row0, H, perm, acc, partial, MAX_CHUNKS, s);
+}
+
+int launch_persistent(const rnn::RecPlan& p, const rnn::RecArgs& a, const DevInfo& di, hipStream_t s,
+                      const char* what) {
+  const long long nwg = (long long)p.nGroups * p.nSlices;
+  if (nwg > FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;
+  const int occ = rnn::max_coresident(p);
+  if (occ < 1 || nwg > (long long)occ * di.cu) {
+    if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, nwg, occ, di.cu);
+    return RNN_ERR_UNSUPPORTED;
+  }
+  if (log_on())
+    fprintf(stderr, "[rnn] %s: %d groups x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu\n", what,
+            p.nGroups, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki, p.lds_bytes);
+  hipError_t e = rnn::launch_rec(p, a, s);
+  if (e != hipSuccess) {
+    if (log_on()) fprintf(stderr, "[rnn] %s: launch failed: %s\n", what, hipGetErrorString(e));
+    return (e == hipErrorCooperativeLaunchTooLarge) ? RNN_ERR_UNSUPPORTED : RNN_ERR_DEVICE;
+  }
+  return RNN_OK;
+}
+
+}  // namespace
+
+RNN_API size_t rnn_workspace_bytes(const rnn_desc_t* d) {
+  if (!desc_ok(d)) return 0;
+  return layout(d).total;
+}
+
+RNN_API const char* rnn_status_string(int st) {
+  switch (st) {
+    case RNN_OK: return "ok";
+    case RNN_ERR_INVALID_ARG: return "invalid argument";
+    case RNN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RNN_ERR_UNSUPPORTED: return "unsupported shape or launch configuration";
+    case RNN_ERR_DEVICE: return "HIP runtime error";
+    case RNN_ERR_TIMEOUT: return "step handshake timed out on the device";
+    default: return "unknown status";
+  }
+}
+
+RNN_API int rnn_last_device_status(const void* workspace) {
+  if (!workspace) return RNN_ERR_INVALID_ARG;
+  int v = 0;
+  if (hipMemcpy(&v, workspace, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return RNN_ERR_DEVICE;
+  return v;
+}
+
+RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const void* c0, const void* W_ih,
+                    const void* W_hh, const void* b_ih, const void* b_hh, void* y, void* hT, void* cT,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_common(d, workspace, ws_bytes);
+  if (st) return st;
+  if (!x || !W_ih || !W_hh || !b_ih || !b_hh || !y) return RNN_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  const Layout L = layout(d);
+  const int cell = cell_of(d);
+  rnn::RecPlan plan;
+  if (!rnn::plan_fwd(cell, d->dtype, d->B, d->H, di.cu, &plan)) return RNN_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int perm[4];
+  inv_perm(d, perm);
+  const int G = gates(d);
+
+  // status word and the forward step counters start at zero
+  if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
+  if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.flags), 0, FLAG_SLOTS, s)))) return st;
+
+  // input projection for every step: Z[t,b][g*H+j] = x . W_ih[g,j] + biases
+  rnn::GemmArgs g{};
+  g.a = rows(x, ldx_of(d));
+  g.b = perm_rows(W_ih, d->I, d->H, perm);
+  g.M = (long long)d->T * d->B;
+  g.N = (long long)G * d->H;
+  g.K = d->I;
+  g.c = ws + L.z;
+  g.ldc = (long long)L.GZ * d->H;
+  g.c_kind = 0;
+  g.H = d->H;
+  for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+  g.bias1 = b_ih;
+  g.bias2 = b_hh;
+  g.bias_skip_gate = (cell == rnn::CELL_GRU_RA) ? RNN_GATE_C : -1;
+  if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+
+  rnn::RecArgs a{};
+  a.T = d->T;
+  a.B = d->B;
+  a.H = d->H;
+  a.dir = d->direction;
+  a.nGroups = plan.nGroups;
+  a.nSlices = plan.nSlices;
+  a.Hs = plan.Hs;
+  for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
+  a.W_hh = W_hh;
+  a.b_hh = b_hh;
+  a.h0 = h0;
+  a.c0 = c0;
+  a.y = y;
+  a.ldy = ldy_of(d);
+  a.z = ws + L.z;
+  a.GZ = L.GZ;
+  a.cbuf = ws + L.c;
+  a.rh = ws + L.rh;
+  a.hT = hT;
+  a.cT = (d->mode == RNN_LSTM) ? cT : nullptr;
+  a.GD = L.GD;
+  a.flags = (int*)(ws + L.flags);
+  a.status = (int*)(ws + L.status);
+  a.timeout_ticks = di.ticks;
+  return launch_persistent(plan, a, di, s, "fwd");
+}
+
+RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh, const void* h0, const void* c0,
+                         const void* y, const void* dy, const void* dhT, const void* dcT, void* dx, void* dh0,
+                         void* dc0, int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_common(d, workspace, ws_bytes);
+  if (st) return st;
+  if (!W_ih || !W_hh || !y || !dy) return RNN_ERR_INVALID_ARG;
+  const void* ptrs[] = {W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  const Layout L = layout(d);
+  const int cell = cell_of(d);
+  rnn::RecPlan plan;
+  if (!rnn::plan_bwd(cell, d->dtype, d->B, d->H, di.cu, &plan)) return RNN_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int perm[4];
+  inv_perm(d, perm);
+  const int G = gates(d);
+  int* flags = (int*)(ws + L.flags) + FLAG_SLOTS;
+
+  if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
+  if ((st = hip_status(rnn::launch_fill_i32(flags, 0, FLAG_SLOTS, s)))) return st;
+
+  rnn::RecArgs a{};
+  a.T = d->T;
+  a.B = d->B;
+  a.H = d->H;
+  a.dir = d->direction;
+  a.nGroups = plan.nGroups;
+  a.nSlices = plan.nSlices;
+  a.Hs = plan.Hs;
+  for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
+  a.W_hh = W_hh;
+  a.h0 = h0;
+  a.c0 = (d->mode == RNN_LSTM) ? c0 : nullptr;
+  a.y = (void*)y;
+  a.ldy = ldy_of(d);
+  a.z = ws + L.z;
+  a.GZ = L.GZ;
+  a.cbuf = ws + L.c;
+  a.rh = ws + L.rh;
+  a.dy = dy;
+  a.dhT = dhT;
+  a.dcT = (d->mode == RNN_LSTM) ? dcT : nullptr;
+  a.dg = ws + L.dg;
+  a.GD = L.GD;
+  a.dh0 = dh0;
+  a.dc0 = (d->mode == RNN_LSTM) ? dc0 : nullptr;
+  a.flags = flags;
+  a.status = (int*)(ws + L.status);
+  a.timeout_ticks = di.ticks;
+  if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;
+
+  if (dx) {
+    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]
+    rnn::GemmArgs g{};
+    g.a = rows(ws + L.dg, (long long)L.GD * d->H);
+    g.b = perm_rows(W_ih, d->I, d->H, perm);
+    g.M = (long long)d->T * d->B;
+    g.N = d->I;
+    g.K = (long long)G * d->H;
+    g.c = dx;
+    g.ldc = ldx_of(d);
+    g.H = d->H;
+    g.accumulate = accumulate ? 1 : 0;
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, true, s)))) return st;
+  }
+  return RNN_OK;
+}
+
+RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, const void* y, void* dW_ih,
+                            void* dW_hh, void* db_ih, void* db_hh, int accumulate, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  int st = check_common(d, workspace, ws_bytes);
+  if (st) return st;
+  if (!x || !y) return RNN_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  const Layout L = layout(d);
+  const int cell = cell_of(d);
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  int perm[4];
+  inv_perm(d, perm);
+  const int G = gates(d);
+  const int H = d->H;
+  const long long TB = (long long)d->T * d->B;
+  const long long GDH = (long long)L.GD * H;
+  const char* dg = ws + L.dg;
+  const size_t s_el = esz(d);
+  float* partial = (float*)(ws + L.partial);
+  const int acc = accumulate ? 1 : 0;
+
+  auto dW = [&](void* out, long long row0, long long nrows, int dg_col, rnn::RowMap act, long long ncols) {
+    rnn::GemmArgs g{};
+    g.a = rows(dg + dg_col * s_el, GDH);   // k-outer: memory row (t,b), elements along gate rows
+    g.b = act;                             // k-outer: memory row (t,b), elements along columns
+    g.M = nrows;
+    g.N = ncols;
+    g.K = TB;
+    g.c = out;
+    g.ldc = ncols;
+    g.c_kind = 1;
+    g.c_row0 = row0;
+    g.H = H;
+    for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+    g.accumulate = acc;
+    return gemm_dt(d->dtype, g, true, true, s);
+  };
+
+  rnn::RowMap hprev{};
+  hprev.ptr = y;
+  hprev.ld = ldy_of(d);
+  hprev.kind = 2;
+  hprev.h0 = h0;
+  hprev.ld0 = H;
+  hprev.B = d->B;
+  hprev.T = d->T;
+  hprev.dir = d->direction;
+
+  if (dW_ih && (st = hip_status(dW(dW_ih, 0, (long long)G * H, 0, rows(x, ldx_of(d)), d->I)))) return st;
+  if (dW_hh) {
+    if (cell == rnn::CELL_LSTM) {
+      if ((st = hip_status(dW(dW_hh, 0, 4LL * H, 0, hprev, H)))) return st;
+    } else {
+      if ((st = hip_status(dW(dW_hh, 0, 2LL * H, 0, hprev, H)))) return st;
+      if (cell == rnn::CELL_GRU_RA) {
+        if ((st = hip_status(dW(dW_hh, 2LL * H, H, 3 * H, hprev, H)))) return st;
+      } else {
+        if ((st = hip_status(dW(dW_hh, 2LL * H, H, 2 * H, rows(ws + L.rh, H), H)))) return st;
+      }
+    }
+  }
+  if (db_ih && (st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, G * H, db_ih, 0, H, perm, acc, partial, s))))
+    return st;
+  if (db_hh) {
+    if (cell == rnn::CELL_GRU_RA) {
+      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, 2 * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
+      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 3 * H, H, db_hh, 2 * H, H, perm, acc, partial, s))))
+        return st;
+    } else {
+      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, G * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
+    }
+  }
+  return RNN_OK;
+}

@@ -1,0 +1,167 @@
+// Internal declarations of the gfx950 LSTM/GRU layer engine.
+//
+// Storage types: float (fp32) and __bf16 (bf16, round-to-nearest-even on
+// store); all arithmetic accumulates in fp32. Gates are held internally in a
+// canonical order (LSTM i,f,g,o; GRU r,u,c); the caller's storage order only
+// appears where weights, biases and their gradients are addressed, through a
+// per-gate block permutation `perm` (perm[g] = caller row block of gate g).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rnn {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f4;
+
+enum Cell { CELL_LSTM = 0, CELL_GRU_RA = 1, CELL_GRU_BASIC = 2 };
+
+// ------------------------------------------------------------ conversions --
+__device__ __forceinline__ float to_f(float v) { return v; }
+__device__ __forceinline__ float to_f(bf16 v) { return (float)v; }
+template <typename TS> __device__ __forceinline__ TS from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float v) { return (bf16)v; }
+
+// elements of TS per 16-byte chunk
+template <typename TS> struct Chunk;
+template <> struct Chunk<float> { static constexpr int KQ = 4; };
+template <> struct Chunk<bf16> { static constexpr int KQ = 8; };
+
+// One "k-step" of a 16x16 output tile: every lane supplies one 16-byte chunk
+// of A (row lane%16) and of B (column lane%16), lane group q = lane/16
+// holding elements [q*KQ, q*KQ+KQ) of a 4*KQ-wide slice of the contraction.
+// bf16: one v_mfma_f32_16x16x32_bf16. fp32: four v_mfma_f32_16x16x4_f32,
+// the s-th taking element s of every lane's chunk (a fixed relabelling of
+// the contraction index, identical for A and B, so the sum is unchanged).
+__device__ __forceinline__ void mma_step(f4& acc, const uint4& a, const uint4& b, bf16*) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_step(f4& acc, const uint4& a, const uint4& b, float*) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+}
+template <typename TS>
+__device__ __forceinline__ void mma(f4& acc, const uint4& a, const uint4& b) {
+  mma_step(acc, a, b, (TS*)nullptr);
+}
+
+__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float tanhf_(float z) {
+  // tanh(z) = 2*sigmoid(2z) - 1, saturating cleanly for large |z|
+  return 2.0f / (1.0f + __expf(-2.0f * z)) - 1.0f;
+}
+
+// -------------------------------------------------------------- row maps --
+// Address of memory row `o` of an operand. kind 0: ptr + o*ld. kind 1: the
+// rows are grouped in blocks of H by gate and block g is read from caller
+// block perm[g]. kind 2: row o = (t, b) of the previous hidden state
+// h_{t-1}: y row of the step processed before t, or h0 row b (NULL -> zeros)
+// at the first processed step.
+struct RowMap {
+  const void* ptr;
+  long long ld;
+  int kind;
+  int H;
+  int perm[4];
+  const void* h0;
+  long long ld0;
+  int B, T, dir;
+};
+
+template <typename TS>
+__device__ __forceinline__ const TS* map_row(const RowMap& m, long long o) {
+  const TS* p = (const TS*)m.ptr;
+  if (m.kind == 1) {
+    long long g = o / m.H;
+    return p + ((long long)m.perm[g] * m.H + (o - g * m.H)) * m.ld;
+  }
+  if (m.kind == 2) {
+    int t = (int)(o / m.B);
+    int b = (int)(o - (long long)t * m.B);
+    int first = m.dir ? (m.T - 1) : 0;
+    if (t == first) return m.h0 ? (const TS*)m.h0 + (long long)b * m.ld0 : nullptr;
+    int tp = m.dir ? t + 1 : t - 1;
+    return p + ((long long)tp * m.B + b) * m.ld;
+  }
+  return p + o * m.ld;
+}
+
+// ---------------------------------------------------------------- GEMM --
+// C[m][n] (+)= sum_k A(m,k) B(n,k) (+ bias[n]); A and B addressed through
+// row maps, either k-contiguous (A_KOUTER=false: memory row = m) or k-outer
+// (memory row = k, elements along m contiguous).
+struct GemmArgs {
+  RowMap a, b;
+  long long M, N, K;
+  void* c;
+  long long ldc;
+  int c_kind;       // 0: row m at c + m*ldc; 1: canonical row c_row0+m, gate-block permuted (perm)
+  long long c_row0;
+  int H;
+  int perm[4];
+  int accumulate;
+  const void* bias1;  // optional: bias1[perm-mapped n] (+ bias2 unless gate == skip)
+  const void* bias2;
+  int bias_skip_gate;
+};
+
+template <typename TS>
+hipError_t launch_gemm(const GemmArgs& g, bool a_kouter, bool b_kouter, hipStream_t s);
+
+// column sums: out[mapped n] (+)= sum_m src[m*lds + col0 + n], n < ncols.
+template <typename TS>
+hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, int ncols,
+                         void* out, int out_row0, int H, const int perm[4], int accumulate,
+                         float* partial, int max_chunks, hipStream_t s);
+
+hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s);
+
+// ------------------------------------------------- persistent recurrences --
+struct RecArgs {
+  int T, B, H, dir;
+  int nGroups, nSlices, Hs;
+  int perm[4];
+  const void* W_hh;
+  const void* b_hh;
+  const void* h0;
+  const void* c0;
+  void* y;          // fwd: output / bwd: forward output (h_{t-1} source)
+  long long ldy;
+  void* z;          // saved gates (in: projected inputs for fwd)
+  int GZ;           // lanes of z rows
+  void* cbuf;       // LSTM cell states
+  void* rh;         // basic GRU r*h_{t-1}
+  void* hT;
+  void* cT;
+  // backward only
+  const void* dy;
+  const void* dhT;
+  const void* dcT;
+  void* dg;         // gate gradients
+  int GD;           // lanes of dg rows
+  void* dh0;
+  void* dc0;
+  int* flags;
+  int* status;
+  long long timeout_ticks;
+};
+
+struct RecPlan {
+  int nw, mb, nt, ki;   // waves per WG, 16-row batch tiles, 16-col output tiles, k-steps per wave
+  int Hs, nGroups, nSlices;
+  const void* func;
+  size_t lds_bytes;
+};
+
+// Choose a plan and report it; returns false when no instantiated plan fits.
+bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p);
+bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p);
+hipError_t launch_rec(const RecPlan& p, const RecArgs& a, hipStream_t s);
+int max_coresident(const RecPlan& p);
+
+}  // namespace rnn

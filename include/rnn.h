@@ -1,0 +1,126 @@
+/*
+ * rnn.h - C ABI of the MI355X (gfx950) LSTM/GRU layer engine (librnn.so).
+ *
+ * One recurrent layer, one direction, per call. Three calls share a
+ * caller-owned workspace, in the order forward -> backward-data ->
+ * backward-weights, like the cuDNN training triple wrapped on the SystemDS
+ * LibMatrixCuDNN page ("singleLayerUnidirectionalRNNForward", "lstmBackward":
+ * forward training fills a reserve space that the backward-data and
+ * backward-weights calls then read).
+ *
+ * The equations are those of the popnn pages:
+ *   LSTM (Lstm.cpp, "basicLstmCellForwardPass", "backwardStepImpl"):
+ *     z = x W_ih^T + b_ih + h W_hh^T + b_hh, i,f,o = sigmoid, g = tanh,
+ *     c_t = f*c_{t-1} + i*g, h_t = o*tanh(c_t).
+ *   GRU (Gru.cpp, "basicGruCellForwardPass", "backwardStepImpl"):
+ *     r,u = sigmoid(x W_i^T + b_i + h W_h^T + b_h),
+ *     basic:       c = tanh(x W_ic^T + b_ic + (r*h) W_hc^T + b_hc),
+ *     reset_after: c = tanh(x W_ic^T + b_ic + r*(h W_hc^T + b_hc))
+ *                  ("gruCellForwardPassCalcUnitsResetAfter"),
+ *     h_t = u*h_{t-1} + (1-u)*c.
+ *
+ * Layouts (all row-major, element type given by desc->dtype):
+ *   x, dx   [T][B][I], row (t,b) at x + (t*B+b)*ldx    (ldx >= I)
+ *   y, dy   [T][B][H], row (t,b) at y + (t*B+b)*ldy    (ldy >= H)
+ *   h0,hT,c0,cT,dh0,dc0,dhT,dcT  [B][H] dense
+ *   W_ih [G*H][I], W_hh [G*H][H], b_ih/b_hh [G*H]; row block k (H rows)
+ *   holds gate gate_order[k]. G = 4 (LSTM), 3 (GRU).
+ *   dW_ih, dW_hh, db_ih, db_hh: same shapes and order as the weights.
+ * Strides let a bidirectional layer write its two halves of one [T][B][2H]
+ * output (pass y + H and ldy = 2H for the reverse half), as the strided
+ * OUTPUT_STRIDE rows of the persistent kernel on the CUDA fragment page.
+ *
+ * Pointers: every tensor pointer is a device pointer, 16-byte aligned.
+ * NULL h0/c0/dhT/dcT mean zeros; NULL hT/cT/dh0/dc0 are not written;
+ * NULL dx skips the input-gradient product. c0/cT/dc0/dcT are ignored for GRU.
+ *
+ * Errors: every call returns RNN_OK (0) or a negative rnn_status. Argument
+ * errors are detected on the host before any device work is queued. Calls are
+ * asynchronous on `stream` (a hipStream_t; NULL = default stream); a device
+ * time-out of the cross-workgroup step handshake is reported through
+ * rnn_last_device_status() after the stream has been synchronised.
+ *
+ * Ownership: the caller owns every buffer. The library allocates no device
+ * memory. The workspace written by rnn_fwd must be passed unchanged to
+ * rnn_bwd_data and then rnn_bwd_weights for the same descriptor and inputs.
+ * Calls that share a workspace must not overlap in time.
+ */
+#ifndef RNN_H_
+#define RNN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum rnn_mode { RNN_LSTM = 0, RNN_GRU = 1 };
+enum rnn_dtype { RNN_F32 = 0, RNN_BF16 = 1 };
+
+/* gate ids used in gate_order */
+enum { RNN_GATE_I = 0, RNN_GATE_F = 1, RNN_GATE_G = 2, RNN_GATE_O = 3 }; /* LSTM */
+enum { RNN_GATE_R = 0, RNN_GATE_U = 1, RNN_GATE_C = 2 };                 /* GRU  */
+
+typedef enum rnn_status {
+  RNN_OK = 0,
+  RNN_ERR_INVALID_ARG = -1,         /* null required pointer, bad size, mode, dtype, order */
+  RNN_ERR_WORKSPACE_TOO_SMALL = -2, /* ws_bytes < rnn_workspace_bytes(desc) */
+  RNN_ERR_UNSUPPORTED = -3,         /* shape outside what the kernels handle (alignment,
+                                       H or I granularity, persistent grid not co-resident) */
+  RNN_ERR_DEVICE = -4,              /* a HIP runtime call failed */
+  RNN_ERR_TIMEOUT = -5              /* (device status) step handshake timed out */
+} rnn_status;
+
+typedef struct rnn_desc {
+  int mode;          /* RNN_LSTM or RNN_GRU */
+  int direction;     /* 0: t = 0..T-1; 1: t = T-1..0 (outputs stay at their own t) */
+  int reset_after;   /* GRU only: 0 basic, 1 reset applied after the recurrent product */
+  int gate_order[4]; /* gate_order[k] = gate id stored in row block k; a permutation of
+                        0..G-1 (LSTM i,f,g,o = 0..3; GRU r,u,c = 0..2). Common orders:
+                        LSTM {0,1,2,3} (i,f,g,o) and {1,0,2,3} (f,i,g,o); GRU {0,1,2} */
+  int dtype;         /* RNN_F32 or RNN_BF16 storage; arithmetic accumulates in fp32 */
+  int T, B, I, H;    /* T,B >= 1; I % 8 == 0; H % 16 == 0 */
+  long long ldx;     /* row stride of x/dx in elements, 0 = I; multiple of 8 */
+  long long ldy;     /* row stride of y/dy in elements, 0 = H; multiple of 8 */
+} rnn_desc_t;
+
+/* Bytes of workspace the three calls need for this descriptor (0 if invalid). */
+size_t rnn_workspace_bytes(const rnn_desc_t* desc);
+
+/* Forward over the sequence: y (every step), hT/cT (final state), and the
+ * per-step activations the backward calls read, kept in the workspace.
+ * Queues: the input projection GEMM, then one persistent recurrent kernel. */
+int rnn_fwd(const rnn_desc_t* desc, const void* x, const void* h0, const void* c0,
+            const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
+            void* y, void* hT, void* cT, void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward through time for the data gradients: dx (overwritten, or added to
+ * when accumulate != 0), dh0, dc0, from dy at every step and dhT/dcT.
+ * y, h0 and c0 are the values given to / produced by rnn_fwd. The per-step
+ * gate gradients are kept in the workspace for rnn_bwd_weights.
+ * Queues: one persistent reverse-time kernel, then the dx GEMM. */
+int rnn_bwd_data(const rnn_desc_t* desc, const void* W_ih, const void* W_hh,
+                 const void* h0, const void* c0, const void* y, const void* dy,
+                 const void* dhT, const void* dcT, void* dx, void* dh0, void* dc0,
+                 int accumulate, void* workspace, size_t ws_bytes, void* stream);
+
+/* Weight gradients summed over every (t, b): dW_ih = sum dG^T x,
+ * dW_hh = sum dG_h^T h_{t-1} (h_{-1} = h0), db_ih, db_hh (popnn
+ * "basicLstmParamUpdate", "basicGruParamUpdate"). accumulate != 0 adds to the
+ * existing contents, otherwise they are overwritten. Any of the four outputs
+ * may be NULL to skip it. Queues: the dW GEMMs and the bias reductions. */
+int rnn_bwd_weights(const rnn_desc_t* desc, const void* x, const void* h0, const void* y,
+                    void* dW_ih, void* dW_hh, void* db_ih, void* db_hh, int accumulate,
+                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Device status word of the workspace (RNN_OK or RNN_ERR_TIMEOUT) after the
+ * caller has synchronised the stream of the last call. Reads 4 bytes. */
+int rnn_last_device_status(const void* workspace);
+
+/* Static description of a status code. */
+const char* rnn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RNN_H_ */

@@ -1,0 +1,95 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/rnn.h declares, sizes workspaces, and rejects bad
+arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gru_layer_fwd_amd as g
+from gru_layer_fwd_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "rnn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rnn_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_abi():
+    assert _declared() == sorted(["rnn_workspace_bytes", "rnn_fwd", "rnn_bwd_data", "rnn_bwd_weights",
+                                  "rnn_last_device_status", "rnn_status_string"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in L._SIGS, name
+
+
+def _desc(**kw):
+    base = dict(mode=L.RNN_LSTM, T=8, B=2, I=16, H=32, dtype=L.RNN_F32)
+    base.update(kw)
+    return g.make_desc(base.pop("mode"), base.pop("T"), base.pop("B"), base.pop("I"), base.pop("H"),
+                       base.pop("dtype"), **base)
+
+
+def test_workspace_size_formula():
+    d = _desc(T=7, B=3, I=16, H=32)
+    n = g.rnn_workspace_bytes(d)
+    # saved gates (4 lanes), cell states and gate gradients dominate: T*B*H*(4+1+4) elements
+    assert n >= 7 * 3 * 32 * 9 * 4
+    d2 = _desc(T=7, B=3, I=16, H=32, dtype=L.RNN_BF16)
+    assert g.rnn_workspace_bytes(d2) < n
+    dg = _desc(mode=L.RNN_GRU, T=7, B=3, I=16, H=32, reset_after=0, gate_order=(0, 1, 2))
+    assert g.rnn_workspace_bytes(dg) > 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(mode=5), dict(dtype=3), dict(direction=2), dict(T=0), dict(B=0), dict(I=0), dict(H=0),
+    dict(gate_order=(0, 0, 2, 3)), dict(gate_order=(0, 1, 2, 4)),
+    dict(mode=L.RNN_GRU, gate_order=(0, 1, 3)), dict(mode=L.RNN_GRU, reset_after=2, gate_order=(0, 1, 2)),
+    dict(ldx=8), dict(ldy=16),
+])
+def test_invalid_descriptors(bad):
+    d = _desc(**bad)
+    assert g.rnn_workspace_bytes(d) == 0
+    assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, 1 << 30, 0) == L.RNN_ERR_INVALID_ARG
+
+
+def test_null_descriptor():
+    lib = L.lib()
+    assert lib.rnn_workspace_bytes(None) == 0
+    assert lib.rnn_fwd(None, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, 1 << 30, None) == L.RNN_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("shape", [dict(H=40), dict(I=12), dict(I=16, ldx=20)])
+def test_unsupported_granularity(shape):
+    d = _desc(**shape)
+    assert g.rnn_workspace_bytes(d) > 0
+    assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, 1 << 30, 0) == L.RNN_ERR_UNSUPPORTED
+
+
+def test_workspace_too_small_and_missing_pointers():
+    d = _desc()
+    n = g.rnn_workspace_bytes(d)
+    assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
+    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
+    assert g.rnn_bwd_weights(d, 16, 0, 16, 0, 0, 0, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
+    # required pointers
+    assert g.rnn_fwd(d, 0, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 0, 0, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_weights(d, 0, 0, 16, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 0, n, 0) == L.RNN_ERR_INVALID_ARG
+    # misaligned tensor pointer
+    assert g.rnn_fwd(d, 18, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, 7):
+        assert isinstance(g.rnn_status_string(st), str) and g.rnn_status_string(st)

@@ -1,0 +1,184 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small and medium cases compare every output element; the full-size
+workloads compare sampled batch rows, computed by the oracle on those rows
+alone (batch rows never interact), with the upstream gradient set to zero on
+all other rows so that the weight and bias gradients are the sums over the
+sampled rows only and can be compared in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gru_layer_fwd_amd import synth
+from rnn_harness import Params, compare, gpu_layer, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+
+
+def _case(name, **changes):
+    wl = synth.small(W[name], **changes)
+    inp = synth.make_inputs(wl)
+    p = inp["params"][0][0]
+    return wl, inp, Params(p.W_ih, p.W_hh, p.b_ih, p.b_hh)
+
+
+def _run(wl, inp, P, direction=0, order=None, dhT=None, dcT=None, **kw):
+    mode, dt = wl.mode, wl.dtype
+    ra = wl.reset_after
+    got = gpu_layer(mode, dt, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order, **kw)
+    ref = oracle_layer(mode, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order)
+    return got, ref
+
+
+def _permute_params(P, order, H):
+    """Store named gates (given in the identity order) in storage order `order`."""
+    def perm(a):
+        return np.concatenate([a[g * H:(g + 1) * H] for g in order], axis=0)
+    return Params(perm(P.W_ih), perm(P.W_hh), perm(P.b_ih), perm(P.b_hh))
+
+
+# ------------------------------------------------------------- small ----
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("order", [(0, 1, 2, 3), (1, 0, 2, 3)])
+def test_lstm_f32_small(direction, order):
+    wl, inp, P = _case("lstm_f32_t8_b2_i16_h32")
+    P = _permute_params(P, order, wl.H)
+    rng = np.random.default_rng(7)
+    dhT, dcT = rng.standard_normal((wl.B, wl.H)), rng.standard_normal((wl.B, wl.H))
+    got, ref = _run(wl, inp, P, direction, order, dhT, dcT)
+    print(compare(got, ref, "f32", extra=f"dir={direction} order={order}"))
+
+
+@pytest.mark.parametrize("ra", [False, True])
+@pytest.mark.parametrize("direction", [0, 1])
+def test_gru_f32_small_ragged(ra, direction):
+    # B=3 (one partial 16-row group), I=24, H=32: ragged GEMM tiles
+    wl, inp, P = _case("grura_f32_t64_b16_i256_h256", T=6, B=3, I=24, H=32, h0_std=1.0, reset_after=ra)
+    order = (2, 0, 1)
+    P = _permute_params(P, order, wl.H)
+    rng = np.random.default_rng(8)
+    dhT = rng.standard_normal((wl.B, wl.H))
+    got, ref = _run(wl, inp, P, direction, order, dhT)
+    print(compare(got, ref, "f32", extra=f"ra={ra} dir={direction}"))
+
+
+def test_lstm_f32_ragged_strided():
+    # B=19 (two batch groups, ragged), M=T*B=95 rows, padded row strides
+    wl, inp, P = _case("lstm_f32_t8_b2_i16_h32", T=5, B=19, I=40, H=48)
+    got, ref = _run(wl, inp, P, 1, None, xpad=8, ypad=16)
+    print(compare(got, ref, "f32"))
+    assert np.all(np.isnan(got["ypad"])), "y written outside its columns"
+    assert np.all(got["dxpad"] == 0), "dx written outside its columns"
+
+
+def test_edge_t1_b1_null_states():
+    wl, inp, P = _case("lstm_f32_t8_b2_i16_h32", T=1, B=1, h0_std=0.0, c0_std=0.0)
+    assert inp["h0"] is None and inp["c0"] is None
+    got, ref = _run(wl, inp, P)
+    print(compare(got, ref, "f32"))
+
+
+def test_accumulate_and_skip_dx():
+    wl, inp, P = _case("lstm_f32_t8_b2_i16_h32")
+    once = gpu_layer("lstm", "f32", P, inp["x"], inp["h0"], inp["c0"], inp["g"])
+    twice = gpu_layer("lstm", "f32", P, inp["x"], inp["h0"], inp["c0"], inp["g"], acc=True, repeat=2)[1]
+    for k in ("dW_ih", "dW_hh", "db_ih", "db_hh", "dx"):
+        np.testing.assert_allclose(twice[k], 2 * once[k], rtol=1e-5, atol=1e-6)
+    nodx = gpu_layer("lstm", "f32", P, inp["x"], inp["h0"], inp["c0"], inp["g"], want_dx=False)
+    for k in ("dW_ih", "dh0", "y"):
+        np.testing.assert_array_equal(nodx[k], once[k])
+
+
+@pytest.mark.parametrize("name", ["gru_f32_t64_b16_i256_h256", "grura_f32_t64_b16_i256_h256"])
+def test_gru_f32_full(name):
+    wl, inp, P = _case(name)
+    got, ref = _run(wl, inp, P)
+    print(compare(got, ref, "f32", extra=name))
+
+
+def test_deterministic_repeats():
+    wl, inp, P = _case("grura_f32_t64_b16_i256_h256", T=16)
+    a, b = gpu_layer("gru", "f32", P, inp["x"], inp["h0"], None, inp["g"], repeat=2)
+    for k in a:
+        np.testing.assert_array_equal(np.nan_to_num(a[k]), np.nan_to_num(b[k]), err_msg=k)
+
+
+# ------------------------------------------------------------ bf16 -------
+
+@pytest.mark.parametrize("name,changes", [
+    ("lstm_bf16_t256_b64_i1024_h1024", dict(T=16, B=32, I=256, H=256)),
+    ("grura_bf16_t128_b128_i2048_h2048", dict(T=16, B=20, I=128, H=128)),
+    ("grura_bf16_t128_b128_i2048_h2048", dict(T=12, B=16, I=64, H=64, reset_after=False)),
+])
+def test_bf16_medium(name, changes):
+    wl, inp, P = _case(name, **changes)
+    got, ref = _run(wl, inp, P)
+    print(compare(got, ref, "bf16", extra=name))
+
+
+# ------------------------------------------------------- full sizes -------
+
+def _sampled(name, rows, direction=0):
+    wl = W[name]
+    inp = synth.make_inputs(wl)
+    p = inp["params"][0][0]
+    P = Params(p.W_ih, p.W_hh, p.b_ih, p.b_hh)
+    g = inp["g"].copy()
+    mask = np.zeros(wl.B, dtype=bool)
+    mask[rows] = True
+    g[:, ~mask] = 0.0
+    got = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], g, None, None, direction,
+                    wl.reset_after)
+    sub = lambda a: None if a is None else a[rows]  # noqa: E731
+    ref = oracle_layer(wl.mode, P, inp["x"][:, rows], sub(inp["h0"]), sub(inp["c0"]), g[:, rows], None, None,
+                       direction, wl.reset_after)
+    return wl, got, ref
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_headline_lstm_bf16_full_size_sampled_rows(direction):
+    rows = [0, 17, 63]
+    wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction)
+    print(compare(got, ref, "bf16", rows=rows))
+
+
+@pytest.mark.parametrize("name", ["lstm_bf16_t128_b128_i2048_h2048", "grura_bf16_t128_b128_i2048_h2048"])
+def test_large_bf16_full_size_sampled_rows(name):
+    rows = [5, 127]
+    wl, got, ref = _sampled(name, rows)
+    print(compare(got, ref, "bf16", rows=rows))
+
+
+def test_bidir_two_layer_stack_full_size_sampled_rows():
+    import oracle as O
+    from gru_layer_fwd_amd.api import RnnStack
+    from rnn_harness import dev, host
+    wl = W["bilstm2_f32_t512_b32_i512_h512"]
+    inp = synth.make_inputs(wl)
+    rows = [3, 30]
+    g = inp["g"].copy()
+    mask = np.zeros(wl.B, dtype=bool)
+    mask[rows] = True
+    g[:, ~mask] = 0.0
+    st = RnnStack("lstm", wl.T, wl.B, wl.I, wl.H, "f32", wl.layers, wl.bidir)
+    params = [[tuple(dev(a, "f32") for a in (p.W_ih, p.W_hh, p.b_ih, p.b_hh)) for p in per] for per in inp["params"]]
+    grads = [[tuple(torch.zeros_like(t) for t in pd) for pd in per] for per in params]
+    x = dev(inp["x"], "f32")
+    dx = torch.empty_like(x)
+    y = st.fwd(x, params)
+    st.bwd(x, params, dev(g, "f32"), dx, grads)
+    torch.cuda.synchronize()
+    recs, y_ref = O.stack_forward("lstm", inp["x"][:, rows], inp["params"], (0, 1, 2, 3), True)
+    gr_ref, dx_ref = O.stack_backward("lstm", recs, g[:, rows])
+    errs = {"y": O.rel_err(host(y)[:, rows], y_ref), "dx": O.rel_err(host(dx)[:, rows], dx_ref)}
+    for li in range(2):
+        for d in range(2):
+            for k, t in zip(("dW_ih", "dW_hh", "db_ih", "db_hh"), grads[li][d]):
+                errs[f"L{li}d{d}.{k}"] = O.rel_err(host(t), gr_ref[li][d][k])
+    print(errs)
+    assert errs["y"] <= 1e-4, errs
+    assert all(v <= 1e-3 for k, v in errs.items() if k != "y"), errs
