@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""One-GPU benchmark of the LSTM/GRU layer engine.
+
+A step is one pass of the whole layer on one batch of seeded synthetic input
+already resident in HBM: rnn_fwd (input projection + persistent forward),
+rnn_bwd_data (persistent BPTT + dx) and rnn_bwd_weights (dW, db). The default
+workload is the single-layer bf16 LSTM at T=256, B=64, I=H=1024.
+
+Prints one JSON line: the throughput in timestep*batch/s, the algorithmic
+TFLOP/s, a roofline entry for the kernel that takes the most time per step
+(timed live with HIP events on the library's stream through the
+rnn_profile_* hook), and the CPU oracle timed on a bounded sample of the same
+workload on the host cores.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+
+
+def _layer_work(wl, li):
+    """(flops, bytes) per label for one layer and direction (one launch
+    group), from the algorithmic counts: every GEMM-shaped product
+    2*M*N*K; bytes = the tensors each step must read and write once."""
+    from gru_layer_fwd_amd.synth import n_gates
+    G = n_gates(wl.mode)
+    dirs = 2 if wl.bidir else 1
+    I = wl.I if li == 0 else wl.H * dirs
+    T, B, H = wl.T, wl.B, wl.H
+    s = 2 if wl.dtype == "bf16" else 4
+    TB = T * B
+    GZ = 4 if (wl.mode == "gru" and wl.reset_after) else G
+    cst = H if wl.mode == "lstm" else 0
+    return {
+        "proj_gemm": (2.0 * TB * G * H * I, s * (TB * I + G * H * I + TB * G * H)),
+        # persistent forward: read P, write y, gates (+c); W_hh stays resident
+        "rec_fwd": (2.0 * TB * G * H * H, s * TB * (G * H + H + GZ * H + cst)),
+        # persistent BPTT: read dy, gates (+c twice, y), write dG
+        "rec_bwd": (2.0 * TB * G * H * H, s * TB * (H + GZ * H + 2 * cst + H + G * H)),
+        "dx_gemm": (2.0 * TB * G * H * I, s * (TB * G * H + G * H * I + TB * I)),
+        "dw_gemm": (2.0 * TB * G * H * (I + H), s * (2 * TB * G * H + TB * (I + H) + G * H * (I + H))),
+        "db_colsum": (2.0 * TB * G * H, s * 2 * TB * G * H),
+    }
+
+
+def _work(wl):
+    tot = {}
+    dirs = 2 if wl.bidir else 1
+    for li in range(wl.layers):
+        for _ in range(dirs):
+            for k, (f, b) in _layer_work(wl, li).items():
+                f0, b0 = tot.get(k, (0.0, 0.0))
+                tot[k] = (f0 + f, b0 + b)
+    return tot
+
+
+def cpu_baseline(wl, inp, rows: int):
+    """The oracle as it stands, on the first `rows` batch rows of the same
+    workload (all T steps, every layer/direction), timed on the host."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    sub = lambda a: None if a is None else a[:rows]  # noqa: E731
+    x = inp["x"][:, :rows]
+    g = inp["g"][:, :rows]
+    order = wl.gate_order()
+    t0 = time.perf_counter()
+    if wl.layers == 1 and not wl.bidir:
+        p = inp["params"][0][0]
+        fw = O.layer_forward(wl.mode, x, sub(inp["h0"]), sub(inp["c0"]), p, order, False, wl.reset_after)
+        O.layer_backward(wl.mode, fw, g)
+    else:
+        recs, _ = O.stack_forward(wl.mode, x, inp["params"], order, wl.bidir, wl.reset_after)
+        O.stack_backward(wl.mode, recs, g)
+    dt = time.perf_counter() - t0
+    units = wl.T * rows
+    return {"value": units / dt, "unit": "timestep*batch/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, fwd+bwd_data+bwd_weights over all T={wl.T} steps on {rows} of "
+                      f"{wl.B} batch rows ({dt:.2f} s on {threads} threads)",
+            "seconds": dt, "np": np.__version__}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--cpu-rows", type=int, default=0, help="batch rows the CPU oracle runs (0 = all)")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer shards over "
+              "batch rows with one dW all-reduce, which is not built here)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gru_layer_fwd_amd import _lib as L
+    from gru_layer_fwd_amd import synth
+    from gru_layer_fwd_amd.api import RnnLayer, RnnStack
+
+    name = args.workload or synth.HEADLINE
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl)
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16}[wl.dtype]
+    dev = lambda a: None if a is None else torch.from_numpy(a).to("cuda", dt)  # noqa: E731
+    x = dev(inp["x"])
+    g = dev(inp["g"])
+    params = [[tuple(dev(a) for a in (p.W_ih, p.W_hh, p.b_ih, p.b_hh)) for p in per] for per in inp["params"]]
+    grads = [[tuple(torch.empty_like(t) for t in pd) for pd in per] for per in params]
+    order = wl.gate_order()
+
+    if wl.layers == 1 and not wl.bidir:
+        lay = RnnLayer(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, reset_after=wl.reset_after, gate_order=order)
+        h0, c0 = dev(inp["h0"]), dev(inp["c0"])
+        y = torch.empty(wl.T, wl.B, wl.H, dtype=dt, device="cuda")
+        hT = torch.empty(wl.B, wl.H, dtype=dt, device="cuda")
+        cT = torch.empty_like(hT) if wl.mode == "lstm" else None
+        dx = torch.empty_like(x)
+        dh0 = torch.empty_like(hT)
+        dc0 = torch.empty_like(hT) if wl.mode == "lstm" else None
+        W_ih, W_hh, b_ih, b_hh = params[0][0]
+
+        def step():
+            lay.fwd(x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT)
+            lay.bwd_data(W_ih, W_hh, h0, c0, y, g, None, None, dx, dh0, dc0)
+            lay.bwd_weights(x, h0, y, *grads[0][0])
+
+        status = lambda: lay.device_status()  # noqa: E731
+    else:
+        st = RnnStack(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, wl.layers, wl.bidir, wl.reset_after, order)
+        dx = torch.empty_like(x)
+
+        def step():
+            st.fwd(x, params)
+            st.bwd(x, params, g, dx, grads)
+
+        status = lambda: max((lay.device_status() for per in st.layers for lay in per), key=abs)  # noqa: E731
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if status() != 0:
+        raise SystemExit(f"device status {status()} after warm-up")
+    L.rnn_profile_read(reset=True)
+    L.rnn_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    L.rnn_profile_enable(False)
+    prof = L.rnn_profile_read(reset=True)
+    if status() != 0:
+        raise SystemExit(f"device status {status()} in the timed region")
+
+    ms = (t1 - t0) * 1e3 / args.steps
+    units = wl.T * wl.B
+    value = units / (ms / 1e3)
+    tflops = wl.flops_gemm() / (ms / 1e3) / 1e12
+    work = _work(wl)
+    kern = {k: {"ms_per_step": v[1] / args.steps, "launches_per_step": v[0] / args.steps} for k, v in prof.items()}
+    # dominant kernel = most time per step; its roofline from the algorithmic work
+    dom = max((k for k in kern if k in work), key=lambda k: kern[k]["ms_per_step"])
+    f_step, b_step = work[dom]
+    t_step = kern[dom]["ms_per_step"] / 1e3
+    t_mfma = f_step / (PEAK_TFLOPS[wl.dtype] * 1e12)
+    t_hbm = b_step / (PEAK_HBM_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": f_step / t_step / 1e12, "peak": PEAK_TFLOPS[wl.dtype],
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": b_step / t_step / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["launch_ms"] = kern[dom]["ms_per_step"] / max(kern[dom]["launches_per_step"], 1)
+    for k in kern:
+        if k in work:
+            f, b = work[k]
+            tk = kern[k]["ms_per_step"] / 1e3
+            kern[k]["tflops"] = f / tk / 1e12 if tk > 0 else None
+            kern[k]["mfma_frac"] = (f / tk / 1e12) / PEAK_TFLOPS[wl.dtype] if tk > 0 else None
+    rec = {}
+    dirs = (2 if wl.bidir else 1) * wl.layers
+    for k in ("rec_fwd", "rec_bwd"):
+        if k in kern:
+            rec[k] = kern[k]["ms_per_step"] * 1e3 / (wl.T * dirs)
+
+    out = {
+        "metric": "LSTM/GRU fwd+bwd timestep*batch/s and TFLOP/s at H=1024 B=64 T=256",
+        "value": value,
+        "unit": "timestep*batch/s",
+        "tflops": tflops,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "cell": wl.mode + ("" if wl.mode == "lstm" else
+                                                       ("_reset_after" if wl.reset_after else "_basic")),
+                   "T": wl.T, "B": wl.B, "I": wl.I, "H": wl.H, "layers": wl.layers,
+                   "bidirectional": wl.bidir, "storage": wl.dtype, "accumulate": "f32"},
+        "roofline": roof,
+        "recurrent_us_per_step": rec,
+        "kernels": kern,
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_rows or wl.B, wl.B))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,8 @@ _SIGS = {
     "rnn_bwd_weights": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
     "rnn_last_device_status": (_c.c_int, [_P]),
     "rnn_status_string": (_c.c_char_p, [_c.c_int]),
+    "rnn_profile_enable": (_c.c_int, [_c.c_int]),
+    "rnn_profile_read": (_c.c_int, [_P, _c.c_int, _c.c_int]),
 }
 
 
@@ -50,6 +52,10 @@ class RnnDesc(ctypes.Structure):
         ("ldx", ctypes.c_longlong),
         ("ldy", ctypes.c_longlong),
     ]
+
+
+class RnnKernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_longlong), ("total_ms", ctypes.c_double)]
 
 
 _lib = None
@@ -117,3 +123,19 @@ def rnn_last_device_status(workspace) -> int:
 
 def rnn_status_string(status: int) -> str:
     return lib().rnn_status_string(status).decode()
+
+
+def rnn_profile_enable(on: bool) -> int:
+    return lib().rnn_profile_enable(int(bool(on)))
+
+
+def rnn_profile_read(reset: bool = True) -> dict:
+    """{label: (launches, total_ms)} of the kernels queued while enabled."""
+    n = lib().rnn_profile_read(None, 0, 0)
+    if n < 0:
+        raise RnnError(n, "rnn_profile_read")
+    buf = (RnnKernelTime * max(n, 1))()
+    n = lib().rnn_profile_read(ctypes.cast(buf, ctypes.c_void_p), n, int(bool(reset)))
+    if n < 0:
+        raise RnnError(n, "rnn_profile_read")
+    return {buf[i].name.decode(): (int(buf[i].launches), float(buf[i].total_ms)) for i in range(n)}

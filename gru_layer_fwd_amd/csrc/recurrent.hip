@@ -34,36 +34,57 @@ namespace {
 
 constexpr int ST_TIMEOUT = -5;
 
+// Coherence of the exchanged vectors is kept per access, not per cache: the
+// producer writes them with device-scope stores (write-through past the
+// per-XCD L2s), waits until its stores are acknowledged, and only then
+// publishes its step counter; consumers poll counters with device-scope loads
+// and read the vector with device-scope loads (never served by a stale L2
+// line). No whole-cache write-back or invalidate is issued per step. Data
+// that only the owning workgroup or a later kernel reads (saved gates, cell
+// states) uses ordinary stores.
 __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout) {
   const int lane = threadIdx.x & 63;
   long long t0 = 0;
-  bool started = false;
-  while (true) {
+  for (int it = 0;; ++it) {
     bool ok = true;
     for (int i = lane; i < n; i += 64)
       ok = ok && (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
     if (__all(ok)) break;
-    if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
-    const long long now = (long long)wall_clock64();
-    if (!started) {
-      t0 = now;
-      started = true;
-    } else if (now - t0 > timeout) {
-      if (lane == 0) __hip_atomic_store(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
+    if ((it & 63) == 0) {
+      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+      const long long now = (long long)wall_clock64();
+      if (it == 0) {
+        t0 = now;
+      } else if (now - t0 > timeout) {
+        if (lane == 0) __hip_atomic_store(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // the vector reads below must not be moved above the poll
+  asm volatile("" ::: "memory");
 }
 
-// Every thread makes its own stores visible at agent scope, the workgroup
-// meets, then one thread publishes the step counter.
-__device__ __forceinline__ void release_flag(int* f, int v) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+// Every wave waits for its device-scope stores to be acknowledged, the
+// workgroup meets, then one thread publishes the step counter.
+__device__ __forceinline__ void publish(int* f, int v) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(f, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// device-scope store of one exchanged element
+__device__ __forceinline__ void xstore(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xstore(bf16* p, float v) {
+  __hip_atomic_store((unsigned short*)p, __builtin_bit_cast(unsigned short, (bf16)v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+constexpr int BUF_RSRC_W3 = 0x00020000;  // buffer resource word 3 for the gfx9 family
+constexpr int CPOL_SC1 = 16;             // device scope
 
 // Workgroup -> (group, slice). Workgroups are dispatched round-robin over the
 // 8 XCDs; consecutive workgroups of one batch group are placed on the same
@@ -84,26 +105,45 @@ template <typename TS, int MB, int NT, int KI>
 __device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const TS* src,
                                          long long ld, int b0, int B, int K, int kshift, int kskip) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
+  constexpr int KB = (MB >= 8) ? 2 : (MB >= 4 ? 4 : (KI < 8 ? KI : 8));  // k-steps per load batch
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
+  if (src == nullptr) return;
+  // rows [0, B) of the source; loads past the end of the resource return 0,
+  // so that every load is issued unconditionally and a batch is in flight
+  // at once
+  const int nbytes = (int)((long long)B * ld * sizeof(TS));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nbytes, BUF_RSRC_W3);
+  int rowoff[MB];
 #pragma unroll
-  for (int ks = 0; ks < KI; ++ks) {
-    const int kb = (w * KI + ks) * KSTEP;
-    if (kb >= K) break;  // wave-uniform
-    const int k = kb + q * KQ;
-    const int kc = k + (k >= kshift ? kskip : 0);
-    uint4 av[MB];
+  for (int mb = 0; mb < MB; ++mb) {
+    const int b = b0 + mb * 16 + r16;
+    rowoff[mb] = (b < B) ? (int)((long long)b * ld * sizeof(TS)) : nbytes;
+  }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int b = b0 + mb * 16 + r16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (src != nullptr && b < B && k < K) v = *(const uint4*)(src + (long long)b * ld + kc);
-      av[mb] = v;
+  for (int k0 = 0; k0 < KI; k0 += KB) {
+    uint4 av[KB][MB];
+#pragma unroll
+    for (int kk = 0; kk < KB; ++kk) {
+      const int k = (w * KI + k0 + kk) * KSTEP + q * KQ;
+      const int kc = k + (k >= kshift ? kskip : 0);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int off = (k < K && k0 + kk < KI) ? rowoff[mb] + kc * (int)sizeof(TS) : nbytes;
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL_SC1);
+        av[kk][mb] = make_uint4(r[0], r[1], r[2], r[3]);
+      }
     }
+    // keep the whole batch of loads ahead of its products
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+    for (int kk = 0; kk < KB; ++kk) {
+      if (k0 + kk >= KI) break;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[mb][nt], av[mb], Wr[nt][ks]);
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[mb][nt], av[kk][mb], Wr[nt][k0 + kk]);
+    }
   }
 }
 
@@ -275,10 +315,10 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         zr[2 * H] = from_f<TS>(c);
         zr[3 * H] = from_f<TS>(nh);
       }
-      *yr = from_f<TS>(h);
+      xstore(yr, h);
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
-    release_flag(myflag, s + 1);
+    publish(myflag, s + 1);
   }
 }
 
@@ -345,9 +385,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       ust[u] = uu;
       zr[0] = from_f<TS>(r);
       zr[H] = from_f<TS>(uu);
-      ((TS*)a.rh)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(r * hst[u]);
+      xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u]);
     }
-    release_flag(myflag, 2 * s + 1);
+    publish(myflag, 2 * s + 1);
     // phase B: candidate and new state
     wait_flags(gflags, a.nSlices, 2 * s + 1, a.status, a.timeout_ticks);
     {
@@ -367,10 +407,10 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       const float h = ust[u] * hst[u] + (1.f - ust[u]) * c;
       hst[u] = h;
       zr[2 * H] = from_f<TS>(c);
-      ((TS*)a.y)[((long long)t * B + b) * a.ldy + J0 + j] = from_f<TS>(h);
+      xstore((TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j, h);
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
-    release_flag(myflag, 2 * s + 2);
+    publish(myflag, 2 * s + 2);
   }
 }
 
@@ -466,10 +506,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_f = dc * cp * fg * (1.f - fg);
         const float d_g = dc * ig * (1.f - gg * gg);
         dcar[u] = dc * fg;
-        gr[0] = from_f<TS>(d_i);
-        gr[H] = from_f<TS>(d_f);
-        gr[2 * H] = from_f<TS>(d_g);
-        gr[3 * H] = from_f<TS>(d_o);
+        xstore(gr, d_i);
+        xstore(gr + H, d_f);
+        xstore(gr + 2 * H, d_g);
+        xstore(gr + 3 * H, d_o);
       } else {
         const float r = to_f(zr[0]), uu = to_f(zr[H]), c = to_f(zr[2 * H]), nh = to_f(zr[3 * H]);
         float hp = 0.f;
@@ -482,13 +522,13 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_u = dh * (hp - c) * uu * (1.f - uu);
         const float d_r = d_c * nh * r * (1.f - r);
         hcar[u] = dh * uu;
-        gr[0] = from_f<TS>(d_r);
-        gr[H] = from_f<TS>(d_u);
-        gr[2 * H] = from_f<TS>(d_c);
-        gr[3 * H] = from_f<TS>(d_c * r);
+        xstore(gr, d_r);
+        xstore(gr + H, d_u);
+        gr[2 * H] = from_f<TS>(d_c);  // input side only: read by later kernels
+        xstore(gr + 3 * H, d_c * r);
       }
     }
-    release_flag(myflag, n + 1);
+    publish(myflag, n + 1);
   }
 }
 
@@ -564,14 +604,14 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const float d_c = dh * (1.f - uu) * (1.f - c * c);
       const float d_u = dh * (hp - c) * uu * (1.f - uu);
       TS* gr = (TS*)a.dg + row * GDH + J0 + j;
-      gr[H] = from_f<TS>(d_u);
-      gr[2 * H] = from_f<TS>(d_c);
+      xstore(gr + H, d_u);
+      xstore(gr + 2 * H, d_c);
       dhs[u] = dh;
       rs[u] = r;
       us[u] = uu;
       hps[u] = hp;
     }
-    release_flag(myflag, 2 * n + 1);
+    publish(myflag, 2 * n + 1);
     wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks);
     {
       f4 acc[MB][NT];
@@ -590,10 +630,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const long long row = (long long)t * B + b;
       const float d_rh = red_sum<NW, BG, HS>(red, bl, j);
       const float d_r = d_rh * hps[u] * rs[u] * (1.f - rs[u]);
-      ((TS*)a.dg)[row * GDH + J0 + j] = from_f<TS>(d_r);
+      xstore((TS*)a.dg + row * GDH + J0 + j, d_r);
       hcar[u] = d_rh * rs[u] + dhs[u] * us[u];
     }
-    release_flag(myflag, 2 * n + 2);
+    publish(myflag, 2 * n + 2);
   }
 }
 

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/rnn.h"
 #include "rnn_internal.hpp"
 
@@ -135,6 +137,52 @@ int check_common(const rnn_desc_t* d, const void* ws, size_t ws_bytes) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_ERR_DEVICE; }
 
+// ---- optional kernel timing (rnn_profile_*) ----
+enum Label { L_FILL, L_PROJ, L_RFWD, L_RBWD, L_DX, L_DW, L_DB, L_COUNT };
+const char* kLabel[L_COUNT] = {"fill", "proj_gemm", "rec_fwd", "rec_bwd", "dx_gemm", "dw_gemm", "db_colsum"};
+struct Pending {
+  int label;
+  hipEvent_t a, b;
+};
+struct Prof {
+  bool on = false;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double total[L_COUNT] = {};
+  long long count[L_COUNT] = {};
+};
+Prof& prof() {
+  static Prof p;
+  return p;
+}
+hipEvent_t take_event() {
+  Prof& p = prof();
+  if (!p.pool.empty()) {
+    hipEvent_t e = p.pool.back();
+    p.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+// Brackets the kernels queued during its lifetime with two events.
+struct ProfScope {
+  int label;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  ProfScope(int l, hipStream_t st) : label(l), s(st) {
+    if (prof().on && (a = take_event())) (void)hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!a) return;
+    hipEvent_t b = take_event();
+    if (!b) return;
+    (void)hipEventRecord(b, s);
+    prof().pending.push_back({label, a, b});
+  }
+};
+
 rnn::RowMap rows(const void* p, long long ld) {
   rnn::RowMap m{};
   m.ptr = p;
@@ -159,6 +207,7 @@ hipError_t gemm_dt(int dtype, const rnn::GemmArgs& g, bool ak, bool bk, hipStrea
 }
 hipError_t colsum_dt(int dtype, const void* src, long long lds, long long M, int col0, int ncols, void* out,
                      int out_row0, int H, const int perm[4], int acc, float* partial, hipStream_t s) {
+  ProfScope ps(L_DB, s);
   if (dtype == RNN_BF16)
     return rnn::launch_colsum<bf16>(src, lds, M, col0, ncols, out, out_row0, H, perm, acc, partial, MAX_CHUNKS, s);
   return rnn::launch_colsum<float>(src, lds, M, col0, ncols, out, out_row0, H, perm, acc, partial, MAX_CHUNKS, s);
@@ -232,8 +281,11 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   const int G = gates(d);
 
   // status word and the forward step counters start at zero
-  if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
-  if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.flags), 0, FLAG_SLOTS, s)))) return st;
+  {
+    ProfScope ps(L_FILL, s);
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.flags), 0, FLAG_SLOTS, s)))) return st;
+  }
 
   // input projection for every step: Z[t,b][g*H+j] = x . W_ih[g,j] + biases
   rnn::GemmArgs g{};
@@ -250,7 +302,10 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   g.bias1 = b_ih;
   g.bias2 = b_hh;
   g.bias_skip_gate = (cell == rnn::CELL_GRU_RA) ? RNN_GATE_C : -1;
-  if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+  {
+    ProfScope ps(L_PROJ, s);
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+  }
 
   rnn::RecArgs a{};
   a.T = d->T;
@@ -277,6 +332,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.flags = (int*)(ws + L.flags);
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
+  ProfScope ps(L_RFWD, s);
   return launch_persistent(plan, a, di, s, "fwd");
 }
 
@@ -302,8 +358,11 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   const int G = gates(d);
   int* flags = (int*)(ws + L.flags) + FLAG_SLOTS;
 
-  if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
-  if ((st = hip_status(rnn::launch_fill_i32(flags, 0, FLAG_SLOTS, s)))) return st;
+  {
+    ProfScope ps(L_FILL, s);
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
+    if ((st = hip_status(rnn::launch_fill_i32(flags, 0, FLAG_SLOTS, s)))) return st;
+  }
 
   rnn::RecArgs a{};
   a.T = d->T;
@@ -333,7 +392,10 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   a.flags = flags;
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
-  if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;
+  {
+    ProfScope ps(L_RBWD, s);
+    if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;
+  }
 
   if (dx) {
     // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]
@@ -347,6 +409,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
     g.ldc = ldx_of(d);
     g.H = d->H;
     g.accumulate = accumulate ? 1 : 0;
+    ProfScope ps(L_DX, s);
     if ((st = hip_status(gemm_dt(d->dtype, g, false, true, s)))) return st;
   }
   return RNN_OK;
@@ -390,6 +453,7 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
     g.H = H;
     for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
     g.accumulate = acc;
+    ProfScope ps(L_DW, s);
     return gemm_dt(d->dtype, g, true, true, s);
   };
 
@@ -428,4 +492,42 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
     }
   }
   return RNN_OK;
+}
+
+RNN_API int rnn_profile_enable(int on) {
+  prof().on = on != 0;
+  return RNN_OK;
+}
+
+RNN_API int rnn_profile_read(rnn_kernel_time_t* out, int max, int reset) {
+  Prof& p = prof();
+  int st = RNN_OK;
+  for (const Pending& e : p.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(e.b) != hipSuccess || hipEventElapsedTime(&ms, e.a, e.b) != hipSuccess) st = RNN_ERR_DEVICE;
+    p.total[e.label] += ms;
+    p.count[e.label] += 1;
+    p.pool.push_back(e.a);
+    p.pool.push_back(e.b);
+  }
+  p.pending.clear();
+  if (st != RNN_OK) return st;
+  int n = 0;
+  for (int l = 0; l < L_COUNT; ++l) {
+    if (p.count[l] == 0) continue;
+    if (out && n < max) {
+      memset(&out[n], 0, sizeof(out[n]));
+      strncpy(out[n].name, kLabel[l], sizeof(out[n].name) - 1);
+      out[n].launches = p.count[l];
+      out[n].total_ms = p.total[l];
+    }
+    ++n;
+  }
+  if (reset) {
+    for (int l = 0; l < L_COUNT; ++l) {
+      p.total[l] = 0;
+      p.count[l] = 0;
+    }
+  }
+  return n;
 }

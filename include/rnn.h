@@ -120,6 +120,28 @@ int rnn_last_device_status(const void* workspace);
 /* Static description of a status code. */
 const char* rnn_status_string(int status);
 
+/* Optional kernel timing, for measurement tools (the tracing hook of the
+ * layer API; off by default). While enabled, every kernel the library queues
+ * is bracketed by two HIP events recorded on the call's stream, under a label
+ * naming the step of the layer it performs: "fill", "proj_gemm" (input
+ * projection), "rec_fwd" (persistent forward), "rec_bwd" (persistent BPTT),
+ * "dx_gemm", "dw_gemm", "db_colsum". Not thread-safe; enable it from one
+ * thread around the calls to be timed. */
+typedef struct rnn_kernel_time {
+  char name[32];
+  long long launches;
+  double total_ms;
+} rnn_kernel_time_t;
+
+/* on != 0 starts recording, 0 stops. Returns RNN_OK. */
+int rnn_profile_enable(int on);
+
+/* Waits for every recorded event, folds the durations into per-label totals
+ * and writes up to `max` entries to `out` (which may be NULL to only count).
+ * reset != 0 clears the totals afterwards. Returns the number of labels, or
+ * RNN_ERR_DEVICE if an event could not be read. */
+int rnn_profile_read(rnn_kernel_time_t* out, int max, int reset);
+
 #ifdef __cplusplus
 }
 #endif

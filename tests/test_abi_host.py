@@ -21,7 +21,8 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted(["rnn_workspace_bytes", "rnn_fwd", "rnn_bwd_data", "rnn_bwd_weights",
-                                  "rnn_last_device_status", "rnn_status_string"])
+                                  "rnn_last_device_status", "rnn_status_string",
+                                  "rnn_profile_enable", "rnn_profile_read"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -93,3 +94,9 @@ def test_workspace_too_small_and_missing_pointers():
 def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5, 7):
         assert isinstance(g.rnn_status_string(st), str) and g.rnn_status_string(st)
+
+
+def test_profile_hook_without_device_work():
+    assert g._lib.rnn_profile_enable(True) == 0
+    assert g._lib.rnn_profile_read() == {}
+    assert g._lib.rnn_profile_enable(False) == 0
