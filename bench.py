@@ -62,6 +62,38 @@ def _work(wl):
     return tot
 
 
+KERNEL_SOURCES = ("gru_layer_fwd_amd/csrc/recurrent.hip", "gru_layer_fwd_amd/csrc/gemm.hip",
+                  "gru_layer_fwd_amd/csrc/rnn_internal.hpp")
+
+
+def kernel_hash() -> str:
+    """Hash of the kernel sources, so that stored counter readings are only
+    used for the kernels they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, label: str):
+    """HBM bytes per launch of `label` from profiles/traffic.json (two
+    rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by a copy
+    kernel of known size), or None when absent or taken on other kernels."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "traffic.json")
+    try:
+        with open(path) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload, {}).get(label)
+    if not e or e.get("kernel_hash") != kernel_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
 def cpu_baseline(wl, inp, rows: int):
     """The oracle as it stands, on the first `rows` batch rows of the same
     workload (all T steps, every layer/direction), timed on the host."""
@@ -101,6 +133,9 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-rows", type=int, default=0, help="batch rows the CPU oracle runs (0 = all)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain device copy of this many MiB (a known-size "
+                         "kernel for calibrating rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the layer shards over "
@@ -187,7 +222,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": b_step / t_step / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = stored_traffic(name, dom)
     roof["kernel"] = dom
     roof["launch_ms"] = kern[dom]["ms_per_step"] / max(kern[dom]["launches_per_step"], 1)
     for k in kern:
@@ -224,6 +259,12 @@ def main():
         "recurrent_us_per_step": rec,
         "kernels": kern,
     }
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = 2 * (args.copy_mib << 20)
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_rows or wl.B, wl.B))
     print(json.dumps(out), flush=True)

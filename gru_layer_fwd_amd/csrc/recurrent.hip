@@ -254,24 +254,37 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     return (long long)a.perm[g] * H + J0 + (col - g * HS);
   });
 
+  // per-unit state; unit = (batch row bl, hidden unit j) of this workgroup
   float cst[UPT], hst[UPT], bhc[UPT];
+  bool live[UPT];
+  int bl_[UPT], j_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
-    cst[u] = 0.f;
-    hst[u] = 0.f;
-    bhc[u] = 0.f;
     const int unit = tid + u * NTH;
-    const int bl = unit / HS, j = unit - (unit / HS) * HS, b = b0 + bl;
-    if (unit < UNITS && b < B) {
-      if (a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
-      if (CELL == CELL_LSTM && a.c0) cst[u] = to_f(((const TS*)a.c0)[(long long)b * H + J0 + j]);
-      if (CELL == CELL_GRU_RA) bhc[u] = to_f(((const TS*)a.b_hh)[(long long)a.perm[2] * H + J0 + j]);
+    bl_[u] = unit / HS;
+    j_[u] = unit - bl_[u] * HS;
+    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    cst[u] = hst[u] = bhc[u] = 0.f;
+    const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
+    if (live[u]) {
+      if (a.h0) hst[u] = to_f(((const TS*)a.h0)[o]);
+      if (CELL == CELL_LSTM && a.c0) cst[u] = to_f(((const TS*)a.c0)[o]);
+      if (CELL == CELL_GRU_RA) bhc[u] = to_f(((const TS*)a.b_hh)[(long long)a.perm[2] * H + J0 + j_[u]]);
     }
   }
 
   for (int s = 0; s < T; ++s) {
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
+    // projected inputs of this step do not depend on the exchange: their
+    // loads are issued before the wait and land while it polls
+    TS pz[UPT][GL];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const TS* zr = (const TS*)a.z + ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u];
+#pragma unroll
+      for (int g = 0; g < GL; ++g) pz[u][g] = live[u] ? zr[g * H] : from_f<TS>(0.f);
+    }
     if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
     f4 acc[MB][NT];
     zero_acc(acc);
@@ -282,21 +295,21 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTH;
-      const int bl = unit / HS, j = unit - (unit / HS) * HS, b = b0 + bl;
-      if (unit >= UNITS || b >= B) continue;
+      if (!live[u]) continue;
+      const int bl = bl_[u], j = j_[u], b = b0 + bl;
       TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
       TS* yr = (TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j;
       float h;
       if constexpr (CELL == CELL_LSTM) {
-        const float zi = red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(zr[0]);
-        const float zf = red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(zr[H]);
-        const float zg = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + to_f(zr[2 * H]);
-        const float zo = red_sum<NW, BG, NCOL>(red, bl, 3 * HS + j) + to_f(zr[3 * H]);
+        const float zi = red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(pz[u][0]);
+        const float zf = red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(pz[u][1]);
+        const float zg = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + to_f(pz[u][2]);
+        const float zo = red_sum<NW, BG, NCOL>(red, bl, 3 * HS + j) + to_f(pz[u][3]);
         const float ig = sigmoidf_(zi), fg = sigmoidf_(zf), gg = tanhf_(zg), og = sigmoidf_(zo);
         const float c = fg * cst[u] + ig * gg;
         cst[u] = c;
         h = og * tanhf_(c);
+        xstore(yr, h);
         zr[0] = from_f<TS>(ig);
         zr[H] = from_f<TS>(fg);
         zr[2 * H] = from_f<TS>(gg);
@@ -304,18 +317,18 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         ((TS*)a.cbuf)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(c);
         if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(c);
       } else {
-        const float r = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(zr[0]));
-        const float uu = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(zr[H]));
+        const float r = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(pz[u][0]));
+        const float uu = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(pz[u][1]));
         const float nh = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + bhc[u];
-        const float c = tanhf_(to_f(zr[2 * H]) + r * nh);
+        const float c = tanhf_(to_f(pz[u][2]) + r * nh);
         h = uu * hst[u] + (1.f - uu) * c;
         hst[u] = h;
+        xstore(yr, h);
         zr[0] = from_f<TS>(r);
         zr[H] = from_f<TS>(uu);
         zr[2 * H] = from_f<TS>(c);
         zr[3 * H] = from_f<TS>(nh);
       }
-      xstore(yr, h);
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
     publish(myflag, s + 1);
@@ -351,18 +364,28 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
                            [&](int col) -> long long { return (long long)a.perm[2] * H + J0 + col; });
 
   float hst[UPT], ust[UPT];
+  bool live[UPT];
+  int bl_[UPT], j_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
-    hst[u] = 0.f;
-    ust[u] = 0.f;
     const int unit = tid + u * NTH;
-    const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-    if (unit < UNITS && b < B && a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
+    bl_[u] = unit / HS;
+    j_[u] = unit - bl_[u] * HS;
+    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    hst[u] = ust[u] = 0.f;
+    if (live[u] && a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
 
   for (int s = 0; s < T; ++s) {
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
+    TS pz[UPT][3];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const TS* zr = (const TS*)a.z + ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u];
+#pragma unroll
+      for (int g = 0; g < 3; ++g) pz[u][g] = live[u] ? zr[g * H] : from_f<TS>(0.f);
+    }
     // phase A: r, u
     if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks);
     {
@@ -376,16 +399,15 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTH;
-      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-      if (unit >= UNITS || b >= B) continue;
+      if (!live[u]) continue;
+      const int bl = bl_[u], j = j_[u], b = b0 + bl;
       TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
-      const float r = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, j) + to_f(zr[0]));
-      const float uu = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, HS + j) + to_f(zr[H]));
+      const float r = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, j) + to_f(pz[u][0]));
+      const float uu = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, HS + j) + to_f(pz[u][1]));
       ust[u] = uu;
+      xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u]);
       zr[0] = from_f<TS>(r);
       zr[H] = from_f<TS>(uu);
-      xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u]);
     }
     publish(myflag, 2 * s + 1);
     // phase B: candidate and new state
@@ -399,15 +421,14 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTH;
-      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-      if (unit >= UNITS || b >= B) continue;
+      if (!live[u]) continue;
+      const int bl = bl_[u], j = j_[u], b = b0 + bl;
       TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
-      const float c = tanhf_(red_sum<NW, BG, HS>(red, bl, j) + to_f(zr[2 * H]));
+      const float c = tanhf_(red_sum<NW, BG, HS>(red, bl, j) + to_f(pz[u][2]));
       const float h = ust[u] * hst[u] + (1.f - ust[u]) * c;
       hst[u] = h;
-      zr[2 * H] = from_f<TS>(c);
       xstore((TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j, h);
+      zr[2 * H] = from_f<TS>(c);
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
     publish(myflag, 2 * s + 2);
@@ -444,19 +465,51 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
   load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K);
 
   float dcar[UPT], hcar[UPT];
+  bool live[UPT];
+  int bl_[UPT], j_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
-    dcar[u] = 0.f;
-    hcar[u] = 0.f;
     const int unit = tid + u * NTH;
-    const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-    if (CELL == CELL_LSTM && unit < UNITS && b < B && a.dcT)
-      dcar[u] = to_f(((const TS*)a.dcT)[(long long)b * H + J0 + j]);
+    bl_[u] = unit / HS;
+    j_[u] = unit - bl_[u] * HS;
+    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    dcar[u] = hcar[u] = 0.f;
+    const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
+    if (live[u]) {
+      if (CELL == CELL_LSTM && a.dcT) dcar[u] = to_f(((const TS*)a.dcT)[o]);
+      if (a.dhT) hcar[u] = to_f(((const TS*)a.dhT)[o]);  // seeds the carried hidden gradient
+    }
   }
 
   for (int n = 0; n <= T; ++n) {
     const int s = T - 1 - n;  // processing index of this step (-1: the final dh0 contraction)
-    f4 acc[MB][1 * NT];
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+    // own-unit operands of the step (independent of the exchange), loaded
+    // ahead of the wait: dy, saved gates, cell states / previous output
+    TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const bool on = live[u] && n < T;
+      const long long row = (long long)t * B + b0 + bl_[u];
+      const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
+      const TS* zr = (const TS*)a.z + row * GZH + J0 + j_[u];
+      pdy[u] = on ? ((const TS*)a.dy)[row * a.ldy + J0 + j_[u]] : from_f<TS>(0.f);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) pz[u][g] = on ? zr[g * H] : from_f<TS>(0.f);
+      if constexpr (CELL == CELL_LSTM) {
+        pc[u] = on ? ((const TS*)a.cbuf)[row * H + J0 + j_[u]] : from_f<TS>(0.f);
+        const TS* cprev = (s == 0) ? (const TS*)a.c0 + o
+                                   : (const TS*)a.cbuf + ((long long)tp * B + b0 + bl_[u]) * H + J0 + j_[u];
+        pprev[u] = (on && (s > 0 || a.c0)) ? *cprev : from_f<TS>(0.f);
+      } else {
+        pc[u] = from_f<TS>(0.f);
+        const TS* hprev = (s == 0) ? (const TS*)a.h0 + o
+                                   : (const TS*)a.y + ((long long)tp * B + b0 + bl_[u]) * a.ldy + J0 + j_[u];
+        pprev[u] = (on && (s > 0 || a.h0)) ? *hprev : from_f<TS>(0.f);
+      }
+    }
+    f4 acc[MB][NT];
     zero_acc(acc);
     if (n > 0) {
       wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks);
@@ -469,36 +522,23 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     if (n == T) {
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
-        const int unit = tid + u * NTH;
-        const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-        if (unit >= UNITS || b >= B) continue;
-        const float dh0 = red_sum<NW, BG, HS>(red, bl, j) + hcar[u];
-        if (a.dh0) ((TS*)a.dh0)[(long long)b * H + J0 + j] = from_f<TS>(dh0);
-        if (CELL == CELL_LSTM && a.dc0) ((TS*)a.dc0)[(long long)b * H + J0 + j] = from_f<TS>(dcar[u]);
+        if (!live[u]) continue;
+        const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
+        const float dh0 = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + hcar[u];
+        if (a.dh0) ((TS*)a.dh0)[o] = from_f<TS>(dh0);
+        if (CELL == CELL_LSTM && a.dc0) ((TS*)a.dc0)[o] = from_f<TS>(dcar[u]);
       }
       break;
     }
-    const int t = a.dir ? T - 1 - s : s;
-    const int tp = a.dir ? t + 1 : t - 1;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTH;
-      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-      if (unit >= UNITS || b >= B) continue;
-      const long long row = (long long)t * B + b;
-      float dh = red_sum<NW, BG, HS>(red, bl, j) + to_f(((const TS*)a.dy)[row * a.ldy + J0 + j]) + hcar[u];
-      if (n == 0 && a.dhT) dh += to_f(((const TS*)a.dhT)[(long long)b * H + J0 + j]);
-      const TS* zr = (const TS*)a.z + row * GZH + J0 + j;
-      TS* gr = (TS*)a.dg + row * GDH + J0 + j;
+      if (!live[u]) continue;
+      const long long row = (long long)t * B + b0 + bl_[u];
+      const float dh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + to_f(pdy[u]) + hcar[u];
+      TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
       if constexpr (CELL == CELL_LSTM) {
-        const float ig = to_f(zr[0]), fg = to_f(zr[H]), gg = to_f(zr[2 * H]), og = to_f(zr[3 * H]);
-        const float c = to_f(((const TS*)a.cbuf)[row * H + J0 + j]);
-        float cp = 0.f;
-        if (s == 0) {
-          if (a.c0) cp = to_f(((const TS*)a.c0)[(long long)b * H + J0 + j]);
-        } else {
-          cp = to_f(((const TS*)a.cbuf)[((long long)tp * B + b) * H + J0 + j]);
-        }
+        const float ig = to_f(pz[u][0]), fg = to_f(pz[u][1]), gg = to_f(pz[u][2]), og = to_f(pz[u][3]);
+        const float c = to_f(pc[u]), cp = to_f(pprev[u]);
         const float tc = tanhf_(c);
         const float d_o = dh * tc * og * (1.f - og);
         const float dc = dh * og * (1.f - tc * tc) + dcar[u];
@@ -506,18 +546,14 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_f = dc * cp * fg * (1.f - fg);
         const float d_g = dc * ig * (1.f - gg * gg);
         dcar[u] = dc * fg;
+        hcar[u] = 0.f;
         xstore(gr, d_i);
         xstore(gr + H, d_f);
         xstore(gr + 2 * H, d_g);
         xstore(gr + 3 * H, d_o);
       } else {
-        const float r = to_f(zr[0]), uu = to_f(zr[H]), c = to_f(zr[2 * H]), nh = to_f(zr[3 * H]);
-        float hp = 0.f;
-        if (s == 0) {
-          if (a.h0) hp = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
-        } else {
-          hp = to_f(((const TS*)a.y)[((long long)tp * B + b) * a.ldy + J0 + j]);
-        }
+        const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]), nh = to_f(pz[u][3]);
+        const float hp = to_f(pprev[u]);
         const float d_c = dh * (1.f - uu) * (1.f - c * c);
         const float d_u = dh * (hp - c) * uu * (1.f - uu);
         const float d_r = d_c * nh * r * (1.f - r);
@@ -556,11 +592,35 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
   load_w_cols<TS, NT, KIB>(WB, (const TS*)a.W_hh, H, a.perm, J0, 2, H);
 
   float hcar[UPT], dhs[UPT], rs[UPT], us[UPT], hps[UPT];
+  bool live[UPT];
+  int bl_[UPT], j_[UPT];
 #pragma unroll
-  for (int u = 0; u < UPT; ++u) hcar[u] = dhs[u] = rs[u] = us[u] = hps[u] = 0.f;
+  for (int u = 0; u < UPT; ++u) {
+    const int unit = tid + u * NTH;
+    bl_[u] = unit / HS;
+    j_[u] = unit - bl_[u] * HS;
+    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    hcar[u] = dhs[u] = rs[u] = us[u] = hps[u] = 0.f;
+    if (live[u] && a.dhT) hcar[u] = to_f(((const TS*)a.dhT)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
+  }
 
   for (int n = 0; n <= T; ++n) {
     const int s = T - 1 - n;
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+    TS pdy[UPT], pz[UPT][3], pprev[UPT];
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const bool on = live[u] && n < T;
+      const long long row = (long long)t * B + b0 + bl_[u];
+      const TS* zr = (const TS*)a.z + row * GZH + J0 + j_[u];
+      pdy[u] = on ? ((const TS*)a.dy)[row * a.ldy + J0 + j_[u]] : from_f<TS>(0.f);
+#pragma unroll
+      for (int g = 0; g < 3; ++g) pz[u][g] = on ? zr[g * H] : from_f<TS>(0.f);
+      const TS* hprev = (s == 0) ? (const TS*)a.h0 + (long long)(b0 + bl_[u]) * H + J0 + j_[u]
+                                 : (const TS*)a.y + ((long long)tp * B + b0 + bl_[u]) * a.ldy + J0 + j_[u];
+      pprev[u] = (on && (s > 0 || a.h0)) ? *hprev : from_f<TS>(0.f);
+    }
     {
       f4 acc[MB][NT];
       zero_acc(acc);
@@ -576,34 +636,22 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     if (n == T) {
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
-        const int unit = tid + u * NTH;
-        const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-        if (unit >= UNITS || b >= B) continue;
-        if (a.dh0) ((TS*)a.dh0)[(long long)b * H + J0 + j] = from_f<TS>(red_sum<NW, BG, HS>(red, bl, j) + hcar[u]);
+        if (!live[u] || !a.dh0) continue;
+        ((TS*)a.dh0)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]] =
+            from_f<TS>(red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + hcar[u]);
       }
       break;
     }
-    const int t = a.dir ? T - 1 - s : s;
-    const int tp = a.dir ? t + 1 : t - 1;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTH;
-      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-      if (unit >= UNITS || b >= B) continue;
-      const long long row = (long long)t * B + b;
-      float dh = red_sum<NW, BG, HS>(red, bl, j) + to_f(((const TS*)a.dy)[row * a.ldy + J0 + j]) + hcar[u];
-      if (n == 0 && a.dhT) dh += to_f(((const TS*)a.dhT)[(long long)b * H + J0 + j]);
-      const TS* zr = (const TS*)a.z + row * GZH + J0 + j;
-      const float r = to_f(zr[0]), uu = to_f(zr[H]), c = to_f(zr[2 * H]);
-      float hp = 0.f;
-      if (s == 0) {
-        if (a.h0) hp = to_f(((const TS*)a.h0)[(long long)b * H + J0 + j]);
-      } else {
-        hp = to_f(((const TS*)a.y)[((long long)tp * B + b) * a.ldy + J0 + j]);
-      }
+      if (!live[u]) continue;
+      const long long row = (long long)t * B + b0 + bl_[u];
+      const float dh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + to_f(pdy[u]) + hcar[u];
+      const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]);
+      const float hp = to_f(pprev[u]);
       const float d_c = dh * (1.f - uu) * (1.f - c * c);
       const float d_u = dh * (hp - c) * uu * (1.f - uu);
-      TS* gr = (TS*)a.dg + row * GDH + J0 + j;
+      TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
       xstore(gr + H, d_u);
       xstore(gr + 2 * H, d_c);
       dhs[u] = dh;
@@ -616,21 +664,18 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     {
       f4 acc[MB][NT];
       zero_acc(acc);
-      const int t2 = a.dir ? T - 1 - s : s;
-      contract<TS, MB, NT, KIB>(acc, WB, (const TS*)a.dg + (long long)t2 * B * GDH + 2 * H, GDH, b0, B, H,
-                                1 << 30, 0);
+      contract<TS, MB, NT, KIB>(acc, WB, (const TS*)a.dg + (long long)t * B * GDH + 2 * H, GDH, b0, B, H, 1 << 30,
+                                0);
       spill_acc(red, acc);
     }
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const int unit = tid + u * NTH;
-      const int bl = unit / HS, j = unit % HS, b = b0 + bl;
-      if (unit >= UNITS || b >= B) continue;
-      const long long row = (long long)t * B + b;
-      const float d_rh = red_sum<NW, BG, HS>(red, bl, j);
+      if (!live[u]) continue;
+      const long long row = (long long)t * B + b0 + bl_[u];
+      const float d_rh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]);
       const float d_r = d_rh * hps[u] * rs[u] * (1.f - rs[u]);
-      xstore((TS*)a.dg + row * GDH + J0 + j, d_r);
+      xstore((TS*)a.dg + row * GDH + J0 + j_[u], d_r);
       hcar[u] = d_rh * rs[u] + dhs[u] * us[u];
     }
     publish(myflag, 2 * n + 2);
