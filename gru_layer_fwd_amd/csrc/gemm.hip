@@ -1,155 +1,352 @@
 // MFMA GEMM for the T-parallel products of the layer:
 //   input projection  P[t,b][g*H+j] = x[t,b] . W_ih[gate g row j] + biases
 //   input gradient    dx[t,b]       = sum_n dG[t,b][n] W_ih[n]
-//   weight gradients  dW[n]         = sum_(t,b) dG[t,b][n] act[t,b]
+//   weight gradients  dW[n]         = sum_(t,b) dG[t,b][n] act[t,b], db[n] = sum dG[t,b][n]
 // (popnn Lstm.cpp "calcSequenceWeightedInputs", "backwardStepImpl",
 // "basicLstmParamUpdate"; Gru.cpp "basicGruParamUpdate").
 //
-// One 256-thread workgroup computes a 128x128 tile of C with a 2x2 grid of
-// waves (64x64 each, 4x4 MFMA 16x16 tiles). A k-tile is 128 bytes of every
-// row (64 bf16 / 32 fp32); operands are staged in LDS as [row][k] with a
-// 16-byte pad per row, double-buffered, the next tile's global loads in
-// flight while the current one is multiplied. Operands that are k-outer in
-// memory (the weight-gradient products and the W_ih of the input gradient)
-// are transposed on their way into LDS.
+// Tiling. A workgroup computes a BM x BN tile of C: 256x256 with 8 waves
+// (2x4, 128x64 each), 256x128 and 128x128 with 4 waves (2x2); every wave
+// holds its part of the tile as 16x16 MFMA accumulators.
+// A k-tile is 128 bytes of every operand row (64 bf16 / 32 fp32). Operand
+// tiles live in LDS as [row][128 B] with the 16-byte chunks XOR-swizzled by
+// (row/2)%8, which keeps both the MFMA operand reads (16 rows x one chunk)
+// and the tile writes free of bank conflicts; two buffers, the next k-tile's
+// global loads in flight while the current one is multiplied.
+//
+// Operands that are k-outer in memory (the weight-gradient products, and
+// W_ih in the input gradient) are transposed in registers on their way into
+// LDS: a thread loads 4 consecutive k rows of 8 (bf16) or 4 (fp32) elements
+// and writes them as 8 (4) row fragments of 4 k values.
+//
+// Placement. Workgroups are dispatched round-robin over the 8 XCDs; tiles
+// are numbered so that each XCD gets a contiguous range, walked in groups of
+// 4 M-tiles, so that the A rows and B columns a group shares stay in that
+// XCD's L2. When the tiles cannot fill the chip (the weight-gradient shapes)
+// the contraction is split into slices whose fp32 partial tiles are summed
+// in a fixed order by a second kernel (deterministic).
+//
+// Bias gradients: when requested, the workgroups of the first N-tile column
+// also sum the A tile over k (dG summed over (t,b)) while staging it.
 #include "rnn_internal.hpp"
 
 namespace rnn {
 
 namespace {
 
-constexpr int NTHR = 256;
-constexpr int TM = 128, TN = 128;
-constexpr int ROWB = 128;              // bytes of a k-tile row
-constexpr int PITCHB = ROWB + 16;      // LDS row pitch in bytes
-constexpr int TILEB = TM * PITCHB;     // bytes of one operand tile in LDS
+constexpr int ROWB = 128;  // bytes of a k-tile row
 
-// k-contiguous operand: 128 rows x 128 bytes -> 1024 chunks, 4 per thread.
-// thread t: chunk t%8 of rows t/8 + 32*i.
-template <typename TS>
-__device__ __forceinline__ void load_kcontig(uint4 (&r)[4], const RowMap& m, long long r0, long long R,
-                                             long long k0, long long K) {
-  constexpr int KQ = Chunk<TS>::KQ;
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+__device__ __forceinline__ int lds_off(int r, int c) { return r * ROWB + swz(r, c) * 16; }
+
+// ---- k-contiguous operand: R rows x 128 bytes; thread t: chunk t%8 of rows t/8 + (NT/8) i.
+// The row pointers do not change along k: resolved once per workgroup.
+template <typename TS, int R, int NT>
+__device__ __forceinline__ void rows_kc(const TS* (&rp)[R * 8 / NT], const RowMap& m, long long r0, long long Rt) {
   const int t = threadIdx.x;
-  const long long kk = k0 + (t & 7) * KQ;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const long long rr = r0 + (t >> 3) + 32 * i;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (rr < R && kk < K) {
-      const TS* p = map_row<TS>(m, rr);
-      if (p) v = *(const uint4*)(p + kk);
+  for (int i = 0; i < R * 8 / NT; ++i) {
+    const long long rr = r0 + (t >> 3) + (NT / 8) * i;
+    rp[i] = (rr < Rt) ? map_row<TS>(m, rr) : nullptr;
+  }
+}
+template <typename TS, int R, int NT>
+__device__ __forceinline__ void load_kc(uint4 (&v)[R * 8 / NT], const TS* const (&rp)[R * 8 / NT], long long k0,
+                                        long long K) {
+  constexpr int KQ = Chunk<TS>::KQ;
+  const long long kk = k0 + (threadIdx.x & 7) * KQ;
+#pragma unroll
+  for (int i = 0; i < R * 8 / NT; ++i) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (rp[i] && kk < K) x = *(const uint4*)(rp[i] + kk);
+    v[i] = x;
+  }
+}
+template <int R, int NT>
+__device__ __forceinline__ void store_kc(char* lds, const uint4 (&v)[R * 8 / NT]) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < R * 8 / NT; ++i) *(uint4*)(lds + lds_off((t >> 3) + (NT / 8) * i, t & 7)) = v[i];
+}
+
+// ---- k-outer operand: BK memory rows (k) of R contiguous elements.
+// Groups of 4 k rows x 16 bytes; 2R groups, 2R/NT per thread; thread t
+// handles group g = t + NT i: k-quad g % KQD, element block g / KQD.
+template <typename TS>
+struct KO {
+  static constexpr int KQ = Chunk<TS>::KQ;      // elements per 16 B
+  static constexpr int BK = ROWB / sizeof(TS);  // k rows per tile
+  static constexpr int KQD = BK / 4;            // k quads per tile
+};
+
+// Rows [k0, k0+BK) of a k-outer operand are usually an affine run
+// (base + k*ld): always for plain maps, for gate-permuted maps when the
+// k-tile stays in one gate block, for the h_{t-1} map when it avoids the
+// first step's rows. Otherwise each row goes through map_row.
+template <typename TS>
+__device__ __forceinline__ bool affine_rows(const RowMap& m, long long k0, int BK, const TS*& base, long long& ld) {
+  const TS* p = (const TS*)m.ptr;
+  ld = m.ld;
+  if (m.kind == 0) {
+    base = p;
+    return true;
+  }
+  if (m.kind == 1) {
+    const long long g = k0 / m.H;
+    if ((k0 + BK - 1) / m.H != g) return false;
+    base = p + ((long long)m.perm[g] - g) * m.H * m.ld;
+    return true;
+  }
+  const long long f0 = (long long)(m.dir ? m.T - 1 : 0) * m.B;  // first step's rows
+  if (k0 + BK > f0 && k0 < f0 + m.B) return false;
+  base = p + (m.dir ? (long long)m.B : -(long long)m.B) * m.ld;  // h_{t-1} is y of t-1 (t+1)
+  return true;
+}
+
+template <typename TS, int R, int NT>
+__device__ __forceinline__ void load_ko(uint4 (&v)[2 * R / NT][4], const RowMap& m, long long r0, long long Rt,
+                                        long long k0, long long K) {
+  constexpr int KQ = KO<TS>::KQ, KQD = KO<TS>::KQD, BK = KO<TS>::BK;
+  const int t = threadIdx.x;
+  const TS* base;
+  long long ld;
+  const bool aff = affine_rows<TS>(m, k0, BK, base, ld);
+#pragma unroll
+  for (int i = 0; i < 2 * R / NT; ++i) {
+    const int g = t + NT * i;
+    const int kq = g % KQD, mo = g / KQD;
+    const long long rr = r0 + (long long)mo * KQ;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const long long k = k0 + kq * 4 + kk;
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (k < K && rr < Rt) {
+        const TS* p = aff ? base + k * ld : map_row<TS>(m, k);
+        if (p) x = *(const uint4*)(p + rr);
+      }
+      v[i][kk] = x;
     }
-    r[i] = v;
-  }
-}
-__device__ __forceinline__ void store_kcontig(char* lds, const uint4 (&r)[4]) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    *(uint4*)(lds + ((t >> 3) + 32 * i) * PITCHB + (t & 7) * 16) = r[i];
-}
-
-// k-outer operand: BK memory rows (k) of 128 contiguous elements (m or n).
-// thread t: lane index = k within the tile (consecutive lanes, consecutive
-// k, so that the transposed LDS writes of one instruction are contiguous);
-// the 16-byte chunk index along m/n comes from the rest of the thread id.
-template <typename TS>
-__device__ __forceinline__ void load_kouter(uint4 (&r)[4], const RowMap& m, long long r0, long long R,
-                                            long long k0, long long K) {
-  constexpr int KQ = Chunk<TS>::KQ;
-  constexpr int BK = ROWB / sizeof(TS);       // 64 (bf16) / 32 (fp32)
-  constexpr int CPR = TM / KQ;                // chunks along m per k row: 16 / 32
-  constexpr int PASS = NTHR / BK;             // chunk rows per pass: 4 / 8
-  const int t = threadIdx.x;
-  const int kl = t % BK;
-  const long long kk = k0 + kl;
-  const TS* p = (kk < K) ? map_row<TS>(m, kk) : nullptr;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ch = t / BK + PASS * i;           // < CPR
-    const long long rr = r0 + (long long)ch * KQ;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (p && rr < R) v = *(const uint4*)(p + rr);
-    r[i] = v;
-  }
-  static_assert(PASS * 4 == CPR, "tile shape");
-}
-template <typename TS>
-__device__ __forceinline__ void store_kouter(char* lds, const uint4 (&r)[4]) {
-  constexpr int KQ = Chunk<TS>::KQ;
-  constexpr int BK = ROWB / sizeof(TS);
-  constexpr int PASS = NTHR / BK;
-  const int t = threadIdx.x;
-  const int kl = t % BK;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ch = t / BK + PASS * i;
-    const TS* e = (const TS*)&r[i];
-#pragma unroll
-    for (int j = 0; j < KQ; ++j)
-      *(TS*)(lds + (ch * KQ + j) * PITCHB + kl * sizeof(TS)) = e[j];
   }
 }
 
-template <typename TS, bool AK, bool BKO>
-__global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs g) {
+__device__ __forceinline__ unsigned pk_lo(unsigned a, unsigned b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ unsigned pk_hi(unsigned a, unsigned b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+template <typename TS, int R, int NT>
+__device__ __forceinline__ void store_ko(char* lds, const uint4 (&v)[2 * R / NT][4]) {
+  constexpr int KQD = KO<TS>::KQD;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 2 * R / NT; ++i) {
+    const int g = t + NT * i;
+    const int kq = g % KQD, mo = g / KQD;
+    const unsigned* a0 = (const unsigned*)&v[i][0];
+    const unsigned* a1 = (const unsigned*)&v[i][1];
+    const unsigned* a2 = (const unsigned*)&v[i][2];
+    const unsigned* a3 = (const unsigned*)&v[i][3];
+    if constexpr (sizeof(TS) == 2) {
+      // 8 rows x 4 k (8 bytes): row mo*8+e, k offset kq*4 -> chunk kq/2, half kq%2
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = e >> 1;
+        uint2 w;
+        w.x = (e & 1) ? pk_hi(a0[d], a1[d]) : pk_lo(a0[d], a1[d]);
+        w.y = (e & 1) ? pk_hi(a2[d], a3[d]) : pk_lo(a2[d], a3[d]);
+        *(uint2*)(lds + lds_off(mo * 8 + e, kq >> 1) + (kq & 1) * 8) = w;
+      }
+    } else {
+      // 4 rows x 4 k (16 bytes): row mo*4+e, chunk kq
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *(uint4*)(lds + lds_off(mo * 4 + e, kq)) = make_uint4(a0[e], a1[e], a2[e], a3[e]);
+    }
+  }
+}
+
+// sum over the 4 k rows of a k-outer group, per element (bias gradients)
+template <typename TS, int R, int NT>
+__device__ __forceinline__ void rowsum_ko(float (&s)[2 * R / NT][8], const uint4 (&v)[2 * R / NT][4]) {
+#pragma unroll
+  for (int i = 0; i < 2 * R / NT; ++i)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const unsigned* a = (const unsigned*)&v[i][kk];
+      if constexpr (sizeof(TS) == 2) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          s[i][2 * d] += __uint_as_float(a[d] << 16);
+          s[i][2 * d + 1] += __uint_as_float(a[d] & 0xFFFF0000u);
+        }
+      } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) s[i][d] += __uint_as_float(a[d]);
+      }
+    }
+}
+
+struct Tile {
+  int m, n, kz;
+};
+
+// XCD-aware tile order: launch index -> (m tile, n tile, k slice)
+__device__ __forceinline__ Tile tile_of(int nM, int nN, int KS) {
+  const int total = nM * nN * KS;
+  int L = blockIdx.x;
+  if ((total & 7) == 0) L = (blockIdx.x & 7) * (total >> 3) + (blockIdx.x >> 3);
+  const int kz = L % KS;
+  const int mn = L / KS;
+  constexpr int GM = 4;
+  const int per_group = GM * nN;
+  const int grp = mn / per_group;
+  const int first_m = grp * GM;
+  const int gm = min(nM - first_m, GM);
+  const int in = mn - grp * per_group;
+  Tile t;
+  t.m = first_m + in % gm;
+  t.n = in / gm;
+  t.kz = kz;
+  return t;
+}
+
+template <int BM, int BN>
+struct Waves {  // 256x256 tiles run 8 waves (2x4), smaller ones 4 (2x2)
+  static constexpr int WGN = (BM == 256 && BN == 256) ? 4 : 2;
+  static constexpr int NT = 64 * 2 * WGN;
+};
+
+template <typename TS, bool AKO, bool BKO, int BM, int BN>
+__global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   extern __shared__ __align__(16) char smem[];
-  auto sA = [&](int buf) { return smem + buf * 2 * TILEB; };
-  auto sB = [&](int buf) { return smem + TILEB + buf * 2 * TILEB; };
-
-  const long long m0 = (long long)blockIdx.y * TM;
-  const long long n0 = (long long)blockIdx.x * TN;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int wm = w >> 1, wn = w & 1;
-  const int r16 = lane & 15, q = lane >> 4;
+  constexpr int NT = Waves<BM, BN>::NT, WGN = Waves<BM, BN>::WGN;
+  constexpr int TILE_A = BM * ROWB, TILE_B = BN * ROWB;
   constexpr int BK = ROWB / sizeof(TS);
-  const int nk = (int)((g.K + BK - 1) / BK);
+  constexpr int WM = BM / 2, WN = BN / WGN;  // wave tile
+  constexpr int FM = WM / 16, FN = WN / 16;
+  auto sA = [&](int b) { return smem + b * (TILE_A + TILE_B); };
+  auto sB = [&](int b) { return smem + b * (TILE_A + TILE_B) + TILE_A; };
 
-  f4 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+  const int nM = (int)((g.M + BM - 1) / BM), nN = (int)((g.N + BN - 1) / BN);
+  const Tile tl = tile_of(nM, nN, g.ksplit);
+  const long long m0 = (long long)tl.m * BM, n0 = (long long)tl.n * BN;
+  const long long kb = (long long)tl.kz * g.kslice;
+  long long ke = kb + g.kslice;
+  if (ke > g.K) ke = g.K;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int wm = w / WGN, wn = w % WGN;
+  const int r16 = lane & 15, q = lane >> 4;
+  const int nk = (ke > kb) ? (int)((ke - kb + BK - 1) / BK) : 0;
+  const bool want_rows = AKO && g.rowsum != nullptr && tl.n == 0;
 
-  uint4 ra[4], rb[4];
+  f4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f4{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int RA = AKO ? 1 : BM * 8 / NT, RB = BKO ? 1 : BN * 8 / NT;
+  constexpr int OA = AKO ? 2 * BM / NT : 1, OB = BKO ? 2 * BN / NT : 1;
+  uint4 ra_c[RA], rb_c[RB];
+  uint4 ra_o[OA][4], rb_o[OB][4];
+  float rs[OA][8];
+#pragma unroll
+  for (int i = 0; i < OA; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) rs[i][e] = 0.f;
+
+  const TS* pa[RA];
+  const TS* pb[RB];
+  if constexpr (!AKO) rows_kc<TS, BM, NT>(pa, g.a, m0, g.M);
+  if constexpr (!BKO) rows_kc<TS, BN, NT>(pb, g.b, n0, g.N);
   auto gload = [&](int kt) {
-    const long long k0 = (long long)kt * BK;
-    if (AK) load_kouter<TS>(ra, g.a, m0, g.M, k0, g.K); else load_kcontig<TS>(ra, g.a, m0, g.M, k0, g.K);
-    if (BKO) load_kouter<TS>(rb, g.b, n0, g.N, k0, g.K); else load_kcontig<TS>(rb, g.b, n0, g.N, k0, g.K);
+    const long long k0 = kb + (long long)kt * BK;
+    if constexpr (AKO) load_ko<TS, BM, NT>(ra_o, g.a, m0, g.M, k0, ke);
+    else load_kc<TS, BM, NT>(ra_c, pa, k0, ke);
+    if constexpr (BKO) load_ko<TS, BN, NT>(rb_o, g.b, n0, g.N, k0, ke);
+    else load_kc<TS, BN, NT>(rb_c, pb, k0, ke);
   };
-  auto sstore = [&](int buf) {
-    if (AK) store_kouter<TS>(sA(buf), ra); else store_kcontig(sA(buf), ra);
-    if (BKO) store_kouter<TS>(sB(buf), rb); else store_kcontig(sB(buf), rb);
+  auto sstore = [&](int b) {
+    if constexpr (AKO) {
+      store_ko<TS, BM, NT>(sA(b), ra_o);
+      if (want_rows) rowsum_ko<TS, BM, NT>(rs, ra_o);
+    } else {
+      store_kc<BM, NT>(sA(b), ra_c);
+    }
+    if constexpr (BKO) store_ko<TS, BN, NT>(sB(b), rb_o);
+    else store_kc<BN, NT>(sB(b), rb_c);
   };
 
-  gload(0);
-  sstore(0);
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+  }
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt & 1;
     if (kt + 1 < nk) gload(kt + 1);
+    const char* A = sA(buf);
+    const char* Bp = sB(buf);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      uint4 a[4], b[4];
+      uint4 a[FM], b[FN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        a[i] = *(const uint4*)(sA(buf) + (wm * 64 + i * 16 + r16) * PITCHB + ks * 64 + q * 16);
-        b[i] = *(const uint4*)(sB(buf) + (wn * 64 + i * 16 + r16) * PITCHB + ks * 64 + q * 16);
-      }
+      for (int i = 0; i < FM; ++i) a[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, ks * 4 + q));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < FN; ++j) b[j] = *(const uint4*)(Bp + lds_off(wn * WN + j * 16 + r16, ks * 4 + q));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mma<TS>(acc[i][j], a[i], b[j]);
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a[i], b[j]);
     }
     if (kt + 1 < nk) sstore(buf ^ 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds rows 4*q+e, column r16 of every 16x16 tile
+  // bias-gradient partial sums of this tile's A rows (k-outer A only)
+  if constexpr (AKO) {
+    if (want_rows) {
+      constexpr int KQ = KO<TS>::KQ, KQD = KO<TS>::KQD;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const long long n = n0 + wn * 64 + j * 16 + r16;
+      for (int i = 0; i < OA; ++i) {
+#pragma unroll
+        for (int e = 0; e < KQ; ++e) {
+          float x = rs[i][e];
+          // the KQD groups of one element block sit on KQD consecutive lanes
+#pragma unroll
+          for (int o = 1; o < KQD; o <<= 1) x += __shfl_xor(x, o, 64);
+          rs[i][e] = x;
+        }
+        const int gi = threadIdx.x + NT * i;
+        const int kq = gi % KQD, mo = gi / KQD;
+        if (kq == 0) {
+#pragma unroll
+          for (int e = 0; e < KQ; ++e) {
+            const long long m = m0 + (long long)mo * KQ + e;
+            if (m < g.M) g.rowsum[(long long)tl.kz * g.M + m] = rs[i][e];
+          }
+        }
+      }
+    }
+  }
+
+  // epilogue: lane holds rows 4q+e, column r16 of every 16x16 tile
+  if (g.ksplit > 1) {
+    float* part = g.part + (long long)tl.kz * g.M * g.N;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const long long n = n0 + wn * WN + j * 16 + r16;
+      if (n >= g.N) continue;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const long long m = m0 + wm * WM + i * 16 + q * 4 + e;
+          if (m < g.M) part[m * g.N + n] = acc[i][j][e];
+        }
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const long long n = n0 + wn * WN + j * 16 + r16;
     if (n >= g.N) continue;
     float bias = 0.f;
     if (g.bias1) {
@@ -159,10 +356,10 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs g) {
       if (g.bias2 && gg != g.bias_skip_gate) bias += to_f(((const TS*)g.bias2)[src]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const long long m = m0 + wm * 64 + i * 16 + q * 4 + e;
+        const long long m = m0 + wm * WM + i * 16 + q * 4 + e;
         if (m >= g.M) continue;
         long long row = m;
         if (g.c_kind == 1) {
@@ -176,6 +373,54 @@ __global__ __launch_bounds__(NTHR) void gemm_kernel(GemmArgs g) {
         *cp = from_f<TS>(v);
       }
     }
+  }
+}
+
+// Split-K finish: C[row(m)][n] (+)= sum_kz part[kz][m][n] (+ bias), in order.
+template <typename TS>
+__global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
+  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= g.M * g.N) return;
+  const long long m = idx / g.N, n = idx - m * g.N;
+  float v = 0.f;
+  for (int kz = 0; kz < g.ksplit; ++kz) v += g.part[(long long)kz * g.M * g.N + idx];
+  if (g.bias1) {
+    const long long gg = n / g.H;
+    const long long src = (long long)g.perm[gg] * g.H + (n - gg * g.H);
+    v += to_f(((const TS*)g.bias1)[src]);
+    if (g.bias2 && gg != g.bias_skip_gate) v += to_f(((const TS*)g.bias2)[src]);
+  }
+  long long row = m;
+  if (g.c_kind == 1) {
+    const long long cm = g.c_row0 + m;
+    const long long gg = cm / g.H;
+    row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
+  }
+  TS* cp = (TS*)g.c + row * g.ldc + n;
+  if (g.accumulate) v += to_f(*cp);
+  *cp = from_f<TS>(v);
+}
+
+// Bias gradients from the per-slice row sums: out[perm(row0+m)] (+)= sum_kz rows[kz][m]
+// (and the same into out2 when the two bias gradients coincide).
+template <typename TS>
+__global__ __launch_bounds__(256) void rowsum_finish(GemmArgs g) {
+  const long long m = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (m >= g.M) return;
+  float v = 0.f;
+  for (int kz = 0; kz < g.ksplit; ++kz) v += g.rowsum[(long long)kz * g.M + m];
+  const long long cm = g.c_row0 + m;
+  const long long gg = cm / g.H;
+  const long long row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
+  TS* o = (TS*)g.rowsum_out + row;
+  float w = v;
+  if (g.accumulate) w += to_f(*o);
+  *o = from_f<TS>(w);
+  if (g.rowsum_out2) {
+    TS* o2 = (TS*)g.rowsum_out2 + row;
+    float w2 = v;
+    if (g.accumulate) w2 += to_f(*o2);
+    *o2 = from_f<TS>(w2);
   }
 }
 
@@ -193,7 +438,9 @@ __global__ __launch_bounds__(256) void colsum_partial(const TS* src, long long l
   partial[(long long)blockIdx.y * ncols + n] = s;
 }
 
-struct Perm4 { int p[4]; };
+struct Perm4 {
+  int p[4];
+};
 
 template <typename TS>
 __global__ __launch_bounds__(256) void colsum_final(const float* partial, int nchunks, int ncols, TS* out,
@@ -214,31 +461,108 @@ __global__ void fill_i32(int* p, int v, long long n) {
   if (i < n) p[i] = v;
 }
 
-}  // namespace
-
-template <typename TS>
-hipError_t launch_gemm(const GemmArgs& g, bool a_kouter, bool b_kouter, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  dim3 grid((unsigned)((g.N + TN - 1) / TN), (unsigned)((g.M + TM - 1) / TM));
-  const size_t lds = 4 * (size_t)TILEB;
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<TS, false, false>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<TS, false, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipFuncSetAttribute((const void*)gemm_kernel<TS, true, true>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    attr_set = true;
+template <typename TS, bool AKO, bool BKO, int BM, int BN>
+hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
+  const void* f = (const void*)gemm_kernel<TS, AKO, BKO, BM, BN>;
+  const int lds = 2 * (BM + BN) * ROWB;
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr = true;
   }
-  if (!a_kouter && !b_kouter) hipLaunchKernelGGL((gemm_kernel<TS, false, false>), grid, dim3(NTHR), lds, s, g);
-  else if (!a_kouter && b_kouter) hipLaunchKernelGGL((gemm_kernel<TS, false, true>), grid, dim3(NTHR), lds, s, g);
-  else if (a_kouter && b_kouter) hipLaunchKernelGGL((gemm_kernel<TS, true, true>), grid, dim3(NTHR), lds, s, g);
-  else return hipErrorInvalidValue;
+  const long long nM = (g.M + BM - 1) / BM, nN = (g.N + BN - 1) / BN;
+  hipLaunchKernelGGL((gemm_kernel<TS, AKO, BKO, BM, BN>), dim3((unsigned)(nM * nN * g.ksplit)),
+                     dim3(Waves<BM, BN>::NT), lds, s, g);
   return hipGetLastError();
 }
 
+template <typename TS, bool AKO, bool BKO>
+hipError_t launch_shape(const GemmArgs& g, int bm, int bn, hipStream_t s) {
+  if (bm == 256 && bn == 256) return launch_tile<TS, AKO, BKO, 256, 256>(g, s);
+  if (bm == 256 && bn == 128) return launch_tile<TS, AKO, BKO, 256, 128>(g, s);
+  return launch_tile<TS, AKO, BKO, 128, 128>(g, s);
+}
+
+}  // namespace
+
+GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long long ws_floats) {
+  GemmPlan p{128, 128, 1, K};
+  const long long t256 = ((M + 255) / 256) * ((N + 255) / 256);
+  const long long t256x128 = ((M + 255) / 256) * ((N + 127) / 128);
+  const long long t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (t256 >= cu_count) {
+    p.bm = p.bn = 256;
+  } else if (K >= 4096 && t256 * 2 <= cu_count && ws_floats > 0) {
+    // few tiles and a long contraction: 256x256 tiles split along K
+    p.bm = p.bn = 256;
+    long long ks = (cu_count + t256 - 1) / t256;
+    if (ks > K / 1024) ks = K / 1024;
+    if (ks > 8) ks = 8;
+    while (ks > 1 && ks * (M * N + M) > ws_floats) --ks;
+    p.ksplit = (int)(ks < 1 ? 1 : ks);
+  } else if (t256x128 >= cu_count) {
+    p.bm = 256;
+    p.bn = 128;
+  } else if (t128 >= cu_count || K < 2048) {
+    p.bm = p.bn = 128;
+  } else {
+    // too few tiles: 256x256 tiles split along K, each slice >= 1024 deep
+    p.bm = p.bn = 256;
+    long long ks = (cu_count + t256 - 1) / t256;
+    const long long maxk = K / 1024;
+    if (ks > maxk) ks = maxk;
+    if (ks > 8) ks = 8;
+    while (ks > 1 && ks * (M * N + M) > ws_floats) --ks;
+    if (ks < 1) ks = 1;
+    p.ksplit = (int)ks;
+  }
+  // slice depth: a multiple of the k-tile (64 elements covers both types)
+  long long sl = (K + p.ksplit - 1) / p.ksplit;
+  sl = (sl + 63) / 64 * 64;
+  p.kslice = sl;
+  return p;
+}
+
+size_t gemm_workspace_floats(long long M, long long N, long long K, int cu_count) {
+  const GemmPlan p = plan_gemm(M, N, K, cu_count, 1LL << 62);
+  return (size_t)p.ksplit * (size_t)(M * N + M);
+}
+
 template <typename TS>
-hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, int ncols, void* out,
-                         int out_row0, int H, const int perm[4], int accumulate, float* partial,
-                         int max_chunks, hipStream_t s) {
+hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_count, hipStream_t s) {
+  if (g0.M <= 0 || g0.N <= 0) return hipSuccess;
+  GemmArgs g = g0;
+  const GemmPlan p = plan_gemm(g.M, g.N, g.K, cu_count, g.part ? g.ws_floats : 0);
+  g.ksplit = p.ksplit;
+  g.kslice = (g.ksplit == 1) ? g.K : p.kslice;
+  if (g.ksplit > 1 && !g.part) return hipErrorInvalidValue;
+  // row sums go to the per-slice buffer after the partial tiles
+  g.rowsum = (g.rowsum_out && g.part) ? g.part + (long long)g.ksplit * g.M * g.N : nullptr;
+  if (g.rowsum_out && !g.rowsum) return hipErrorInvalidValue;
+  if (g.part && (long long)g.ksplit * (g.M * g.N + g.M) > g.ws_floats && (g.ksplit > 1 || g.rowsum_out))
+    return hipErrorInvalidValue;
+  hipError_t e;
+  if (!a_kouter && !b_kouter) e = launch_shape<TS, false, false>(g, p.bm, p.bn, s);
+  else if (!a_kouter && b_kouter) e = launch_shape<TS, false, true>(g, p.bm, p.bn, s);
+  else if (a_kouter && b_kouter) e = launch_shape<TS, true, true>(g, p.bm, p.bn, s);
+  else return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  if (g.ksplit > 1) {
+    const long long n = g.M * g.N;
+    hipLaunchKernelGGL(splitk_finish<TS>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (g.rowsum_out) {
+    hipLaunchKernelGGL(rowsum_finish<TS>, dim3((unsigned)((g.M + 255) / 256)), dim3(256), 0, s, g);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <typename TS>
+hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, int ncols, void* out, int out_row0,
+                         int H, const int perm[4], int accumulate, float* partial, int max_chunks, hipStream_t s) {
   if (ncols <= 0) return hipSuccess;
   long long nch = (M + 255) / 256;
   if (nch > max_chunks) nch = max_chunks;
@@ -260,11 +584,11 @@ hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s) {
   return hipGetLastError();
 }
 
-template hipError_t launch_gemm<float>(const GemmArgs&, bool, bool, hipStream_t);
-template hipError_t launch_gemm<bf16>(const GemmArgs&, bool, bool, hipStream_t);
-template hipError_t launch_colsum<float>(const void*, long long, long long, int, int, void*, int, int,
-                                         const int*, int, float*, int, hipStream_t);
-template hipError_t launch_colsum<bf16>(const void*, long long, long long, int, int, void*, int, int,
-                                        const int*, int, float*, int, hipStream_t);
+template hipError_t launch_gemm<float>(const GemmArgs&, bool, bool, int, hipStream_t);
+template hipError_t launch_gemm<bf16>(const GemmArgs&, bool, bool, int, hipStream_t);
+template hipError_t launch_colsum<float>(const void*, long long, long long, int, int, void*, int, int, const int*,
+                                         int, float*, int, hipStream_t);
+template hipError_t launch_colsum<bf16>(const void*, long long, long long, int, int, void*, int, int, const int*, int,
+                                        float*, int, hipStream_t);
 
 }  // namespace rnn

@@ -33,9 +33,14 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : d->H; }
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, z, c, rh, dg, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, total;
+  size_t gemm_floats;
   int GZ, GD;
 };
+
+// CU count the workspace is sized for (MI355X); a device with more CUs
+// simply splits less when the scratch would not fit
+constexpr int PLAN_CUS = 256;
 
 bool desc_ok(const rnn_desc_t* d) {
   if (!d) return false;
@@ -78,6 +83,19 @@ Layout layout(const rnn_desc_t* d) {
   off += up(2 * FLAG_SLOTS * sizeof(int));
   L.partial = off;
   off += up((size_t)MAX_CHUNKS * 4 * H * sizeof(float));
+  {
+    // GEMM scratch: the largest split-K product (the weight gradients)
+    const long long GH = (long long)gates(d) * d->H;
+    const long long nmax = d->I > d->H ? d->I : d->H;
+    size_t f = rnn::gemm_workspace_floats(GH, nmax, (long long)TB, PLAN_CUS);
+    const size_t f2 = rnn::gemm_workspace_floats((long long)TB, GH, d->I, PLAN_CUS);
+    const size_t f3 = rnn::gemm_workspace_floats((long long)TB, d->I, GH, PLAN_CUS);
+    if (f2 > f) f = f2;
+    if (f3 > f) f = f3;
+    L.gemm = off;
+    L.gemm_floats = f;
+    off += up(f * sizeof(float));
+  }
   L.z = off;
   off += up(TB * L.GZ * H * s);
   L.c = off;
@@ -198,12 +216,11 @@ rnn::RowMap perm_rows(const void* p, long long ld, int H, const int perm[4]) {
   return m;
 }
 
-template <typename TS>
-hipError_t gemm(const rnn::GemmArgs& g, bool ak, bool bk, hipStream_t s) {
-  return rnn::launch_gemm<TS>(g, ak, bk, s);
-}
+int g_cu_count = PLAN_CUS;  // refreshed from the device before every call that launches
+
 hipError_t gemm_dt(int dtype, const rnn::GemmArgs& g, bool ak, bool bk, hipStream_t s) {
-  return dtype == RNN_BF16 ? gemm<bf16>(g, ak, bk, s) : gemm<float>(g, ak, bk, s);
+  return dtype == RNN_BF16 ? rnn::launch_gemm<bf16>(g, ak, bk, g_cu_count, s)
+                           : rnn::launch_gemm<float>(g, ak, bk, g_cu_count, s);
 }
 hipError_t colsum_dt(int dtype, const void* src, long long lds, long long M, int col0, int ncols, void* out,
                      int out_row0, int H, const int perm[4], int acc, float* partial, hipStream_t s) {
@@ -270,6 +287,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
   if ((st = dev_info(&di))) return st;
+  g_cu_count = di.cu;
   const Layout L = layout(d);
   const int cell = cell_of(d);
   rnn::RecPlan plan;
@@ -302,6 +320,8 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   g.bias1 = b_ih;
   g.bias2 = b_hh;
   g.bias_skip_gate = (cell == rnn::CELL_GRU_RA) ? RNN_GATE_C : -1;
+  g.part = (float*)(ws + L.gemm);
+  g.ws_floats = (long long)L.gemm_floats;
   {
     ProfScope ps(L_PROJ, s);
     if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
@@ -347,6 +367,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
   if ((st = dev_info(&di))) return st;
+  g_cu_count = di.cu;
   const Layout L = layout(d);
   const int cell = cell_of(d);
   rnn::RecPlan plan;
@@ -409,6 +430,8 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
     g.ldc = ldx_of(d);
     g.H = d->H;
     g.accumulate = accumulate ? 1 : 0;
+    g.part = (float*)(ws + L.gemm);
+    g.ws_floats = (long long)L.gemm_floats;
     ProfScope ps(L_DX, s);
     if ((st = hip_status(gemm_dt(d->dtype, g, false, true, s)))) return st;
   }
@@ -424,6 +447,9 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  g_cu_count = di.cu;
   const Layout L = layout(d);
   const int cell = cell_of(d);
   hipStream_t s = (hipStream_t)stream;
@@ -439,7 +465,10 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   float* partial = (float*)(ws + L.partial);
   const int acc = accumulate ? 1 : 0;
 
-  auto dW = [&](void* out, long long row0, long long nrows, int dg_col, rnn::RowMap act, long long ncols) {
+  // dW rows [row0, row0+nrows) = dG[:, dg_col..]^T act, plus (optionally)
+  // the bias gradient of the same rows = sum over (t,b) of those dG columns
+  auto dW = [&](void* out, long long row0, long long nrows, int dg_col, rnn::RowMap act, long long ncols,
+                void* bias_out) {
     rnn::GemmArgs g{};
     g.a = rows(dg + dg_col * s_el, GDH);   // k-outer: memory row (t,b), elements along gate rows
     g.b = act;                             // k-outer: memory row (t,b), elements along columns
@@ -453,6 +482,9 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
     g.H = H;
     for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
     g.accumulate = acc;
+    g.part = (float*)(ws + L.gemm);
+    g.ws_floats = (long long)L.gemm_floats;
+    g.rowsum_out = bias_out;
     ProfScope ps(L_DW, s);
     return gemm_dt(d->dtype, g, true, true, s);
   };
@@ -467,28 +499,29 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   hprev.T = d->T;
   hprev.dir = d->direction;
 
-  if (dW_ih && (st = hip_status(dW(dW_ih, 0, (long long)G * H, 0, rows(x, ldx_of(d)), d->I)))) return st;
+  // input side: dW_ih and db_ih from the input-side lanes [0, G*H)
+  if (dW_ih) {
+    if ((st = hip_status(dW(dW_ih, 0, (long long)G * H, 0, rows(x, ldx_of(d)), d->I, db_ih)))) return st;
+  } else if (db_ih) {
+    if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, G * H, db_ih, 0, H, perm, acc, partial, s)))) return st;
+  }
+  // recurrent side: lanes of dG_h (LSTM: all; GRU: r,u, then the candidate rows)
+  const int ccol = (cell == rnn::CELL_GRU_RA) ? 3 * H : 2 * H;  // candidate lane of dG_h
   if (dW_hh) {
     if (cell == rnn::CELL_LSTM) {
-      if ((st = hip_status(dW(dW_hh, 0, 4LL * H, 0, hprev, H)))) return st;
+      if ((st = hip_status(dW(dW_hh, 0, 4LL * H, 0, hprev, H, db_hh)))) return st;
     } else {
-      if ((st = hip_status(dW(dW_hh, 0, 2LL * H, 0, hprev, H)))) return st;
-      if (cell == rnn::CELL_GRU_RA) {
-        if ((st = hip_status(dW(dW_hh, 2LL * H, H, 3 * H, hprev, H)))) return st;
-      } else {
-        if ((st = hip_status(dW(dW_hh, 2LL * H, H, 2 * H, rows(ws + L.rh, H), H)))) return st;
-      }
+      if ((st = hip_status(dW(dW_hh, 0, 2LL * H, 0, hprev, H, db_hh)))) return st;
+      rnn::RowMap cact = (cell == rnn::CELL_GRU_RA) ? hprev : rows(ws + L.rh, H);
+      if ((st = hip_status(dW(dW_hh, 2LL * H, H, ccol, cact, H, db_hh)))) return st;
     }
-  }
-  if (db_ih && (st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, G * H, db_ih, 0, H, perm, acc, partial, s))))
-    return st;
-  if (db_hh) {
-    if (cell == rnn::CELL_GRU_RA) {
-      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, 2 * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
-      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 3 * H, H, db_hh, 2 * H, H, perm, acc, partial, s))))
-        return st;
+  } else if (db_hh) {
+    if (cell == rnn::CELL_LSTM) {
+      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, 4 * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
     } else {
-      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, G * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
+      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, 2 * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
+      if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, ccol, H, db_hh, 2 * H, H, perm, acc, partial, s))))
+        return st;
     }
   }
   return RNN_OK;

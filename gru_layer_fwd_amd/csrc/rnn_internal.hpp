@@ -108,10 +108,29 @@ struct GemmArgs {
   const void* bias1;  // optional: bias1[perm-mapped n] (+ bias2 unless gate == skip)
   const void* bias2;
   int bias_skip_gate;
+  // fp32 scratch: split-K partial tiles [ksplit][M][N], then row sums [ksplit][M]
+  float* part;
+  long long ws_floats;
+  // optional bias gradients = row sums of a k-outer A over k, written like
+  // the rows of C (perm, c_row0); rowsum_out2 receives the same values
+  void* rowsum_out;
+  void* rowsum_out2;
+  // set by the launcher
+  int ksplit;
+  long long kslice;
+  float* rowsum;
 };
 
+struct GemmPlan {
+  int bm, bn, ksplit;
+  long long kslice;
+};
+GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long long ws_floats);
+// fp32 scratch floats the launcher may use for a product of these sizes
+size_t gemm_workspace_floats(long long M, long long N, long long K, int cu_count);
+
 template <typename TS>
-hipError_t launch_gemm(const GemmArgs& g, bool a_kouter, bool b_kouter, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& g, bool a_kouter, bool b_kouter, int cu_count, hipStream_t s);
 
 // column sums: out[mapped n] (+)= sum_m src[m*lds + col0 + n], n < ncols.
 template <typename TS>
