@@ -48,7 +48,7 @@ __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int*
   for (int it = 0;; ++it) {
     bool ok = true;
     for (int i = lane; i < n; i += 64)
-      ok = ok && (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
+      ok = ok && (__hip_atomic_load(f + i * FSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
     if (__all(ok)) break;
     if ((it & 63) == 0) {
       if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
@@ -99,8 +99,9 @@ __device__ __forceinline__ void wg_coords(int nGroups, int nSlices, int& grp, in
 }
 
 // acc[mb][nt] += A[b0+mb*16.., k] . Wr[nt][k] over this wave's k-steps, with
-// A(b, k) = src[b*ld + k + (k >= kshift ? kskip : 0)] (zero when b >= B or
-// src is NULL). The wave owns k-steps [w*KI, w*KI+KI) of the contraction.
+// A(b, k) = src[b*ld + k + (k >= kshift ? kskip : 0)] (zero for rows b >= B,
+// the end of the batch group, or when src is NULL). The wave owns k-steps
+// [w*KI, w*KI+KI) of the contraction.
 template <typename TS, int MB, int NT, int KI>
 __device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const TS* src,
                                          long long ld, int b0, int B, int K, int kshift, int kskip) {
@@ -241,11 +242,12 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
 
   int grp, sl;
   wg_coords(a.nGroups, a.nSlices, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
+  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
-  const int J0 = sl * HS, b0 = grp * BG;
+  const int J0 = sl * HS, b0 = grp * a.bg;
+  const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
 
   uint4 Wr[NT][KI];
@@ -263,7 +265,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     const int unit = tid + u * NTH;
     bl_[u] = unit / HS;
     j_[u] = unit - bl_[u] * HS;
-    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    live[u] = unit < UNITS && b0 + bl_[u] < bend;
     cst[u] = hst[u] = bhc[u] = 0.f;
     const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
     if (live[u]) {
@@ -278,19 +280,21 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     const int tp = a.dir ? t + 1 : t - 1;
     // projected inputs of this step do not depend on the exchange: their
     // loads are issued before the wait and land while it polls
+    // (unconditional loads from a valid address: a branch per load would
+    // make the compiler wait for each one on the spot)
     TS pz[UPT][GL];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const TS* zr = (const TS*)a.z + ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u];
+      const TS* zr = (const TS*)a.z + (live[u] ? ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
 #pragma unroll
-      for (int g = 0; g < GL; ++g) pz[u][g] = live[u] ? zr[g * H] : from_f<TS>(0.f);
+      for (int g = 0; g < GL; ++g) pz[u][g] = zr[g * H];
     }
     if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
     f4 acc[MB][NT];
     zero_acc(acc);
     const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
     const long long ld = (s == 0) ? H : a.ldy;
-    contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, B, H, 1 << 30, 0);
+    contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, bend, H, 1 << 30, 0);
     spill_acc(red, acc);
     __syncthreads();
 #pragma unroll
@@ -348,11 +352,12 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
 
   int grp, sl;
   wg_coords(a.nGroups, a.nSlices, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
+  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
-  const int J0 = sl * HS, b0 = grp * BG;
+  const int J0 = sl * HS, b0 = grp * a.bg;
+  const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
 
   uint4 WA[NTA][KI], WB[NTB][KI];
@@ -371,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
     const int unit = tid + u * NTH;
     bl_[u] = unit / HS;
     j_[u] = unit - bl_[u] * HS;
-    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    live[u] = unit < UNITS && b0 + bl_[u] < bend;
     hst[u] = ust[u] = 0.f;
     if (live[u] && a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
@@ -382,9 +387,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
     TS pz[UPT][3];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const TS* zr = (const TS*)a.z + ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u];
+      const TS* zr = (const TS*)a.z + (live[u] ? ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
 #pragma unroll
-      for (int g = 0; g < 3; ++g) pz[u][g] = live[u] ? zr[g * H] : from_f<TS>(0.f);
+      for (int g = 0; g < 3; ++g) pz[u][g] = zr[g * H];
     }
     // phase A: r, u
     if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks);
@@ -393,7 +398,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       zero_acc(acc);
       const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
       const long long ld = (s == 0) ? H : a.ldy;
-      contract<TS, MB, NTA, KI>(acc, WA, src, ld, b0, B, H, 1 << 30, 0);
+      contract<TS, MB, NTA, KI>(acc, WA, src, ld, b0, bend, H, 1 << 30, 0);
       spill_acc(red, acc);
     }
     __syncthreads();
@@ -415,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
     {
       f4 acc[MB][NTB];
       zero_acc(acc);
-      contract<TS, MB, NTB, KI>(acc, WB, (const TS*)a.rh + (long long)t * B * H, H, b0, B, H, 1 << 30, 0);
+      contract<TS, MB, NTB, KI>(acc, WB, (const TS*)a.rh + (long long)t * B * H, H, b0, bend, H, 1 << 30, 0);
       spill_acc(red, acc);
     }
     __syncthreads();
@@ -450,11 +455,12 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
 
   int grp, sl;
   wg_coords(a.nGroups, a.nSlices, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
+  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
-  const int J0 = sl * HS, b0 = grp * BG;
+  const int J0 = sl * HS, b0 = grp * a.bg;
+  const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
   const int K = GK * H;
   // GRU: lanes r, u, then the recurrent candidate lane d_c*r stored in lane 3
@@ -472,7 +478,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     const int unit = tid + u * NTH;
     bl_[u] = unit / HS;
     j_[u] = unit - bl_[u] * HS;
-    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    live[u] = unit < UNITS && b0 + bl_[u] < bend;
     dcar[u] = hcar[u] = 0.f;
     const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
     if (live[u]) {
@@ -487,26 +493,32 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     const int tp = a.dir ? t + 1 : t - 1;
     // own-unit operands of the step (independent of the exchange), loaded
     // ahead of the wait: dy, saved gates, cell states / previous output
+    // (unconditional loads from valid addresses; `on` selects at use)
     TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT];
+    bool pvalid[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const bool on = live[u] && n < T;
-      const long long row = (long long)t * B + b0 + bl_[u];
-      const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
-      const TS* zr = (const TS*)a.z + row * GZH + J0 + j_[u];
-      pdy[u] = on ? ((const TS*)a.dy)[row * a.ldy + J0 + j_[u]] : from_f<TS>(0.f);
+      const long long row = on ? (long long)t * B + b0 + bl_[u] : 0;
+      const long long o = on ? (long long)(b0 + bl_[u]) * H + J0 + j_[u] : 0;
+      const int jj = on ? J0 + j_[u] : 0;
+      const TS* zr = (const TS*)a.z + row * GZH + jj;
+      pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) pz[u][g] = on ? zr[g * H] : from_f<TS>(0.f);
+      for (int g = 0; g < 4; ++g) pz[u][g] = zr[g * H];
+      const bool first = (s == 0);
       if constexpr (CELL == CELL_LSTM) {
-        pc[u] = on ? ((const TS*)a.cbuf)[row * H + J0 + j_[u]] : from_f<TS>(0.f);
-        const TS* cprev = (s == 0) ? (const TS*)a.c0 + o
-                                   : (const TS*)a.cbuf + ((long long)tp * B + b0 + bl_[u]) * H + J0 + j_[u];
-        pprev[u] = (on && (s > 0 || a.c0)) ? *cprev : from_f<TS>(0.f);
+        pc[u] = ((const TS*)a.cbuf)[row * H + jj];
+        pvalid[u] = on && (!first || a.c0);
+        const TS* cprev = (first && a.c0) ? (const TS*)a.c0 + o
+                        : (const TS*)a.cbuf + (first || !on ? 0 : ((long long)tp * B + b0 + bl_[u]) * H + jj);
+        pprev[u] = *cprev;
       } else {
         pc[u] = from_f<TS>(0.f);
-        const TS* hprev = (s == 0) ? (const TS*)a.h0 + o
-                                   : (const TS*)a.y + ((long long)tp * B + b0 + bl_[u]) * a.ldy + J0 + j_[u];
-        pprev[u] = (on && (s > 0 || a.h0)) ? *hprev : from_f<TS>(0.f);
+        pvalid[u] = on && (!first || a.h0);
+        const TS* hprev = (first && a.h0) ? (const TS*)a.h0 + o
+                        : (const TS*)a.y + (first || !on ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
+        pprev[u] = *hprev;
       }
     }
     f4 acc[MB][NT];
@@ -514,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     if (n > 0) {
       wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks);
       const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
-      contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, B, K, kshift,
+      contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
                                kskip);
     }
     spill_acc(red, acc);
@@ -538,7 +550,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
       if constexpr (CELL == CELL_LSTM) {
         const float ig = to_f(pz[u][0]), fg = to_f(pz[u][1]), gg = to_f(pz[u][2]), og = to_f(pz[u][3]);
-        const float c = to_f(pc[u]), cp = to_f(pprev[u]);
+        const float c = to_f(pc[u]), cp = pvalid[u] ? to_f(pprev[u]) : 0.f;
         const float tc = tanhf_(c);
         const float d_o = dh * tc * og * (1.f - og);
         const float dc = dh * og * (1.f - tc * tc) + dcar[u];
@@ -553,7 +565,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         xstore(gr + 3 * H, d_o);
       } else {
         const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]), nh = to_f(pz[u][3]);
-        const float hp = to_f(pprev[u]);
+        const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
         const float d_c = dh * (1.f - uu) * (1.f - c * c);
         const float d_u = dh * (hp - c) * uu * (1.f - uu);
         const float d_r = d_c * nh * r * (1.f - r);
@@ -580,11 +592,12 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
 
   int grp, sl;
   wg_coords(a.nGroups, a.nSlices, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
+  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
-  const int J0 = sl * HS, b0 = grp * BG;
+  const int J0 = sl * HS, b0 = grp * a.bg;
+  const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
 
   uint4 WA[NT][KIA], WB[NT][KIB];
@@ -599,7 +612,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     const int unit = tid + u * NTH;
     bl_[u] = unit / HS;
     j_[u] = unit - bl_[u] * HS;
-    live[u] = unit < UNITS && b0 + bl_[u] < B;
+    live[u] = unit < UNITS && b0 + bl_[u] < bend;
     hcar[u] = dhs[u] = rs[u] = us[u] = hps[u] = 0.f;
     if (live[u] && a.dhT) hcar[u] = to_f(((const TS*)a.dhT)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
@@ -609,17 +622,21 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
     TS pdy[UPT], pz[UPT][3], pprev[UPT];
+    bool pvalid[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const bool on = live[u] && n < T;
-      const long long row = (long long)t * B + b0 + bl_[u];
-      const TS* zr = (const TS*)a.z + row * GZH + J0 + j_[u];
-      pdy[u] = on ? ((const TS*)a.dy)[row * a.ldy + J0 + j_[u]] : from_f<TS>(0.f);
+      const long long row = on ? (long long)t * B + b0 + bl_[u] : 0;
+      const int jj = on ? J0 + j_[u] : 0;
+      const TS* zr = (const TS*)a.z + row * GZH + jj;
+      pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
 #pragma unroll
-      for (int g = 0; g < 3; ++g) pz[u][g] = on ? zr[g * H] : from_f<TS>(0.f);
-      const TS* hprev = (s == 0) ? (const TS*)a.h0 + (long long)(b0 + bl_[u]) * H + J0 + j_[u]
-                                 : (const TS*)a.y + ((long long)tp * B + b0 + bl_[u]) * a.ldy + J0 + j_[u];
-      pprev[u] = (on && (s > 0 || a.h0)) ? *hprev : from_f<TS>(0.f);
+      for (int g = 0; g < 3; ++g) pz[u][g] = zr[g * H];
+      const bool first = (s == 0);
+      pvalid[u] = on && (!first || a.h0);
+      const TS* hprev = (first && a.h0) ? (const TS*)a.h0 + (on ? (long long)(b0 + bl_[u]) * H + jj : 0)
+                      : (const TS*)a.y + (first || !on ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
+      pprev[u] = *hprev;
     }
     {
       f4 acc[MB][NT];
@@ -627,7 +644,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       if (n > 0) {
         wait_flags(gflags, a.nSlices, 2 * n, a.status, a.timeout_ticks);
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);
-        contract<TS, MB, NT, KIA>(acc, WA, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, B, 2 * H, 1 << 30,
+        contract<TS, MB, NT, KIA>(acc, WA, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, 2 * H, 1 << 30,
                                   0);
       }
       spill_acc(red, acc);
@@ -648,7 +665,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const long long row = (long long)t * B + b0 + bl_[u];
       const float dh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + to_f(pdy[u]) + hcar[u];
       const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]);
-      const float hp = to_f(pprev[u]);
+      const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
       const float d_c = dh * (1.f - uu) * (1.f - c * c);
       const float d_u = dh * (hp - c) * uu * (1.f - uu);
       TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
@@ -664,7 +681,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     {
       f4 acc[MB][NT];
       zero_acc(acc);
-      contract<TS, MB, NT, KIB>(acc, WB, (const TS*)a.dg + (long long)t * B * GDH + 2 * H, GDH, b0, B, H, 1 << 30,
+      contract<TS, MB, NT, KIB>(acc, WB, (const TS*)a.dg + (long long)t * B * GDH + 2 * H, GDH, b0, bend, H, 1 << 30,
                                 0);
       spill_acc(red, acc);
     }
@@ -698,11 +715,14 @@ const Entry kTable[] = {
     // forward LSTM
     {CELL_LSTM, 1, 1, 4, 1, 4, 8, 0, F_LSTM(bf16, 4, 1, 4, 8)},
     {CELL_LSTM, 1, 1, 4, 1, 1, 8, 0, F_LSTM(bf16, 4, 1, 1, 8)},
+    {CELL_LSTM, 1, 1, 8, 1, 8, 4, 0, F_LSTM(bf16, 8, 1, 8, 4)},
     {CELL_LSTM, 1, 1, 4, 8, 2, 16, 0, F_LSTM(bf16, 4, 8, 2, 16)},
     {CELL_LSTM, 0, 1, 4, 1, 4, 8, 0, F_LSTM(float, 4, 1, 4, 8)},
     {CELL_LSTM, 0, 1, 4, 1, 1, 8, 0, F_LSTM(float, 4, 1, 1, 8)},
+    {CELL_LSTM, 0, 1, 8, 1, 4, 4, 0, F_LSTM(float, 8, 1, 4, 4)},
     // forward reset-after GRU
     {CELL_GRU_RA, 1, 1, 4, 1, 3, 8, 0, F_GRA(bf16, 4, 1, 3, 8)},
+    {CELL_GRU_RA, 1, 1, 8, 1, 6, 4, 0, F_GRA(bf16, 8, 1, 6, 4)},
     {CELL_GRU_RA, 1, 1, 8, 4, 3, 8, 0, F_GRA(bf16, 8, 4, 3, 8)},
     {CELL_GRU_RA, 0, 1, 4, 1, 3, 8, 0, F_GRA(float, 4, 1, 3, 8)},
     // forward basic GRU (nt = candidate tiles)
@@ -710,10 +730,13 @@ const Entry kTable[] = {
     {CELL_GRU_BASIC, 0, 1, 4, 1, 1, 8, 0, (const void*)rec_fwd_grub<float, 4, 1, 1, 8>},
     // backward LSTM
     {CELL_LSTM, 1, 0, 4, 1, 1, 32, 0, B_LSTM(bf16, 4, 1, 1, 32)},
+    {CELL_LSTM, 1, 0, 8, 1, 2, 16, 0, B_LSTM(bf16, 8, 1, 2, 16)},
     {CELL_LSTM, 1, 0, 8, 4, 1, 32, 0, B_LSTM(bf16, 8, 4, 1, 32)},
     {CELL_LSTM, 0, 0, 4, 1, 1, 32, 0, B_LSTM(float, 4, 1, 1, 32)},
+    {CELL_LSTM, 0, 0, 8, 1, 1, 16, 0, B_LSTM(float, 8, 1, 1, 16)},
     // backward reset-after GRU
     {CELL_GRU_RA, 1, 0, 4, 1, 1, 32, 0, B_GRA(bf16, 4, 1, 1, 32)},
+    {CELL_GRU_RA, 1, 0, 8, 1, 2, 16, 0, B_GRA(bf16, 8, 1, 2, 16)},
     {CELL_GRU_RA, 1, 0, 8, 4, 1, 32, 0, B_GRA(bf16, 8, 4, 1, 32)},
     {CELL_GRU_RA, 0, 0, 4, 1, 1, 32, 0, B_GRA(float, 4, 1, 1, 32)},
     // backward basic GRU (ki = phase A k-steps, kib = phase B)
@@ -735,8 +758,39 @@ size_t lds_of(const Entry& e) {
   return (size_t)e.nw * e.mb * 16 * ncol * sizeof(float);
 }
 
+// XCDs a batch group of `slices` workgroups covers under wg_coords: with
+// nwg % 8 == 0 each XCD holds nwg/8 consecutive slots, otherwise slots are
+// spread round-robin.
+int xcd_span(long long nwg, int slices) {
+  if (nwg % 8 == 0) {
+    const long long per = nwg / 8;
+    return (int)((slices + per - 1) / per);
+  }
+  return slices < 8 ? slices : 8;
+}
+
+// Modelled time of one step (us), from measurements of the exchange on
+// MI355X: a counter handshake costs ~0.8 us when a batch group sits on one
+// XCD, ~1.8 us across two and ~3.5 us beyond; the exchanged vector streams at
+// ~5 TB/s through the device coherence point; MFMA issue per SIMD at 16
+// (bf16 16x16x32) or 128 (four fp32 16x16x4) cycles per k-step and tile,
+// 2.4 GHz.
+double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize) {
+  const int span = xcd_span((long long)groups * slices, slices);
+  const double hand = span <= 1 ? 0.8 : (span <= 2 ? 1.8 : 3.5);
+  const int phases = (e.cell == CELL_GRU_BASIC) ? 2 : 1;
+  const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
+  const double waves_per_simd = e.nw / 4.0;
+  const double cyc = (kstep == 32) ? 16.0 : 128.0;
+  const double mfma = e.mb * e.nt * kused * waves_per_simd * cyc / 2400.0;
+  const double bytes = (double)groups * slices * bg * K * esize;
+  const double data = bytes / 5.0e6;
+  return phases * hand + mfma + data;
+}
+
 bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p) {
   const int kstep = dtype ? 32 : 16;
+  const int esize = dtype ? 2 : 4;
   double best = 1e300;
   bool found = false;
   for (const Entry& e : kTable) {
@@ -748,18 +802,21 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p
     if (!fwd) K = (cell == CELL_LSTM) ? 4 * H : (cell == CELL_GRU_RA ? 3 * H : 2 * H);
     if ((long long)e.nw * e.ki * kstep < K) continue;
     if (cell == CELL_GRU_BASIC && !fwd && (long long)e.nw * e.kib * kstep < H) continue;
-    const int bg = e.mb * 16;
-    const int groups = (B + bg - 1) / bg;
-    const long long nwg = (long long)groups * (H / hs);
-    RecPlan cand{e.nw, e.mb, e.nt, e.ki, hs, groups, H / hs, e.func, lds_of(e)};
-    if (nwg > cu_count) continue;  // at most one persistent workgroup per CU
-    // cost: MFMA issue per SIMD per step, waves sharing a SIMD serialise
-    const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
-    const double cost = (double)e.mb * e.nt * kused * (e.nw > 4 ? e.nw / 4.0 : 1.0) + 1e-3 * nwg;
-    if (cost < best) {
-      best = cost;
-      *p = cand;
-      found = true;
+    const int rows = e.mb * 16;
+    // batch rows per group: the full MFMA tile, or half of it (more, smaller
+    // groups: shorter handshakes, half the rows of the tile idle)
+    for (int bg : {rows, rows / 2, rows / 4}) {
+      if (bg < 4 || (bg != rows && e.mb != 1)) continue;
+      const int groups = (B + bg - 1) / bg;
+      const int slices = H / hs;
+      const long long nwg = (long long)groups * slices;
+      if (nwg > cu_count) continue;  // at most one persistent workgroup per CU
+      const double cost = step_cost(e, bg, groups, slices, K, kstep, esize);
+      if (cost < best) {
+        best = cost;
+        *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e)};
+        found = true;
+      }
     }
   }
   return found;

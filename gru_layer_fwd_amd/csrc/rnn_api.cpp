@@ -17,7 +17,7 @@ namespace {
 using rnn::bf16;
 
 constexpr size_t ALIGN = 256;
-constexpr int FLAG_SLOTS = 4096;   // per region; >= persistent workgroups
+constexpr int FLAG_SLOTS = 1024;   // per region; >= persistent workgroups (one counter line each)
 constexpr int MAX_CHUNKS = 64;     // bias-gradient partial sums
 constexpr double TIMEOUT_S = 10.0;
 
@@ -80,7 +80,7 @@ Layout layout(const rnn_desc_t* d) {
   L.status = off;
   off += ALIGN;
   L.flags = off;
-  off += up(2 * FLAG_SLOTS * sizeof(int));
+  off += up(2 * (size_t)FLAG_SLOTS * rnn::FSTRIDE * sizeof(int));
   L.partial = off;
   off += up((size_t)MAX_CHUNKS * 4 * H * sizeof(float));
   {
@@ -240,8 +240,10 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecArgs& a, const DevInf
     return RNN_ERR_UNSUPPORTED;
   }
   if (log_on())
-    fprintf(stderr, "[rnn] %s: %d groups x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu\n", what,
-            p.nGroups, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki, p.lds_bytes);
+    fprintf(stderr,
+            "[rnn] %s: %d groups of %d rows x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu, "
+            "model %.2f us/step\n",
+            what, p.nGroups, p.bg, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki, p.lds_bytes, p.cost_us);
   hipError_t e = rnn::launch_rec(p, a, s);
   if (e != hipSuccess) {
     if (log_on()) fprintf(stderr, "[rnn] %s: launch failed: %s\n", what, hipGetErrorString(e));
@@ -302,7 +304,9 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   {
     ProfScope ps(L_FILL, s);
     if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
-    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.flags), 0, FLAG_SLOTS, s)))) return st;
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.flags), 0,
+                                              (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE, s))))
+      return st;
   }
 
   // input projection for every step: Z[t,b][g*H+j] = x . W_ih[g,j] + biases
@@ -335,6 +339,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.nGroups = plan.nGroups;
   a.nSlices = plan.nSlices;
   a.Hs = plan.Hs;
+  a.bg = plan.bg;
   for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
   a.W_hh = W_hh;
   a.b_hh = b_hh;
@@ -377,12 +382,14 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   int perm[4];
   inv_perm(d, perm);
   const int G = gates(d);
-  int* flags = (int*)(ws + L.flags) + FLAG_SLOTS;
+  int* flags = (int*)(ws + L.flags) + FLAG_SLOTS * rnn::FSTRIDE;
 
   {
     ProfScope ps(L_FILL, s);
     if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
-    if ((st = hip_status(rnn::launch_fill_i32(flags, 0, FLAG_SLOTS, s)))) return st;
+    if ((st = hip_status(
+             rnn::launch_fill_i32(flags, 0, (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE, s))))
+      return st;
   }
 
   rnn::RecArgs a{};
@@ -393,6 +400,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   a.nGroups = plan.nGroups;
   a.nSlices = plan.nSlices;
   a.Hs = plan.Hs;
+  a.bg = plan.bg;
   for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
   a.W_hh = W_hh;
   a.h0 = h0;

@@ -141,9 +141,13 @@ hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, 
 hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 
 // ------------------------------------------------- persistent recurrences --
+// step counters sit on their own 128-byte lines (stride in ints)
+constexpr int FSTRIDE = 32;
+
 struct RecArgs {
   int T, B, H, dir;
   int nGroups, nSlices, Hs;
+  int bg;           // batch rows per group (<= the MFMA rows of the kernel)
   int perm[4];
   const void* W_hh;
   const void* b_hh;
@@ -173,6 +177,8 @@ struct RecArgs {
 struct RecPlan {
   int nw, mb, nt, ki;   // waves per WG, 16-row batch tiles, 16-col output tiles, k-steps per wave
   int Hs, nGroups, nSlices;
+  int bg;               // batch rows per group
+  double cost_us;       // modelled time per step
   const void* func;
   size_t lds_bytes;
 };
