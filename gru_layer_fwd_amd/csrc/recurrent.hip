@@ -156,18 +156,22 @@ __device__ __forceinline__ void zero_acc(f4 (&acc)[MB][NT]) {
     for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = f4{0.f, 0.f, 0.f, 0.f};
 }
 
-// Partial products of every wave to LDS: red[w][row][col], row < BG, col < NCOL.
+// Partial products of every wave to LDS: red[w][row][col], row < BG, col < NCOL
+// (rows at or past `rows`, the padding of a batch group smaller than the
+// MFMA tile, are not written: nothing reads them).
 template <int MB, int NT>
-__device__ __forceinline__ void spill_acc(float* red, const f4 (&acc)[MB][NT]) {
+__device__ __forceinline__ void spill_acc(float* red, const f4 (&acc)[MB][NT], int rows) {
   constexpr int BG = MB * 16, NCOL = NT * 16;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb)
+  for (int mb = 0; mb < MB; ++mb) {
+    if (mb * 16 + q * 4 >= rows) continue;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[(w * BG + mb * 16 + q * 4 + e) * NCOL + nt * 16 + r16] = acc[mb][nt][e];
+  }
 }
 
 template <int NW, int BG, int NCOL>
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
     const long long ld = (s == 0) ? H : a.ldy;
     contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, bend, H, 1 << 30, 0);
-    spill_acc(red, acc);
+    spill_acc(red, acc, bend - b0);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
       const long long ld = (s == 0) ? H : a.ldy;
       contract<TS, MB, NTA, KI>(acc, WA, src, ld, b0, bend, H, 1 << 30, 0);
-      spill_acc(red, acc);
+      spill_acc(red, acc, bend - b0);
     }
     __syncthreads();
 #pragma unroll
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       f4 acc[MB][NTB];
       zero_acc(acc);
       contract<TS, MB, NTB, KI>(acc, WB, (const TS*)a.rh + (long long)t * B * H, H, b0, bend, H, 1 << 30, 0);
-      spill_acc(red, acc);
+      spill_acc(red, acc, bend - b0);
     }
     __syncthreads();
 #pragma unroll
@@ -529,7 +533,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
                                kskip);
     }
-    spill_acc(red, acc);
+    spill_acc(red, acc, bend - b0);
     __syncthreads();
     if (n == T) {
 #pragma unroll
@@ -647,7 +651,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
         contract<TS, MB, NT, KIA>(acc, WA, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, 2 * H, 1 << 30,
                                   0);
       }
-      spill_acc(red, acc);
+      spill_acc(red, acc, bend - b0);
     }
     __syncthreads();
     if (n == T) {
@@ -683,7 +687,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       zero_acc(acc);
       contract<TS, MB, NT, KIB>(acc, WB, (const TS*)a.dg + (long long)t * B * GDH + 2 * H, GDH, b0, bend, H, 1 << 30,
                                 0);
-      spill_acc(red, acc);
+      spill_acc(red, acc, bend - b0);
     }
     __syncthreads();
 #pragma unroll

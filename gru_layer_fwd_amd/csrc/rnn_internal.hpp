@@ -50,10 +50,12 @@ __device__ __forceinline__ void mma(f4& acc, const uint4& a, const uint4& b) {
   mma_step(acc, a, b, (TS*)nullptr);
 }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// Logistic sigmoid and tanh from the hardware exponential and reciprocal
+// (v_exp_f32, v_rcp_f32: about 1 ulp each); tanh(z) = 2*sigmoid(2z) - 1,
+// which saturates cleanly for large |z|.
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float tanhf_(float z) {
-  // tanh(z) = 2*sigmoid(2z) - 1, saturating cleanly for large |z|
-  return 2.0f / (1.0f + __expf(-2.0f * z)) - 1.0f;
+  return 2.0f * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * z)) - 1.0f;
 }
 
 // -------------------------------------------------------------- row maps --
