@@ -14,12 +14,24 @@
 // Exchange. The only data that crosses workgroups is the recurrent vector of
 // a step (forward: h_t, backward: the gate gradients dG_t), which every
 // workgroup of the batch group reads in full at the next step. Producers
-// store it to HBM, release it at agent scope and publish a per-workgroup step
-// counter; consumers poll the counters of their group (one coalesced load per
-// wave), acquire, and then read the vector. The CUDA fragment's kernel waits
-// on the data itself (a -0.0 sentinel) with no bound; here every wait is
-// bounded by a wall-clock time-out that sets a status word, after which all
-// waits are skipped so that every wave still runs to the end of the grid.
+// store it, wait until their stores are acknowledged and publish a
+// per-workgroup step counter; consumers poll the counters of their group
+// (one coalesced load per wave) and then read the vector. The CUDA
+// fragment's kernel waits on the data itself (a -0.0 sentinel) with no
+// bound; here every wait is bounded by a wall-clock time-out that sets a
+// status word, after which all waits are skipped so that every wave still
+// runs to the end of the grid.
+//
+// Coherence point. Each XCD has its own L2, which is coherent for the CUs of
+// that XCD: a plain store is acknowledged once it sits in the L2, and a load
+// with the device-scope bit (sc1) skips the CU's L1 and is served by the
+// L2. A batch group whose workgroups all run on one XCD therefore exchanges
+// through its L2 (plain stores, sc1 loads). At launch every workgroup
+// publishes its XCC id with a device-scope store and reads those of its
+// group; only when they all match does the group use the L2 path. Otherwise
+// it falls back to device-scope stores, which write through to memory and
+// are seen by sc1 loads from any XCD. No whole-cache write-back or
+// invalidate is issued per step.
 //
 // Equations (canonical gate order, fp32 arithmetic, storage rounding on
 // store): LSTM popnn Lstm.cpp "basicLstmCellForwardPass" and
@@ -34,14 +46,11 @@ namespace {
 
 constexpr int ST_TIMEOUT = -5;
 
-// Coherence of the exchanged vectors is kept per access, not per cache: the
-// producer writes them with device-scope stores (write-through past the
-// per-XCD L2s), waits until its stores are acknowledged, and only then
-// publishes its step counter; consumers poll counters with device-scope loads
-// and read the vector with device-scope loads (never served by a stale L2
-// line). No whole-cache write-back or invalidate is issued per step. Data
-// that only the owning workgroup or a later kernel reads (saved gates, cell
-// states) uses ordinary stores.
+// Step counters and exchanged vectors are read with device-scope (sc1)
+// loads: they skip the CU's L1 and never return a stale line. Writers use
+// plain stores when the whole batch group shares one XCD's L2 (`local`) and
+// device-scope stores otherwise. Data that only the owning workgroup or a
+// later kernel reads (saved gates, cell states) always uses plain stores.
 __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout) {
   const int lane = threadIdx.x & 63;
   long long t0 = 0;
@@ -66,21 +75,44 @@ __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int*
   asm volatile("" ::: "memory");
 }
 
-// Every wave waits for its device-scope stores to be acknowledged, the
-// workgroup meets, then one thread publishes the step counter.
-__device__ __forceinline__ void publish(int* f, int v) {
+// Every wave waits for its stores of the exchanged vector to be
+// acknowledged, the workgroup meets, then one thread publishes the step
+// counter.
+__device__ __forceinline__ void publish(int* f, int v, bool local) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) {
+    if (local) *f = v;
+    else __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-// device-scope store of one exchanged element
-__device__ __forceinline__ void xstore(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// store of one exchanged element: plain within one XCD, device scope across
+__device__ __forceinline__ void xstore(float* p, float v, bool local) {
+  if (local) *p = v;
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void xstore(bf16* p, float v) {
-  __hip_atomic_store((unsigned short*)p, __builtin_bit_cast(unsigned short, (bf16)v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void xstore(bf16* p, float v, bool local) {
+  const unsigned short u = __builtin_bit_cast(unsigned short, (bf16)v);
+  if (local) *(unsigned short*)p = u;
+  else __hip_atomic_store((unsigned short*)p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Placement check at launch: every workgroup publishes 1 + its XCC id in the
+// second word of its counter line with a device-scope store, waits (device
+// scope) until all members of its batch group have done so and compares.
+// Every wave reads the same published values, so the whole group agrees.
+__device__ __forceinline__ bool group_is_local(int* myflag, const int* gflags, int n, int* status,
+                                               long long timeout) {
+  int x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  x = (x & 15) + 1;
+  if (threadIdx.x == 0) __hip_atomic_store(myflag + 1, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_flags(gflags + 1, n, 1, status, timeout);
+  bool same = true;
+  for (int i = threadIdx.x & 63; i < n; i += 64)
+    same = same && (__hip_atomic_load(gflags + i * FSTRIDE + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == x);
+  return __all(same);
 }
 
 constexpr int BUF_RSRC_W3 = 0x00020000;  // buffer resource word 3 for the gfx9 family
@@ -98,6 +130,81 @@ __device__ __forceinline__ void wg_coords(int nGroups, int nSlices, int& grp, in
   sl = L - grp * nSlices;
 }
 
+// Exchange ring. A consumer wave reads the vector of the previous step as
+// MFMA A operands: for k-step ks, lane (r16, q) needs row r16 and the q-th
+// 16-byte chunk of the k-step. Read from y or dg rows directly, one load
+// instruction touches 16 rows a full row pitch apart; in the ring every
+// operand tile is stored as 64 consecutive 16-byte chunks in lane order, so
+// that each load instruction reads 1 KiB contiguously. With at most 8 live
+// rows a tile holds two k-steps: lanes 0..7 of every 16 carry k-step 2p and
+// lanes 8..15 k-step 2p+1 of the same rows; the second operand is the same
+// register rotated by 8 lanes within each row of 16 (DPP row_ror:8), and
+// output rows 8..15, which the rotation fills with the other k-step, are
+// never read. Producers store their own units into the tiles (two slots,
+// alternating by step: a slot is rewritten two steps later, after every
+// consumer has published the step that read it).
+template <typename TS>
+__device__ __forceinline__ int xoff(int row, int kg, bool packed) {
+  constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
+  const int ks = kg / KSTEP, e = kg - ks * KSTEP, q = e / KQ, el = e - q * KQ;
+  const int lane = (packed ? row + 8 * (ks & 1) : row) + 16 * q;
+  const int tile = packed ? (ks >> 1) : ks;
+  return tile * 1024 + lane * 16 + el * (int)sizeof(TS);
+}
+
+__device__ __forceinline__ unsigned rot8(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+}
+__device__ __forceinline__ uint4 rot8(const uint4& v) { return make_uint4(rot8(v.x), rot8(v.y), rot8(v.z), rot8(v.w)); }
+
+// acc[0][nt] += (previous step's vector, k-steps [w*KI, w*KI+KI)) . Wr[nt][.]
+// from the exchange ring tile `xb` of this group (nbytes valid; loads past it
+// return zero).
+template <typename TS, int NT, int KI>
+__device__ __forceinline__ void contract_x(f4 (&acc)[1][NT], const uint4 (&Wr)[NT][KI], const char* xb, int nbytes,
+                                           bool packed) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, nbytes, BUF_RSRC_W3);
+  if constexpr (KI % 2 == 0) {
+    if (packed) {
+    constexpr int NL = KI / 2;
+    uint4 v[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, ((w * KI) / 2 + i) * 1024 + lane * 16, 0, CPOL_SC1);
+      v[i] = make_uint4(r[0], r[1], r[2], r[3]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+      const uint4 odd = rot8(v[i]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], v[i], Wr[nt][2 * i]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], odd, Wr[nt][2 * i + 1]);
+    }
+    return;
+    }
+  }
+  {
+    constexpr int KB = KI < 16 ? KI : 16;
+#pragma unroll
+    for (int k0 = 0; k0 < KI; k0 += KB) {
+      uint4 v[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, (w * KI + k0 + i) * 1024 + lane * 16, 0, CPOL_SC1);
+        v[i] = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < KB; ++i)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], v[i], Wr[nt][k0 + i]);
+    }
+  }
+}
+
 // acc[mb][nt] += A[b0+mb*16.., k] . Wr[nt][k] over this wave's k-steps, with
 // A(b, k) = src[b*ld + k + (k >= kshift ? kskip : 0)] (zero for rows b >= B,
 // the end of the batch group, or when src is NULL). The wave owns k-steps
@@ -106,7 +213,8 @@ template <typename TS, int MB, int NT, int KI>
 __device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const TS* src,
                                          long long ld, int b0, int B, int K, int kshift, int kskip) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
-  constexpr int KB = (MB >= 8) ? 2 : (MB >= 4 ? 4 : (KI < 8 ? KI : 8));  // k-steps per load batch
+  // k-steps per load batch: every load of the step at once where registers allow
+  constexpr int KB = (MB >= 8) ? 2 : (MB >= 4 ? 4 : (KI <= 16 ? KI : 16));
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   if (src == nullptr) return;
@@ -248,11 +356,17 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
   wg_coords(a.nGroups, a.nSlices, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
+  // exchange ring (single row-tile plans)
+  const bool tiled = (MB == 1) && a.xbuf != nullptr;
+  const bool packed = a.xpacked != 0;
+  const int xbytes = H * (packed ? 8 : 16) * (int)sizeof(TS);
+  auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
   load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, [&](int col) -> long long {
@@ -296,9 +410,14 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
     f4 acc[MB][NT];
     zero_acc(acc);
-    const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
-    const long long ld = (s == 0) ? H : a.ldy;
-    contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, bend, H, 1 << 30, 0);
+    if constexpr (MB == 1) {
+      if (tiled && s > 0) contract_x<TS, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
+    }
+    if (!tiled || s == 0) {
+      const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
+      const long long ld = (s == 0) ? H : a.ldy;
+      contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, bend, H, 1 << 30, 0);
+    }
     spill_acc(red, acc, bend - b0);
     __syncthreads();
 #pragma unroll
@@ -317,7 +436,12 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         const float c = fg * cst[u] + ig * gg;
         cst[u] = c;
         h = og * tanhf_(c);
-        xstore(yr, h);
+        if (tiled) {
+          *yr = from_f<TS>(h);
+          xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed)), h, local);
+        } else {
+          xstore(yr, h, local);
+        }
         zr[0] = from_f<TS>(ig);
         zr[H] = from_f<TS>(fg);
         zr[2 * H] = from_f<TS>(gg);
@@ -331,7 +455,12 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         const float c = tanhf_(to_f(pz[u][2]) + r * nh);
         h = uu * hst[u] + (1.f - uu) * c;
         hst[u] = h;
-        xstore(yr, h);
+        if (tiled) {
+          *yr = from_f<TS>(h);
+          xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed)), h, local);
+        } else {
+          xstore(yr, h, local);
+        }
         zr[0] = from_f<TS>(r);
         zr[H] = from_f<TS>(uu);
         zr[2 * H] = from_f<TS>(c);
@@ -339,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
       }
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
-    publish(myflag, s + 1);
+    publish(myflag, s + 1, local);
   }
 }
 
@@ -358,6 +487,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
   wg_coords(a.nGroups, a.nSlices, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -414,11 +544,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       const float r = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, j) + to_f(pz[u][0]));
       const float uu = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, HS + j) + to_f(pz[u][1]));
       ust[u] = uu;
-      xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u]);
+      xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u], local);
       zr[0] = from_f<TS>(r);
       zr[H] = from_f<TS>(uu);
     }
-    publish(myflag, 2 * s + 1);
+    publish(myflag, 2 * s + 1, local);
     // phase B: candidate and new state
     wait_flags(gflags, a.nSlices, 2 * s + 1, a.status, a.timeout_ticks);
     {
@@ -436,11 +566,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       const float c = tanhf_(red_sum<NW, BG, HS>(red, bl, j) + to_f(pz[u][2]));
       const float h = ust[u] * hst[u] + (1.f - ust[u]) * c;
       hst[u] = h;
-      xstore((TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j, h);
+      xstore((TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j, h, local);
       zr[2 * H] = from_f<TS>(c);
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
-    publish(myflag, 2 * s + 2);
+    publish(myflag, 2 * s + 2, local);
   }
 }
 
@@ -461,6 +591,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
   wg_coords(a.nGroups, a.nSlices, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -470,6 +601,11 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
   // GRU: lanes r, u, then the recurrent candidate lane d_c*r stored in lane 3
   const int kshift = (CELL == CELL_LSTM) ? (1 << 30) : 2 * H;
   const int kskip = (CELL == CELL_LSTM) ? 0 : H;
+  // exchange ring (single row-tile plans): the contracted lanes only
+  const bool tiled = (MB == 1) && a.xbuf != nullptr;
+  const bool packed = a.xpacked != 0;
+  const int xbytes = K * (packed ? 8 : 16) * (int)sizeof(TS);
+  auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
   load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K);
@@ -529,9 +665,14 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     zero_acc(acc);
     if (n > 0) {
       wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks);
-      const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
-      contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
-                               kskip);
+      if constexpr (MB == 1) {
+        if (tiled) contract_x<TS, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
+      }
+      if (!tiled) {
+        const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
+        contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
+                                 kskip);
+      }
     }
     spill_acc(red, acc, bend - b0);
     __syncthreads();
@@ -563,10 +704,23 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_g = dc * ig * (1.f - gg * gg);
         dcar[u] = dc * fg;
         hcar[u] = 0.f;
-        xstore(gr, d_i);
-        xstore(gr + H, d_f);
-        xstore(gr + 2 * H, d_g);
-        xstore(gr + 3 * H, d_o);
+        if (tiled) {
+          gr[0] = from_f<TS>(d_i);
+          gr[H] = from_f<TS>(d_f);
+          gr[2 * H] = from_f<TS>(d_g);
+          gr[3 * H] = from_f<TS>(d_o);
+          char* xs = xslot(n);
+          const int jj = J0 + j_[u];
+          xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed)), d_i, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], H + jj, packed)), d_f, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], 2 * H + jj, packed)), d_g, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], 3 * H + jj, packed)), d_o, local);
+        } else {
+          xstore(gr, d_i, local);
+          xstore(gr + H, d_f, local);
+          xstore(gr + 2 * H, d_g, local);
+          xstore(gr + 3 * H, d_o, local);
+        }
       } else {
         const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]), nh = to_f(pz[u][3]);
         const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
@@ -574,13 +728,24 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_u = dh * (hp - c) * uu * (1.f - uu);
         const float d_r = d_c * nh * r * (1.f - r);
         hcar[u] = dh * uu;
-        xstore(gr, d_r);
-        xstore(gr + H, d_u);
         gr[2 * H] = from_f<TS>(d_c);  // input side only: read by later kernels
-        xstore(gr + 3 * H, d_c * r);
+        if (tiled) {
+          gr[0] = from_f<TS>(d_r);
+          gr[H] = from_f<TS>(d_u);
+          gr[3 * H] = from_f<TS>(d_c * r);
+          char* xs = xslot(n);
+          const int jj = J0 + j_[u];
+          xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed)), d_r, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], H + jj, packed)), d_u, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], 2 * H + jj, packed)), d_c * r, local);
+        } else {
+          xstore(gr, d_r, local);
+          xstore(gr + H, d_u, local);
+          xstore(gr + 3 * H, d_c * r, local);
+        }
       }
     }
-    publish(myflag, n + 1);
+    publish(myflag, n + 1, local);
   }
 }
 
@@ -598,6 +763,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
   wg_coords(a.nGroups, a.nSlices, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -673,14 +839,14 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const float d_c = dh * (1.f - uu) * (1.f - c * c);
       const float d_u = dh * (hp - c) * uu * (1.f - uu);
       TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
-      xstore(gr + H, d_u);
-      xstore(gr + 2 * H, d_c);
+      xstore(gr + H, d_u, local);
+      xstore(gr + 2 * H, d_c, local);
       dhs[u] = dh;
       rs[u] = r;
       us[u] = uu;
       hps[u] = hp;
     }
-    publish(myflag, 2 * n + 1);
+    publish(myflag, 2 * n + 1, local);
     wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks);
     {
       f4 acc[MB][NT];
@@ -696,10 +862,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const long long row = (long long)t * B + b0 + bl_[u];
       const float d_rh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]);
       const float d_r = d_rh * hps[u] * rs[u] * (1.f - rs[u]);
-      xstore((TS*)a.dg + row * GDH + J0 + j_[u], d_r);
+      xstore((TS*)a.dg + row * GDH + J0 + j_[u], d_r, local);
       hcar[u] = d_rh * rs[u] + dhs[u] * us[u];
     }
-    publish(myflag, 2 * n + 2);
+    publish(myflag, 2 * n + 2, local);
   }
 }
 

@@ -33,7 +33,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : d->H; }
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -104,6 +104,12 @@ Layout layout(const rnn_desc_t* d) {
   if (cell == rnn::CELL_GRU_BASIC) off += up(TB * H * s);
   L.dg = off;
   off += up(TB * L.GD * H * s);
+  // exchange ring of the persistent kernels: two slots of every batch
+  // group's operand tiles (16 padded rows per group, groups of >= 4 rows, a
+  // contraction of at most 4H)
+  L.xb = off;
+  L.xb_bytes = 2 * (size_t)16 * ((d->B + 3) / 4) * 4 * H * s;
+  off += up(L.xb_bytes);
   L.total = off;
   return L;
 }
@@ -230,6 +236,22 @@ hipError_t colsum_dt(int dtype, const void* src, long long lds, long long M, int
   return rnn::launch_colsum<float>(src, lds, M, col0, ncols, out, out_row0, H, perm, acc, partial, MAX_CHUNKS, s);
 }
 
+// Exchange ring for single row-tile plans; K = contraction length of the
+// exchanged vector. Pairs of k-steps share a tile when groups have <= 8 rows.
+void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws, long long K, size_t esize) {
+  a.xbuf = nullptr;
+  a.xg_bytes = 0;
+  a.xpacked = 0;
+  if (p.mb != 1 || p.bg > 16) return;
+  if ((K * (long long)esize) % 64 != 0) return;  // whole k-steps only
+  const long long gbytes = K * 16 * (long long)esize;
+  if ((size_t)(2 * p.nGroups * gbytes) > L.xb_bytes) return;
+  const long long ksteps = K * (long long)esize / 64;
+  a.xpacked = (p.bg <= 8 && ksteps % 2 == 0 && p.ki % 2 == 0) ? 1 : 0;
+  a.xg_bytes = gbytes;
+  a.xbuf = ws + L.xb;
+}
+
 int launch_persistent(const rnn::RecPlan& p, const rnn::RecArgs& a, const DevInfo& di, hipStream_t s,
                       const char* what) {
   const long long nwg = (long long)p.nGroups * p.nSlices;
@@ -242,8 +264,9 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecArgs& a, const DevInf
   if (log_on())
     fprintf(stderr,
             "[rnn] %s: %d groups of %d rows x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu, "
-            "model %.2f us/step\n",
-            what, p.nGroups, p.bg, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki, p.lds_bytes, p.cost_us);
+            "ring=%s, model %.2f us/step\n",
+            what, p.nGroups, p.bg, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki, p.lds_bytes,
+            a.xbuf ? (a.xpacked ? "packed" : "tiled") : "off", p.cost_us);
   hipError_t e = rnn::launch_rec(p, a, s);
   if (e != hipSuccess) {
     if (log_on()) fprintf(stderr, "[rnn] %s: launch failed: %s\n", what, hipGetErrorString(e));
@@ -357,6 +380,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.flags = (int*)(ws + L.flags);
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
+  if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, d->H, esz(d));
   ProfScope ps(L_RFWD, s);
   return launch_persistent(plan, a, di, s, "fwd");
 }
@@ -421,6 +445,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   a.flags = flags;
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
+  if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
   {
     ProfScope ps(L_RBWD, s);
     if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;

@@ -174,6 +174,11 @@ struct RecArgs {
   int* flags;
   int* status;
   long long timeout_ticks;
+  // exchange ring in the MFMA operand layout (NULL: the vector is read from
+  // y / dg directly): two slots of nGroups group tiles of xg_bytes each
+  char* xbuf;
+  long long xg_bytes;
+  int xpacked;      // two k-steps of 8 rows per 1 KiB tile (batch groups of <= 8 rows)
 };
 
 struct RecPlan {
