@@ -28,6 +28,8 @@
 //
 // Bias gradients: when requested, the workgroups of the first N-tile column
 // also sum the A tile over k (dG summed over (t,b)) while staging it.
+#include <type_traits>
+
 #include "rnn_internal.hpp"
 
 namespace rnn {
@@ -327,53 +329,90 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     }
   }
 
-  // epilogue: lane holds rows 4q+e, column r16 of every 16x16 tile
-  if (g.ksplit > 1) {
-    float* part = g.part + (long long)tl.kz * g.M * g.N;
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const long long n = n0 + wn * WN + j * 16 + r16;
-      if (n >= g.N) continue;
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const long long m = m0 + wm * WM + i * 16 + q * 4 + e;
-          if (m < g.M) part[m * g.N + n] = acc[i][j][e];
-        }
-    }
-    return;
-  }
+  // Epilogue. Each wave stages its WM x WN sub-tile in a private 16 KiB
+  // region of LDS (free after the main loop), in row-major order with 32-byte
+  // (bf16) or 64-byte (fp32) blocks XOR-swizzled by row so that the MFMA
+  // layout writes (lane: column r16 of rows 4q+e) spread over the banks, and
+  // writes it back as whole 16-byte chunks, 8 or 16 lanes per output row.
+  // Split-K slices store their raw fp32 partial tiles; otherwise the column
+  // bias is added, rows are mapped (gate-block permutation for c_kind 1) and
+  // the storage type is written (added to C when accumulating).
+  const bool part_out = g.ksplit > 1;
+  float colbias[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
+    colbias[j] = 0.f;
     const long long n = n0 + wn * WN + j * 16 + r16;
-    if (n >= g.N) continue;
-    float bias = 0.f;
-    if (g.bias1) {
+    if (!part_out && g.bias1 && n < g.N) {
       const long long gg = n / g.H;
       const long long src = (long long)g.perm[gg] * g.H + (n - gg * g.H);
-      bias = to_f(((const TS*)g.bias1)[src]);
-      if (g.bias2 && gg != g.bias_skip_gate) bias += to_f(((const TS*)g.bias2)[src]);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const long long m = m0 + wm * WM + i * 16 + q * 4 + e;
-        if (m >= g.M) continue;
-        long long row = m;
-        if (g.c_kind == 1) {
-          const long long cm = g.c_row0 + m;
-          const long long gg = cm / g.H;
-          row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
-        }
-        TS* cp = (TS*)g.c + row * g.ldc + n;
-        float v = acc[i][j][e] + bias;
-        if (g.accumulate) v += to_f(*cp);
-        *cp = from_f<TS>(v);
-      }
+      colbias[j] = to_f(((const TS*)g.bias1)[src]);
+      if (g.bias2 && gg != g.bias_skip_gate) colbias[j] += to_f(((const TS*)g.bias2)[src]);
     }
   }
+  char* stage = smem + w * 16384;
+  auto run = [&](auto zero_ot) {
+    using OT = decltype(zero_ot);
+    constexpr int RB = WN * (int)sizeof(OT);       // staged row bytes
+    constexpr int CH = 16384 / RB < WM ? 16384 / RB : WM;
+    constexpr int CPR = RB / 16;                   // 16-byte chunks per row
+    constexpr int EPC = 16 / (int)sizeof(OT);      // elements per chunk
+    auto sw = [](int r) { return (RB == 128) ? (((r >> 2) & 3) << 5) : (((r >> 2) & 1) << 6); };
+#pragma unroll
+    for (int c0 = 0; c0 < WM; c0 += CH) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        if (i * 16 < c0 || i * 16 >= c0 + CH) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = i * 16 + q * 4 + e - c0;
+            const int byte = (j * 16 + r16) * (int)sizeof(OT);
+            *(OT*)(stage + r * RB + (byte ^ sw(r))) = (OT)(acc[i][j][e] + colbias[j]);
+          }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int it = 0; it < CH * CPR / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int r = idx / CPR, c = idx - r * CPR;
+        const uint4 v = *(const uint4*)(stage + r * RB + ((c * 16) ^ sw(r)));
+        const long long m = m0 + wm * WM + c0 + r;
+        const long long n = n0 + wn * WN + c * EPC;
+        if (m >= g.M || n >= g.N) continue;
+        if constexpr (sizeof(OT) == 4 && !std::is_same<OT, TS>::value) {
+          // fp32 split-K partial (TS = bf16)
+          *(uint4*)(g.part + (long long)tl.kz * g.M * g.N + m * g.N + n) = v;
+        } else {
+          if (part_out) {
+            *(uint4*)(g.part + (long long)tl.kz * g.M * g.N + m * g.N + n) = v;
+            continue;
+          }
+          long long row = m;
+          if (g.c_kind == 1) {
+            const long long cm = g.c_row0 + m;
+            const long long gg = cm / g.H;
+            row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
+          }
+          uint4* cp = (uint4*)((TS*)g.c + row * g.ldc + n);
+          uint4 o = v;
+          if (g.accumulate) {
+            const uint4 old = *cp;
+            const OT* a0 = (const OT*)&old;
+            OT* b0 = (OT*)&o;
+#pragma unroll
+            for (int k = 0; k < EPC; ++k) b0[k] = (OT)(to_f(b0[k]) + to_f(a0[k]));
+          }
+          *cp = o;
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  };
+  if (part_out) run(0.f);
+  else run(from_f<TS>(0.f));
 }
 
 // Split-K finish: C[row(m)][n] (+)= sum_kz part[kz][m][n] (+ bias), in order.
