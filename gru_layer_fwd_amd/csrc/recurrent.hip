@@ -420,11 +420,14 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     }
     spill_acc(red, acc, bend - b0);
     __syncthreads();
+    // the exchanged vector is stored first; what only later kernels read
+    // (y when the ring carries the exchange, saved gates, cell states) is
+    // kept in registers and stored after the step counter is published
+    float sv[UPT][4], hv[UPT], cv[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
       const int bl = bl_[u], j = j_[u], b = b0 + bl;
-      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
       TS* yr = (TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j;
       float h;
       if constexpr (CELL == CELL_LSTM) {
@@ -436,18 +439,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         const float c = fg * cst[u] + ig * gg;
         cst[u] = c;
         h = og * tanhf_(c);
-        if (tiled) {
-          *yr = from_f<TS>(h);
-          xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed)), h, local);
-        } else {
-          xstore(yr, h, local);
-        }
-        zr[0] = from_f<TS>(ig);
-        zr[H] = from_f<TS>(fg);
-        zr[2 * H] = from_f<TS>(gg);
-        zr[3 * H] = from_f<TS>(og);
-        ((TS*)a.cbuf)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(c);
-        if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(c);
+        sv[u][0] = ig;
+        sv[u][1] = fg;
+        sv[u][2] = gg;
+        sv[u][3] = og;
+        cv[u] = c;
       } else {
         const float r = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(pz[u][0]));
         const float uu = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(pz[u][1]));
@@ -455,20 +451,31 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         const float c = tanhf_(to_f(pz[u][2]) + r * nh);
         h = uu * hst[u] + (1.f - uu) * c;
         hst[u] = h;
-        if (tiled) {
-          *yr = from_f<TS>(h);
-          xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed)), h, local);
-        } else {
-          xstore(yr, h, local);
-        }
-        zr[0] = from_f<TS>(r);
-        zr[H] = from_f<TS>(uu);
-        zr[2 * H] = from_f<TS>(c);
-        zr[3 * H] = from_f<TS>(nh);
+        sv[u][0] = r;
+        sv[u][1] = uu;
+        sv[u][2] = c;
+        sv[u][3] = nh;
+        cv[u] = 0.f;
       }
-      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
+      hv[u] = h;
+      if (tiled) xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed)), h, local);
+      else xstore(yr, h, local);
     }
     publish(myflag, s + 1, local);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      if (!live[u]) continue;
+      const int bl = bl_[u], j = j_[u], b = b0 + bl;
+      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
+      if (tiled) ((TS*)a.y)[((long long)t * B + b) * a.ldy + J0 + j] = from_f<TS>(hv[u]);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) zr[g * H] = from_f<TS>(sv[u][g]);
+      if constexpr (CELL == CELL_LSTM) {
+        ((TS*)a.cbuf)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(cv[u]);
+        if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(cv[u]);
+      }
+      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hv[u]);
+    }
   }
 }
 
@@ -687,6 +694,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       }
       break;
     }
+    float dv[UPT][4];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
@@ -704,11 +712,11 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_g = dc * ig * (1.f - gg * gg);
         dcar[u] = dc * fg;
         hcar[u] = 0.f;
+        dv[u][0] = d_i;
+        dv[u][1] = d_f;
+        dv[u][2] = d_g;
+        dv[u][3] = d_o;
         if (tiled) {
-          gr[0] = from_f<TS>(d_i);
-          gr[H] = from_f<TS>(d_f);
-          gr[2 * H] = from_f<TS>(d_g);
-          gr[3 * H] = from_f<TS>(d_o);
           char* xs = xslot(n);
           const int jj = J0 + j_[u];
           xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed)), d_i, local);
@@ -728,11 +736,12 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         const float d_u = dh * (hp - c) * uu * (1.f - uu);
         const float d_r = d_c * nh * r * (1.f - r);
         hcar[u] = dh * uu;
-        gr[2 * H] = from_f<TS>(d_c);  // input side only: read by later kernels
+        dv[u][0] = d_r;
+        dv[u][1] = d_u;
+        dv[u][2] = d_c;  // input side only: read by later kernels
+        dv[u][3] = d_c * r;
+        if (!tiled) gr[2 * H] = from_f<TS>(d_c);
         if (tiled) {
-          gr[0] = from_f<TS>(d_r);
-          gr[H] = from_f<TS>(d_u);
-          gr[3 * H] = from_f<TS>(d_c * r);
           char* xs = xslot(n);
           const int jj = J0 + j_[u];
           xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed)), d_r, local);
@@ -746,6 +755,16 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       }
     }
     publish(myflag, n + 1, local);
+    if (tiled) {
+      // gate gradients for the later kernels (the ring carried the exchange)
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        if (!live[u]) continue;
+        TS* gr = (TS*)a.dg + ((long long)t * B + b0 + bl_[u]) * GDH + J0 + j_[u];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) gr[g * H] = from_f<TS>(dv[u][g]);
+      }
+    }
   }
 }
 
