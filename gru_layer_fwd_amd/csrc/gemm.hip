@@ -543,8 +543,17 @@ GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long lon
   } else if (t256x128 >= cu_count) {
     p.bm = 256;
     p.bn = 128;
-  } else if (t128 >= cu_count || K < 2048) {
+  } else if (t128 >= cu_count || K < 512) {
     p.bm = p.bn = 128;
+  } else if (K < 2048) {
+    // few 128x128 tiles and a moderate contraction: split it into slices of
+    // at least 256 so that more CUs take part
+    p.bm = p.bn = 128;
+    long long ks = (cu_count + t128 - 1) / t128;
+    if (ks > K / 256) ks = K / 256;
+    if (ks > 8) ks = 8;
+    while (ks > 1 && ks * (M * N + M) > ws_floats) --ks;
+    p.ksplit = (int)(ks < 1 ? 1 : ks);
   } else {
     // too few tiles: 256x256 tiles split along K, each slice >= 1024 deep
     p.bm = p.bn = 256;

@@ -144,12 +144,12 @@ __device__ __forceinline__ void wg_coords(int nGroups, int nSlices, int& grp, in
 // alternating by step: a slot is rewritten two steps later, after every
 // consumer has published the step that read it).
 template <typename TS>
-__device__ __forceinline__ int xoff(int row, int kg, bool packed) {
+__device__ __forceinline__ int xoff(int row, int kg, bool packed, int mbt) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   const int ks = kg / KSTEP, e = kg - ks * KSTEP, q = e / KQ, el = e - q * KQ;
-  const int lane = (packed ? row + 8 * (ks & 1) : row) + 16 * q;
-  const int tile = packed ? (ks >> 1) : ks;
-  return tile * 1024 + lane * 16 + el * (int)sizeof(TS);
+  if (packed) return (ks >> 1) * 1024 + (row + 8 * (ks & 1) + 16 * q) * 16 + el * (int)sizeof(TS);
+  // one 1 KiB tile per (k-step, 16-row tile of the group)
+  return (ks * mbt + (row >> 4)) * 1024 + ((row & 15) + 16 * q) * 16 + el * (int)sizeof(TS);
 }
 
 __device__ __forceinline__ unsigned rot8(unsigned v) {
@@ -157,50 +157,58 @@ __device__ __forceinline__ unsigned rot8(unsigned v) {
 }
 __device__ __forceinline__ uint4 rot8(const uint4& v) { return make_uint4(rot8(v.x), rot8(v.y), rot8(v.z), rot8(v.w)); }
 
-// acc[0][nt] += (previous step's vector, k-steps [w*KI, w*KI+KI)) . Wr[nt][.]
-// from the exchange ring tile `xb` of this group (nbytes valid; loads past it
-// return zero).
-template <typename TS, int NT, int KI>
-__device__ __forceinline__ void contract_x(f4 (&acc)[1][NT], const uint4 (&Wr)[NT][KI], const char* xb, int nbytes,
+// acc[mb][nt] += (previous step's vector, k-steps [w*KI, w*KI+KI)) . Wr[nt][.]
+// from the exchange ring tiles `xb` of this group (nbytes valid; loads past
+// it return zero). Unpacked tiles are ordered (k-step, row tile).
+template <typename TS, int MB, int NT, int KI>
+__device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const char* xb, int nbytes,
                                            bool packed) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, nbytes, BUF_RSRC_W3);
-  if constexpr (KI % 2 == 0) {
+  if constexpr (MB == 1 && KI % 2 == 0) {
     if (packed) {
-    constexpr int NL = KI / 2;
-    uint4 v[NL];
+      constexpr int NL = KI / 2;
+      uint4 v[NL];
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, ((w * KI) / 2 + i) * 1024 + lane * 16, 0, CPOL_SC1);
-      v[i] = make_uint4(r[0], r[1], r[2], r[3]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      const uint4 odd = rot8(v[i]);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], v[i], Wr[nt][2 * i]);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], odd, Wr[nt][2 * i + 1]);
-    }
-    return;
-    }
-  }
-  {
-    constexpr int KB = KI < 16 ? KI : 16;
-#pragma unroll
-    for (int k0 = 0; k0 < KI; k0 += KB) {
-      uint4 v[KB];
-#pragma unroll
-      for (int i = 0; i < KB; ++i) {
-        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, (w * KI + k0 + i) * 1024 + lane * 16, 0, CPOL_SC1);
+      for (int i = 0; i < NL; ++i) {
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, ((w * KI) / 2 + i) * 1024 + lane * 16, 0, CPOL_SC1);
         v[i] = make_uint4(r[0], r[1], r[2], r[3]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < KB; ++i)
+      for (int i = 0; i < NL; ++i) {
+        const uint4 odd = rot8(v[i]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], v[i], Wr[nt][k0 + i]);
+        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], v[i], Wr[nt][2 * i]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], odd, Wr[nt][2 * i + 1]);
+      }
+      return;
+    }
+  }
+  // loads per batch: at most 16 tiles in flight for one row tile, 8 for more
+  constexpr int LIM = (MB == 1) ? 4 : 8;
+  constexpr int KB = (LIM / MB) < 1 ? 1 : ((LIM / MB) < KI ? (LIM / MB) : KI);
+#pragma unroll
+  for (int k0 = 0; k0 < KI; k0 += KB) {
+    uint4 v[KB][MB];
+#pragma unroll
+    for (int i = 0; i < KB; ++i)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const int ks = w * KI + k0 + i;
+        const int off = (k0 + i < KI) ? ((ks * MB + mb) * 1024 + lane * 16) : nbytes;
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, CPOL_SC1);
+        v[i][mb] = make_uint4(r[0], r[1], r[2], r[3]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < KB; ++i) {
+      if (k0 + i >= KI) break;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[mb][nt], v[i][mb], Wr[nt][k0 + i]);
     }
   }
 }
@@ -214,7 +222,7 @@ __device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT
                                          long long ld, int b0, int B, int K, int kshift, int kskip) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   // k-steps per load batch: every load of the step at once where registers allow
-  constexpr int KB = (MB >= 8) ? 2 : (MB >= 4 ? 4 : (KI <= 16 ? KI : 16));
+  constexpr int KB = (MB >= 4) ? 2 : (KI <= 16 ? KI : 16);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   if (src == nullptr) return;
@@ -363,9 +371,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
   // exchange ring (single row-tile plans)
-  const bool tiled = (MB == 1) && a.xbuf != nullptr;
+  const bool tiled = a.xbuf != nullptr;
   const bool packed = a.xpacked != 0;
-  const int xbytes = H * (packed ? 8 : 16) * (int)sizeof(TS);
+  const int xbytes = H * (packed ? 8 : 16 * MB) * (int)sizeof(TS);
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
@@ -410,9 +418,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
     f4 acc[MB][NT];
     zero_acc(acc);
-    if constexpr (MB == 1) {
-      if (tiled && s > 0) contract_x<TS, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
-    }
+    if (tiled && s > 0) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
     if (!tiled || s == 0) {
       const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
       const long long ld = (s == 0) ? H : a.ldy;
@@ -458,7 +464,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         cv[u] = 0.f;
       }
       hv[u] = h;
-      if (tiled) xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed)), h, local);
+      if (tiled) xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed, MB)), h, local);
       else xstore(yr, h, local);
     }
     publish(myflag, s + 1, local);
@@ -609,9 +615,9 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
   const int kshift = (CELL == CELL_LSTM) ? (1 << 30) : 2 * H;
   const int kskip = (CELL == CELL_LSTM) ? 0 : H;
   // exchange ring (single row-tile plans): the contracted lanes only
-  const bool tiled = (MB == 1) && a.xbuf != nullptr;
+  const bool tiled = a.xbuf != nullptr;
   const bool packed = a.xpacked != 0;
-  const int xbytes = K * (packed ? 8 : 16) * (int)sizeof(TS);
+  const int xbytes = K * (packed ? 8 : 16 * MB) * (int)sizeof(TS);
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
@@ -672,9 +678,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     zero_acc(acc);
     if (n > 0) {
       wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks);
-      if constexpr (MB == 1) {
-        if (tiled) contract_x<TS, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
-      }
+      if (tiled) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
       if (!tiled) {
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
         contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
@@ -719,10 +723,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         if (tiled) {
           char* xs = xslot(n);
           const int jj = J0 + j_[u];
-          xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed)), d_i, local);
-          xstore((TS*)(xs + xoff<TS>(bl_[u], H + jj, packed)), d_f, local);
-          xstore((TS*)(xs + xoff<TS>(bl_[u], 2 * H + jj, packed)), d_g, local);
-          xstore((TS*)(xs + xoff<TS>(bl_[u], 3 * H + jj, packed)), d_o, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed, MB)), d_i, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], H + jj, packed, MB)), d_f, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], 2 * H + jj, packed, MB)), d_g, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], 3 * H + jj, packed, MB)), d_o, local);
         } else {
           xstore(gr, d_i, local);
           xstore(gr + H, d_f, local);
@@ -744,9 +748,9 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
         if (tiled) {
           char* xs = xslot(n);
           const int jj = J0 + j_[u];
-          xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed)), d_r, local);
-          xstore((TS*)(xs + xoff<TS>(bl_[u], H + jj, packed)), d_u, local);
-          xstore((TS*)(xs + xoff<TS>(bl_[u], 2 * H + jj, packed)), d_c * r, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed, MB)), d_r, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], H + jj, packed, MB)), d_u, local);
+          xstore((TS*)(xs + xoff<TS>(bl_[u], 2 * H + jj, packed, MB)), d_c * r, local);
         } else {
           xstore(gr, d_r, local);
           xstore(gr + H, d_u, local);
@@ -906,6 +910,7 @@ const Entry kTable[] = {
     {CELL_LSTM, 1, 1, 4, 1, 1, 8, 0, F_LSTM(bf16, 4, 1, 1, 8)},
     {CELL_LSTM, 1, 1, 8, 1, 8, 4, 0, F_LSTM(bf16, 8, 1, 8, 4)},
     {CELL_LSTM, 1, 1, 4, 8, 2, 16, 0, F_LSTM(bf16, 4, 8, 2, 16)},
+    {CELL_LSTM, 1, 1, 8, 8, 2, 8, 0, F_LSTM(bf16, 8, 8, 2, 8)},
     {CELL_LSTM, 0, 1, 4, 1, 4, 8, 0, F_LSTM(float, 4, 1, 4, 8)},
     {CELL_LSTM, 0, 1, 4, 1, 1, 8, 0, F_LSTM(float, 4, 1, 1, 8)},
     {CELL_LSTM, 0, 1, 8, 1, 4, 4, 0, F_LSTM(float, 8, 1, 4, 4)},
@@ -926,7 +931,7 @@ const Entry kTable[] = {
     // backward reset-after GRU
     {CELL_GRU_RA, 1, 0, 4, 1, 1, 32, 0, B_GRA(bf16, 4, 1, 1, 32)},
     {CELL_GRU_RA, 1, 0, 8, 1, 2, 16, 0, B_GRA(bf16, 8, 1, 2, 16)},
-    {CELL_GRU_RA, 1, 0, 8, 4, 1, 32, 0, B_GRA(bf16, 8, 4, 1, 32)},
+    {CELL_GRU_RA, 1, 0, 4, 4, 1, 48, 0, B_GRA(bf16, 4, 4, 1, 48)},
     {CELL_GRU_RA, 0, 0, 4, 1, 1, 32, 0, B_GRA(float, 4, 1, 1, 32)},
     // backward basic GRU (ki = phase A k-steps, kib = phase B)
     {CELL_GRU_BASIC, 1, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<bf16, 4, 1, 1, 16, 8>},
@@ -958,23 +963,25 @@ int xcd_span(long long nwg, int slices) {
   return slices < 8 ? slices : 8;
 }
 
-// Modelled time of one step (us), from measurements of the exchange on
-// MI355X: a counter handshake costs ~0.8 us when a batch group sits on one
-// XCD, ~1.8 us across two and ~3.5 us beyond; the exchanged vector streams at
-// ~5 TB/s through the device coherence point; MFMA issue per SIMD at 16
-// (bf16 16x16x32) or 128 (four fp32 16x16x4) cycles per k-step and tile,
-// 2.4 GHz.
-double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize) {
+// Modelled time of one step (us), from measurements on MI355X: a step
+// handshake costs ~1 us when a batch group shares one XCD and ~2 us across
+// XCDs; a 16x16x32 bf16 MFMA issues every ~3.7 ns per SIMD with two or more
+// waves per SIMD and every ~10.8 ns with one (fp32: four 16x16x4 per k-step,
+// taken as ~2.5x the bf16 time); every CU reads the whole exchanged vector
+// of its group per step, ~150 GB/s from the tiled ring and ~75 GB/s from row
+// layout; the gate epilogue costs ~0.2 us per unit a thread carries.
+double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize, bool ring) {
   const int span = xcd_span((long long)groups * slices, slices);
-  const double hand = span <= 1 ? 0.8 : (span <= 2 ? 1.8 : 3.5);
+  const double hand = span <= 1 ? 1.0 : 2.0;
   const int phases = (e.cell == CELL_GRU_BASIC) ? 2 : 1;
   const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
-  const double waves_per_simd = e.nw / 4.0;
-  const double cyc = (kstep == 32) ? 16.0 : 128.0;
-  const double mfma = e.mb * e.nt * kused * waves_per_simd * cyc / 2400.0;
-  const double bytes = (double)groups * slices * bg * K * esize;
-  const double data = bytes / 5.0e6;
-  return phases * hand + mfma + data;
+  const double wps = e.nw / 4.0;  // waves per SIMD
+  const double t_inst = (wps >= 2 ? 3.7e-3 : 10.8e-3) * (kstep == 32 ? 1.0 : 2.5);
+  const double mfma = wps * e.mb * e.nt * kused * t_inst;
+  const double data = (double)bg * K * esize / (ring ? 150e3 : 75e3);
+  const int units = e.mb * 16 * units_per_wg(e);
+  const int upt = (units + e.nw * 64 - 1) / (e.nw * 64);
+  return phases * hand + mfma + data + 0.2 * upt;
 }
 
 bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p) {
@@ -1000,7 +1007,8 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p
       const int slices = H / hs;
       const long long nwg = (long long)groups * slices;
       if (nwg > cu_count) continue;  // at most one persistent workgroup per CU
-      const double cost = step_cost(e, bg, groups, slices, K, kstep, esize);
+      const bool ring = (cell != CELL_GRU_BASIC) && ((long long)K * esize) % 64 == 0 && bg <= 16 * e.mb;
+      const double cost = step_cost(e, bg, groups, slices, K, kstep, esize, ring);
       if (cost < best) {
         best = cost;
         *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e)};

@@ -242,12 +242,12 @@ void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws,
   a.xbuf = nullptr;
   a.xg_bytes = 0;
   a.xpacked = 0;
-  if (p.mb != 1 || p.bg > 16) return;
+  if (p.bg > 16 * p.mb) return;
   if ((K * (long long)esize) % 64 != 0) return;  // whole k-steps only
-  const long long gbytes = K * 16 * (long long)esize;
+  const long long gbytes = K * 16 * (long long)p.mb * (long long)esize;  // a 1 KiB tile per (k-step, row tile)
   if ((size_t)(2 * p.nGroups * gbytes) > L.xb_bytes) return;
   const long long ksteps = K * (long long)esize / 64;
-  a.xpacked = (p.bg <= 8 && ksteps % 2 == 0 && p.ki % 2 == 0) ? 1 : 0;
+  a.xpacked = (p.mb == 1 && p.bg <= 8 && ksteps % 2 == 0 && p.ki % 2 == 0) ? 1 : 0;
   a.xg_bytes = gbytes;
   a.xbuf = ws + L.xb;
 }
