@@ -32,6 +32,15 @@ Conventions (readings where the pages leave a point open):
 * dh carry is seeded from dhT (and dcT for LSTM); None means zero.
 * Weight gradients are sums over (t, b); db_ih and db_hh are reported
   separately (they differ only for the reset-after candidate row block).
+* Variable sequence lengths (popnn's per-batch time-step limits: the gates of
+  steps past a row's limit are masked to zero, the output sequence is
+  zero-filled, and the state and the carried gradient state are latched,
+  i.e. not updated, on those steps): row b has lengths[b] in [0, T] steps
+  and step t is active for it iff t < lengths[b]. An inactive step outputs
+  zero, saves zero gates, keeps the state and (backward) has zero gate
+  gradients while the carries pass through unchanged. In the reverse
+  direction a row therefore starts at its own step lengths[b]-1 from h0/c0.
+  lengths=None means every row runs all T steps.
 """
 from __future__ import annotations
 
@@ -59,9 +68,31 @@ def _steps(T, reverse):
     return range(T - 1, -1, -1) if reverse else range(T)
 
 
+def _lengths(lengths, T, B):
+    if lengths is None:
+        return np.full(B, T, dtype=np.int64)
+    L = np.asarray(lengths, dtype=np.int64)
+    assert L.shape == (B,) and np.all((L >= 0) & (L <= T)), "lengths must be B values in [0, T]"
+    return L
+
+
+def _first(t, L, T, reverse):
+    """Per row: is t the first step processed for that row (its previous
+    state is the initial one)?"""
+    return (t == L - 1) if reverse else np.full(L.shape, t == 0)
+
+
+def _prev(seq, t, first, init, reverse):
+    """Per row: the state before step t (init on the row's first step)."""
+    T = seq.shape[0]
+    tp = (t + 1) if reverse else (t - 1)
+    before = seq[tp] if 0 <= tp < T else np.zeros_like(init)
+    return np.where(first[:, None], init, before)
+
+
 # ---------------------------------------------------------------- LSTM ----
 
-def lstm_forward(x, h0, c0, W_ih, W_hh, b_ih, b_hh, order=(0, 1, 2, 3), reverse=False):
+def lstm_forward(x, h0, c0, W_ih, W_hh, b_ih, b_hh, order=(0, 1, 2, 3), reverse=False, lengths=None):
     """LSTM layer forward over a sequence x [T, B, I].
 
     Returns a dict with y [T,B,H], hT, cT and the per-step activations the
@@ -69,22 +100,26 @@ def lstm_forward(x, h0, c0, W_ih, W_hh, b_ih, b_hh, order=(0, 1, 2, 3), reverse=
     x, W_ih, W_hh, b_ih, b_hh = map(_f64, (x, W_ih, W_hh, b_ih, b_hh))
     T, B, _ = x.shape
     H = W_hh.shape[1]
+    L = _lengths(lengths, T, B)
     h = np.zeros((B, H)) if h0 is None else _f64(h0).copy()
     c = np.zeros((B, H)) if c0 is None else _f64(c0).copy()
     s = {k: _slot(order, k, H) for k in (LSTM_I, LSTM_F, LSTM_G, LSTM_O)}
     st = {k: np.zeros((T, B, H)) for k in ("i", "f", "g", "o", "c", "y")}
     for t in _steps(T, reverse):
+        m = (t < L)[:, None]                                  # rows with a step at t
         z = x[t] @ W_ih.T + b_ih + h @ W_hh.T + b_hh        # [B, 4H], storage order
-        i = sigmoid(z[:, s[LSTM_I]])
-        f = sigmoid(z[:, s[LSTM_F]])
-        g = np.tanh(z[:, s[LSTM_G]])
-        o = sigmoid(z[:, s[LSTM_O]])
-        c = f * c + i * g
-        h = o * np.tanh(c)
-        for k, v in (("i", i), ("f", f), ("g", g), ("o", o), ("c", c), ("y", h)):
+        i = np.where(m, sigmoid(z[:, s[LSTM_I]]), 0.0)      # gates masked past a row's limit
+        f = np.where(m, sigmoid(z[:, s[LSTM_F]]), 0.0)
+        g = np.where(m, np.tanh(z[:, s[LSTM_G]]), 0.0)
+        o = np.where(m, sigmoid(z[:, s[LSTM_O]]), 0.0)
+        c_new = f * c + i * g
+        h_new = o * np.tanh(c_new)
+        c = np.where(m, c_new, c)                             # state latched past the limit
+        h = np.where(m, h_new, h)
+        for k, v in (("i", i), ("f", f), ("g", g), ("o", o), ("c", c_new), ("y", h_new)):
             st[k][t] = v
     st.update(hT=h, cT=c, x=x, h0=h0, c0=c0, W_ih=W_ih, W_hh=W_hh,
-              order=tuple(order), reverse=reverse)
+              order=tuple(order), reverse=reverse, lengths=L)
     return st
 
 
@@ -109,11 +144,12 @@ def lstm_backward(fw, dy, dhT=None, dcT=None):
     dW_hh = np.zeros_like(W_hh)
     db = np.zeros(W_hh.shape[0])
     dG_all = np.zeros((T, B, 4 * H))
+    L = fw["lengths"]
     for t in reversed(list(_steps(T, reverse))):
-        tp = (t + 1) if reverse else (t - 1)          # the step processed before t
-        first = (t == T - 1) if reverse else (t == 0)
-        c_prev = c0 if first else fw["c"][tp]
-        h_prev = h0 if first else fw["y"][tp]
+        m = (t < L)[:, None]
+        first = _first(t, L, T, reverse)
+        c_prev = _prev(fw["c"], t, first, c0, reverse)
+        h_prev = _prev(fw["y"], t, first, h0, reverse)
         i, f, g, o, c = (fw[k][t] for k in ("i", "f", "g", "o", "c"))
         dh = dy[t] + dh_carry
         tc = np.tanh(c)
@@ -125,9 +161,10 @@ def lstm_backward(fw, dy, dhT=None, dcT=None):
         dG = np.zeros((B, 4 * H))
         dG[:, s[LSTM_I]], dG[:, s[LSTM_F]] = d_i, d_f
         dG[:, s[LSTM_G]], dG[:, s[LSTM_O]] = d_g, d_o
+        dG = np.where(m, dG, 0.0)                     # no gradient past a row's limit
         dG_all[t] = dG
-        dh_carry = dG @ W_hh
-        dc_carry = dc * f
+        dh_carry = np.where(m, dG @ W_hh, dh_carry)   # carries latched past the limit
+        dc_carry = np.where(m, dc * f, dc_carry)
         dx[t] = dG @ W_ih
         dW_ih += dG.T @ x[t]
         dW_hh += dG.T @ h_prev
@@ -138,7 +175,7 @@ def lstm_backward(fw, dy, dhT=None, dcT=None):
 
 # ----------------------------------------------------------------- GRU ----
 
-def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), reverse=False):
+def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), reverse=False, lengths=None):
     """GRU layer forward over x [T, B, I] (basic or reset-after variant).
 
     Returns y, hT and the per-step r, u, c (activated), n_h (reset-after:
@@ -147,10 +184,12 @@ def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), rev
     x, W_ih, W_hh, b_ih, b_hh = map(_f64, (x, W_ih, W_hh, b_ih, b_hh))
     T, B, _ = x.shape
     H = W_hh.shape[1]
+    L = _lengths(lengths, T, B)
     h = np.zeros((B, H)) if h0 is None else _f64(h0).copy()
     sr, su, sc = (_slot(order, k, H) for k in (GRU_R, GRU_U, GRU_C))
     st = {k: np.zeros((T, B, H)) for k in ("r", "u", "c", "nh", "rh", "y")}
     for t in _steps(T, reverse):
+        m = (t < L)[:, None]
         xi = x[t] @ W_ih.T + b_ih                 # input parts, storage order
         hr = h @ W_hh.T + b_hh                    # recurrent parts, storage order
         r = sigmoid(xi[:, sr] + hr[:, sr])
@@ -158,15 +197,17 @@ def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), rev
         if reset_after:
             nh = hr[:, sc]
             c = np.tanh(xi[:, sc] + r * nh)
-            st["nh"][t] = nh
+            st["nh"][t] = np.where(m, nh, 0.0)
         else:
             rh = r * h
             c = np.tanh(xi[:, sc] + rh @ W_hh[sc].T + b_hh[sc])
-            st["rh"][t] = rh
-        h = u * h + (1 - u) * c
-        st["r"][t], st["u"][t], st["c"][t], st["y"][t] = r, u, c, h
+            st["rh"][t] = np.where(m, rh, 0.0)
+        h_new = u * h + (1 - u) * c
+        h = np.where(m, h_new, h)                 # state latched past a row's limit
+        st["r"][t], st["u"][t], st["c"][t] = (np.where(m, v, 0.0) for v in (r, u, c))
+        st["y"][t] = np.where(m, h_new, 0.0)
     st.update(hT=h, x=x, h0=h0, W_ih=W_ih, W_hh=W_hh, order=tuple(order),
-              reverse=reverse, reset_after=reset_after)
+              reverse=reverse, reset_after=reset_after, lengths=L)
     return st
 
 
@@ -191,10 +232,11 @@ def gru_backward(fw, dy, dhT=None):
     db_hh = np.zeros(W_hh.shape[0])
     dGi_all = np.zeros((T, B, 3 * H))
     dGh_all = np.zeros((T, B, 3 * H))
+    L = fw["lengths"]
     for t in reversed(list(_steps(T, reverse))):
-        tp = (t + 1) if reverse else (t - 1)
-        first = (t == T - 1) if reverse else (t == 0)
-        h_prev = h0 if first else fw["y"][tp]
+        m = (t < L)[:, None]
+        first = _first(t, L, T, reverse)
+        h_prev = _prev(fw["y"], t, first, h0, reverse)
         r, u, c = fw["r"][t], fw["u"][t], fw["c"][t]
         dh = dy[t] + carry
         d_c = dh * (1 - u) * (1 - c * c)
@@ -205,17 +247,19 @@ def gru_backward(fw, dy, dhT=None):
             d_r = d_c * fw["nh"][t] * r * (1 - r)
             dGi[:, sr], dGi[:, su], dGi[:, sc] = d_r, d_u, d_c
             dGh[:, sr], dGh[:, su], dGh[:, sc] = d_r, d_u, d_c * r
-            carry = dGh @ W_hh + dh * u
+            dGi, dGh = np.where(m, dGi, 0.0), np.where(m, dGh, 0.0)
+            carry = np.where(m, dGh @ W_hh + dh * u, carry)
             dW_hh += dGh.T @ h_prev
         else:
             d_rh = d_c @ W_hh[sc]                 # gradient wrt r*h_prev
             d_r = d_rh * h_prev * r * (1 - r)
             dGi[:, sr], dGi[:, su], dGi[:, sc] = d_r, d_u, d_c
+            dGi = np.where(m, dGi, 0.0)
             dGh[:] = dGi
-            carry = d_rh * r + dh * u + dGh[:, sr] @ W_hh[sr] + dGh[:, su] @ W_hh[su]
-            dW_hh[sr] += d_r.T @ h_prev
-            dW_hh[su] += d_u.T @ h_prev
-            dW_hh[sc] += d_c.T @ fw["rh"][t]
+            carry = np.where(m, d_rh * r + dh * u + dGh[:, sr] @ W_hh[sr] + dGh[:, su] @ W_hh[su], carry)
+            dW_hh[sr] += dGh[:, sr].T @ h_prev
+            dW_hh[su] += dGh[:, su].T @ h_prev
+            dW_hh[sc] += dGh[:, sc].T @ fw["rh"][t]
         dGi_all[t], dGh_all[t] = dGi, dGh
         dx[t] = dGi @ W_ih
         dW_ih += dGi.T @ x[t]
@@ -227,11 +271,11 @@ def gru_backward(fw, dy, dhT=None):
 
 # ------------------------------------------------------ layer wrappers ----
 
-def layer_forward(mode, x, h0, c0, p, order, reverse=False, reset_after=True):
+def layer_forward(mode, x, h0, c0, p, order, reverse=False, reset_after=True, lengths=None):
     """One layer and direction; p has W_ih, W_hh, b_ih, b_hh."""
     if mode == "lstm":
-        return lstm_forward(x, h0, c0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, order, reverse)
-    return gru_forward(x, h0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, reset_after, order, reverse)
+        return lstm_forward(x, h0, c0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, order, reverse, lengths)
+    return gru_forward(x, h0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, reset_after, order, reverse, lengths)
 
 
 def layer_backward(mode, fw, dy, dhT=None, dcT=None):
@@ -240,7 +284,7 @@ def layer_backward(mode, fw, dy, dhT=None, dcT=None):
     return gru_backward(fw, dy, dhT)
 
 
-def stack_forward(mode, x, params, order, bidir, reset_after=True, h0=None, c0=None):
+def stack_forward(mode, x, params, order, bidir, reset_after=True, h0=None, c0=None, lengths=None):
     """Stacked (optionally bidirectional) layers: layer l+1 reads the
     concatenation [y_fwd, y_rev] of layer l along the feature axis (the
     strided-output layout of the CUDA fragment's OUTPUT_STRIDE rows).
@@ -248,8 +292,8 @@ def stack_forward(mode, x, params, order, bidir, reset_after=True, h0=None, c0=N
     recs = []
     inp = _f64(x)
     for layer_params in params:
-        fws = [layer_forward(mode, inp, h0, c0, p, order, reverse=(d == 1), reset_after=reset_after)
-               for d, p in enumerate(layer_params)]
+        fws = [layer_forward(mode, inp, h0, c0, p, order, reverse=(d == 1), reset_after=reset_after,
+                             lengths=lengths) for d, p in enumerate(layer_params)]
         recs.append(fws)
         inp = np.concatenate([fw["y"] for fw in fws], axis=2)
         if not bidir:

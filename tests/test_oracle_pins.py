@@ -407,3 +407,131 @@ def test_zero_recurrent_weights_reduce_to_independent_steps():
         i, fg, o = 1 / (1 + np.exp(-i)), 1 / (1 + np.exp(-fg)), 1 / (1 + np.exp(-o))
         c_prev = np.zeros((B, H)) if t == 0 else f["c"][t - 1]
         np.testing.assert_allclose(f["c"][t], fg * c_prev + i * np.tanh(g), atol=1e-13)
+
+
+# ------------------------------------------------- variable sequence lengths --
+# Reading (popnn's per-batch step limits): steps past a row's length output
+# zero, keep the state and pass the carried gradients through; a reverse
+# direction row starts at its own last step. torch's packed sequences define
+# the same thing independently: outputs zero-padded, h_n/c_n the state at the
+# row's last valid step, the reverse direction starting at each row's end.
+
+def _torch_packed(module, x, lengths, h0, c0, gy, ghT, gcT):
+    from torch.nn.utils.rnn import pack_padded_sequence, pad_packed_sequence
+    xt = torch.tensor(x, requires_grad=True)
+    h0t = torch.tensor(h0, requires_grad=True)
+    packed = pack_padded_sequence(xt, torch.tensor(lengths), enforce_sorted=False)
+    if c0 is not None:
+        c0t = torch.tensor(c0, requires_grad=True)
+        out, (hT, cT) = module(packed, (h0t, c0t))
+    else:
+        c0t, cT = None, None
+        out, hT = module(packed, h0t)
+    y, _ = pad_packed_sequence(out, total_length=x.shape[0])
+    loss = (y * torch.tensor(gy)).sum() + (hT * torch.tensor(ghT)).sum()
+    if cT is not None:
+        loss = loss + (cT * torch.tensor(gcT)).sum()
+    loss.backward()
+    return dict(y=y.detach().numpy(), hT=hT.detach().numpy(), cT=None if cT is None else cT.detach().numpy(),
+                dx=xt.grad.numpy(), dh0=h0t.grad.numpy(), dc0=None if c0t is None else c0t.grad.numpy())
+
+
+@pytest.mark.parametrize("mode", ["lstm", "gru"])
+@pytest.mark.parametrize("bidir", [False, True])
+def test_variable_lengths_match_torch_packed_sequences(mode, bidir):
+    rng = _rng(11)
+    T, B, I, H = 7, 5, 3, 4
+    lengths = [7, 3, 1, 5, 6]
+    dirs = 2 if bidir else 1
+    m = (torch.nn.LSTM if mode == "lstm" else torch.nn.GRU)(I, H, bidirectional=bidir).double()
+    x = rng.standard_normal((T, B, I))
+    h0 = rng.standard_normal((dirs, B, H))
+    c0 = rng.standard_normal((dirs, B, H)) if mode == "lstm" else None
+    gy = rng.standard_normal((T, B, dirs * H))
+    ghT = rng.standard_normal((dirs, B, H))
+    gcT = rng.standard_normal((dirs, B, H))
+    ref = _torch_packed(m, x, lengths, h0, c0, gy, ghT, gcT)
+    dx = np.zeros_like(x)
+    for d in range(dirs):
+        sfx = "_l0" + ("_reverse" if d else "")
+        P = [getattr(m, n + sfx).detach().numpy() for n in ("weight_ih", "weight_hh", "bias_ih", "bias_hh")]
+        if mode == "lstm":
+            fw = O.lstm_forward(x, h0[d], c0[d], *P, order=(0, 1, 2, 3), reverse=bool(d), lengths=lengths)
+            gr = O.lstm_backward(fw, gy[:, :, d * H:(d + 1) * H], ghT[d], gcT[d])
+            np.testing.assert_allclose(fw["cT"], ref["cT"][d], atol=1e-12)
+            np.testing.assert_allclose(gr["dc0"], ref["dc0"][d], atol=1e-11)
+        else:
+            fw = O.gru_forward(x, h0[d], *P, reset_after=True, order=(0, 1, 2), reverse=bool(d), lengths=lengths)
+            gr = O.gru_backward(fw, gy[:, :, d * H:(d + 1) * H], ghT[d])
+        np.testing.assert_allclose(fw["y"], ref["y"][:, :, d * H:(d + 1) * H], atol=1e-12)
+        np.testing.assert_allclose(fw["hT"], ref["hT"][d], atol=1e-12)
+        np.testing.assert_allclose(gr["dh0"], ref["dh0"][d], atol=1e-11)
+        for ours, theirs in (("dW_ih", "weight_ih"), ("dW_hh", "weight_hh"), ("db_ih", "bias_ih"), ("db_hh", "bias_hh")):
+            np.testing.assert_allclose(gr[ours], getattr(m, theirs + sfx).grad.numpy(), atol=1e-11)
+        dx += gr["dx"]
+    np.testing.assert_allclose(dx, ref["dx"], atol=1e-11)
+
+
+@pytest.mark.parametrize("mode,ra", [("lstm", None), ("gru", False), ("gru", True)])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_variable_lengths_equal_truncated_sequences(mode, ra, reverse):
+    """Every row equals the fixed-length recurrence over its own first
+    lengths[b] steps (zero steps: outputs zero, state and gradients pass
+    through); the weight gradients are the sums of those runs."""
+    rng = _rng(12)
+    T, B, I, H = 6, 4, 3, 5
+    G = 4 if mode == "lstm" else 3
+    lengths = np.array([6, 2, 0, 4])
+    W_ih, W_hh, b_ih, b_hh = _params(rng, G, H, I)
+
+    class P:
+        pass
+    p = P()
+    p.W_ih, p.W_hh, p.b_ih, p.b_hh = W_ih, W_hh, b_ih, b_hh
+    order = (0, 1, 2, 3) if mode == "lstm" else (0, 1, 2)
+    x = rng.standard_normal((T, B, I))
+    h0 = rng.standard_normal((B, H))
+    c0 = rng.standard_normal((B, H)) if mode == "lstm" else None
+    dy = rng.standard_normal((T, B, H))
+    dhT = rng.standard_normal((B, H))
+    dcT = rng.standard_normal((B, H)) if mode == "lstm" else None
+    fw = O.layer_forward(mode, x, h0, c0, p, order, reverse, bool(ra), lengths=lengths)
+    gr = O.layer_backward(mode, fw, dy, dhT, dcT)
+    acc = {k: np.zeros_like(gr[k]) for k in ("dW_ih", "dW_hh", "db_ih", "db_hh")}
+    for b, L in enumerate(lengths):
+        sub = lambda a: None if a is None else a[b:b + 1]  # noqa: E731
+        if L == 0:
+            np.testing.assert_array_equal(fw["y"][:, b], 0.0)
+            np.testing.assert_array_equal(fw["hT"][b], h0[b])
+            np.testing.assert_array_equal(gr["dh0"][b], dhT[b])
+            np.testing.assert_array_equal(gr["dx"][:, b], 0.0)
+            if mode == "lstm":
+                np.testing.assert_array_equal(fw["cT"][b], c0[b])
+                np.testing.assert_array_equal(gr["dc0"][b], dcT[b])
+            continue
+        fr = O.layer_forward(mode, x[:L, b:b + 1], sub(h0), sub(c0), p, order, reverse, bool(ra))
+        rr = O.layer_backward(mode, fr, dy[:L, b:b + 1], sub(dhT), sub(dcT))
+        np.testing.assert_allclose(fw["y"][:L, b], fr["y"][:, 0], atol=1e-13)
+        np.testing.assert_array_equal(fw["y"][L:, b], 0.0)
+        np.testing.assert_allclose(fw["hT"][b], fr["hT"][0], atol=1e-13)
+        np.testing.assert_allclose(gr["dx"][:L, b], rr["dx"][:, 0], atol=1e-12)
+        np.testing.assert_array_equal(gr["dx"][L:, b], 0.0)
+        np.testing.assert_allclose(gr["dh0"][b], rr["dh0"][0], atol=1e-12)
+        if mode == "lstm":
+            np.testing.assert_allclose(fw["cT"][b], fr["cT"][0], atol=1e-13)
+            np.testing.assert_allclose(gr["dc0"][b], rr["dc0"][0], atol=1e-12)
+        for k in acc:
+            acc[k] += rr[k]
+    for k in acc:
+        np.testing.assert_allclose(gr[k], acc[k], atol=1e-11)
+
+
+def test_full_lengths_equal_no_lengths():
+    rng = _rng(13)
+    T, B, I, H = 5, 3, 2, 4
+    W = _params(rng, 4, H, I)
+    x = rng.standard_normal((T, B, I))
+    a = O.lstm_forward(x, None, None, *W, reverse=True)
+    b = O.lstm_forward(x, None, None, *W, reverse=True, lengths=[T] * B)
+    for k in ("y", "hT", "cT", "c"):
+        np.testing.assert_array_equal(a[k], b[k])
