@@ -33,11 +33,18 @@ class RnnLayer:
     """One layer and direction: descriptor plus its workspace."""
 
     def __init__(self, mode: str, T: int, B: int, I: int, H: int, dtype: str, direction: int = 0,
-                 reset_after: bool = True, gate_order=None, ldx: int = 0, ldy: int = 0, device="cuda"):
+                 reset_after: bool = True, gate_order=None, ldx: int = 0, ldy: int = 0, device="cuda",
+                 lengths=None):
+        """`lengths`: optional int32 device tensor [B] of per-row sequence
+        lengths (kept referenced by the layer; the three calls read it)."""
         self.mode, self.dtype = mode, dtype
         self.T, self.B, self.I, self.H = T, B, I, H
+        if lengths is not None:
+            assert lengths.dtype == torch.int32 and lengths.is_cuda and tuple(lengths.shape) == (B,)
+            lengths = lengths.contiguous()
+        self.lengths = lengths
         self.desc = L.make_desc(MODE_OF[mode], T, B, I, H, DT_OF[dtype], direction,
-                                int(bool(reset_after)), gate_order, ldx, ldy)
+                                int(bool(reset_after)), gate_order, ldx, ldy, _p(lengths))
         self.ws_bytes = L.rnn_workspace_bytes(self.desc)
         if self.ws_bytes == 0:
             raise L.RnnError(L.RNN_ERR_INVALID_ARG, "rnn_workspace_bytes")
@@ -80,7 +87,7 @@ class RnnStack:
     """
 
     def __init__(self, mode, T, B, I, H, dtype, layers, bidir, reset_after=True, gate_order=None,
-                 device="cuda"):
+                 device="cuda", lengths=None):
         self.dirs = 2 if bidir else 1
         self.T, self.B, self.I, self.H = T, B, I, H
         self.layers = []
@@ -88,7 +95,7 @@ class RnnStack:
             Il = I if layer == 0 else H * self.dirs
             self.layers.append([
                 RnnLayer(mode, T, B, Il, H, dtype, direction=d, reset_after=reset_after,
-                         gate_order=gate_order, ldx=Il, ldy=H * self.dirs, device=device)
+                         gate_order=gate_order, ldx=Il, ldy=H * self.dirs, device=device, lengths=lengths)
                 for d in range(self.dirs)])
         dt = self.layers[0][0].torch_dtype
         self.ys = [torch.empty(T, B, H * self.dirs, dtype=dt, device=device) for _ in range(layers)]

@@ -495,6 +495,38 @@ __global__ __launch_bounds__(256) void colsum_final(const float* partial, int nc
   *o = from_f<TS>(s);
 }
 
+// Variable sequence lengths: zero the outputs of inactive steps, and gather
+// the gate gradients of each row's step lengths[b]-1 (the first step the
+// reverse direction processes for that row).
+__device__ __forceinline__ int clamp_len(const int* lengths, int b, int T) {
+  const int L = lengths[b];
+  return L < 0 ? 0 : (L > T ? T : L);
+}
+
+// one-dimensional grids: block = (row, block of 256 columns)
+template <typename TS>
+__global__ __launch_bounds__(256) void zero_inactive(TS* y, long long ldy, const int* lengths, int T, int B, int H) {
+  const int ncb = (H + 255) / 256;
+  const long long row = blockIdx.x / ncb;  // (t, b)
+  const int t = (int)(row / B), b = (int)(row - (long long)t * B);
+  const int j = (int)(blockIdx.x - row * ncb) * 256 + threadIdx.x;
+  if (j >= H || t < clamp_len(lengths, b, T)) return;
+  y[row * ldy + j] = from_f<TS>(0.f);
+}
+
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_first_rows(const TS* src, long long lds, int col0, int ncols,
+                                                         const int* lengths, int T, int B, TS* out) {
+  const int ncb = (ncols + 255) / 256;
+  const int b = blockIdx.x / ncb;
+  const int c = (blockIdx.x - b * ncb) * 256 + threadIdx.x;
+  if (c >= ncols) return;
+  const int L = clamp_len(lengths, b, T);
+  TS v = from_f<TS>(0.f);
+  if (L >= 1 && L < T) v = src[((long long)(L - 1) * B + b) * lds + col0 + c];
+  out[(long long)b * ncols + c] = v;
+}
+
 __global__ void fill_i32(int* p, int v, long long n) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -625,6 +657,33 @@ hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, 
                      (TS*)out, out_row0, H, p4, accumulate);
   return hipGetLastError();
 }
+
+template <typename TS>
+hipError_t launch_zero_inactive(void* y, long long ldy, const int* lengths, int T, int B, int H, hipStream_t s) {
+  const long long blocks = (long long)T * B * ((H + 255) / 256);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((zero_inactive<TS>), dim3((unsigned)blocks), dim3(256), 0, s, (TS*)y, ldy, lengths, T, B, H);
+  return hipGetLastError();
+}
+
+template <typename TS>
+hipError_t launch_gather_first_rows(const void* src, long long lds, int col0, int ncols, const int* lengths, int T,
+                                    int B, void* out, hipStream_t s) {
+  const long long blocks = (long long)B * ((ncols + 255) / 256);
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gather_first_rows<TS>), dim3((unsigned)blocks), dim3(256), 0, s, (const TS*)src, lds, col0,
+                     ncols, lengths, T, B, (TS*)out);
+  return hipGetLastError();
+}
+
+template hipError_t launch_zero_inactive<float>(void*, long long, const int*, int, int, int, hipStream_t);
+template hipError_t launch_zero_inactive<bf16>(void*, long long, const int*, int, int, int, hipStream_t);
+template hipError_t launch_gather_first_rows<float>(const void*, long long, int, int, const int*, int, int, void*,
+                                                    hipStream_t);
+template hipError_t launch_gather_first_rows<bf16>(const void*, long long, int, int, const int*, int, int, void*,
+                                                   hipStream_t);
 
 hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

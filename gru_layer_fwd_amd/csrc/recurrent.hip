@@ -385,7 +385,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
   // per-unit state; unit = (batch row bl, hidden unit j) of this workgroup
   float cst[UPT], hst[UPT], bhc[UPT];
   bool live[UPT];
-  int bl_[UPT], j_[UPT];
+  int bl_[UPT], j_[UPT], len_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int unit = tid + u * NTH;
@@ -393,6 +393,8 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     j_[u] = unit - bl_[u] * HS;
     live[u] = unit < UNITS && b0 + bl_[u] < bend;
     cst[u] = hst[u] = bhc[u] = 0.f;
+    len_[u] = T;
+    if (live[u] && a.lengths) len_[u] = min(max(a.lengths[b0 + bl_[u]], 0), T);
     const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
     if (live[u]) {
       if (a.h0) hst[u] = to_f(((const TS*)a.h0)[o]);
@@ -429,11 +431,15 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     // the exchanged vector is stored first; what only later kernels read
     // (y when the ring carries the exchange, saved gates, cell states) is
     // kept in registers and stored after the step counter is published
+    // A step past a row's length (variable lengths) keeps the state, saves
+    // zero gates and outputs zero; the exchange still carries the kept state
+    // (without the ring, y carries it and is zeroed by a later pass).
     float sv[UPT][4], hv[UPT], cv[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
       const int bl = bl_[u], j = j_[u], b = b0 + bl;
+      const bool act = t < len_[u];
       TS* yr = (TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j;
       float h;
       if constexpr (CELL == CELL_LSTM) {
@@ -443,27 +449,30 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         const float zo = red_sum<NW, BG, NCOL>(red, bl, 3 * HS + j) + to_f(pz[u][3]);
         const float ig = sigmoidf_(zi), fg = sigmoidf_(zf), gg = tanhf_(zg), og = sigmoidf_(zo);
         const float c = fg * cst[u] + ig * gg;
-        cst[u] = c;
-        h = og * tanhf_(c);
-        sv[u][0] = ig;
-        sv[u][1] = fg;
-        sv[u][2] = gg;
-        sv[u][3] = og;
-        cv[u] = c;
+        const float hn = og * tanhf_(c);
+        cst[u] = act ? c : cst[u];
+        hst[u] = act ? hn : hst[u];
+        h = hst[u];
+        sv[u][0] = act ? ig : 0.f;
+        sv[u][1] = act ? fg : 0.f;
+        sv[u][2] = act ? gg : 0.f;
+        sv[u][3] = act ? og : 0.f;
+        cv[u] = act ? c : 0.f;
       } else {
         const float r = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(pz[u][0]));
         const float uu = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(pz[u][1]));
         const float nh = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + bhc[u];
         const float c = tanhf_(to_f(pz[u][2]) + r * nh);
-        h = uu * hst[u] + (1.f - uu) * c;
-        hst[u] = h;
-        sv[u][0] = r;
-        sv[u][1] = uu;
-        sv[u][2] = c;
-        sv[u][3] = nh;
+        const float hn = uu * hst[u] + (1.f - uu) * c;
+        hst[u] = act ? hn : hst[u];
+        h = hst[u];
+        sv[u][0] = act ? r : 0.f;
+        sv[u][1] = act ? uu : 0.f;
+        sv[u][2] = act ? c : 0.f;
+        sv[u][3] = act ? nh : 0.f;
         cv[u] = 0.f;
       }
-      hv[u] = h;
+      hv[u] = act ? h : 0.f;  // the output
       if (tiled) xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed, MB)), h, local);
       else xstore(yr, h, local);
     }
@@ -478,9 +487,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
       for (int g = 0; g < 4; ++g) zr[g * H] = from_f<TS>(sv[u][g]);
       if constexpr (CELL == CELL_LSTM) {
         ((TS*)a.cbuf)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(cv[u]);
-        if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(cv[u]);
+        if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(cst[u]);
       }
-      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hv[u]);
+      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hst[u]);
     }
   }
 }
@@ -517,7 +526,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
 
   float hst[UPT], ust[UPT];
   bool live[UPT];
-  int bl_[UPT], j_[UPT];
+  int bl_[UPT], j_[UPT], len_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int unit = tid + u * NTH;
@@ -525,6 +534,8 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
     j_[u] = unit - bl_[u] * HS;
     live[u] = unit < UNITS && b0 + bl_[u] < bend;
     hst[u] = ust[u] = 0.f;
+    len_[u] = T;
+    if (live[u] && a.lengths) len_[u] = min(max(a.lengths[b0 + bl_[u]], 0), T);
     if (live[u] && a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
 
@@ -556,10 +567,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
       const float r = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, j) + to_f(pz[u][0]));
       const float uu = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, HS + j) + to_f(pz[u][1]));
+      const bool act = t < len_[u];
       ust[u] = uu;
       xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u], local);
-      zr[0] = from_f<TS>(r);
-      zr[H] = from_f<TS>(uu);
+      zr[0] = from_f<TS>(act ? r : 0.f);
+      zr[H] = from_f<TS>(act ? uu : 0.f);
     }
     publish(myflag, 2 * s + 1, local);
     // phase B: candidate and new state
@@ -577,10 +589,13 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       const int bl = bl_[u], j = j_[u], b = b0 + bl;
       TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
       const float c = tanhf_(red_sum<NW, BG, HS>(red, bl, j) + to_f(pz[u][2]));
-      const float h = ust[u] * hst[u] + (1.f - ust[u]) * c;
+      const bool act = t < len_[u];
+      // past a row's length the state is kept (and carried through y, which a
+      // later pass zeroes on those steps)
+      const float h = act ? ust[u] * hst[u] + (1.f - ust[u]) * c : hst[u];
       hst[u] = h;
       xstore((TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j, h, local);
-      zr[2 * H] = from_f<TS>(c);
+      zr[2 * H] = from_f<TS>(act ? c : 0.f);
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
     }
     publish(myflag, 2 * s + 2, local);
@@ -625,7 +640,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
 
   float dcar[UPT], hcar[UPT];
   bool live[UPT];
-  int bl_[UPT], j_[UPT];
+  int bl_[UPT], j_[UPT], len_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int unit = tid + u * NTH;
@@ -633,6 +648,8 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     j_[u] = unit - bl_[u] * HS;
     live[u] = unit < UNITS && b0 + bl_[u] < bend;
     dcar[u] = hcar[u] = 0.f;
+    len_[u] = T;
+    if (live[u] && a.lengths) len_[u] = min(max(a.lengths[b0 + bl_[u]], 0), T);
     const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
     if (live[u]) {
       if (CELL == CELL_LSTM && a.dcT) dcar[u] = to_f(((const TS*)a.dcT)[o]);
@@ -659,18 +676,21 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
 #pragma unroll
       for (int g = 0; g < 4; ++g) pz[u][g] = zr[g * H];
-      const bool first = (s == 0);
+      // the row's first processed step takes its previous state from h0/c0
+      // (direction 1 with variable lengths: the row's own last step)
+      const bool first = a.dir ? (t == len_[u] - 1) : (t == 0);
+      const bool inseq = tp >= 0 && tp < T;
       if constexpr (CELL == CELL_LSTM) {
         pc[u] = ((const TS*)a.cbuf)[row * H + jj];
         pvalid[u] = on && (!first || a.c0);
         const TS* cprev = (first && a.c0) ? (const TS*)a.c0 + o
-                        : (const TS*)a.cbuf + (first || !on ? 0 : ((long long)tp * B + b0 + bl_[u]) * H + jj);
+                        : (const TS*)a.cbuf + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * H + jj);
         pprev[u] = *cprev;
       } else {
         pc[u] = from_f<TS>(0.f);
         pvalid[u] = on && (!first || a.h0);
         const TS* hprev = (first && a.h0) ? (const TS*)a.h0 + o
-                        : (const TS*)a.y + (first || !on ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
+                        : (const TS*)a.y + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
         pprev[u] = *hprev;
       }
     }
@@ -703,19 +723,23 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
       const long long row = (long long)t * B + b0 + bl_[u];
-      const float dh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + to_f(pdy[u]) + hcar[u];
+      // a step past the row's length has zero gate gradients; the gradient
+      // arriving at it is carried on unchanged
+      const bool act = t < len_[u];
+      const float dh_in = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + hcar[u];
+      const float dh = dh_in + to_f(pdy[u]);
       TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
       if constexpr (CELL == CELL_LSTM) {
         const float ig = to_f(pz[u][0]), fg = to_f(pz[u][1]), gg = to_f(pz[u][2]), og = to_f(pz[u][3]);
         const float c = to_f(pc[u]), cp = pvalid[u] ? to_f(pprev[u]) : 0.f;
         const float tc = tanhf_(c);
-        const float d_o = dh * tc * og * (1.f - og);
         const float dc = dh * og * (1.f - tc * tc) + dcar[u];
-        const float d_i = dc * gg * ig * (1.f - ig);
-        const float d_f = dc * cp * fg * (1.f - fg);
-        const float d_g = dc * ig * (1.f - gg * gg);
-        dcar[u] = dc * fg;
-        hcar[u] = 0.f;
+        const float d_o = act ? dh * tc * og * (1.f - og) : 0.f;
+        const float d_i = act ? dc * gg * ig * (1.f - ig) : 0.f;
+        const float d_f = act ? dc * cp * fg * (1.f - fg) : 0.f;
+        const float d_g = act ? dc * ig * (1.f - gg * gg) : 0.f;
+        dcar[u] = act ? dc * fg : dcar[u];
+        hcar[u] = act ? 0.f : dh_in;
         dv[u][0] = d_i;
         dv[u][1] = d_f;
         dv[u][2] = d_g;
@@ -736,10 +760,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       } else {
         const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]), nh = to_f(pz[u][3]);
         const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
-        const float d_c = dh * (1.f - uu) * (1.f - c * c);
-        const float d_u = dh * (hp - c) * uu * (1.f - uu);
+        const float d_c = act ? dh * (1.f - uu) * (1.f - c * c) : 0.f;
+        const float d_u = act ? dh * (hp - c) * uu * (1.f - uu) : 0.f;
         const float d_r = d_c * nh * r * (1.f - r);
-        hcar[u] = dh * uu;
+        hcar[u] = act ? dh * uu : dh_in;
         dv[u][0] = d_r;
         dv[u][1] = d_u;
         dv[u][2] = d_c;  // input side only: read by later kernels
@@ -799,7 +823,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
 
   float hcar[UPT], dhs[UPT], rs[UPT], us[UPT], hps[UPT];
   bool live[UPT];
-  int bl_[UPT], j_[UPT];
+  int bl_[UPT], j_[UPT], len_[UPT];
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int unit = tid + u * NTH;
@@ -807,6 +831,8 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     j_[u] = unit - bl_[u] * HS;
     live[u] = unit < UNITS && b0 + bl_[u] < bend;
     hcar[u] = dhs[u] = rs[u] = us[u] = hps[u] = 0.f;
+    len_[u] = T;
+    if (live[u] && a.lengths) len_[u] = min(max(a.lengths[b0 + bl_[u]], 0), T);
     if (live[u] && a.dhT) hcar[u] = to_f(((const TS*)a.dhT)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
 
@@ -825,10 +851,11 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
 #pragma unroll
       for (int g = 0; g < 3; ++g) pz[u][g] = zr[g * H];
-      const bool first = (s == 0);
+      const bool first = a.dir ? (t == len_[u] - 1) : (t == 0);
+      const bool inseq = tp >= 0 && tp < T;
       pvalid[u] = on && (!first || a.h0);
       const TS* hprev = (first && a.h0) ? (const TS*)a.h0 + (on ? (long long)(b0 + bl_[u]) * H + jj : 0)
-                      : (const TS*)a.y + (first || !on ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
+                      : (const TS*)a.y + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
       pprev[u] = *hprev;
     }
     {
@@ -856,15 +883,19 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
       const long long row = (long long)t * B + b0 + bl_[u];
-      const float dh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + to_f(pdy[u]) + hcar[u];
+      // past the row's length: zero gate gradients, carry passed on unchanged
+      const bool act = t < len_[u];
+      const float dh_in = red_sum<NW, BG, HS>(red, bl_[u], j_[u]) + hcar[u];
+      const float dh = dh_in + to_f(pdy[u]);
       const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]);
       const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
-      const float d_c = dh * (1.f - uu) * (1.f - c * c);
-      const float d_u = dh * (hp - c) * uu * (1.f - uu);
+      const float d_c = act ? dh * (1.f - uu) * (1.f - c * c) : 0.f;
+      const float d_u = act ? dh * (hp - c) * uu * (1.f - uu) : 0.f;
       TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
       xstore(gr + H, d_u, local);
       xstore(gr + 2 * H, d_c, local);
-      dhs[u] = dh;
+      // an inactive row keeps its incoming carry here (its d_rh is zero)
+      dhs[u] = act ? dh : dh_in;
       rs[u] = r;
       us[u] = uu;
       hps[u] = hp;
@@ -884,9 +915,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       if (!live[u]) continue;
       const long long row = (long long)t * B + b0 + bl_[u];
       const float d_rh = red_sum<NW, BG, HS>(red, bl_[u], j_[u]);
-      const float d_r = d_rh * hps[u] * rs[u] * (1.f - rs[u]);
+      const bool act = t < len_[u];
+      const float d_r = act ? d_rh * hps[u] * rs[u] * (1.f - rs[u]) : 0.f;
       xstore((TS*)a.dg + row * GDH + J0 + j_[u], d_r, local);
-      hcar[u] = d_rh * rs[u] + dhs[u] * us[u];
+      hcar[u] = act ? d_rh * rs[u] + dhs[u] * us[u] : dhs[u];
     }
     publish(myflag, 2 * n + 2, local);
   }

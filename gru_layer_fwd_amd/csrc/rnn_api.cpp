@@ -33,7 +33,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : d->H; }
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -110,6 +110,10 @@ Layout layout(const rnn_desc_t* d) {
   L.xb = off;
   L.xb_bytes = 2 * (size_t)16 * ((d->B + 3) / 4) * 4 * H * s;
   off += up(L.xb_bytes);
+  // per batch row, the gate gradients of its own first step (direction 1
+  // with variable lengths: the weight gradient's h0 term)
+  L.gath = off;
+  off += up((size_t)d->B * L.GD * H * s);
   L.total = off;
   return L;
 }
@@ -307,7 +311,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   int st = check_common(d, workspace, ws_bytes);
   if (st) return st;
   if (!x || !W_ih || !W_hh || !b_ih || !b_hh || !y) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT};
+  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, d->lengths};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
@@ -380,9 +384,22 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.flags = (int*)(ws + L.flags);
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
+  a.lengths = d->lengths;
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, d->H, esz(d));
-  ProfScope ps(L_RFWD, s);
-  return launch_persistent(plan, a, di, s, "fwd");
+  {
+    ProfScope ps(L_RFWD, s);
+    if ((st = launch_persistent(plan, a, di, s, "fwd"))) return st;
+  }
+  // Past a row's length the kernels keep the latched state in y when it is
+  // also their exchange buffer; the output there is zero.
+  if (d->lengths && !a.xbuf) {
+    ProfScope ps(L_FILL, s);
+    const hipError_t e = d->dtype == RNN_BF16
+                             ? rnn::launch_zero_inactive<bf16>(y, a.ldy, d->lengths, d->T, d->B, d->H, s)
+                             : rnn::launch_zero_inactive<float>(y, a.ldy, d->lengths, d->T, d->B, d->H, s);
+    if ((st = hip_status(e))) return st;
+  }
+  return RNN_OK;
 }
 
 RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh, const void* h0, const void* c0,
@@ -391,7 +408,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   int st = check_common(d, workspace, ws_bytes);
   if (st) return st;
   if (!W_ih || !W_hh || !y || !dy) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0};
+  const void* ptrs[] = {W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, d->lengths};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
@@ -445,6 +462,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   a.flags = flags;
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
+  a.lengths = d->lengths;
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
   {
     ProfScope ps(L_RBWD, s);
@@ -477,7 +495,7 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   int st = check_common(d, workspace, ws_bytes);
   if (st) return st;
   if (!x || !y) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh};
+  const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh, d->lengths};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
@@ -547,6 +565,47 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
       if ((st = hip_status(dW(dW_hh, 0, 2LL * H, 0, hprev, H, db_hh)))) return st;
       rnn::RowMap cact = (cell == rnn::CELL_GRU_RA) ? hprev : rows(ws + L.rh, H);
       if ((st = hip_status(dW(dW_hh, 2LL * H, H, ccol, cact, H, db_hh)))) return st;
+    }
+    // Direction 1 with variable lengths: a row b with 0 < L_b < T starts at
+    // step L_b - 1 from h0, where the h_{t-1} map reads y of step L_b (zero
+    // there). Add those rows' dG^T h0 terms from a gathered copy of their
+    // gate gradients. The basic GRU's candidate rows see r*h_{t-1}, which
+    // the forward kept with the right state.
+    if (d->direction == 1 && d->lengths && h0) {
+      char* gath = ws + L.gath;
+      {
+        ProfScope ps(L_FILL, s);
+        const hipError_t e =
+            d->dtype == RNN_BF16
+                ? rnn::launch_gather_first_rows<bf16>(dg, GDH, 0, (int)GDH, d->lengths, d->T, d->B, gath, s)
+                : rnn::launch_gather_first_rows<float>(dg, GDH, 0, (int)GDH, d->lengths, d->T, d->B, gath, s);
+        if ((st = hip_status(e))) return st;
+      }
+      auto corr = [&](long long row0, long long nrows, int col) {
+        rnn::GemmArgs g{};
+        g.a = rows(gath + col * s_el, GDH);
+        g.b = rows(h0, H);
+        g.M = nrows;
+        g.N = H;
+        g.K = d->B;
+        g.c = dW_hh;
+        g.ldc = H;
+        g.c_kind = 1;
+        g.c_row0 = row0;
+        g.H = H;
+        for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+        g.accumulate = 1;
+        g.part = (float*)(ws + L.gemm);
+        g.ws_floats = (long long)L.gemm_floats;
+        ProfScope ps(L_DW, s);
+        return gemm_dt(d->dtype, g, true, true, s);
+      };
+      if (cell == rnn::CELL_LSTM) {
+        if ((st = hip_status(corr(0, 4LL * H, 0)))) return st;
+      } else {
+        if ((st = hip_status(corr(0, 2LL * H, 0)))) return st;
+        if (cell == rnn::CELL_GRU_RA && (st = hip_status(corr(2LL * H, H, ccol)))) return st;
+      }
     }
   } else if (db_hh) {
     if (cell == rnn::CELL_LSTM) {

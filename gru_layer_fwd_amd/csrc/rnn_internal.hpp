@@ -142,6 +142,15 @@ hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, 
 
 hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 
+// y[t][b][0..H) = 0 for every step t >= lengths[b] (clamped to [0, T]).
+template <typename TS>
+hipError_t launch_zero_inactive(void* y, long long ldy, const int* lengths, int T, int B, int H, hipStream_t s);
+// out[b][0..ncols) = src[((L_b - 1) * B + b) * lds + col0 + ..] when 1 <= L_b < T
+// (L_b = lengths[b] clamped to [0, T]), zero otherwise.
+template <typename TS>
+hipError_t launch_gather_first_rows(const void* src, long long lds, int col0, int ncols, const int* lengths, int T,
+                                    int B, void* out, hipStream_t s);
+
 // ------------------------------------------------- persistent recurrences --
 // step counters sit on their own 128-byte lines (stride in ints)
 constexpr int FSTRIDE = 32;
@@ -179,6 +188,7 @@ struct RecArgs {
   char* xbuf;
   long long xg_bytes;
   int xpacked;      // two k-steps of 8 rows per 1 KiB tile (batch groups of <= 8 rows)
+  const int* lengths;  // per batch row step count (NULL: T); clamped to [0, T]
 };
 
 struct RecPlan {

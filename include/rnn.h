@@ -82,6 +82,20 @@ typedef struct rnn_desc {
   int T, B, I, H;    /* T,B >= 1; I % 8 == 0; H % 16 == 0 */
   long long ldx;     /* row stride of x/dx in elements, 0 = I; multiple of 8 */
   long long ldy;     /* row stride of y/dy in elements, 0 = H; multiple of 8 */
+  const int* lengths; /* optional, device memory: int32 lengths[B], the number of
+                        steps of each batch row (values clamped to [0, T]); NULL =
+                        every row has T steps. Step t is active for row b iff
+                        t < lengths[b] (popnn Gru.cpp / Lstm.cpp per-batch step
+                        limits, "batchwiseFlags": masked gates, zero-filled output
+                        sequence, latched state): an inactive step writes zero to
+                        y and dx, keeps the state and passes the carried gradients
+                        through, so hT/cT are the state after the row's last
+                        active step and dh0/dc0 the gradients reaching its first;
+                        in direction 1 a row starts at its own step lengths[b]-1
+                        from h0/c0. The same array must be given to the three
+                        calls and stay unchanged between them, and the y passed
+                        to the backward calls is rnn_fwd's (zero past each
+                        row's length). */
 } rnn_desc_t;
 
 /* Bytes of workspace the three calls need for this descriptor (0 if invalid). */

@@ -28,14 +28,16 @@ def host(t):
 
 
 def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=0, reset_after=True,
-              order=None, xpad=0, ypad=0, want_dx=True, acc=False, repeat=1):
+              order=None, xpad=0, ypad=0, want_dx=True, acc=False, repeat=1, lengths=None):
     """Forward, backward-data and backward-weights of one layer on the GPU.
-    xpad/ypad > 0 store x/dx and y/dy with a larger row stride."""
+    xpad/ypad > 0 store x/dx and y/dy with a larger row stride; lengths is
+    an optional host array of B per-row step counts."""
     T, B, I = x.shape
     H = params.W_hh.shape[1]
     ldx, ldy = I + xpad, H + ypad
+    lens = None if lengths is None else torch.as_tensor(np.asarray(lengths), dtype=torch.int32).to("cuda")
     lay = RnnLayer(mode, T, B, I, H, dtype, direction=direction, reset_after=reset_after,
-                   gate_order=order, ldx=ldx, ldy=ldy)
+                   gate_order=order, ldx=ldx, ldy=ldy, lengths=lens)
     dt = TDT[dtype]
     xs = torch.zeros(T, B, ldx, dtype=dt, device="cuda")
     xs[:, :, :I] = dev(x, dtype)
@@ -74,10 +76,12 @@ def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=
     return out if repeat > 1 else out[0]
 
 
-def oracle_layer(mode, params, x, h0, c0, dy, dhT=None, dcT=None, direction=0, reset_after=True, order=None):
+def oracle_layer(mode, params, x, h0, c0, dy, dhT=None, dcT=None, direction=0, reset_after=True, order=None,
+                 lengths=None):
     if order is None:
         order = (0, 1, 2, 3) if mode == "lstm" else (0, 1, 2)
-    fw = O.layer_forward(mode, x, h0, c0, params, order, reverse=bool(direction), reset_after=reset_after)
+    fw = O.layer_forward(mode, x, h0, c0, params, order, reverse=bool(direction), reset_after=reset_after,
+                         lengths=lengths)
     gr = O.layer_backward(mode, fw, dy, dhT, dcT)
     r = dict(y=fw["y"], hT=fw["hT"], dx=gr["dx"], dh0=gr["dh0"], dW_ih=gr["dW_ih"], dW_hh=gr["dW_hh"],
              db_ih=gr["db_ih"], db_hh=gr["db_hh"])

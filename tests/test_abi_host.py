@@ -100,3 +100,35 @@ def test_profile_hook_without_device_work():
     assert g._lib.rnn_profile_enable(True) == 0
     assert g._lib.rnn_profile_read() == {}
     assert g._lib.rnn_profile_enable(False) == 0
+
+
+def test_descriptor_layout_matches_the_header(tmp_path):
+    """The ctypes descriptor has the C struct's size and field offsets
+    (compiled from include/rnn.h with the host compiler)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    fields = [f[0] for f in L.RnnDesc._fields_]
+    src = tmp_path / "off.c"
+    src.write_text("#include <stdio.h>\n#include <stddef.h>\n#include \"rnn.h\"\nint main(void){\n"
+                   "printf(\"size %zu\\n\", sizeof(rnn_desc_t));\n"
+                   + "".join(f"printf(\"{f} %zu\\n\", offsetof(rnn_desc_t, {f}));\n" for f in fields)
+                   + "return 0;}\n")
+    exe = tmp_path / "off"
+    subprocess.run([cc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = dict(line.split() for line in subprocess.run([str(exe)], capture_output=True, text=True,
+                                                        check=True).stdout.splitlines())
+    assert int(out["size"]) == ctypes.sizeof(L.RnnDesc)
+    for f in fields:
+        assert int(out[f]) == getattr(L.RnnDesc, f).offset, f
+
+
+def test_misaligned_lengths_rejected_before_device_work():
+    d = _desc(lengths=20)
+    n = g.rnn_workspace_bytes(d)
+    assert n > 0
+    assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_weights(d, 16, 0, 16, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG

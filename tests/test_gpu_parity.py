@@ -25,11 +25,13 @@ def _case(name, **changes):
     return wl, inp, Params(p.W_ih, p.W_hh, p.b_ih, p.b_hh)
 
 
-def _run(wl, inp, P, direction=0, order=None, dhT=None, dcT=None, **kw):
+def _run(wl, inp, P, direction=0, order=None, dhT=None, dcT=None, lengths=None, **kw):
     mode, dt = wl.mode, wl.dtype
     ra = wl.reset_after
-    got = gpu_layer(mode, dt, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order, **kw)
-    ref = oracle_layer(mode, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order)
+    got = gpu_layer(mode, dt, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order,
+                    lengths=lengths, **kw)
+    ref = oracle_layer(mode, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order,
+                       lengths=lengths)
     return got, ref
 
 
@@ -122,7 +124,7 @@ def test_bf16_medium(name, changes):
 
 # ------------------------------------------------------- full sizes -------
 
-def _sampled(name, rows, direction=0):
+def _sampled(name, rows, direction=0, lengths=None):
     wl = W[name]
     inp = synth.make_inputs(wl)
     p = inp["params"][0][0]
@@ -132,10 +134,10 @@ def _sampled(name, rows, direction=0):
     mask[rows] = True
     g[:, ~mask] = 0.0
     got = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], g, None, None, direction,
-                    wl.reset_after)
+                    wl.reset_after, lengths=lengths)
     sub = lambda a: None if a is None else a[rows]  # noqa: E731
     ref = oracle_layer(wl.mode, P, inp["x"][:, rows], sub(inp["h0"]), sub(inp["c0"]), g[:, rows], None, None,
-                       direction, wl.reset_after)
+                       direction, wl.reset_after, lengths=sub(lengths))
     return wl, got, ref
 
 
@@ -182,3 +184,49 @@ def test_bidir_two_layer_stack_full_size_sampled_rows():
     print(errs)
     assert errs["y"] <= 1e-4, errs
     assert all(v <= 1e-3 for k, v in errs.items() if k != "y"), errs
+
+
+# ------------------------------------------------- variable lengths -------
+
+def _ragged_lengths(B, T, seed):
+    """Per-row step counts with the special values 0, 1, T-1 and T present."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(0, T + 1, size=B)
+    L[: min(B, 4)] = [0, 1, T - 1, T][: min(B, 4)]
+    return rng.permutation(L).astype(np.int32)
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
+def test_variable_lengths_f32_small(cell, direction):
+    # nonzero h0/c0, so that direction 1 checks each row starting from them
+    # at its own last step
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=11, B=13, I=40, H=48, w_scale=0.15, h0_std=0.5, c0_std=0.5)
+    if cell != "lstm":
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    L = _ragged_lengths(wl.B, wl.T, 7 + direction)
+    got, ref = _run(wl, inp, P, direction, lengths=L)
+    print(compare(got, ref, "f32", extra=f"{cell} dir{direction} lengths={L.tolist()}"))
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("cell,H", [("lstm", 48), ("lstm", 256), ("gru_ra", 48), ("gru_ra", 128)])
+def test_variable_lengths_bf16_medium(cell, H, direction):
+    # H=48 in bf16 runs without the exchange ring (y carries the state and a
+    # later pass zeroes it past each row's length); the larger H use the ring
+    name = "lstm_bf16_t256_b64_i1024_h1024" if cell == "lstm" else "grura_bf16_t128_b128_i2048_h2048"
+    wl, inp, P = _case(name, T=14, B=24, I=64, H=H, h0_std=0.3, c0_std=0.3)
+    L = _ragged_lengths(wl.B, wl.T, 11 + direction)
+    got, ref = _run(wl, inp, P, direction, lengths=L)
+    print(compare(got, ref, "bf16", extra=f"{cell} H{H} dir{direction}"))
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_headline_lstm_bf16_variable_lengths_sampled_rows(direction):
+    wl = W["lstm_bf16_t256_b64_i1024_h1024"]
+    L = _ragged_lengths(wl.B, wl.T, 3)
+    rows = [int(np.argmin(L)), int(np.argmax(L)), 17, 40]
+    wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction, lengths=L)
+    print(compare(got, ref, "bf16", rows=rows))
