@@ -230,3 +230,41 @@ def test_headline_lstm_bf16_variable_lengths_sampled_rows(direction):
     rows = [int(np.argmin(L)), int(np.argmax(L)), 17, 40]
     wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction, lengths=L)
     print(compare(got, ref, "bf16", rows=rows))
+
+
+@pytest.mark.parametrize("mode", ["lstm", "gru"])
+def test_bidir_stack_variable_lengths(mode):
+    """Two bidirectional layers sharing one lengths array and nonzero h0/c0:
+    the reverse halves start each row at its own last step in both layers."""
+    import oracle as O
+    from gru_layer_fwd_amd.api import RnnStack
+    from rnn_harness import dev, host
+    T, B, I, H = 10, 7, 32, 48
+    base = "bilstm2_f32_t512_b32_i512_h512" if mode == "lstm" else "grura_f32_t64_b16_i256_h256"
+    wl = synth.small(W[base], T=T, B=B, I=I, H=H, layers=2, bidir=True, w_scale=0.15)
+    inp = synth.make_inputs(wl)
+    rng = np.random.default_rng(5)
+    h0 = rng.standard_normal((B, H)) * 0.5
+    c0 = rng.standard_normal((B, H)) * 0.5 if mode == "lstm" else None
+    L = _ragged_lengths(B, T, 9)
+    order = (0, 1, 2, 3) if mode == "lstm" else (0, 1, 2)
+    lens = torch.as_tensor(L, dtype=torch.int32).to("cuda")
+    st = RnnStack(mode, T, B, I, H, "f32", 2, True, lengths=lens)
+    params = [[tuple(dev(a, "f32") for a in (p.W_ih, p.W_hh, p.b_ih, p.b_hh)) for p in per] for per in inp["params"]]
+    grads = [[tuple(torch.zeros_like(t) for t in pd) for pd in per] for per in params]
+    x = dev(inp["x"], "f32")
+    dx = torch.empty_like(x)
+    h0d, c0d = dev(h0, "f32"), dev(c0, "f32")
+    y = st.fwd(x, params, h0d, c0d)
+    st.bwd(x, params, dev(inp["g"], "f32"), dx, grads, h0d, c0d)
+    torch.cuda.synchronize()
+    recs, y_ref = O.stack_forward(mode, inp["x"], inp["params"], order, True, True, h0, c0, lengths=L)
+    gr_ref, dx_ref = O.stack_backward(mode, recs, inp["g"])
+    errs = {"y": O.rel_err(host(y), y_ref), "dx": O.rel_err(host(dx), dx_ref)}
+    for li in range(2):
+        for d in range(2):
+            for k, t in zip(("dW_ih", "dW_hh", "db_ih", "db_hh"), grads[li][d]):
+                errs[f"L{li}d{d}.{k}"] = O.rel_err(host(t), gr_ref[li][d][k])
+    print(errs)
+    assert errs["y"] <= 1e-4, errs
+    assert all(v <= 1e-3 for k, v in errs.items() if k != "y"), errs
