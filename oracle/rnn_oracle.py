@@ -21,6 +21,13 @@ order and notation of the pages it follows:
 * GRU backward: popnn Gru.cpp page, "backwardStepImpl" (basic) and
   "backwardStepImplResetAfter"; weight gradients "basicGruParamUpdate";
   cross-checked by the GRU (linear-before-reset) branch of the CUDA fragment.
+* AUGRU: popnn Gru.cpp page, the attention-score branch of the GRU forward
+  step ("UpdateScores": the update gate becomes u - a*u with a = att[t, b],
+  one score per step and batch row) and of the backward step
+  ("AttentionsGrad": the score gradient is minus the sum over hidden units
+  of the update-gate gradient times the unscaled gate). Written here as the
+  plain chain rule of h = ua*h_prev + (1-ua)*c with ua = (1-a)*u; the
+  unscaled u is kept, so no division by 1-a is needed.
 
 Conventions (readings where the pages leave a point open):
 * Gate storage order: order[k] is the gate id stored in row block k of W_ih,
@@ -175,16 +182,20 @@ def lstm_backward(fw, dy, dhT=None, dcT=None):
 
 # ----------------------------------------------------------------- GRU ----
 
-def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), reverse=False, lengths=None):
+def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), reverse=False, lengths=None,
+                att=None):
     """GRU layer forward over x [T, B, I] (basic or reset-after variant).
 
     Returns y, hT and the per-step r, u, c (activated), n_h (reset-after:
     h_prev W_hc^T + b_hc, saved before the reset gate is applied) and
-    rh = r*h_prev (basic: the activation the candidate weights see)."""
+    rh = r*h_prev (basic: the activation the candidate weights see).
+    att [T, B] (AUGRU) scales the update gate: ua = (1 - att[t, b]) * u."""
     x, W_ih, W_hh, b_ih, b_hh = map(_f64, (x, W_ih, W_hh, b_ih, b_hh))
     T, B, _ = x.shape
     H = W_hh.shape[1]
     L = _lengths(lengths, T, B)
+    A = None if att is None else _f64(att)
+    assert A is None or A.shape == (T, B), "att must be [T, B]"
     h = np.zeros((B, H)) if h0 is None else _f64(h0).copy()
     sr, su, sc = (_slot(order, k, H) for k in (GRU_R, GRU_U, GRU_C))
     st = {k: np.zeros((T, B, H)) for k in ("r", "u", "c", "nh", "rh", "y")}
@@ -202,12 +213,13 @@ def gru_forward(x, h0, W_ih, W_hh, b_ih, b_hh, reset_after, order=(0, 1, 2), rev
             rh = r * h
             c = np.tanh(xi[:, sc] + rh @ W_hh[sc].T + b_hh[sc])
             st["rh"][t] = np.where(m, rh, 0.0)
-        h_new = u * h + (1 - u) * c
+        ua = u if A is None else (1 - A[t][:, None]) * u   # attention-scaled update gate
+        h_new = ua * h + (1 - ua) * c
         h = np.where(m, h_new, h)                 # state latched past a row's limit
         st["r"][t], st["u"][t], st["c"][t] = (np.where(m, v, 0.0) for v in (r, u, c))
         st["y"][t] = np.where(m, h_new, 0.0)
     st.update(hT=h, x=x, h0=h0, W_ih=W_ih, W_hh=W_hh, order=tuple(order),
-              reverse=reverse, reset_after=reset_after, lengths=L)
+              reverse=reverse, reset_after=reset_after, lengths=L, att=A)
     return st
 
 
@@ -216,7 +228,8 @@ def gru_backward(fw, dy, dhT=None):
 
     Returns dx, dh0, dW_ih, dW_hh, db_ih, db_hh and the per-step
     pre-activation gradients dGi (input side: [d_r, d_u, d_c]) and dGh
-    (recurrent side), both [T,B,3H] in storage order."""
+    (recurrent side), both [T,B,3H] in storage order; with attention scores
+    also datt [T, B]."""
     x, W_ih, W_hh, order, reverse = fw["x"], fw["W_ih"], fw["W_hh"], fw["order"], fw["reverse"]
     ra = fw["reset_after"]
     T, B, _ = x.shape
@@ -233,14 +246,21 @@ def gru_backward(fw, dy, dhT=None):
     dGi_all = np.zeros((T, B, 3 * H))
     dGh_all = np.zeros((T, B, 3 * H))
     L = fw["lengths"]
+    A = fw.get("att")
+    datt = None if A is None else np.zeros((T, B))
     for t in reversed(list(_steps(T, reverse))):
         m = (t < L)[:, None]
         first = _first(t, L, T, reverse)
         h_prev = _prev(fw["y"], t, first, h0, reverse)
         r, u, c = fw["r"][t], fw["u"][t], fw["c"][t]
+        s = 1.0 if A is None else (1 - A[t][:, None])   # update-gate scale
+        ua = s * u
         dh = dy[t] + carry
-        d_c = dh * (1 - u) * (1 - c * c)
-        d_u = dh * (h_prev - c) * u * (1 - u)
+        d_c = dh * (1 - ua) * (1 - c * c)
+        d_ua = dh * (h_prev - c)                  # gradient wrt the scaled gate
+        d_u = d_ua * s * u * (1 - u)
+        if A is not None:
+            datt[t] = np.where(m[:, 0], -(d_ua * u).sum(axis=1), 0.0)
         dGi = np.zeros((B, 3 * H))
         dGh = np.zeros((B, 3 * H))
         if ra:
@@ -248,7 +268,7 @@ def gru_backward(fw, dy, dhT=None):
             dGi[:, sr], dGi[:, su], dGi[:, sc] = d_r, d_u, d_c
             dGh[:, sr], dGh[:, su], dGh[:, sc] = d_r, d_u, d_c * r
             dGi, dGh = np.where(m, dGi, 0.0), np.where(m, dGh, 0.0)
-            carry = np.where(m, dGh @ W_hh + dh * u, carry)
+            carry = np.where(m, dGh @ W_hh + dh * ua, carry)
             dW_hh += dGh.T @ h_prev
         else:
             d_rh = d_c @ W_hh[sc]                 # gradient wrt r*h_prev
@@ -256,7 +276,7 @@ def gru_backward(fw, dy, dhT=None):
             dGi[:, sr], dGi[:, su], dGi[:, sc] = d_r, d_u, d_c
             dGi = np.where(m, dGi, 0.0)
             dGh[:] = dGi
-            carry = np.where(m, d_rh * r + dh * u + dGh[:, sr] @ W_hh[sr] + dGh[:, su] @ W_hh[su], carry)
+            carry = np.where(m, d_rh * r + dh * ua + dGh[:, sr] @ W_hh[sr] + dGh[:, su] @ W_hh[su], carry)
             dW_hh[sr] += dGh[:, sr].T @ h_prev
             dW_hh[su] += dGh[:, su].T @ h_prev
             dW_hh[sc] += dGh[:, sc].T @ fw["rh"][t]
@@ -265,17 +285,22 @@ def gru_backward(fw, dy, dhT=None):
         dW_ih += dGi.T @ x[t]
         db_ih += dGi.sum(axis=0)
         db_hh += dGh.sum(axis=0)
-    return dict(dx=dx, dh0=carry, dW_ih=dW_ih, dW_hh=dW_hh, db_ih=db_ih,
-                db_hh=db_hh, dGi=dGi_all, dGh=dGh_all)
+    out = dict(dx=dx, dh0=carry, dW_ih=dW_ih, dW_hh=dW_hh, db_ih=db_ih,
+               db_hh=db_hh, dGi=dGi_all, dGh=dGh_all)
+    if datt is not None:
+        out["datt"] = datt
+    return out
 
 
 # ------------------------------------------------------ layer wrappers ----
 
-def layer_forward(mode, x, h0, c0, p, order, reverse=False, reset_after=True, lengths=None):
-    """One layer and direction; p has W_ih, W_hh, b_ih, b_hh."""
+def layer_forward(mode, x, h0, c0, p, order, reverse=False, reset_after=True, lengths=None, att=None):
+    """One layer and direction; p has W_ih, W_hh, b_ih, b_hh; att (GRU
+    only) the AUGRU attention scores [T, B]."""
     if mode == "lstm":
+        assert att is None, "attention scores apply to the GRU only"
         return lstm_forward(x, h0, c0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, order, reverse, lengths)
-    return gru_forward(x, h0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, reset_after, order, reverse, lengths)
+    return gru_forward(x, h0, p.W_ih, p.W_hh, p.b_ih, p.b_hh, reset_after, order, reverse, lengths, att)
 
 
 def layer_backward(mode, fw, dy, dhT=None, dcT=None):

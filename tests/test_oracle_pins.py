@@ -535,3 +535,92 @@ def test_full_lengths_equal_no_lengths():
     b = O.lstm_forward(x, None, None, *W, reverse=True, lengths=[T] * B)
     for k in ("y", "hT", "cT", "c"):
         np.testing.assert_array_equal(a[k], b[k])
+
+
+# ---------------------------------------------------------------- AUGRU --
+# The attention-scaled update gate ua = (1 - a) u has no library routine to
+# compare with; it is pinned by the two ends of the score range (a = 0 is the
+# GRU, itself pinned above; a = 1 closes the update gate, which a GRU with
+# the gate forced shut reproduces) and by finite differences of every
+# gradient, the score gradient included.
+
+def _augru_case(seed, T=5, B=3, I=4, H=6):
+    rng = _rng(seed)
+    P = list(_params(rng, 3, H, I))
+    x = rng.standard_normal((T, B, I))
+    h0 = rng.standard_normal((B, H))
+    att = rng.uniform(0.0, 1.0, (T, B))
+    gy = rng.standard_normal((T, B, H))
+    ghT = rng.standard_normal((B, H))
+    return P, x, h0, att, gy, ghT
+
+
+@pytest.mark.parametrize("ra", [False, True])
+@pytest.mark.parametrize("rev", [False, True])
+def test_augru_zero_scores_are_the_gru(ra, rev):
+    P, x, h0, att, gy, ghT = _augru_case(21)
+    fa = O.gru_forward(x, h0, *P, reset_after=ra, reverse=rev, att=np.zeros_like(att))
+    fg = O.gru_forward(x, h0, *P, reset_after=ra, reverse=rev)
+    ga, gg = O.gru_backward(fa, gy, ghT), O.gru_backward(fg, gy, ghT)
+    for k in ("y", "hT"):
+        np.testing.assert_array_equal(fa[k], fg[k])
+    for k in ("dx", "dh0", "dW_ih", "dW_hh", "db_ih", "db_hh"):
+        np.testing.assert_array_equal(ga[k], gg[k])
+    assert ga["datt"].shape == att.shape and "datt" not in gg
+
+
+@pytest.mark.parametrize("ra", [False, True])
+def test_augru_unit_scores_replace_the_state_by_the_candidate(ra):
+    P, x, h0, att, gy, ghT = _augru_case(22)
+    H = h0.shape[1]
+    fa = O.gru_forward(x, h0, *P, reset_after=ra, att=np.ones_like(att))
+    np.testing.assert_allclose(fa["y"], fa["c"], rtol=0, atol=1e-15)
+    # the same layer with its update gate forced shut (order r,u,c)
+    Q = [a.copy() for a in P]
+    Q[0][H:2 * H] = 0
+    Q[1][H:2 * H] = 0
+    Q[2][H:2 * H] = -60.0
+    Q[3][H:2 * H] = 0
+    fq = O.gru_forward(x, h0, *Q, reset_after=ra)
+    np.testing.assert_allclose(fa["y"], fq["y"], rtol=0, atol=1e-12)
+    ga, gq = O.gru_backward(fa, gy, ghT), O.gru_backward(fq, gy, ghT)
+    keep = np.r_[0:H, 2 * H:3 * H]          # rows of r and c (u rows hold other weights)
+    for k in ("dx", "dh0"):
+        np.testing.assert_allclose(ga[k], gq[k], rtol=0, atol=1e-12)
+    for k in ("dW_ih", "dW_hh", "db_ih", "db_hh"):
+        np.testing.assert_allclose(ga[k][keep], gq[k][keep], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ga[k][H:2 * H], 0.0, atol=1e-15)
+
+
+def _augru_loss(ra, rev, x, h0, P, att, gy, ghT, lengths=None):
+    fw = O.gru_forward(x, h0, *P, reset_after=ra, reverse=rev, lengths=lengths, att=att)
+    return (fw["y"] * gy).sum() + (fw["hT"] * ghT).sum()
+
+
+@pytest.mark.parametrize("ra,rev,lengths", [(False, False, None), (True, True, None),
+                                            (True, False, [5, 0, 3]), (False, True, [2, 5, 4])])
+def test_augru_finite_differences(ra, rev, lengths):
+    P, x, h0, att, gy, ghT = _augru_case(23)
+    fw = O.gru_forward(x, h0, *P, reset_after=ra, reverse=rev, lengths=lengths, att=att)
+    gr = O.gru_backward(fw, gy, ghT)
+    targets = {"datt": att, "dx": x, "dh0": h0, "dW_ih": P[0], "dW_hh": P[1], "db_ih": P[2], "db_hh": P[3]}
+    eps = 1e-6
+    pick = _rng(24)
+    for name, arr in targets.items():
+        flat = arr.reshape(-1)
+        idx = range(flat.size) if name == "datt" else pick.choice(flat.size, size=min(flat.size, 20),
+                                                                    replace=False)
+        for j in idx:
+            old = flat[j]
+            flat[j] = old + eps
+            lp = _augru_loss(ra, rev, x, h0, P, att, gy, ghT, lengths)
+            flat[j] = old - eps
+            lm = _augru_loss(ra, rev, x, h0, P, att, gy, ghT, lengths)
+            flat[j] = old
+            fd = (lp - lm) / (2 * eps)
+            an = gr[name].reshape(-1)[j]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (name, j, fd, an)
+    if lengths is not None:
+        T = x.shape[0]
+        for b, Lb in enumerate(lengths):
+            np.testing.assert_array_equal(gr["datt"][Lb:T, b], 0.0)
