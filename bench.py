@@ -133,6 +133,11 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-rows", type=int, default=0, help="batch rows the CPU oracle runs (0 = all)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--ragged", action="store_true",
+                    help="single-layer workloads: per-row sequence lengths drawn uniformly from [1, T] "
+                         "(the timed work still covers all T steps; value counts T*B)")
+    ap.add_argument("--att", action="store_true",
+                    help="GRU workloads: AUGRU attention scores drawn uniformly from [0, 1], and their gradient")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (a known-size "
                          "kernel for calibrating rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -142,6 +147,7 @@ def main():
               "batch rows with one dW all-reduce, which is not built here)", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     from gru_layer_fwd_amd import _lib as L
@@ -159,8 +165,21 @@ def main():
     grads = [[tuple(torch.empty_like(t) for t in pd) for pd in per] for per in params]
     order = wl.gate_order()
 
+    if (args.ragged or args.att) and (wl.layers != 1 or wl.bidir):
+        raise SystemExit("--ragged / --att apply to single-layer workloads")
+    if args.att and wl.mode != "gru":
+        raise SystemExit("--att applies to GRU workloads")
+    extra_rng = np.random.Generator(np.random.PCG64(wl.seed + 500))
+    lengths = att = datt = None
+    if args.ragged:
+        lengths = torch.from_numpy(extra_rng.integers(1, wl.T + 1, size=wl.B).astype(np.int32)).to("cuda")
+    if args.att:
+        att = dev(synth.round_to(extra_rng.uniform(0.0, 1.0, (wl.T, wl.B)), wl.dtype))
+        datt = torch.empty_like(att)
+
     if wl.layers == 1 and not wl.bidir:
-        lay = RnnLayer(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, reset_after=wl.reset_after, gate_order=order)
+        lay = RnnLayer(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, reset_after=wl.reset_after, gate_order=order,
+                       lengths=lengths, att=att)
         h0, c0 = dev(inp["h0"]), dev(inp["c0"])
         y = torch.empty(wl.T, wl.B, wl.H, dtype=dt, device="cuda")
         hT = torch.empty(wl.B, wl.H, dtype=dt, device="cuda")
@@ -172,7 +191,7 @@ def main():
 
         def step():
             lay.fwd(x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT)
-            lay.bwd_data(W_ih, W_hh, h0, c0, y, g, None, None, dx, dh0, dc0)
+            lay.bwd_data(W_ih, W_hh, h0, c0, y, g, None, None, dx, dh0, dc0, datt=datt)
             lay.bwd_weights(x, h0, y, *grads[0][0])
 
         status = lambda: lay.device_status()  # noqa: E731
@@ -254,7 +273,9 @@ def main():
         "config": {"workload": name, "cell": wl.mode + ("" if wl.mode == "lstm" else
                                                        ("_reset_after" if wl.reset_after else "_basic")),
                    "T": wl.T, "B": wl.B, "I": wl.I, "H": wl.H, "layers": wl.layers,
-                   "bidirectional": wl.bidir, "storage": wl.dtype, "accumulate": "f32"},
+                   "bidirectional": wl.bidir, "storage": wl.dtype, "accumulate": "f32",
+                   **({"lengths": "uniform [1, T] per row"} if args.ragged else {}),
+                   **({"augru_scores": "uniform [0, 1]"} if args.att else {})},
         "roofline": roof,
         "recurrent_us_per_step": rec,
         "kernels": kern,

@@ -29,7 +29,8 @@ _P = _c.c_void_p
 _SIGS = {
     "rnn_workspace_bytes": (_c.c_size_t, [_P]),
     "rnn_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_size_t, _P]),
-    "rnn_bwd_data": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
+    "rnn_bwd_data": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t,
+                                _P]),
     "rnn_bwd_weights": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
     "rnn_last_device_status": (_c.c_int, [_P]),
     "rnn_status_string": (_c.c_char_p, [_c.c_int]),
@@ -52,6 +53,7 @@ class RnnDesc(ctypes.Structure):
         ("ldx", ctypes.c_longlong),
         ("ldy", ctypes.c_longlong),
         ("lengths", ctypes.c_void_p),
+        ("att", ctypes.c_void_p),
     ]
 
 
@@ -85,12 +87,15 @@ class RnnError(RuntimeError):
 
 
 def make_desc(mode: int, T: int, B: int, I: int, H: int, dtype: int, direction: int = 0,
-              reset_after: int = 1, gate_order=None, ldx: int = 0, ldy: int = 0, lengths: int = 0) -> RnnDesc:
-    """`lengths`: device address of int32[B] sequence lengths (0 = all T)."""
+              reset_after: int = 1, gate_order=None, ldx: int = 0, ldy: int = 0, lengths: int = 0,
+              att: int = 0) -> RnnDesc:
+    """`lengths`: device address of int32[B] sequence lengths (0 = all T);
+    `att`: device address of the [T][B] AUGRU attention scores (0 = none)."""
     d = RnnDesc()
     d.mode, d.direction, d.reset_after, d.dtype = mode, direction, reset_after, dtype
     d.T, d.B, d.I, d.H, d.ldx, d.ldy = T, B, I, H, ldx, ldy
     d.lengths = lengths or None
+    d.att = att or None
     if gate_order is None:
         gate_order = (0, 1, 2, 3) if mode == RNN_LSTM else (0, 1, 2)
     order = list(gate_order) + [0] * (4 - len(gate_order))
@@ -108,10 +113,10 @@ def rnn_fwd(desc, x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, workspace, ws_by
                          workspace, ws_bytes, stream)
 
 
-def rnn_bwd_data(desc, W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, accumulate,
+def rnn_bwd_data(desc, W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, datt, accumulate,
                  workspace, ws_bytes, stream) -> int:
     return lib().rnn_bwd_data(ctypes.byref(desc), W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0,
-                              accumulate, workspace, ws_bytes, stream)
+                              datt, accumulate, workspace, ws_bytes, stream)
 
 
 def rnn_bwd_weights(desc, x, h0, y, dW_ih, dW_hh, db_ih, db_hh, accumulate, workspace, ws_bytes,

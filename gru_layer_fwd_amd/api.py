@@ -34,17 +34,23 @@ class RnnLayer:
 
     def __init__(self, mode: str, T: int, B: int, I: int, H: int, dtype: str, direction: int = 0,
                  reset_after: bool = True, gate_order=None, ldx: int = 0, ldy: int = 0, device="cuda",
-                 lengths=None):
+                 lengths=None, att=None):
         """`lengths`: optional int32 device tensor [B] of per-row sequence
-        lengths (kept referenced by the layer; the three calls read it)."""
+        lengths; `att`: optional [T, B] device tensor of AUGRU attention
+        scores in the layer's dtype (GRU only). Both are kept referenced by
+        the layer; the three calls read them."""
         self.mode, self.dtype = mode, dtype
         self.T, self.B, self.I, self.H = T, B, I, H
         if lengths is not None:
             assert lengths.dtype == torch.int32 and lengths.is_cuda and tuple(lengths.shape) == (B,)
             lengths = lengths.contiguous()
-        self.lengths = lengths
+        if att is not None:
+            assert mode == "gru" and att.is_cuda and tuple(att.shape) == (T, B)
+            assert att.dtype == TORCH_DT[DT_OF[dtype]]
+            att = att.contiguous()
+        self.lengths, self.att = lengths, att
         self.desc = L.make_desc(MODE_OF[mode], T, B, I, H, DT_OF[dtype], direction,
-                                int(bool(reset_after)), gate_order, ldx, ldy, _p(lengths))
+                                int(bool(reset_after)), gate_order, ldx, ldy, _p(lengths), _p(att))
         self.ws_bytes = L.rnn_workspace_bytes(self.desc)
         if self.ws_bytes == 0:
             raise L.RnnError(L.RNN_ERR_INVALID_ARG, "rnn_workspace_bytes")
@@ -60,9 +66,9 @@ class RnnLayer:
                "rnn_fwd")
 
     def bwd_data(self, W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0=None, dc0=None, accumulate=False,
-                 stream=None):
+                 stream=None, datt=None):
         _check(L.rnn_bwd_data(self.desc, _p(W_ih), _p(W_hh), _p(h0), _p(c0), _p(y), _p(dy), _p(dhT),
-                              _p(dcT), _p(dx), _p(dh0), _p(dc0), int(bool(accumulate)),
+                              _p(dcT), _p(dx), _p(dh0), _p(dc0), _p(datt), int(bool(accumulate)),
                               _p(self.workspace), self.ws_bytes, _stream(stream)),
                "rnn_bwd_data")
 

@@ -527,6 +527,15 @@ __global__ __launch_bounds__(256) void gather_first_rows(const TS* src, long lon
   out[(long long)b * ncols + c] = v;
 }
 
+template <typename TS>
+__global__ __launch_bounds__(256) void att_reduce(const float* part, int nslices, long long TB, TS* datt, int acc) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= TB) return;
+  float sum = acc ? to_f(datt[i]) : 0.f;
+  for (int s = 0; s < nslices; ++s) sum += part[i * nslices + s];
+  datt[i] = from_f<TS>(sum);
+}
+
 __global__ void fill_i32(int* p, int v, long long n) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -678,6 +687,18 @@ hipError_t launch_gather_first_rows(const void* src, long long lds, int col0, in
   return hipGetLastError();
 }
 
+template <typename TS>
+hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void* datt, int accumulate, hipStream_t s) {
+  const long long blocks = (TB + 255) / 256;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((att_reduce<TS>), dim3((unsigned)blocks), dim3(256), 0, s, part, nslices, TB, (TS*)datt,
+                     accumulate);
+  return hipGetLastError();
+}
+
+template hipError_t launch_att_reduce<float>(const float*, int, long long, void*, int, hipStream_t);
+template hipError_t launch_att_reduce<bf16>(const float*, int, long long, void*, int, hipStream_t);
 template hipError_t launch_zero_inactive<float>(void*, long long, const int*, int, int, int, hipStream_t);
 template hipError_t launch_zero_inactive<bf16>(void*, long long, const int*, int, int, int, hipStream_t);
 template hipError_t launch_gather_first_rows<float>(const void*, long long, int, int, const int*, int, int, void*,

@@ -410,12 +410,17 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
     // loads are issued before the wait and land while it polls
     // (unconditional loads from a valid address: a branch per load would
     // make the compiler wait for each one on the spot)
-    TS pz[UPT][GL];
+    TS pz[UPT][GL], pa[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const TS* zr = (const TS*)a.z + (live[u] ? ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
 #pragma unroll
       for (int g = 0; g < GL; ++g) pz[u][g] = zr[g * H];
+      // AUGRU attention score of this step and row
+      if constexpr (CELL == CELL_GRU_RA) {
+        const TS* ap = a.att ? (const TS*)a.att + (live[u] ? (long long)t * B + b0 + bl_[u] : 0) : zr;
+        pa[u] = *ap;
+      }
     }
     if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
     f4 acc[MB][NT];
@@ -463,7 +468,8 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
         const float uu = sigmoidf_(red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(pz[u][1]));
         const float nh = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + bhc[u];
         const float c = tanhf_(to_f(pz[u][2]) + r * nh);
-        const float hn = uu * hst[u] + (1.f - uu) * c;
+        const float us = a.att ? (1.f - to_f(pa[u])) * uu : uu;  // AUGRU: scaled update gate
+        const float hn = us * hst[u] + (1.f - us) * c;
         hst[u] = act ? hn : hst[u];
         h = hst[u];
         sv[u][0] = act ? r : 0.f;
@@ -542,12 +548,14 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
   for (int s = 0; s < T; ++s) {
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
-    TS pz[UPT][3];
+    TS pz[UPT][3], pa[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       const TS* zr = (const TS*)a.z + (live[u] ? ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
 #pragma unroll
       for (int g = 0; g < 3; ++g) pz[u][g] = zr[g * H];
+      const TS* ap = a.att ? (const TS*)a.att + (live[u] ? (long long)t * B + b0 + bl_[u] : 0) : zr;
+      pa[u] = *ap;  // AUGRU attention score of this step and row
     }
     // phase A: r, u
     if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks);
@@ -568,7 +576,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
       const float r = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, j) + to_f(pz[u][0]));
       const float uu = sigmoidf_(red_sum<NW, BG, 2 * HS>(red, bl, HS + j) + to_f(pz[u][1]));
       const bool act = t < len_[u];
-      ust[u] = uu;
+      ust[u] = a.att ? (1.f - to_f(pa[u])) * uu : uu;  // AUGRU: scaled update gate
       xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u], local);
       zr[0] = from_f<TS>(act ? r : 0.f);
       zr[H] = from_f<TS>(act ? uu : 0.f);
@@ -602,6 +610,20 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
   }
 }
 
+// AUGRU score gradient: sum the per-unit shares of each batch row (in LDS,
+// written before the last barrier) over this workgroup's units, in a fixed
+// order, into the partial of its hidden slice: part[(t*B + b)*nSlices + sl].
+template <int HS>
+__device__ __forceinline__ void att_rows(const float* attl, float* part, int t, int B, int b0, int bend, int nSlices,
+                                         int sl) {
+  for (int r = threadIdx.x; r < bend - b0; r += blockDim.x) {
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < HS; ++j) sum += attl[r * HS + j];
+    part[((long long)t * B + b0 + r) * nSlices + sl] = sum;
+  }
+}
+
 // ----------------------------------------------------- backward kernels --
 // LSTM and reset-after GRU: the carried hidden gradient of step t is
 // dG'_{t+1} W_hh (dG' = [di,df,dg,do], or [d_r, d_u, d_c*r] for the GRU),
@@ -614,6 +636,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
+  float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
   wg_coords(a.nGroups, a.nSlices, grp, sl);
@@ -664,7 +687,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
     // own-unit operands of the step (independent of the exchange), loaded
     // ahead of the wait: dy, saved gates, cell states / previous output
     // (unconditional loads from valid addresses; `on` selects at use)
-    TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT];
+    TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT], pa[UPT];
     bool pvalid[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -674,6 +697,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       const int jj = on ? J0 + j_[u] : 0;
       const TS* zr = (const TS*)a.z + row * GZH + jj;
       pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
+      if constexpr (CELL == CELL_GRU_RA) {
+        const TS* ap = a.att ? (const TS*)a.att + row : (const TS*)a.dy;
+        pa[u] = *ap;
+      }
 #pragma unroll
       for (int g = 0; g < 4; ++g) pz[u][g] = zr[g * H];
       // the row's first processed step takes its previous state from h0/c0
@@ -760,10 +787,16 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       } else {
         const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]), nh = to_f(pz[u][3]);
         const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
-        const float d_c = act ? dh * (1.f - uu) * (1.f - c * c) : 0.f;
-        const float d_u = act ? dh * (hp - c) * uu * (1.f - uu) : 0.f;
+        // AUGRU: the state update uses the scaled gate us = (1 - att) * uu
+        const float sa = a.att ? 1.f - to_f(pa[u]) : 1.f;
+        const float us = sa * uu;
+        const float d_us = dh * (hp - c);
+        const float d_c = act ? dh * (1.f - us) * (1.f - c * c) : 0.f;
+        const float d_u = act ? d_us * sa * uu * (1.f - uu) : 0.f;
         const float d_r = d_c * nh * r * (1.f - r);
-        hcar[u] = act ? dh * uu : dh_in;
+        hcar[u] = act ? dh * us : dh_in;
+        // this unit's share of the score gradient, summed per row below
+        if (a.att) attl[bl_[u] * HS + j_[u]] = act ? -d_us * uu : 0.f;
         dv[u][0] = d_r;
         dv[u][1] = d_u;
         dv[u][2] = d_c;  // input side only: read by later kernels
@@ -783,6 +816,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       }
     }
     publish(myflag, n + 1, local);
+    if (CELL == CELL_GRU_RA && a.att) att_rows<HS>(attl, a.datt_part, t, B, b0, bend, a.nSlices, sl);
     if (tiled) {
       // gate gradients for the later kernels (the ring carried the exchange)
 #pragma unroll
@@ -805,6 +839,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
+  float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
   wg_coords(a.nGroups, a.nSlices, grp, sl);
@@ -840,7 +875,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
     const int s = T - 1 - n;
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
-    TS pdy[UPT], pz[UPT][3], pprev[UPT];
+    TS pdy[UPT], pz[UPT][3], pprev[UPT], pa[UPT];
     bool pvalid[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -849,6 +884,8 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const int jj = on ? J0 + j_[u] : 0;
       const TS* zr = (const TS*)a.z + row * GZH + jj;
       pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
+      const TS* ap = a.att ? (const TS*)a.att + row : (const TS*)a.dy;
+      pa[u] = *ap;
 #pragma unroll
       for (int g = 0; g < 3; ++g) pz[u][g] = zr[g * H];
       const bool first = a.dir ? (t == len_[u] - 1) : (t == 0);
@@ -889,18 +926,23 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
       const float dh = dh_in + to_f(pdy[u]);
       const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]);
       const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
-      const float d_c = act ? dh * (1.f - uu) * (1.f - c * c) : 0.f;
-      const float d_u = act ? dh * (hp - c) * uu * (1.f - uu) : 0.f;
+      // AUGRU: the state update uses the scaled gate (1 - att) * uu
+      const float sa = a.att ? 1.f - to_f(pa[u]) : 1.f;
+      const float d_us = dh * (hp - c);
+      const float d_c = act ? dh * (1.f - sa * uu) * (1.f - c * c) : 0.f;
+      const float d_u = act ? d_us * sa * uu * (1.f - uu) : 0.f;
+      if (a.att) attl[bl_[u] * HS + j_[u]] = act ? -d_us * uu : 0.f;
       TS* gr = (TS*)a.dg + row * GDH + J0 + j_[u];
       xstore(gr + H, d_u, local);
       xstore(gr + 2 * H, d_c, local);
       // an inactive row keeps its incoming carry here (its d_rh is zero)
       dhs[u] = act ? dh : dh_in;
       rs[u] = r;
-      us[u] = uu;
+      us[u] = sa * uu;
       hps[u] = hp;
     }
     publish(myflag, 2 * n + 1, local);
+    if (a.att) att_rows<HS>(attl, a.datt_part, t, B, b0, bend, a.nSlices, sl);
     wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks);
     {
       f4 acc[MB][NT];

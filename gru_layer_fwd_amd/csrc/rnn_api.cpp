@@ -33,7 +33,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : d->H; }
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -48,6 +48,7 @@ bool desc_ok(const rnn_desc_t* d) {
   if (d->dtype != RNN_F32 && d->dtype != RNN_BF16) return false;
   if (d->direction != 0 && d->direction != 1) return false;
   if (d->mode == RNN_GRU && d->reset_after != 0 && d->reset_after != 1) return false;
+  if (d->att && d->mode != RNN_GRU) return false;  // attention scores scale the GRU update gate
   if (d->T < 1 || d->B < 1 || d->I < 1 || d->H < 1) return false;
   const int G = gates(d);
   int seen = 0;
@@ -114,6 +115,9 @@ Layout layout(const rnn_desc_t* d) {
   // with variable lengths: the weight gradient's h0 term)
   L.gath = off;
   off += up((size_t)d->B * L.GD * H * s);
+  // AUGRU: per hidden slice partial score gradients (slices hold >= 16 units)
+  L.attp = off;
+  if (d->att) off += up(TB * (H / 16) * sizeof(float));
   L.total = off;
   return L;
 }
@@ -311,7 +315,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   int st = check_common(d, workspace, ws_bytes);
   if (st) return st;
   if (!x || !W_ih || !W_hh || !b_ih || !b_hh || !y) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, d->lengths};
+  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, d->lengths, d->att};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
@@ -385,6 +389,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
   a.lengths = d->lengths;
+  a.att = d->att;
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, d->H, esz(d));
   {
     ProfScope ps(L_RFWD, s);
@@ -404,11 +409,12 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
 
 RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh, const void* h0, const void* c0,
                          const void* y, const void* dy, const void* dhT, const void* dcT, void* dx, void* dh0,
-                         void* dc0, int accumulate, void* workspace, size_t ws_bytes, void* stream) {
+                         void* dc0, void* datt, int accumulate, void* workspace, size_t ws_bytes,
+                         void* stream) {
   int st = check_common(d, workspace, ws_bytes);
   if (st) return st;
   if (!W_ih || !W_hh || !y || !dy) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, d->lengths};
+  const void* ptrs[] = {W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, datt, d->lengths, d->att};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
   DevInfo di;
@@ -463,10 +469,23 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   a.status = (int*)(ws + L.status);
   a.timeout_ticks = di.ticks;
   a.lengths = d->lengths;
+  a.att = d->att;
+  a.datt_part = (float*)(ws + L.attp);
+  // the score-gradient shares of a workgroup's units sit after its reduction buffer
+  if (d->att) plan.lds_bytes += (size_t)plan.mb * 16 * plan.Hs * sizeof(float);
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
   {
     ProfScope ps(L_RBWD, s);
     if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;
+  }
+  if (d->att && datt) {
+    ProfScope ps(L_FILL, s);
+    const long long TB = (long long)d->T * d->B;
+    const hipError_t e =
+        d->dtype == RNN_BF16
+            ? rnn::launch_att_reduce<bf16>(a.datt_part, plan.nSlices, TB, datt, accumulate ? 1 : 0, s)
+            : rnn::launch_att_reduce<float>(a.datt_part, plan.nSlices, TB, datt, accumulate ? 1 : 0, s);
+    if ((st = hip_status(e))) return st;
   }
 
   if (dx) {

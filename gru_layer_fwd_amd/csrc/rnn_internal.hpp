@@ -150,6 +150,11 @@ hipError_t launch_zero_inactive(void* y, long long ldy, const int* lengths, int 
 template <typename TS>
 hipError_t launch_gather_first_rows(const void* src, long long lds, int col0, int ncols, const int* lengths, int T,
                                     int B, void* out, hipStream_t s);
+// datt[t*B + b] = (accumulate ? datt : 0) + sum over s < nslices of
+// part[(t*B + b)*nslices + s], in that order (the AUGRU score gradient).
+template <typename TS>
+hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void* datt, int accumulate, hipStream_t s);
+
 
 // ------------------------------------------------- persistent recurrences --
 // step counters sit on their own 128-byte lines (stride in ints)
@@ -189,6 +194,8 @@ struct RecArgs {
   long long xg_bytes;
   int xpacked;      // two k-steps of 8 rows per 1 KiB tile (batch groups of <= 8 rows)
   const int* lengths;  // per batch row step count (NULL: T); clamped to [0, T]
+  const void* att;     // GRU only: AUGRU attention scores [T][B] (NULL: plain GRU)
+  float* datt_part;    // backward with att: per-slice partial score gradients [T][B][nSlices]
 };
 
 struct RecPlan {

@@ -96,6 +96,13 @@ typedef struct rnn_desc {
                         calls and stay unchanged between them, and the y passed
                         to the backward calls is rnn_fwd's (zero past each
                         row's length). */
+  const void* att;    /* optional, GRU only (else RNN_ERR_INVALID_ARG), device
+                        memory of the storage type: AUGRU attention scores
+                        att[T][B], row t*B+b (popnn Gru.cpp, the attention-score
+                        forward and backward steps): the update gate u of step
+                        t, row b is replaced by (1 - att[t][b]) * u in the state
+                        update h = u*h_prev + (1-u)*c. NULL = plain GRU. The
+                        same array must be given to the three calls. */
 } rnn_desc_t;
 
 /* Bytes of workspace the three calls need for this descriptor (0 if invalid). */
@@ -110,13 +117,18 @@ int rnn_fwd(const rnn_desc_t* desc, const void* x, const void* h0, const void* c
 
 /* Backward through time for the data gradients: dx (overwritten, or added to
  * when accumulate != 0), dh0, dc0, from dy at every step and dhT/dcT.
+ * With attention scores (desc->att), datt [T][B] (storage type; NULL = not
+ * written) receives their gradient, minus the sum over hidden units of the
+ * scaled update gate's gradient times the unscaled gate, zero past a row's
+ * length; it follows the same overwrite / accumulate rule as dx.
  * y, h0 and c0 are the values given to / produced by rnn_fwd. The per-step
  * gate gradients are kept in the workspace for rnn_bwd_weights.
- * Queues: one persistent reverse-time kernel, then the dx GEMM. */
+ * Queues: one persistent reverse-time kernel, the score-gradient sum (with
+ * datt), then the dx GEMM. */
 int rnn_bwd_data(const rnn_desc_t* desc, const void* W_ih, const void* W_hh,
                  const void* h0, const void* c0, const void* y, const void* dy,
                  const void* dhT, const void* dcT, void* dx, void* dh0, void* dc0,
-                 int accumulate, void* workspace, size_t ws_bytes, void* stream);
+                 void* datt, int accumulate, void* workspace, size_t ws_bytes, void* stream);
 
 /* Weight gradients summed over every (t, b): dW_ih = sum dG^T x,
  * dW_hh = sum dG_h^T h_{t-1} (h_{-1} = h0), db_ih, db_hh (popnn

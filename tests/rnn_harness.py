@@ -28,17 +28,20 @@ def host(t):
 
 
 def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=0, reset_after=True,
-              order=None, xpad=0, ypad=0, want_dx=True, acc=False, repeat=1, lengths=None):
+              order=None, xpad=0, ypad=0, want_dx=True, acc=False, repeat=1, lengths=None, att=None):
     """Forward, backward-data and backward-weights of one layer on the GPU.
     xpad/ypad > 0 store x/dx and y/dy with a larger row stride; lengths is
-    an optional host array of B per-row step counts."""
+    an optional host array of B per-row step counts, att optional [T, B]
+    AUGRU attention scores (GRU)."""
     T, B, I = x.shape
     H = params.W_hh.shape[1]
     ldx, ldy = I + xpad, H + ypad
     lens = None if lengths is None else torch.as_tensor(np.asarray(lengths), dtype=torch.int32).to("cuda")
-    lay = RnnLayer(mode, T, B, I, H, dtype, direction=direction, reset_after=reset_after,
-                   gate_order=order, ldx=ldx, ldy=ldy, lengths=lens)
     dt = TDT[dtype]
+    attd = None if att is None else dev(att, dtype)
+    lay = RnnLayer(mode, T, B, I, H, dtype, direction=direction, reset_after=reset_after,
+                   gate_order=order, ldx=ldx, ldy=ldy, lengths=lens, att=attd)
+    datt = None if att is None else torch.zeros(T, B, dtype=dt, device="cuda")
     xs = torch.zeros(T, B, ldx, dtype=dt, device="cuda")
     xs[:, :, :I] = dev(x, dtype)
     ys = torch.full((T, B, ldy), float("nan"), dtype=dt, device="cuda")
@@ -60,7 +63,7 @@ def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=
     out = []
     for _ in range(repeat):
         lay.fwd(xs, h0d, c0d, W_ih, W_hh, b_ih, b_hh, ys, hT, cT)
-        lay.bwd_data(W_ih, W_hh, h0d, c0d, ys, dys, dhTd, dcTd, dxs, dh0, dc0, accumulate=acc)
+        lay.bwd_data(W_ih, W_hh, h0d, c0d, ys, dys, dhTd, dcTd, dxs, dh0, dc0, accumulate=acc, datt=datt)
         lay.bwd_weights(xs, h0d, ys, dW_ih, dW_hh, db_ih, db_hh, accumulate=acc)
         torch.cuda.synchronize()
         st = lay.device_status()
@@ -72,26 +75,30 @@ def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=
             r["dxpad"] = host(dxs[:, :, I:])
         if mode == "lstm":
             r["cT"], r["dc0"] = host(cT), host(dc0)
+        if datt is not None:
+            r["datt"] = host(datt)
         out.append(r)
     return out if repeat > 1 else out[0]
 
 
 def oracle_layer(mode, params, x, h0, c0, dy, dhT=None, dcT=None, direction=0, reset_after=True, order=None,
-                 lengths=None):
+                 lengths=None, att=None):
     if order is None:
         order = (0, 1, 2, 3) if mode == "lstm" else (0, 1, 2)
     fw = O.layer_forward(mode, x, h0, c0, params, order, reverse=bool(direction), reset_after=reset_after,
-                         lengths=lengths)
+                         lengths=lengths, att=att)
     gr = O.layer_backward(mode, fw, dy, dhT, dcT)
     r = dict(y=fw["y"], hT=fw["hT"], dx=gr["dx"], dh0=gr["dh0"], dW_ih=gr["dW_ih"], dW_hh=gr["dW_hh"],
              db_ih=gr["db_ih"], db_hh=gr["db_hh"])
     if mode == "lstm":
         r["cT"], r["dc0"] = fw["cT"], gr["dc0"]
+    if "datt" in gr:
+        r["datt"] = gr["datt"]
     return r
 
 
 FWD_KEYS = ("y", "hT", "cT")
-GRAD_KEYS = ("dx", "dh0", "dc0", "dW_ih", "dW_hh", "db_ih", "db_hh")
+GRAD_KEYS = ("dx", "dh0", "dc0", "dW_ih", "dW_hh", "db_ih", "db_hh", "datt")
 
 
 def compare(got, ref, dtype, keys=None, rows=None, extra=""):
@@ -101,7 +108,7 @@ def compare(got, ref, dtype, keys=None, rows=None, extra=""):
         if k not in ref or k not in got:
             continue
         g, r = got[k], ref[k]
-        if rows is not None and k in ("y", "dx"):
+        if rows is not None and k in ("y", "dx", "datt"):
             g = g[:, rows]
         elif rows is not None and k in ("hT", "cT", "dh0", "dc0"):
             g = g[rows]

@@ -79,12 +79,12 @@ def test_workspace_too_small_and_missing_pointers():
     d = _desc()
     n = g.rnn_workspace_bytes(d)
     assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
-    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
+    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
     assert g.rnn_bwd_weights(d, 16, 0, 16, 0, 0, 0, 0, 0, 256, n - 1, 0) == L.RNN_ERR_WORKSPACE_TOO_SMALL
     # required pointers
     assert g.rnn_fwd(d, 0, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
     assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
-    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 0, 0, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 0, 0, 0, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
     assert g.rnn_bwd_weights(d, 0, 0, 16, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
     assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 0, n, 0) == L.RNN_ERR_INVALID_ARG
     # misaligned tensor pointer
@@ -130,5 +130,16 @@ def test_misaligned_lengths_rejected_before_device_work():
     n = g.rnn_workspace_bytes(d)
     assert n > 0
     assert g.rnn_fwd(d, 16, 0, 0, 16, 16, 16, 16, 16, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
-    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_data(d, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
     assert g.rnn_bwd_weights(d, 16, 0, 16, 0, 0, 0, 0, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+
+
+def test_attention_scores_only_for_the_gru():
+    assert g.rnn_workspace_bytes(_desc(att=256)) == 0           # LSTM with scores: invalid
+    dg = _desc(mode=L.RNN_GRU, gate_order=(0, 1, 2), att=256)
+    n = g.rnn_workspace_bytes(dg)
+    assert n > g.rnn_workspace_bytes(_desc(mode=L.RNN_GRU, gate_order=(0, 1, 2)))  # score partials
+    # misaligned scores or score gradient: rejected before device work
+    assert g.rnn_fwd(_desc(mode=L.RNN_GRU, gate_order=(0, 1, 2), att=260), 16, 0, 0, 16, 16, 16, 16, 16, 0, 0,
+                     256, n, 0) == L.RNN_ERR_INVALID_ARG
+    assert g.rnn_bwd_data(dg, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 20, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG

@@ -25,13 +25,13 @@ def _case(name, **changes):
     return wl, inp, Params(p.W_ih, p.W_hh, p.b_ih, p.b_hh)
 
 
-def _run(wl, inp, P, direction=0, order=None, dhT=None, dcT=None, lengths=None, **kw):
+def _run(wl, inp, P, direction=0, order=None, dhT=None, dcT=None, lengths=None, att=None, **kw):
     mode, dt = wl.mode, wl.dtype
     ra = wl.reset_after
     got = gpu_layer(mode, dt, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order,
-                    lengths=lengths, **kw)
+                    lengths=lengths, att=att, **kw)
     ref = oracle_layer(mode, P, inp["x"], inp["h0"], inp["c0"], inp["g"], dhT, dcT, direction, ra, order,
-                       lengths=lengths)
+                       lengths=lengths, att=att)
     return got, ref
 
 
@@ -124,7 +124,7 @@ def test_bf16_medium(name, changes):
 
 # ------------------------------------------------------- full sizes -------
 
-def _sampled(name, rows, direction=0, lengths=None):
+def _sampled(name, rows, direction=0, lengths=None, att=None):
     wl = W[name]
     inp = synth.make_inputs(wl)
     p = inp["params"][0][0]
@@ -134,10 +134,10 @@ def _sampled(name, rows, direction=0, lengths=None):
     mask[rows] = True
     g[:, ~mask] = 0.0
     got = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], g, None, None, direction,
-                    wl.reset_after, lengths=lengths)
+                    wl.reset_after, lengths=lengths, att=att)
     sub = lambda a: None if a is None else a[rows]  # noqa: E731
     ref = oracle_layer(wl.mode, P, inp["x"][:, rows], sub(inp["h0"]), sub(inp["c0"]), g[:, rows], None, None,
-                       direction, wl.reset_after, lengths=sub(lengths))
+                       direction, wl.reset_after, lengths=sub(lengths), att=None if att is None else att[:, rows])
     return wl, got, ref
 
 
@@ -268,3 +268,45 @@ def test_bidir_stack_variable_lengths(mode):
     print(errs)
     assert errs["y"] <= 1e-4, errs
     assert all(v <= 1e-3 for k, v in errs.items() if k != "y"), errs
+
+
+
+# ------------------------------------------------------------ AUGRU -------
+
+def _scores(T, B, seed, dtype):
+    """Attention scores in [0, 1], rounded to the storage type as the GPU sees them."""
+    from gru_layer_fwd_amd.synth import round_to
+    a = np.random.default_rng(seed).uniform(0.0, 1.0, (T, B))
+    a[0, 0], a[-1, -1] = 0.0, 1.0
+    return round_to(a, dtype)
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("ra", [False, True])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_augru_f32_small(ra, direction, ragged):
+    wl, inp, P = _case("grura_f32_t64_b16_i256_h256", T=11, B=13, I=40, H=48, w_scale=0.15, h0_std=0.5,
+                       reset_after=ra)
+    att = _scores(wl.T, wl.B, 31 + direction, "f32")
+    L = _ragged_lengths(wl.B, wl.T, 17) if ragged else None
+    got, ref = _run(wl, inp, P, direction, lengths=L, att=att)
+    print(compare(got, ref, "f32", extra=f"augru ra={ra} dir{direction} ragged={ragged}"))
+
+
+@pytest.mark.parametrize("H", [48, 128])
+@pytest.mark.parametrize("ra", [False, True])
+def test_augru_bf16_medium(ra, H):
+    wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=14, B=24, I=64, H=H, h0_std=0.3, reset_after=ra)
+    att = _scores(wl.T, wl.B, 41, "bf16")
+    got, ref = _run(wl, inp, P, 1, lengths=_ragged_lengths(wl.B, wl.T, 19), att=att)
+    print(compare(got, ref, "bf16", extra=f"augru ra={ra} H{H}"))
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_augru_bf16_full_size_sampled_rows(direction):
+    wl = W["grura_bf16_t128_b128_i2048_h2048"]
+    att = _scores(wl.T, wl.B, 51, "bf16")
+    L = _ragged_lengths(wl.B, wl.T, 23)
+    rows = [int(np.argmin(L)), int(np.argmax(L)), 77]
+    wl, got, ref = _sampled("grura_bf16_t128_b128_i2048_h2048", rows, direction, lengths=L, att=att)
+    print(compare(got, ref, "bf16", rows=rows))
