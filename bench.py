@@ -136,6 +136,9 @@ def main():
     ap.add_argument("--ragged", action="store_true",
                     help="single-layer workloads: per-row sequence lengths drawn uniformly from [1, T] "
                          "(the timed work still covers all T steps; value counts T*B)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="LSTM workloads: keep only the gates between forward and backward and rebuild the "
+                         "cell states in the backward call")
     ap.add_argument("--att", action="store_true",
                     help="GRU workloads: AUGRU attention scores drawn uniformly from [0, 1], and their gradient")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -165,8 +168,10 @@ def main():
     grads = [[tuple(torch.empty_like(t) for t in pd) for pd in per] for per in params]
     order = wl.gate_order()
 
-    if (args.ragged or args.att) and (wl.layers != 1 or wl.bidir):
-        raise SystemExit("--ragged / --att apply to single-layer workloads")
+    if (args.ragged or args.att or args.recompute) and (wl.layers != 1 or wl.bidir):
+        raise SystemExit("--ragged / --att / --recompute apply to single-layer workloads")
+    if args.recompute and wl.mode != "lstm":
+        raise SystemExit("--recompute applies to LSTM workloads")
     if args.att and wl.mode != "gru":
         raise SystemExit("--att applies to GRU workloads")
     extra_rng = np.random.Generator(np.random.PCG64(wl.seed + 500))
@@ -179,7 +184,7 @@ def main():
 
     if wl.layers == 1 and not wl.bidir:
         lay = RnnLayer(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, reset_after=wl.reset_after, gate_order=order,
-                       lengths=lengths, att=att)
+                       lengths=lengths, att=att, recompute=args.recompute)
         h0, c0 = dev(inp["h0"]), dev(inp["c0"])
         y = torch.empty(wl.T, wl.B, wl.H, dtype=dt, device="cuda")
         hT = torch.empty(wl.B, wl.H, dtype=dt, device="cuda")
@@ -275,7 +280,8 @@ def main():
                    "T": wl.T, "B": wl.B, "I": wl.I, "H": wl.H, "layers": wl.layers,
                    "bidirectional": wl.bidir, "storage": wl.dtype, "accumulate": "f32",
                    **({"lengths": "uniform [1, T] per row"} if args.ragged else {}),
-                   **({"augru_scores": "uniform [0, 1]"} if args.att else {})},
+                   **({"augru_scores": "uniform [0, 1]"} if args.att else {}),
+                   **({"cell_states": "recomputed in the backward call"} if args.recompute else {})},
         "roofline": roof,
         "recurrent_us_per_step": rec,
         "kernels": kern,

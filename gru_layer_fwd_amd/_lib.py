@@ -54,6 +54,7 @@ class RnnDesc(ctypes.Structure):
         ("ldy", ctypes.c_longlong),
         ("lengths", ctypes.c_void_p),
         ("att", ctypes.c_void_p),
+        ("recompute", ctypes.c_int),
     ]
 
 
@@ -88,14 +89,16 @@ class RnnError(RuntimeError):
 
 def make_desc(mode: int, T: int, B: int, I: int, H: int, dtype: int, direction: int = 0,
               reset_after: int = 1, gate_order=None, ldx: int = 0, ldy: int = 0, lengths: int = 0,
-              att: int = 0) -> RnnDesc:
+              att: int = 0, recompute: int = 0) -> RnnDesc:
     """`lengths`: device address of int32[B] sequence lengths (0 = all T);
-    `att`: device address of the [T][B] AUGRU attention scores (0 = none)."""
+    `att`: device address of the [T][B] AUGRU attention scores (0 = none);
+    `recompute`: 1 = LSTM cell states rebuilt in the backward pass."""
     d = RnnDesc()
     d.mode, d.direction, d.reset_after, d.dtype = mode, direction, reset_after, dtype
     d.T, d.B, d.I, d.H, d.ldx, d.ldy = T, B, I, H, ldx, ldy
     d.lengths = lengths or None
     d.att = att or None
+    d.recompute = recompute
     if gate_order is None:
         gate_order = (0, 1, 2, 3) if mode == RNN_LSTM else (0, 1, 2)
     order = list(gate_order) + [0] * (4 - len(gate_order))

@@ -492,7 +492,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) zr[g * H] = from_f<TS>(sv[u][g]);
       if constexpr (CELL == CELL_LSTM) {
-        ((TS*)a.cbuf)[((long long)t * B + b) * H + J0 + j] = from_f<TS>(cv[u]);
+        if (a.cbuf) ((TS*)a.cbuf)[((long long)t * B + b) * a.ldc + J0 + j] = from_f<TS>(cv[u]);
         if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(cst[u]);
       }
       if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hst[u]);
@@ -708,10 +708,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
       const bool first = a.dir ? (t == len_[u] - 1) : (t == 0);
       const bool inseq = tp >= 0 && tp < T;
       if constexpr (CELL == CELL_LSTM) {
-        pc[u] = ((const TS*)a.cbuf)[row * H + jj];
+        pc[u] = ((const TS*)a.cbuf)[row * a.ldc + jj];
         pvalid[u] = on && (!first || a.c0);
         const TS* cprev = (first && a.c0) ? (const TS*)a.c0 + o
-                        : (const TS*)a.cbuf + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * H + jj);
+                        : (const TS*)a.cbuf + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldc + jj);
         pprev[u] = *cprev;
       } else {
         pc[u] = from_f<TS>(0.f);

@@ -49,6 +49,7 @@ bool desc_ok(const rnn_desc_t* d) {
   if (d->direction != 0 && d->direction != 1) return false;
   if (d->mode == RNN_GRU && d->reset_after != 0 && d->reset_after != 1) return false;
   if (d->att && d->mode != RNN_GRU) return false;  // attention scores scale the GRU update gate
+  if (d->recompute != 0 && !(d->recompute == 1 && d->mode == RNN_LSTM)) return false;
   if (d->T < 1 || d->B < 1 || d->I < 1 || d->H < 1) return false;
   const int G = gates(d);
   int seen = 0;
@@ -100,7 +101,7 @@ Layout layout(const rnn_desc_t* d) {
   L.z = off;
   off += up(TB * L.GZ * H * s);
   L.c = off;
-  if (cell == rnn::CELL_LSTM) off += up(TB * H * s);
+  if (cell == rnn::CELL_LSTM && !d->recompute) off += up(TB * H * s);
   L.rh = off;
   if (cell == rnn::CELL_GRU_BASIC) off += up(TB * H * s);
   L.dg = off;
@@ -170,8 +171,8 @@ int check_common(const rnn_desc_t* d, const void* ws, size_t ws_bytes) {
 int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_ERR_DEVICE; }
 
 // ---- optional kernel timing (rnn_profile_*) ----
-enum Label { L_FILL, L_PROJ, L_RFWD, L_RBWD, L_DX, L_DW, L_DB, L_COUNT };
-const char* kLabel[L_COUNT] = {"fill", "proj_gemm", "rec_fwd", "rec_bwd", "dx_gemm", "dw_gemm", "db_colsum"};
+enum Label { L_FILL, L_PROJ, L_RFWD, L_RBWD, L_DX, L_DW, L_DB, L_AUX, L_COUNT };
+const char* kLabel[L_COUNT] = {"fill", "proj_gemm", "rec_fwd", "rec_bwd", "dx_gemm", "dw_gemm", "db_colsum", "aux"};
 struct Pending {
   int label;
   hipEvent_t a, b;
@@ -380,7 +381,8 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.ldy = ldy_of(d);
   a.z = ws + L.z;
   a.GZ = L.GZ;
-  a.cbuf = ws + L.c;
+  a.cbuf = (cell == rnn::CELL_LSTM && !d->recompute) ? ws + L.c : nullptr;
+  a.ldc = d->H;
   a.rh = ws + L.rh;
   a.hT = hT;
   a.cT = (d->mode == RNN_LSTM) ? cT : nullptr;
@@ -398,7 +400,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   // Past a row's length the kernels keep the latched state in y when it is
   // also their exchange buffer; the output there is zero.
   if (d->lengths && !a.xbuf) {
-    ProfScope ps(L_FILL, s);
+    ProfScope ps(L_AUX, s);
     const hipError_t e = d->dtype == RNN_BF16
                              ? rnn::launch_zero_inactive<bf16>(y, a.ldy, d->lengths, d->T, d->B, d->H, s)
                              : rnn::launch_zero_inactive<float>(y, a.ldy, d->lengths, d->T, d->B, d->H, s);
@@ -457,6 +459,22 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   a.z = ws + L.z;
   a.GZ = L.GZ;
   a.cbuf = ws + L.c;
+  a.ldc = d->H;
+  if (d->recompute) {
+    // cell states rebuilt from the saved gates into the input-gate lane of
+    // the gate-gradient rows: step t's lane is read by the BPTT kernel
+    // before its own gradients overwrite it, and by no step after that
+    ProfScope ps(L_AUX, s);
+    const hipError_t e =
+        d->dtype == RNN_BF16
+            ? rnn::launch_lstm_cell_scan<bf16>(ws + L.z, (long long)L.GZ * d->H, c0, d->lengths, d->T, d->B, d->H,
+                                               d->direction, ws + L.dg, (long long)L.GD * d->H, s)
+            : rnn::launch_lstm_cell_scan<float>(ws + L.z, (long long)L.GZ * d->H, c0, d->lengths, d->T, d->B, d->H,
+                                                d->direction, ws + L.dg, (long long)L.GD * d->H, s);
+    if ((st = hip_status(e))) return st;
+    a.cbuf = ws + L.dg;
+    a.ldc = (long long)L.GD * d->H;
+  }
   a.rh = ws + L.rh;
   a.dy = dy;
   a.dhT = dhT;
@@ -479,7 +497,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
     if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;
   }
   if (d->att && datt) {
-    ProfScope ps(L_FILL, s);
+    ProfScope ps(L_AUX, s);
     const long long TB = (long long)d->T * d->B;
     const hipError_t e =
         d->dtype == RNN_BF16
@@ -593,7 +611,7 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
     if (d->direction == 1 && d->lengths && h0) {
       char* gath = ws + L.gath;
       {
-        ProfScope ps(L_FILL, s);
+        ProfScope ps(L_AUX, s);
         const hipError_t e =
             d->dtype == RNN_BF16
                 ? rnn::launch_gather_first_rows<bf16>(dg, GDH, 0, (int)GDH, d->lengths, d->T, d->B, gath, s)

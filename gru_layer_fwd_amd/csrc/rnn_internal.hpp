@@ -152,6 +152,14 @@ hipError_t launch_gather_first_rows(const void* src, long long lds, int col0, in
                                     int B, void* out, hipStream_t s);
 // datt[t*B + b] = (accumulate ? datt : 0) + sum over s < nslices of
 // part[(t*B + b)*nslices + s], in that order (the AUGRU score gradient).
+// LSTM cell states recomputed from the saved activated gates:
+// c_t = f_t*c_{t-1} + i_t*g_t in the direction's order from c0 (NULL = 0),
+// kept past a row's length; out[(t*B+b)*ldo + j] = c_t on active steps and 0
+// otherwise. z rows (t*B+b) hold i, f, g, o in H-column blocks (stride ldz).
+template <typename TS>
+hipError_t launch_lstm_cell_scan(const void* z, long long ldz, const void* c0, const int* lengths, int T, int B,
+                                 int H, int dir, void* out, long long ldo, hipStream_t s);
+
 template <typename TS>
 hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void* datt, int accumulate, hipStream_t s);
 
@@ -173,7 +181,8 @@ struct RecArgs {
   long long ldy;
   void* z;          // saved gates (in: projected inputs for fwd)
   int GZ;           // lanes of z rows
-  void* cbuf;       // LSTM cell states
+  void* cbuf;       // LSTM cell states (forward: NULL = not saved)
+  long long ldc;    // row stride of cbuf in elements
   void* rh;         // basic GRU r*h_{t-1}
   void* hT;
   void* cT;

@@ -26,7 +26,8 @@ import sys
 LABELS = (("rec_fwd", "rec_fwd"), ("rec_bwd", "rec_bwd"), ("gemm_kernelIDF16bLb0ELb0E", "proj_gemm"),
           ("gemm_kernelIfLb0ELb0E", "proj_gemm"), ("gemm_kernelIDF16bLb0ELb1E", "dx_gemm"),
           ("gemm_kernelIfLb0ELb1E", "dx_gemm"), ("gemm_kernel<bool", "dw_gemm"), ("gemm_kernelIDF16bLb1ELb1E", "dw_gemm"),
-          ("gemm_kernelIfLb1ELb1E", "dw_gemm"), ("colsum", "db_colsum"), ("fill", "fill"))
+          ("gemm_kernelIfLb1ELb1E", "dw_gemm"), ("colsum", "db_colsum"), ("fill", "fill"),
+          ("lstm_cell_scan", "aux"), ("zero_inactive", "aux"), ("gather_first_rows", "aux"), ("att_reduce", "aux"))
 
 
 def label_of(name: str) -> str:

@@ -103,6 +103,12 @@ typedef struct rnn_desc {
                         t, row b is replaced by (1 - att[t][b]) * u in the state
                         update h = u*h_prev + (1-u)*c. NULL = plain GRU. The
                         same array must be given to the three calls. */
+  int recompute;      /* LSTM only (else 0): 0 = rnn_fwd keeps the cell-state
+                        sequence for the backward calls; 1 = it keeps only the
+                        four gates and rnn_bwd_data rebuilds the cell states
+                        from them and c0 before BPTT (popnn Lstm.cpp,
+                        "cellAndTanh" recomputation): T*B*H fewer workspace
+                        elements for one extra elementwise pass. */
 } rnn_desc_t;
 
 /* Bytes of workspace the three calls need for this descriptor (0 if invalid). */

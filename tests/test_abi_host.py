@@ -143,3 +143,12 @@ def test_attention_scores_only_for_the_gru():
     assert g.rnn_fwd(_desc(mode=L.RNN_GRU, gate_order=(0, 1, 2), att=260), 16, 0, 0, 16, 16, 16, 16, 16, 0, 0,
                      256, n, 0) == L.RNN_ERR_INVALID_ARG
     assert g.rnn_bwd_data(dg, 16, 16, 0, 0, 16, 16, 0, 0, 0, 0, 0, 20, 0, 256, n, 0) == L.RNN_ERR_INVALID_ARG
+
+
+def test_recompute_mode_is_lstm_only_and_drops_the_cell_sequence():
+    T, B, H = 7, 3, 32
+    n0 = g.rnn_workspace_bytes(_desc(T=T, B=B, H=H))
+    n1 = g.rnn_workspace_bytes(_desc(T=T, B=B, H=H, recompute=1))
+    assert n1 > 0 and n0 - n1 >= T * B * H * 4
+    assert g.rnn_workspace_bytes(_desc(recompute=2)) == 0
+    assert g.rnn_workspace_bytes(_desc(mode=L.RNN_GRU, gate_order=(0, 1, 2), recompute=1)) == 0

@@ -124,7 +124,7 @@ def test_bf16_medium(name, changes):
 
 # ------------------------------------------------------- full sizes -------
 
-def _sampled(name, rows, direction=0, lengths=None, att=None):
+def _sampled(name, rows, direction=0, lengths=None, att=None, recompute=False):
     wl = W[name]
     inp = synth.make_inputs(wl)
     p = inp["params"][0][0]
@@ -134,7 +134,7 @@ def _sampled(name, rows, direction=0, lengths=None, att=None):
     mask[rows] = True
     g[:, ~mask] = 0.0
     got = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], g, None, None, direction,
-                    wl.reset_after, lengths=lengths, att=att)
+                    wl.reset_after, lengths=lengths, att=att, recompute=recompute)
     sub = lambda a: None if a is None else a[rows]  # noqa: E731
     ref = oracle_layer(wl.mode, P, inp["x"][:, rows], sub(inp["h0"]), sub(inp["c0"]), g[:, rows], None, None,
                        direction, wl.reset_after, lengths=sub(lengths), att=None if att is None else att[:, rows])
@@ -309,4 +309,35 @@ def test_augru_bf16_full_size_sampled_rows(direction):
     L = _ragged_lengths(wl.B, wl.T, 23)
     rows = [int(np.argmin(L)), int(np.argmax(L)), 77]
     wl, got, ref = _sampled("grura_bf16_t128_b128_i2048_h2048", rows, direction, lengths=L, att=att)
+    print(compare(got, ref, "bf16", rows=rows))
+
+
+
+# ---------------------------------------- LSTM cell-state recomputation ----
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("ragged", [False, True])
+def test_lstm_recompute_f32_small(direction, ragged):
+    wl, inp, P = _case("lstm_f32_t8_b2_i16_h32", T=11, B=13, I=40, H=48, w_scale=0.15, h0_std=0.5, c0_std=0.5)
+    L = _ragged_lengths(wl.B, wl.T, 29) if ragged else None
+    got, ref = _run(wl, inp, P, direction, lengths=L, recompute=True)
+    print(compare(got, ref, "f32", extra=f"recompute dir{direction} ragged={ragged}"))
+    # fp32 gates rebuild the same cell states the forward kept: the two modes agree to rounding
+    base = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], inp["g"], None, None, direction,
+                     lengths=L)
+    for k in base:
+        np.testing.assert_allclose(got[k], base[k], rtol=1e-5, atol=1e-6, err_msg=k)
+
+
+@pytest.mark.parametrize("H", [48, 256])
+def test_lstm_recompute_bf16_medium(H):
+    wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=14, B=24, I=64, H=H, h0_std=0.3, c0_std=0.3)
+    got, ref = _run(wl, inp, P, 1, lengths=_ragged_lengths(wl.B, wl.T, 37), recompute=True)
+    print(compare(got, ref, "bf16", extra=f"recompute H{H}"))
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_headline_lstm_recompute_sampled_rows(direction):
+    rows = [0, 33, 63]
+    wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction, recompute=True)
     print(compare(got, ref, "bf16", rows=rows))
