@@ -341,3 +341,26 @@ def test_headline_lstm_recompute_sampled_rows(direction):
     rows = [0, 33, 63]
     wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction, recompute=True)
     print(compare(got, ref, "bf16", rows=rows))
+
+
+# ------------------------------------------- more ring configurations -----
+# H = 512 bf16 (16 k-steps, two per packed tile) and H = 1024 with 5 rows
+# (packed ring, 4-row groups) and 128 rows (the grid only fits 16-row groups:
+# one k-step per tile).
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_lstm_bf16_h512_ragged(direction):
+    wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=10, B=12, I=64, H=512, h0_std=0.3, c0_std=0.3)
+    got, ref = _run(wl, inp, P, direction, lengths=_ragged_lengths(wl.B, wl.T, 43))
+    print(compare(got, ref, "bf16", extra=f"lstm h512 dir{direction}"))
+
+
+@pytest.mark.parametrize("rows", [5, 128])
+def test_grura_bf16_h1024_augru(rows):
+    # 5 rows: groups of <= 8 rows (two k-steps per ring tile); 128 rows: the
+    # grid only fits with 16-row groups (one k-step per tile)
+    wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=4, B=rows, I=64, H=1024, w_scale=1 / 32,
+                       h0_std=0.3)
+    att = _scores(wl.T, wl.B, 61, "bf16")
+    got, ref = _run(wl, inp, P, 0, att=att)
+    print(compare(got, ref, "bf16", extra=f"grura h1024 B{rows}"))
