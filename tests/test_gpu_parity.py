@@ -364,3 +364,70 @@ def test_grura_bf16_h1024_augru(rows):
     att = _scores(wl.T, wl.B, 61, "bf16")
     got, ref = _run(wl, inp, P, 0, att=att)
     print(compare(got, ref, "bf16", extra=f"grura h1024 B{rows}"))
+
+
+# -------------------------------------------- lengths / scores: edges ----
+
+def _edge_case(mode, ra, **sizes):
+    name = "lstm_f32_t8_b2_i16_h32" if mode == "lstm" else "grura_f32_t64_b16_i256_h256"
+    kw = dict(h0_std=0.7, c0_std=0.7, w_scale=0.3, **sizes)
+    if mode == "gru":
+        kw["reset_after"] = ra
+    return _case(name, **kw)
+
+
+def _final_grads(wl, seed):
+    rng = np.random.default_rng(seed)
+    dhT = rng.standard_normal((wl.B, wl.H))
+    dcT = rng.standard_normal((wl.B, wl.H)) if wl.mode == "lstm" else None
+    return dhT, dcT
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("mode,ra", [("lstm", None), ("gru", True), ("gru", False)])
+def test_lengths_single_step_rows(mode, ra, direction):
+    wl, inp, P = _edge_case(mode, ra, T=1, B=3, I=16, H=32)
+    dhT, dcT = _final_grads(wl, 5)
+    got, ref = _run(wl, inp, P, direction, None, dhT, dcT, lengths=np.array([0, 1, 0], np.int32))
+    print(compare(got, ref, "f32", extra=f"{mode} ra={ra} dir{direction}"))
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("mode,ra", [("lstm", None), ("gru", True), ("gru", False)])
+def test_lengths_all_rows_empty(mode, ra, direction):
+    # nothing runs: zero output, the state and its gradients pass through,
+    # zero input and weight gradients
+    wl, inp, P = _edge_case(mode, ra, T=5, B=4, I=16, H=32)
+    dhT, dcT = _final_grads(wl, 6)
+    got, ref = _run(wl, inp, P, direction, None, dhT, dcT, lengths=np.zeros(wl.B, np.int32))
+    print(compare(got, ref, "f32", extra=f"{mode} ra={ra} dir{direction}"))
+    assert np.all(got["y"] == 0) and np.all(got["dx"] == 0)
+    for k in ("dW_ih", "dW_hh", "db_ih", "db_hh"):
+        assert np.all(got[k] == 0), k
+    np.testing.assert_array_equal(got["hT"], inp["h0"].astype(np.float32))
+    np.testing.assert_array_equal(got["dh0"], dhT.astype(np.float32))
+    if mode == "lstm":
+        np.testing.assert_array_equal(got["cT"], inp["c0"].astype(np.float32))
+        np.testing.assert_array_equal(got["dc0"], dcT.astype(np.float32))
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_augru_final_state_gradient_and_accumulated_scores(direction):
+    wl, inp, P = _edge_case("gru", True, T=7, B=5, I=24, H=32)
+    att = _scores(wl.T, wl.B, 71, "f32")
+    dhT, _ = _final_grads(wl, 7)
+    got, ref = _run(wl, inp, P, direction, None, dhT, att=att, lengths=np.array([7, 0, 3, 6, 1], np.int32))
+    print(compare(got, ref, "f32", extra=f"dir{direction}"))
+    once = gpu_layer("gru", "f32", P, inp["x"], inp["h0"], None, inp["g"], dhT, None, direction, att=att)
+    twice = gpu_layer("gru", "f32", P, inp["x"], inp["h0"], None, inp["g"], dhT, None, direction, att=att,
+                      acc=True, repeat=2)[1]
+    np.testing.assert_allclose(twice["datt"], 2 * once["datt"], rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("direction", [0, 1])
+def test_lstm_recompute_with_final_state_gradients(direction):
+    wl, inp, P = _edge_case("lstm", None, T=9, B=6, I=16, H=32)
+    dhT, dcT = _final_grads(wl, 8)
+    got, ref = _run(wl, inp, P, direction, None, dhT, dcT, lengths=np.array([9, 4, 0, 1, 8, 9], np.int32),
+                    recompute=True)
+    print(compare(got, ref, "f32", extra=f"dir{direction}"))
