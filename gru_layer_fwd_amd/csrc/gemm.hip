@@ -229,6 +229,11 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   const int nM = (int)((g.M + BM - 1) / BM), nN = (int)((g.N + BN - 1) / BN);
   const Tile tl = tile_of(nM, nN, g.ksplit);
   const long long m0 = (long long)tl.m * BM, n0 = (long long)tl.n * BN;
+  // output part of this tile: B rows, first column and column count of the part
+  const bool sec = g.n_split > 0 && n0 >= g.n_split;
+  const RowMap& bmap = sec ? g.b2 : g.b;
+  const long long nb0 = sec ? n0 - g.n_split : n0;
+  const long long nend = g.n_split > 0 ? (sec ? g.N - g.n_split : g.n_split) : g.N;
   const long long kb = (long long)tl.kz * g.kslice;
   long long ke = kb + g.kslice;
   if (ke > g.K) ke = g.K;
@@ -257,12 +262,12 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   const TS* pa[RA];
   const TS* pb[RB];
   if constexpr (!AKO) rows_kc<TS, BM, NT>(pa, g.a, m0, g.M);
-  if constexpr (!BKO) rows_kc<TS, BN, NT>(pb, g.b, n0, g.N);
+  if constexpr (!BKO) rows_kc<TS, BN, NT>(pb, bmap, nb0, nend);
   auto gload = [&](int kt) {
     const long long k0 = kb + (long long)kt * BK;
     if constexpr (AKO) load_ko<TS, BM, NT>(ra_o, g.a, m0, g.M, k0, ke);
     else load_kc<TS, BM, NT>(ra_c, pa, k0, ke);
-    if constexpr (BKO) load_ko<TS, BN, NT>(rb_o, g.b, n0, g.N, k0, ke);
+    if constexpr (BKO) load_ko<TS, BN, NT>(rb_o, bmap, nb0, nend, k0, ke);
     else load_kc<TS, BN, NT>(rb_c, pb, k0, ke);
   };
   auto sstore = [&](int b) {
@@ -381,7 +386,8 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
         const uint4 v = *(const uint4*)(stage + r * RB + ((c * 16) ^ sw(r)));
         const long long m = m0 + wm * WM + c0 + r;
         const long long n = n0 + wn * WN + c * EPC;
-        if (m >= g.M || n >= g.N) continue;
+        const long long nl = nb0 + wn * WN + c * EPC;  // column within the output part
+        if (m >= g.M || nl >= nend) continue;
         if constexpr (sizeof(OT) == 4 && !std::is_same<OT, TS>::value) {
           // fp32 split-K partial (TS = bf16)
           *(uint4*)(g.part + (long long)tl.kz * g.M * g.N + m * g.N + n) = v;
@@ -396,7 +402,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
             const long long gg = cm / g.H;
             row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
           }
-          uint4* cp = (uint4*)((TS*)g.c + row * g.ldc + n);
+          uint4* cp = sec ? (uint4*)((TS*)g.c2 + row * g.ldc2 + nl) : (uint4*)((TS*)g.c + row * g.ldc + nl);
           uint4 o = v;
           if (g.accumulate) {
             const uint4 old = *cp;
@@ -435,7 +441,8 @@ __global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
     const long long gg = cm / g.H;
     row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
   }
-  TS* cp = (TS*)g.c + row * g.ldc + n;
+  const bool sec = g.n_split > 0 && n >= g.n_split;
+  TS* cp = sec ? (TS*)g.c2 + row * g.ldc2 + (n - g.n_split) : (TS*)g.c + row * g.ldc + n;
   if (g.accumulate) v += to_f(*cp);
   *cp = from_f<TS>(v);
 }
@@ -655,6 +662,7 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
   // row sums go to the per-slice buffer after the partial tiles
   g.rowsum = (g.rowsum_out && g.part) ? g.part + (long long)g.ksplit * g.M * g.N : nullptr;
   if (g.rowsum_out && !g.rowsum) return hipErrorInvalidValue;
+  if (g.n_split > 0 && (g.bias1 || g.n_split >= g.N || g.n_split % p.bn != 0)) return hipErrorInvalidValue;
   if (g.part && (long long)g.ksplit * (g.M * g.N + g.M) > g.ws_floats && (g.ksplit > 1 || g.rowsum_out))
     return hipErrorInvalidValue;
   hipError_t e;

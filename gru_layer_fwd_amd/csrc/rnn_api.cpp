@@ -92,8 +92,11 @@ Layout layout(const rnn_desc_t* d) {
     size_t f = rnn::gemm_workspace_floats(GH, nmax, (long long)TB, PLAN_CUS);
     const size_t f2 = rnn::gemm_workspace_floats((long long)TB, GH, d->I, PLAN_CUS);
     const size_t f3 = rnn::gemm_workspace_floats((long long)TB, d->I, GH, PLAN_CUS);
+    // the LSTM's two weight gradients as one product with two output parts
+    const size_t f4 = rnn::gemm_workspace_floats(GH, (long long)d->I + d->H, (long long)TB, PLAN_CUS);
     if (f2 > f) f = f2;
     if (f3 > f) f = f3;
+    if (cell == rnn::CELL_LSTM && f4 > f) f = f4;
     L.gemm = off;
     L.gemm_floats = f;
     off += up(f * sizeof(float));
@@ -587,8 +590,35 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   hprev.T = d->T;
   hprev.dir = d->direction;
 
-  // input side: dW_ih and db_ih from the input-side lanes [0, G*H)
-  if (dW_ih) {
+  // LSTM with both weight gradients: one product over [x | h_{t-1}] with two
+  // output parts (dG is read once, one split-K finish); the bias gradients
+  // (equal for the two biases) come from its row sums
+  const bool merged = cell == rnn::CELL_LSTM && dW_ih && dW_hh && d->I % 256 == 0;
+  if (merged) {
+    rnn::GemmArgs g{};
+    g.a = rows(dg, GDH);
+    g.b = rows(x, ldx_of(d));
+    g.b2 = hprev;
+    g.n_split = d->I;
+    g.M = (long long)G * H;
+    g.N = (long long)d->I + H;
+    g.K = TB;
+    g.c = dW_ih;
+    g.ldc = d->I;
+    g.c2 = dW_hh;
+    g.ldc2 = H;
+    g.c_kind = 1;
+    g.c_row0 = 0;
+    g.H = H;
+    for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+    g.accumulate = acc;
+    g.part = (float*)(ws + L.gemm);
+    g.ws_floats = (long long)L.gemm_floats;
+    g.rowsum_out = db_ih ? db_ih : db_hh;
+    g.rowsum_out2 = db_ih ? db_hh : nullptr;
+    ProfScope ps(L_DW, s);
+    if ((st = hip_status(gemm_dt(d->dtype, g, true, true, s)))) return st;
+  } else if (dW_ih) {
     if ((st = hip_status(dW(dW_ih, 0, (long long)G * H, 0, rows(x, ldx_of(d)), d->I, db_ih)))) return st;
   } else if (db_ih) {
     if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, G * H, db_ih, 0, H, perm, acc, partial, s)))) return st;
@@ -596,7 +626,9 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   // recurrent side: lanes of dG_h (LSTM: all; GRU: r,u, then the candidate rows)
   const int ccol = (cell == rnn::CELL_GRU_RA) ? 3 * H : 2 * H;  // candidate lane of dG_h
   if (dW_hh) {
-    if (cell == rnn::CELL_LSTM) {
+    if (merged) {
+      // done above
+    } else if (cell == rnn::CELL_LSTM) {
       if ((st = hip_status(dW(dW_hh, 0, 4LL * H, 0, hprev, H, db_hh)))) return st;
     } else {
       if ((st = hip_status(dW(dW_hh, 0, 2LL * H, 0, hprev, H, db_hh)))) return st;

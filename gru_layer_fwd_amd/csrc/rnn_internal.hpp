@@ -117,6 +117,13 @@ struct GemmArgs {
   // the rows of C (perm, c_row0); rowsum_out2 receives the same values
   void* rowsum_out;
   void* rowsum_out2;
+  // optional second output part: columns n >= n_split (a multiple of the
+  // tile width) read B rows through b2 and go to c2 (row stride ldc2) at
+  // column n - n_split; 0 = one part. No bias with two parts.
+  long long n_split;
+  RowMap b2;
+  void* c2;
+  long long ldc2;
   // set by the launcher
   int ksplit;
   long long kslice;
