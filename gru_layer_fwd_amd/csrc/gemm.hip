@@ -422,18 +422,33 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 }
 
 // Split-K finish: C[row(m)][n] (+)= sum_kz part[kz][m][n] (+ bias), in order.
+// A thread takes 8 consecutive columns (N is a multiple of 8: 16-byte fp32
+// loads, one 16-byte bf16 or two fp32 stores), so the pass runs at stream
+// rate rather than at the latency of single-element accesses.
 template <typename TS>
 __global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
-  const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
+  constexpr int V = 8;
+  const long long idx = ((long long)blockIdx.x * 256 + threadIdx.x) * V;
   if (idx >= g.M * g.N) return;
   const long long m = idx / g.N, n = idx - m * g.N;
-  float v = 0.f;
-  for (int kz = 0; kz < g.ksplit; ++kz) v += g.part[(long long)kz * g.M * g.N + idx];
+  float v[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) v[e] = 0.f;
+  for (int kz = 0; kz < g.ksplit; ++kz) {
+    const float4* pp = (const float4*)(g.part + (long long)kz * g.M * g.N + idx);
+    const float4 a = pp[0], b = pp[1];
+    v[0] += a.x; v[1] += a.y; v[2] += a.z; v[3] += a.w;
+    v[4] += b.x; v[5] += b.y; v[6] += b.z; v[7] += b.w;
+  }
   if (g.bias1) {
-    const long long gg = n / g.H;
-    const long long src = (long long)g.perm[gg] * g.H + (n - gg * g.H);
-    v += to_f(((const TS*)g.bias1)[src]);
-    if (g.bias2 && gg != g.bias_skip_gate) v += to_f(((const TS*)g.bias2)[src]);
+#pragma unroll
+    for (int e = 0; e < V; ++e) {
+      const long long nn = n + e;
+      const long long gg = nn / g.H;
+      const long long src = (long long)g.perm[gg] * g.H + (nn - gg * g.H);
+      v[e] += to_f(((const TS*)g.bias1)[src]);
+      if (g.bias2 && gg != g.bias_skip_gate) v[e] += to_f(((const TS*)g.bias2)[src]);
+    }
   }
   long long row = m;
   if (g.c_kind == 1) {
@@ -443,8 +458,19 @@ __global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
   }
   const bool sec = g.n_split > 0 && n >= g.n_split;
   TS* cp = sec ? (TS*)g.c2 + row * g.ldc2 + (n - g.n_split) : (TS*)g.c + row * g.ldc + n;
-  if (g.accumulate) v += to_f(*cp);
-  *cp = from_f<TS>(v);
+  TS o[V];
+  if (g.accumulate) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) v[e] += to_f(cp[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < V; ++e) o[e] = from_f<TS>(v[e]);
+  if constexpr (sizeof(TS) == 2) {
+    *(uint4*)cp = *(const uint4*)o;
+  } else {
+    ((uint4*)cp)[0] = ((const uint4*)o)[0];
+    ((uint4*)cp)[1] = ((const uint4*)o)[1];
+  }
 }
 
 // Bias gradients from the per-slice row sums: out[perm(row0+m)] (+)= sum_kz rows[kz][m]
@@ -673,7 +699,9 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
   if (e != hipSuccess) return e;
   if (g.ksplit > 1) {
     const long long n = g.M * g.N;
-    hipLaunchKernelGGL(splitk_finish<TS>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g);
+    if (g.N % 8 != 0 || g.ldc % 8 != 0 || (g.n_split > 0 && (g.ldc2 % 8 != 0 || g.n_split % 8 != 0)))
+      return hipErrorInvalidValue;  // whole 8-column groups with 16-byte aligned rows
+    hipLaunchKernelGGL(splitk_finish<TS>, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s, g);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (g.rowsum_out) {
