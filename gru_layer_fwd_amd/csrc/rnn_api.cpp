@@ -337,11 +337,11 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
 
   // status word and the forward step counters start at zero
   {
+    // one fill from the status word through the last counter this launch uses
     ProfScope ps(L_FILL, s);
-    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
-    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.flags), 0,
-                                              (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE, s))))
-      return st;
+    const long long n = (long long)(L.flags - L.status) / sizeof(int) +
+                        (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE;
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
   }
 
   // input projection for every step: Z[t,b][g*H+j] = x . W_ih[g,j] + biases
@@ -437,11 +437,12 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   int* flags = (int*)(ws + L.flags) + FLAG_SLOTS * rnn::FSTRIDE;
 
   {
+    // one fill from the status word through the last backward counter (the
+    // forward counters in between are no longer read)
     ProfScope ps(L_FILL, s);
-    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, 1, s)))) return st;
-    if ((st = hip_status(
-             rnn::launch_fill_i32(flags, 0, (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE, s))))
-      return st;
+    const long long n = (long long)(flags - (int*)(ws + L.status)) +
+                        (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE;
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
   }
 
   rnn::RecArgs a{};
