@@ -164,8 +164,17 @@ def main():
     dev = lambda a: None if a is None else torch.from_numpy(a).to("cuda", dt)  # noqa: E731
     x = dev(inp["x"])
     g = dev(inp["g"])
-    params = [[tuple(dev(a) for a in (p.W_ih, p.W_hh, p.b_ih, p.b_hh)) for p in per] for per in inp["params"]]
-    grads = [[tuple(torch.empty_like(t) for t in pd) for pd in per] for per in params]
+    # per layer, each parameter of all directions in one [dirs, ...] tensor;
+    # params[l][d] are views of it (a bidirectional layer reads both at once)
+    def stacked(per):
+        ts = [torch.stack([dev(getattr(p, k)) for p in per]) for k in ("W_ih", "W_hh", "b_ih", "b_hh")]
+        return [tuple(t[d] for t in ts) for d in range(len(per))]
+
+    params = [stacked(per) for per in inp["params"]]
+    grads = []
+    for per in params:
+        gts = [torch.empty((len(per),) + tuple(t.shape), dtype=t.dtype, device=t.device) for t in per[0]]
+        grads.append([tuple(t[d] for t in gts) for d in range(len(per))])
     order = wl.gate_order()
 
     if (args.ragged or args.att or args.recompute) and (wl.layers != 1 or wl.bidir):
@@ -208,7 +217,7 @@ def main():
             st.fwd(x, params)
             st.bwd(x, params, g, dx, grads)
 
-        status = lambda: max((lay.device_status() for per in st.layers for lay in per), key=abs)  # noqa: E731
+        status = lambda: max((lay.device_status() for lay in st.layers), key=abs)  # noqa: E731
 
     for _ in range(args.warmup):
         step()

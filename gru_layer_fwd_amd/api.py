@@ -89,9 +89,16 @@ class RnnStack:
 
     Layer l writes [T, B, dirs*H]: the forward direction in columns [0, H),
     the reverse one in [H, 2H) (row stride dirs*H), and layer l+1 reads that
-    tensor as its input. Backward: the input gradient of layer l+1 (both
-    directions accumulated into one buffer) is the output gradient of layer l.
-    Parameters: params[l][d] = (W_ih, W_hh, b_ih, b_hh) device tensors.
+    tensor as its input. A bidirectional layer is one direction-2 layer of
+    the C ABI: both directions share one persistent launch per pass.
+    Backward: the input gradient of layer l+1 (both directions summed) is the
+    output gradient of layer l.
+    Parameters: params[l][d] = (W_ih, W_hh, b_ih, b_hh) device tensors; for
+    a bidirectional layer the two directions' tensors are passed without a
+    copy when they already sit back to back in one [2, ...] tensor (views of
+    it), and are stacked into a temporary otherwise. The same holds for the
+    weight gradients grads[l][d]. h0/c0 ([B, H]) apply to every layer and
+    direction.
     """
 
     def __init__(self, mode, T, B, I, H, dtype, layers, bidir, reset_after=True, gate_order=None,
@@ -101,22 +108,41 @@ class RnnStack:
         self.layers = []
         for layer in range(layers):
             Il = I if layer == 0 else H * self.dirs
-            self.layers.append([
-                RnnLayer(mode, T, B, Il, H, dtype, direction=d, reset_after=reset_after,
-                         gate_order=gate_order, ldx=Il, ldy=H * self.dirs, device=device, lengths=lengths)
-                for d in range(self.dirs)])
-        dt = self.layers[0][0].torch_dtype
+            self.layers.append(RnnLayer(mode, T, B, Il, H, dtype, direction=2 if bidir else 0,
+                                        reset_after=reset_after, gate_order=gate_order, ldx=Il,
+                                        ldy=H * self.dirs, device=device, lengths=lengths))
+        dt = self.layers[0].torch_dtype
         self.ys = [torch.empty(T, B, H * self.dirs, dtype=dt, device=device) for _ in range(layers)]
         # input gradients of layers 1.. (the output gradients of the layer below)
         self.dxs = [None] + [torch.empty(T, B, H * self.dirs, dtype=dt, device=device)
                              for _ in range(layers - 1)]
 
+    @staticmethod
+    def _pair(a, b):
+        """([2, ...] tensor holding a and b, whether it is a view of them)."""
+        if (a.shape == b.shape and a.dtype == b.dtype and a.is_contiguous() and b.is_contiguous()
+                and a.untyped_storage().data_ptr() == b.untyped_storage().data_ptr()
+                and b.storage_offset() == a.storage_offset() + a.numel()):
+            return torch.as_strided(a, (2,) + tuple(a.shape), (a.numel(),) + tuple(a.stride()),
+                                    a.storage_offset()), True
+        return torch.stack([a, b]), False
+
+    def _layer_params(self, li, params):
+        if self.dirs == 1:
+            return params[li][0]
+        return tuple(self._pair(params[li][0][i], params[li][1][i])[0] for i in range(4))
+
+    def _state(self, t):
+        if t is None or self.dirs == 1:
+            return t
+        return torch.stack([t, t])
+
     def fwd(self, x, params, h0=None, c0=None, stream=None):
         inp = x
-        for li, per in enumerate(self.layers):
-            for d, lay in enumerate(per):
-                W_ih, W_hh, b_ih, b_hh = params[li][d]
-                lay.fwd(inp, h0, c0, W_ih, W_hh, b_ih, b_hh, self.ys[li][:, :, d * self.H:], stream=stream)
+        h0s, c0s = self._state(h0), self._state(c0)
+        for li, lay in enumerate(self.layers):
+            W_ih, W_hh, b_ih, b_hh = self._layer_params(li, params)
+            lay.fwd(inp, h0s, c0s, W_ih, W_hh, b_ih, b_hh, self.ys[li], stream=stream)
             inp = self.ys[li]
         return self.ys[-1]
 
@@ -124,14 +150,22 @@ class RnnStack:
         """dy: gradient of the last layer's output. grads[l][d] = (dW_ih, dW_hh, db_ih, db_hh)
         (or None to skip the weight gradients)."""
         d_out = dy
+        h0s, c0s = self._state(h0), self._state(c0)
         for li in range(len(self.layers) - 1, -1, -1):
+            lay = self.layers[li]
             d_in = dx if li == 0 else self.dxs[li]
-            for d, lay in enumerate(self.layers[li]):
-                W_ih, W_hh, _, _ = params[li][d]
-                lay.bwd_data(W_ih, W_hh, h0, c0, self.ys[li][:, :, d * self.H:],
-                             d_out[:, :, d * self.H:], None, None, d_in, accumulate=(d > 0), stream=stream)
-                if grads is not None:
-                    inp = x if li == 0 else self.ys[li - 1]
-                    lay.bwd_weights(inp, h0, self.ys[li][:, :, d * self.H:], *grads[li][d], stream=stream)
+            W_ih, W_hh, _, _ = self._layer_params(li, params)
+            lay.bwd_data(W_ih, W_hh, h0s, c0s, self.ys[li], d_out, None, None, d_in, stream=stream)
+            if grads is not None:
+                inp = x if li == 0 else self.ys[li - 1]
+                if self.dirs == 1:
+                    lay.bwd_weights(inp, h0s, self.ys[li], *grads[li][0], stream=stream)
+                else:
+                    pairs = [self._pair(grads[li][0][i], grads[li][1][i]) for i in range(4)]
+                    lay.bwd_weights(inp, h0s, self.ys[li], *(t for t, _ in pairs), stream=stream)
+                    for i, (t, view) in enumerate(pairs):
+                        if not view:
+                            grads[li][0][i].copy_(t[0])
+                            grads[li][1][i].copy_(t[1])
             d_out = d_in
         return dx

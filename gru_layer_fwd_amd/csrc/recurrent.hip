@@ -122,12 +122,29 @@ constexpr int CPOL_SC1 = 16;             // device scope
 // 8 XCDs; consecutive workgroups of one batch group are placed on the same
 // XCD where the counts allow, so that the vector they exchange stays in few
 // L2s. Correctness does not depend on the placement.
-__device__ __forceinline__ void wg_coords(int nGroups, int nSlices, int& grp, int& sl) {
-  const int n = nGroups * nSlices;
-  int L = blockIdx.x;
-  if ((n & 7) == 0) L = (blockIdx.x & 7) * (n >> 3) + (blockIdx.x >> 3);
-  grp = L / nSlices;
-  sl = L - grp * nSlices;
+// Direction and workgroup coordinates of this block. One direction: block b
+// sits on XCD b%8 (round-robin dispatch); with a workgroup count divisible by
+// 8 the logical index is XCD-contiguous, so a batch group (nSlices
+// consecutive indices) shares an XCD where it fits in one. Dual launch:
+// blocks on XCDs 0-3 run direction 0 and those on XCDs 4-7 direction 1, each
+// XCD holding n/4 consecutive indices of its direction.
+typedef const __attribute__((address_space(4))) RecArgs RecArgsK;
+static_assert(offsetof(RecLaunch, d) == 0, "RecLaunch.d leads the kernel arguments");
+
+__device__ __forceinline__ RecArgsK& launch_slot(const RecLaunch& L, int& grp, int& sl) {
+  const int b = blockIdx.x;
+  const int n = L.d[0].nGroups * L.d[0].nSlices;
+  int d = 0, lw;
+  if (!L.dual) {
+    lw = ((n & 7) == 0) ? (b & 7) * (n >> 3) + (b >> 3) : b;
+  } else {
+    d = (b & 7) >> 2;
+    lw = (b & 3) * (n >> 2) + (b >> 3);
+  }
+  RecArgsK& a = ((RecArgsK*)__builtin_amdgcn_kernarg_segment_ptr())[d];
+  grp = lw / a.nSlices;
+  sl = lw - grp * a.nSlices;
+  return a;
 }
 
 // Exchange ring. A consumer wave reads the vector of the previous step as
@@ -321,8 +338,8 @@ __device__ __forceinline__ void load_w_rows(uint4 (&Wr)[NT][KI], const TS* W, in
 // Load the B-operand tiles of W_hh columns (backward: output column col is
 // hidden unit J0+col, contraction index k runs over canonical gate rows
 // kb + [0, K): W_hh[perm[g]*H + k%H][J0+col] with g = k/H).
-template <typename TS, int NT, int KI>
-__device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, int H, const int* perm, int J0,
+template <typename TS, int NT, int KI, typename Perm>
+__device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, int H, const Perm& perm, int J0,
                                             int gate0, int K) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -351,7 +368,7 @@ __device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, in
 // LSTM (GL = 4 gate lanes) and reset-after GRU (GL = 3: r, u and the
 // recurrent candidate term n_h = h W_hc^T + b_hc, kept apart).
 template <int CELL, typename TS, int NW, int MB, int NT, int KI>
-__global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
+__global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, NCOL = NT * 16;
   constexpr int GL = (CELL == CELL_LSTM) ? 4 : 3;
   constexpr int HS = NCOL / GL;
@@ -361,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
   extern __shared__ float red[];
 
   int grp, sl;
-  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  RecArgsK& a = launch_slot(L, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
@@ -504,7 +521,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecArgs a) {
 // step has two exchanges (h_{t-1}, then r*h_{t-1}); phase counters advance by
 // two per step. Workgroup columns: phase A r,u (2*HS), phase B candidate (HS).
 template <typename TS, int NW, int MB, int NTB, int KI>
-__global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
+__global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, HS = NTB * 16;
   constexpr int NTA = 2 * NTB;
   constexpr int UNITS = BG * HS;
@@ -512,7 +529,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecArgs a) {
   extern __shared__ float red[];
 
   int grp, sl;
-  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  RecArgsK& a = launch_slot(L, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
@@ -630,7 +647,7 @@ __device__ __forceinline__ void att_rows(const float* attl, float* part, int t, 
 // contracted over all gate rows; the workgroup holds the W_hh columns of its
 // HS units. Steps are processed in the reverse of the forward order.
 template <int CELL, typename TS, int NW, int MB, int NT, int KI>
-__global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
+__global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, HS = NT * 16;
   constexpr int GK = (CELL == CELL_LSTM) ? 4 : 3;
   constexpr int UNITS = BG * HS;
@@ -639,7 +656,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
-  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  RecArgsK& a = launch_slot(L, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
@@ -834,7 +851,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecArgs a) {
 // forms d_c, d_u; phase B contracts d_c_t with W_hc (gradient of r*h_{t-1})
 // and forms d_r. Counters advance by two per step.
 template <typename TS, int NW, int MB, int NT, int KIA, int KIB>
-__global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
+__global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, HS = NT * 16;
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
@@ -842,7 +859,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecArgs a) {
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
-  wg_coords(a.nGroups, a.nSlices, grp, sl);
+  RecArgsK& a = launch_slot(L, grp, sl);
   int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
   const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
@@ -1026,12 +1043,13 @@ size_t lds_of(const Entry& e) {
   return (size_t)e.nw * e.mb * 16 * ncol * sizeof(float);
 }
 
-// XCDs a batch group of `slices` workgroups covers under wg_coords: with
-// nwg % 8 == 0 each XCD holds nwg/8 consecutive slots, otherwise slots are
-// spread round-robin.
-int xcd_span(long long nwg, int slices) {
-  if (nwg % 8 == 0) {
-    const long long per = nwg / 8;
+// XCDs a batch group of `slices` workgroups covers under launch_slot, for a
+// direction of nwg workgroups spread over `xcds` XCDs: with nwg a multiple of
+// xcds each XCD holds nwg/xcds consecutive indices, otherwise the blocks are
+// spread round-robin over all 8.
+int xcd_span(long long nwg, int slices, int xcds) {
+  if (nwg % xcds == 0) {
+    const long long per = nwg / xcds;
     return (int)((slices + per - 1) / per);
   }
   return slices < 8 ? slices : 8;
@@ -1044,8 +1062,9 @@ int xcd_span(long long nwg, int slices) {
 // taken as ~2.5x the bf16 time); every CU reads the whole exchanged vector
 // of its group per step, ~150 GB/s from the tiled ring and ~75 GB/s from row
 // layout; the gate epilogue costs ~0.2 us per unit a thread carries.
-double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize, bool ring) {
-  const int span = xcd_span((long long)groups * slices, slices);
+double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize, bool ring,
+                 int xcds) {
+  const int span = xcd_span((long long)groups * slices, slices, xcds);
   const double hand = span <= 1 ? 1.0 : 2.0;
   const int phases = (e.cell == CELL_GRU_BASIC) ? 2 : 1;
   const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
@@ -1058,7 +1077,7 @@ double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kste
   return phases * hand + mfma + data + 0.2 * upt;
 }
 
-bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p) {
+bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, RecPlan* p) {
   const int kstep = dtype ? 32 : 16;
   const int esize = dtype ? 2 : 4;
   double best = 1e300;
@@ -1082,7 +1101,7 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p
       const long long nwg = (long long)groups * slices;
       if (nwg > cu_count) continue;  // at most one persistent workgroup per CU
       const bool ring = (cell != CELL_GRU_BASIC) && ((long long)K * esize) % 64 == 0 && bg <= 16 * e.mb;
-      const double cost = step_cost(e, bg, groups, slices, K, kstep, esize, ring);
+      const double cost = step_cost(e, bg, groups, slices, K, kstep, esize, ring, xcds);
       if (cost < best) {
         best = cost;
         *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e)};
@@ -1095,11 +1114,11 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, RecPlan* p
 
 }  // namespace
 
-bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p) {
-  return choose(cell, dtype, 1, B, H, cu_count, p);
+bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p) {
+  return choose(cell, dtype, 1, B, H, cu_count, xcds, p);
 }
-bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p) {
-  return choose(cell, dtype, 0, B, H, cu_count, p);
+bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p) {
+  return choose(cell, dtype, 0, B, H, cu_count, xcds, p);
 }
 
 int max_coresident(const RecPlan& p) {
@@ -1108,13 +1127,15 @@ int max_coresident(const RecPlan& p) {
   return n;
 }
 
-hipError_t launch_rec(const RecPlan& p, const RecArgs& a, hipStream_t s) {
+hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(p.func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
   if (e != hipSuccess) return e;
-  RecArgs args = a;
+  const int n = p.nGroups * p.nSlices;
+  if (L.dual && n % 4 != 0) return hipErrorInvalidValue;
+  RecLaunch args = L;
   void* kargs[] = {&args};
-  return hipLaunchCooperativeKernel(p.func, dim3(p.nGroups * p.nSlices), dim3(p.nw * 64), kargs,
-                                    (unsigned)p.lds_bytes, s);
+  return hipLaunchCooperativeKernel(p.func, dim3(L.dual ? 2 * n : n), dim3(p.nw * 64), kargs, (unsigned)p.lds_bytes,
+                                    s);
 }
 
 }  // namespace rnn

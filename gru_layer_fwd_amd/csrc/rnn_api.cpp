@@ -29,7 +29,7 @@ int cell_of(const rnn_desc_t* d) {
   return d->reset_after ? rnn::CELL_GRU_RA : rnn::CELL_GRU_BASIC;
 }
 long long ldx_of(const rnn_desc_t* d) { return d->ldx ? d->ldx : d->I; }
-long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : d->H; }
+long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : (d->direction == 2 ? 2LL : 1LL) * d->H; }
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
@@ -46,7 +46,7 @@ bool desc_ok(const rnn_desc_t* d) {
   if (!d) return false;
   if (d->mode != RNN_LSTM && d->mode != RNN_GRU) return false;
   if (d->dtype != RNN_F32 && d->dtype != RNN_BF16) return false;
-  if (d->direction != 0 && d->direction != 1) return false;
+  if (d->direction < 0 || d->direction > 2) return false;
   if (d->mode == RNN_GRU && d->reset_after != 0 && d->reset_after != 1) return false;
   if (d->att && d->mode != RNN_GRU) return false;  // attention scores scale the GRU update gate
   if (d->recompute != 0 && !(d->recompute == 1 && d->mode == RNN_LSTM)) return false;
@@ -59,7 +59,7 @@ bool desc_ok(const rnn_desc_t* d) {
     seen |= 1 << g;
   }
   if (d->ldx != 0 && d->ldx < d->I) return false;
-  if (d->ldy != 0 && d->ldy < d->H) return false;
+  if (d->ldy != 0 && d->ldy < (d->direction == 2 ? 2LL : 1LL) * d->H) return false;
   return true;
 }
 
@@ -128,6 +128,25 @@ Layout layout(const rnn_desc_t* d) {
 
 bool aligned(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// A bidirectional layer (direction 2) runs as its two single-direction
+// halves, each over its own half of the workspace.
+rnn_desc_t half_desc(const rnn_desc_t* d, int k) {
+  rnn_desc_t h = *d;
+  if (d->direction == 2) {
+    h.direction = k;
+    h.ldy = ldy_of(d);
+  }
+  return h;
+}
+size_t ws_total(const rnn_desc_t* d) {
+  if (d->direction != 2) return layout(d).total;
+  const rnn_desc_t h = half_desc(d, 0);
+  return 2 * layout(&h).total;
+}
+// element offsets into the [2][...] stacked arrays of a bidirectional layer
+const void* at(const void* p, long long elems, size_t es) { return p ? (const char*)p + elems * (long long)es : nullptr; }
+void* at(void* p, long long elems, size_t es) { return p ? (char*)p + elems * (long long)es : nullptr; }
+
 struct DevInfo {
   int cu = 0;
   long long ticks = 0;
@@ -167,7 +186,7 @@ int check_common(const rnn_desc_t* d, const void* ws, size_t ws_bytes) {
   if (!desc_ok(d)) return RNN_ERR_INVALID_ARG;
   if (!shape_supported(d)) return RNN_ERR_UNSUPPORTED;
   if (!ws || !aligned(ws)) return RNN_ERR_INVALID_ARG;
-  if (ws_bytes < layout(d).total) return RNN_ERR_WORKSPACE_TOO_SMALL;
+  if (ws_bytes < ws_total(d)) return RNN_ERR_WORKSPACE_TOO_SMALL;
   return RNN_OK;
 }
 
@@ -264,25 +283,57 @@ void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws,
   a.xbuf = ws + L.xb;
 }
 
-int launch_persistent(const rnn::RecPlan& p, const rnn::RecArgs& a, const DevInfo& di, hipStream_t s,
+int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const DevInfo& di, hipStream_t s,
                       const char* what) {
   const long long nwg = (long long)p.nGroups * p.nSlices;
+  const long long grid = Lr.dual ? 2 * nwg : nwg;
   if (nwg > FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;
   const int occ = rnn::max_coresident(p);
-  if (occ < 1 || nwg > (long long)occ * di.cu) {
-    if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, nwg, occ, di.cu);
+  if (occ < 1 || grid > (long long)occ * di.cu) {
+    if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, grid, occ, di.cu);
     return RNN_ERR_UNSUPPORTED;
   }
+  const rnn::RecArgs& a = Lr.d[0];
   if (log_on())
     fprintf(stderr,
-            "[rnn] %s: %d groups of %d rows x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu, "
+            "[rnn] %s: %s%d groups of %d rows x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu, "
             "ring=%s, model %.2f us/step\n",
-            what, p.nGroups, p.bg, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki, p.lds_bytes,
-            a.xbuf ? (a.xpacked ? "packed" : "tiled") : "off", p.cost_us);
-  hipError_t e = rnn::launch_rec(p, a, s);
+            what, Lr.dual ? "2 directions x " : "", p.nGroups, p.bg, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki,
+            p.lds_bytes, a.xbuf ? (a.xpacked ? "packed" : "tiled") : "off", p.cost_us);
+  hipError_t e = rnn::launch_rec(p, Lr, s);
   if (e != hipSuccess) {
     if (log_on()) fprintf(stderr, "[rnn] %s: launch failed: %s\n", what, hipGetErrorString(e));
     return (e == hipErrorCooperativeLaunchTooLarge) ? RNN_ERR_UNSUPPORTED : RNN_ERR_DEVICE;
+  }
+  return RNN_OK;
+}
+
+// Plan of the persistent kernels: a bidirectional layer runs both halves in
+// one launch on half the chip each when the plan's workgroups divide over
+// the 4 XCDs of a half; otherwise each half gets the whole chip in turn.
+template <typename F>
+bool choose_plan(F planner, bool bidir, const DevInfo& di, rnn::RecPlan* plan, bool* dual) {
+  *dual = false;
+  if (bidir && planner(di.cu / 2, 4, plan) && (plan->nGroups * plan->nSlices) % 4 == 0) {
+    *dual = true;
+    return true;
+  }
+  return planner(di.cu, 8, plan);
+}
+
+int run_persistent(const rnn::RecPlan& plan, bool dual, int halves, const rnn::RecArgs (&args)[2],
+                   const DevInfo& di, hipStream_t s, const char* what) {
+  if (dual) {
+    rnn::RecLaunch Lr{};
+    Lr.d[0] = args[0];
+    Lr.d[1] = args[1];
+    Lr.dual = 1;
+    return launch_persistent(plan, Lr, di, s, what);
+  }
+  for (int k = 0; k < halves; ++k) {
+    rnn::RecLaunch Lr{};
+    Lr.d[0] = args[k];
+    if (int st = launch_persistent(plan, Lr, di, s, what)) return st;
   }
   return RNN_OK;
 }
@@ -291,7 +342,7 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecArgs& a, const DevInf
 
 RNN_API size_t rnn_workspace_bytes(const rnn_desc_t* d) {
   if (!desc_ok(d)) return 0;
-  return layout(d).total;
+  return ws_total(d);
 }
 
 RNN_API const char* rnn_status_string(int st) {
@@ -313,24 +364,37 @@ RNN_API int rnn_last_device_status(const void* workspace) {
   return v;
 }
 
-RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const void* c0, const void* W_ih,
-                    const void* W_hh, const void* b_ih, const void* b_hh, void* y, void* hT, void* cT,
-                    void* workspace, size_t ws_bytes, void* stream) {
-  int st = check_common(d, workspace, ws_bytes);
-  if (st) return st;
-  if (!x || !W_ih || !W_hh || !b_ih || !b_hh || !y) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, d->lengths, d->att};
-  for (const void* p : ptrs)
-    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
-  DevInfo di;
-  if ((st = dev_info(&di))) return st;
-  g_cu_count = di.cu;
+namespace {
+
+struct FwdIO {
+  const void *x, *h0, *c0, *W_ih, *W_hh, *b_ih, *b_hh;
+  void *y, *hT, *cT;
+};
+
+FwdIO fwd_half(const rnn_desc_t* d, const FwdIO& io, int k) {
+  if (d->direction != 2) return io;
+  const size_t es = esz(d);
+  const long long G = gates(d), H = d->H, BH = (long long)d->B * d->H;
+  FwdIO o = io;
+  o.W_ih = at(io.W_ih, k * G * H * d->I, es);
+  o.W_hh = at(io.W_hh, k * G * H * H, es);
+  o.b_ih = at(io.b_ih, k * G * H, es);
+  o.b_hh = at(io.b_hh, k * G * H, es);
+  o.h0 = at(io.h0, k * BH, es);
+  o.c0 = at(io.c0, k * BH, es);
+  o.hT = at(io.hT, k * BH, es);
+  o.cT = at(io.cT, k * BH, es);
+  o.y = at(io.y, k * H, es);
+  return o;
+}
+
+// One direction up to its persistent kernel: the counter fill, the input
+// projection and the kernel's arguments.
+int fwd_begin(const rnn_desc_t* d, const FwdIO& io, char* ws, const rnn::RecPlan& plan, const DevInfo& di,
+              int* status, hipStream_t s, rnn::RecArgs& a) {
+  int st;
   const Layout L = layout(d);
   const int cell = cell_of(d);
-  rnn::RecPlan plan;
-  if (!rnn::plan_fwd(cell, d->dtype, d->B, d->H, di.cu, &plan)) return RNN_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
   int perm[4];
   inv_perm(d, perm);
   const int G = gates(d);
@@ -346,8 +410,8 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
 
   // input projection for every step: Z[t,b][g*H+j] = x . W_ih[g,j] + biases
   rnn::GemmArgs g{};
-  g.a = rows(x, ldx_of(d));
-  g.b = perm_rows(W_ih, d->I, d->H, perm);
+  g.a = rows(io.x, ldx_of(d));
+  g.b = perm_rows(io.W_ih, d->I, d->H, perm);
   g.M = (long long)d->T * d->B;
   g.N = (long long)G * d->H;
   g.K = d->I;
@@ -356,8 +420,8 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   g.c_kind = 0;
   g.H = d->H;
   for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
-  g.bias1 = b_ih;
-  g.bias2 = b_hh;
+  g.bias1 = io.b_ih;
+  g.bias2 = io.b_hh;
   g.bias_skip_gate = (cell == rnn::CELL_GRU_RA) ? RNN_GATE_C : -1;
   g.part = (float*)(ws + L.gemm);
   g.ws_floats = (long long)L.gemm_floats;
@@ -366,7 +430,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
     if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
   }
 
-  rnn::RecArgs a{};
+  a = rnn::RecArgs{};
   a.T = d->T;
   a.B = d->B;
   a.H = d->H;
@@ -376,39 +440,210 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   a.Hs = plan.Hs;
   a.bg = plan.bg;
   for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
-  a.W_hh = W_hh;
-  a.b_hh = b_hh;
-  a.h0 = h0;
-  a.c0 = c0;
-  a.y = y;
+  a.W_hh = io.W_hh;
+  a.b_hh = io.b_hh;
+  a.h0 = io.h0;
+  a.c0 = io.c0;
+  a.y = io.y;
   a.ldy = ldy_of(d);
   a.z = ws + L.z;
   a.GZ = L.GZ;
   a.cbuf = (cell == rnn::CELL_LSTM && !d->recompute) ? ws + L.c : nullptr;
   a.ldc = d->H;
   a.rh = ws + L.rh;
-  a.hT = hT;
-  a.cT = (d->mode == RNN_LSTM) ? cT : nullptr;
+  a.hT = io.hT;
+  a.cT = (d->mode == RNN_LSTM) ? io.cT : nullptr;
   a.GD = L.GD;
   a.flags = (int*)(ws + L.flags);
-  a.status = (int*)(ws + L.status);
+  a.status = status;
   a.timeout_ticks = di.ticks;
   a.lengths = d->lengths;
   a.att = d->att;
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, d->H, esz(d));
-  {
-    ProfScope ps(L_RFWD, s);
-    if ((st = launch_persistent(plan, a, di, s, "fwd"))) return st;
-  }
-  // Past a row's length the kernels keep the latched state in y when it is
-  // also their exchange buffer; the output there is zero.
+  return RNN_OK;
+}
+
+// Past a row's length the kernels keep the latched state in y when it is
+// also their exchange buffer; the output there is zero.
+int fwd_end(const rnn_desc_t* d, const rnn::RecArgs& a, hipStream_t s) {
   if (d->lengths && !a.xbuf) {
     ProfScope ps(L_AUX, s);
     const hipError_t e = d->dtype == RNN_BF16
-                             ? rnn::launch_zero_inactive<bf16>(y, a.ldy, d->lengths, d->T, d->B, d->H, s)
-                             : rnn::launch_zero_inactive<float>(y, a.ldy, d->lengths, d->T, d->B, d->H, s);
+                             ? rnn::launch_zero_inactive<bf16>(a.y, a.ldy, d->lengths, d->T, d->B, d->H, s)
+                             : rnn::launch_zero_inactive<float>(a.y, a.ldy, d->lengths, d->T, d->B, d->H, s);
+    return hip_status(e);
+  }
+  return RNN_OK;
+}
+
+struct BwdIO {
+  const void *W_ih, *W_hh, *h0, *c0, *y, *dy, *dhT, *dcT;
+  void *dx, *dh0, *dc0, *datt;
+};
+
+BwdIO bwd_half(const rnn_desc_t* d, const BwdIO& io, int k) {
+  if (d->direction != 2) return io;
+  const size_t es = esz(d);
+  const long long G = gates(d), H = d->H, BH = (long long)d->B * d->H;
+  BwdIO o = io;
+  o.W_ih = at(io.W_ih, k * G * H * d->I, es);
+  o.W_hh = at(io.W_hh, k * G * H * H, es);
+  o.h0 = at(io.h0, k * BH, es);
+  o.c0 = at(io.c0, k * BH, es);
+  o.y = at(io.y, k * H, es);
+  o.dy = at(io.dy, k * H, es);
+  o.dhT = at(io.dhT, k * BH, es);
+  o.dcT = at(io.dcT, k * BH, es);
+  o.dh0 = at(io.dh0, k * BH, es);
+  o.dc0 = at(io.dc0, k * BH, es);
+  return o;  // dx and datt are shared: the second half adds to them
+}
+
+// One direction up to its BPTT kernel: the counter fill, the cell-state
+// rebuild (recompute mode) and the kernel's arguments.
+int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& plan, const DevInfo& di,
+              int* status, hipStream_t s, rnn::RecArgs& a) {
+  int st;
+  const Layout L = layout(d);
+  const int cell = cell_of(d);
+  int perm[4];
+  inv_perm(d, perm);
+  int* flags = (int*)(ws + L.flags) + FLAG_SLOTS * rnn::FSTRIDE;
+  {
+    // one fill from the status word through the last backward counter (the
+    // forward counters in between are no longer read)
+    ProfScope ps(L_FILL, s);
+    const long long n = (long long)(flags - (int*)(ws + L.status)) +
+                        (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE;
+    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
+  }
+
+  a = rnn::RecArgs{};
+  a.T = d->T;
+  a.B = d->B;
+  a.H = d->H;
+  a.dir = d->direction;
+  a.nGroups = plan.nGroups;
+  a.nSlices = plan.nSlices;
+  a.Hs = plan.Hs;
+  a.bg = plan.bg;
+  for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
+  a.W_hh = io.W_hh;
+  a.h0 = io.h0;
+  a.c0 = (d->mode == RNN_LSTM) ? io.c0 : nullptr;
+  a.y = (void*)io.y;
+  a.ldy = ldy_of(d);
+  a.z = ws + L.z;
+  a.GZ = L.GZ;
+  a.cbuf = ws + L.c;
+  a.ldc = d->H;
+  if (d->recompute) {
+    // cell states rebuilt from the saved gates into the input-gate lane of
+    // the gate-gradient rows: step t's lane is read by the BPTT kernel
+    // before its own gradients overwrite it, and by no step after that
+    ProfScope ps(L_AUX, s);
+    const hipError_t e =
+        d->dtype == RNN_BF16
+            ? rnn::launch_lstm_cell_scan<bf16>(ws + L.z, (long long)L.GZ * d->H, io.c0, d->lengths, d->T, d->B,
+                                               d->H, d->direction, ws + L.dg, (long long)L.GD * d->H, s)
+            : rnn::launch_lstm_cell_scan<float>(ws + L.z, (long long)L.GZ * d->H, io.c0, d->lengths, d->T, d->B,
+                                                d->H, d->direction, ws + L.dg, (long long)L.GD * d->H, s);
+    if ((st = hip_status(e))) return st;
+    a.cbuf = ws + L.dg;
+    a.ldc = (long long)L.GD * d->H;
+  }
+  a.rh = ws + L.rh;
+  a.dy = io.dy;
+  a.dhT = io.dhT;
+  a.dcT = (d->mode == RNN_LSTM) ? io.dcT : nullptr;
+  a.dg = ws + L.dg;
+  a.GD = L.GD;
+  a.dh0 = io.dh0;
+  a.dc0 = (d->mode == RNN_LSTM) ? io.dc0 : nullptr;
+  a.flags = flags;
+  a.status = status;
+  a.timeout_ticks = di.ticks;
+  a.lengths = d->lengths;
+  a.att = d->att;
+  a.datt_part = (float*)(ws + L.attp);
+  if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
+  return RNN_OK;
+}
+
+// After the BPTT kernel: the score-gradient sum and the input gradient.
+int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& plan, const rnn::RecArgs& a,
+            int accumulate, hipStream_t s) {
+  int st;
+  const Layout L = layout(d);
+  int perm[4];
+  inv_perm(d, perm);
+  const int G = gates(d);
+  if (d->att && io.datt) {
+    ProfScope ps(L_AUX, s);
+    const long long TB = (long long)d->T * d->B;
+    const hipError_t e =
+        d->dtype == RNN_BF16
+            ? rnn::launch_att_reduce<bf16>(a.datt_part, plan.nSlices, TB, io.datt, accumulate ? 1 : 0, s)
+            : rnn::launch_att_reduce<float>(a.datt_part, plan.nSlices, TB, io.datt, accumulate ? 1 : 0, s);
     if ((st = hip_status(e))) return st;
   }
+  if (io.dx) {
+    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]
+    rnn::GemmArgs g{};
+    g.a = rows(ws + L.dg, (long long)L.GD * d->H);
+    g.b = perm_rows(io.W_ih, d->I, d->H, perm);
+    g.M = (long long)d->T * d->B;
+    g.N = d->I;
+    g.K = (long long)G * d->H;
+    g.c = io.dx;
+    g.ldc = ldx_of(d);
+    g.H = d->H;
+    g.accumulate = accumulate ? 1 : 0;
+    g.part = (float*)(ws + L.gemm);
+    g.ws_floats = (long long)L.gemm_floats;
+    ProfScope ps(L_DX, s);
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, true, s)))) return st;
+  }
+  return RNN_OK;
+}
+
+}  // namespace
+
+RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const void* c0, const void* W_ih,
+                    const void* W_hh, const void* b_ih, const void* b_hh, void* y, void* hT, void* cT,
+                    void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_common(d, workspace, ws_bytes);
+  if (st) return st;
+  if (!x || !W_ih || !W_hh || !b_ih || !b_hh || !y) return RNN_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, d->lengths, d->att};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  g_cu_count = di.cu;
+  const int cell = cell_of(d);
+  const bool bidir = d->direction == 2;
+  const int halves = bidir ? 2 : 1;
+  rnn::RecPlan plan;
+  bool dual;
+  if (!choose_plan([&](int cu, int xcds, rnn::RecPlan* p) { return rnn::plan_fwd(cell, d->dtype, d->B, d->H, cu, xcds, p); },
+                   bidir, di, &plan, &dual))
+    return RNN_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const rnn_desc_t hd[2] = {half_desc(d, 0), half_desc(d, 1)};
+  const size_t half_bytes = layout(&hd[0]).total;
+  int* status = (int*)(ws + layout(&hd[0]).status);
+  const FwdIO io{x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT};
+  rnn::RecArgs args[2]{};
+  for (int k = 0; k < halves; ++k)
+    if ((st = fwd_begin(&hd[k], fwd_half(d, io, k), ws + k * half_bytes, plan, di, status, s, args[k]))) return st;
+  {
+    ProfScope ps(L_RFWD, s);
+    if ((st = run_persistent(plan, dual, halves, args, di, s, "fwd"))) return st;
+  }
+  for (int k = 0; k < halves; ++k)
+    if ((st = fwd_end(&hd[k], args[k], s))) return st;
   return RNN_OK;
 }
 
@@ -425,108 +660,33 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   DevInfo di;
   if ((st = dev_info(&di))) return st;
   g_cu_count = di.cu;
-  const Layout L = layout(d);
   const int cell = cell_of(d);
+  const bool bidir = d->direction == 2;
+  const int halves = bidir ? 2 : 1;
   rnn::RecPlan plan;
-  if (!rnn::plan_bwd(cell, d->dtype, d->B, d->H, di.cu, &plan)) return RNN_ERR_UNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  int perm[4];
-  inv_perm(d, perm);
-  const int G = gates(d);
-  int* flags = (int*)(ws + L.flags) + FLAG_SLOTS * rnn::FSTRIDE;
-
-  {
-    // one fill from the status word through the last backward counter (the
-    // forward counters in between are no longer read)
-    ProfScope ps(L_FILL, s);
-    const long long n = (long long)(flags - (int*)(ws + L.status)) +
-                        (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE;
-    if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
-  }
-
-  rnn::RecArgs a{};
-  a.T = d->T;
-  a.B = d->B;
-  a.H = d->H;
-  a.dir = d->direction;
-  a.nGroups = plan.nGroups;
-  a.nSlices = plan.nSlices;
-  a.Hs = plan.Hs;
-  a.bg = plan.bg;
-  for (int i = 0; i < 4; ++i) a.perm[i] = perm[i];
-  a.W_hh = W_hh;
-  a.h0 = h0;
-  a.c0 = (d->mode == RNN_LSTM) ? c0 : nullptr;
-  a.y = (void*)y;
-  a.ldy = ldy_of(d);
-  a.z = ws + L.z;
-  a.GZ = L.GZ;
-  a.cbuf = ws + L.c;
-  a.ldc = d->H;
-  if (d->recompute) {
-    // cell states rebuilt from the saved gates into the input-gate lane of
-    // the gate-gradient rows: step t's lane is read by the BPTT kernel
-    // before its own gradients overwrite it, and by no step after that
-    ProfScope ps(L_AUX, s);
-    const hipError_t e =
-        d->dtype == RNN_BF16
-            ? rnn::launch_lstm_cell_scan<bf16>(ws + L.z, (long long)L.GZ * d->H, c0, d->lengths, d->T, d->B, d->H,
-                                               d->direction, ws + L.dg, (long long)L.GD * d->H, s)
-            : rnn::launch_lstm_cell_scan<float>(ws + L.z, (long long)L.GZ * d->H, c0, d->lengths, d->T, d->B, d->H,
-                                                d->direction, ws + L.dg, (long long)L.GD * d->H, s);
-    if ((st = hip_status(e))) return st;
-    a.cbuf = ws + L.dg;
-    a.ldc = (long long)L.GD * d->H;
-  }
-  a.rh = ws + L.rh;
-  a.dy = dy;
-  a.dhT = dhT;
-  a.dcT = (d->mode == RNN_LSTM) ? dcT : nullptr;
-  a.dg = ws + L.dg;
-  a.GD = L.GD;
-  a.dh0 = dh0;
-  a.dc0 = (d->mode == RNN_LSTM) ? dc0 : nullptr;
-  a.flags = flags;
-  a.status = (int*)(ws + L.status);
-  a.timeout_ticks = di.ticks;
-  a.lengths = d->lengths;
-  a.att = d->att;
-  a.datt_part = (float*)(ws + L.attp);
+  bool dual;
+  if (!choose_plan([&](int cu, int xcds, rnn::RecPlan* p) { return rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p); },
+                   bidir, di, &plan, &dual))
+    return RNN_ERR_UNSUPPORTED;
   // the score-gradient shares of a workgroup's units sit after its reduction buffer
   if (d->att) plan.lds_bytes += (size_t)plan.mb * 16 * plan.Hs * sizeof(float);
-  if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const rnn_desc_t hd[2] = {half_desc(d, 0), half_desc(d, 1)};
+  const size_t half_bytes = layout(&hd[0]).total;
+  int* status = (int*)(ws + layout(&hd[0]).status);
+  const BwdIO io{W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, datt};
+  rnn::RecArgs args[2]{};
+  for (int k = 0; k < halves; ++k)
+    if ((st = bwd_begin(&hd[k], bwd_half(d, io, k), ws + k * half_bytes, plan, di, status, s, args[k]))) return st;
   {
     ProfScope ps(L_RBWD, s);
-    if ((st = launch_persistent(plan, a, di, s, "bwd"))) return st;
+    if ((st = run_persistent(plan, dual, halves, args, di, s, "bwd"))) return st;
   }
-  if (d->att && datt) {
-    ProfScope ps(L_AUX, s);
-    const long long TB = (long long)d->T * d->B;
-    const hipError_t e =
-        d->dtype == RNN_BF16
-            ? rnn::launch_att_reduce<bf16>(a.datt_part, plan.nSlices, TB, datt, accumulate ? 1 : 0, s)
-            : rnn::launch_att_reduce<float>(a.datt_part, plan.nSlices, TB, datt, accumulate ? 1 : 0, s);
-    if ((st = hip_status(e))) return st;
-  }
-
-  if (dx) {
-    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]
-    rnn::GemmArgs g{};
-    g.a = rows(ws + L.dg, (long long)L.GD * d->H);
-    g.b = perm_rows(W_ih, d->I, d->H, perm);
-    g.M = (long long)d->T * d->B;
-    g.N = d->I;
-    g.K = (long long)G * d->H;
-    g.c = dx;
-    g.ldc = ldx_of(d);
-    g.H = d->H;
-    g.accumulate = accumulate ? 1 : 0;
-    g.part = (float*)(ws + L.gemm);
-    g.ws_floats = (long long)L.gemm_floats;
-    ProfScope ps(L_DX, s);
-    if ((st = hip_status(gemm_dt(d->dtype, g, false, true, s)))) return st;
-  }
+  // the second half of a bidirectional layer adds its dx and score gradient
+  for (int k = 0; k < halves; ++k)
+    if ((st = bwd_end(&hd[k], bwd_half(d, io, k), ws + k * half_bytes, plan, args[k], k == 0 ? accumulate : 1, s)))
+      return st;
   return RNN_OK;
 }
 
@@ -539,6 +699,20 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh, d->lengths};
   for (const void* p : ptrs)
     if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  if (d->direction == 2) {
+    // the two halves in turn, each over its own workspace half and [2][...] slice
+    const size_t es = esz(d);
+    const long long G = gates(d), H = d->H, BH = (long long)d->B * d->H;
+    for (int k = 0; k < 2; ++k) {
+      const rnn_desc_t h = half_desc(d, k);
+      const size_t hb = layout(&h).total;
+      if ((st = rnn_bwd_weights(&h, x, at(h0, k * BH, es), at(y, k * H, es), at(dW_ih, k * G * H * d->I, es),
+                                at(dW_hh, k * G * H * H, es), at(db_ih, k * G * H, es), at(db_hh, k * G * H, es),
+                                accumulate, (char*)workspace + k * hb, hb, stream)))
+        return st;
+    }
+    return RNN_OK;
+  }
   DevInfo di;
   if ((st = dev_info(&di))) return st;
   g_cu_count = di.cu;

@@ -214,6 +214,15 @@ struct RecArgs {
   float* datt_part;    // backward with att: per-slice partial score gradients [T][B][nSlices]
 };
 
+// Kernel argument of the persistent kernels: one direction (dual = 0), or
+// both directions of a bidirectional layer in one cooperative launch
+// (dual = 1: the blocks dispatched to XCDs 0-3 run d[0], those on XCDs 4-7
+// d[1]; each direction has nGroups*nSlices workgroups, a multiple of 4).
+struct RecLaunch {
+  RecArgs d[2];
+  int dual;
+};
+
 struct RecPlan {
   int nw, mb, nt, ki;   // waves per WG, 16-row batch tiles, 16-col output tiles, k-steps per wave
   int Hs, nGroups, nSlices;
@@ -224,9 +233,10 @@ struct RecPlan {
 };
 
 // Choose a plan and report it; returns false when no instantiated plan fits.
-bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p);
-bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, RecPlan* p);
-hipError_t launch_rec(const RecPlan& p, const RecArgs& a, hipStream_t s);
+// xcds: the XCDs one direction's workgroups spread over (8, or 4 in a dual launch).
+bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p);
+bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p);
+hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s);
 int max_coresident(const RecPlan& p);
 
 }  // namespace rnn

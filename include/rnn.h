@@ -1,7 +1,7 @@
 /*
  * rnn.h - C ABI of the MI355X (gfx950) LSTM/GRU layer engine (librnn.so).
  *
- * One recurrent layer, one direction, per call. Three calls share a
+ * One recurrent layer (one direction, or both) per call. Three calls share a
  * caller-owned workspace, in the order forward -> backward-data ->
  * backward-weights, like the cuDNN training triple wrapped on the SystemDS
  * LibMatrixCuDNN page ("singleLayerUnidirectionalRNNForward", "lstmBackward":
@@ -29,6 +29,16 @@
  * Strides let a bidirectional layer write its two halves of one [T][B][2H]
  * output (pass y + H and ldy = 2H for the reverse half), as the strided
  * OUTPUT_STRIDE rows of the persistent kernel on the CUDA fragment page.
+ *
+ * Bidirectional layer (direction 2): one call runs both directions, their
+ * persistent kernels sharing one launch (each on half of the chip) when the
+ * plan divides that way. Every per-direction array is stacked [2][...],
+ * direction 0 first: W_ih [2][G*H][I], W_hh [2][G*H][H], b_ih/b_hh [2][G*H],
+ * h0,hT,c0,cT,dh0,dc0,dhT,dcT [2][B][H], dW_ih/dW_hh/db_ih/db_hh likewise;
+ * y and dy hold direction 0 in columns [0, H) and direction 1 in [H, 2H)
+ * (ldy >= 2H, 0 = 2H); dx receives the sum of both directions (added to
+ * dx's contents when accumulate != 0), and so does datt. lengths and att
+ * apply to both directions. The workspace is twice a single direction's.
  *
  * Pointers: every tensor pointer is a device pointer, 16-byte aligned.
  * NULL h0/c0/dhT/dcT mean zeros; NULL hT/cT/dh0/dc0 are not written;
@@ -73,7 +83,8 @@ typedef enum rnn_status {
 
 typedef struct rnn_desc {
   int mode;          /* RNN_LSTM or RNN_GRU */
-  int direction;     /* 0: t = 0..T-1; 1: t = T-1..0 (outputs stay at their own t) */
+  int direction;     /* 0: t = 0..T-1; 1: t = T-1..0 (outputs stay at their own t);
+                        2: both (bidirectional layer, see above) */
   int reset_after;   /* GRU only: 0 basic, 1 reset applied after the recurrent product */
   int gate_order[4]; /* gate_order[k] = gate id stored in row block k; a permutation of
                         0..G-1 (LSTM i,f,g,o = 0..3; GRU r,u,c = 0..2). Common orders:
@@ -81,7 +92,7 @@ typedef struct rnn_desc {
   int dtype;         /* RNN_F32 or RNN_BF16 storage; arithmetic accumulates in fp32 */
   int T, B, I, H;    /* T,B >= 1; I % 8 == 0; H % 16 == 0 */
   long long ldx;     /* row stride of x/dx in elements, 0 = I; multiple of 8 */
-  long long ldy;     /* row stride of y/dy in elements, 0 = H; multiple of 8 */
+  long long ldy;     /* row stride of y/dy in elements, 0 = H (direction 2: 2H); multiple of 8 */
   const int* lengths; /* optional, device memory: int32 lengths[B], the number of
                         steps of each batch row (values clamped to [0, T]); NULL =
                         every row has T steps. Step t is active for row b iff

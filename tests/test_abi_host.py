@@ -51,10 +51,10 @@ def test_workspace_size_formula():
 
 
 @pytest.mark.parametrize("bad", [
-    dict(mode=5), dict(dtype=3), dict(direction=2), dict(T=0), dict(B=0), dict(I=0), dict(H=0),
+    dict(mode=5), dict(dtype=3), dict(direction=3), dict(direction=-1), dict(T=0), dict(B=0), dict(I=0), dict(H=0),
     dict(gate_order=(0, 0, 2, 3)), dict(gate_order=(0, 1, 2, 4)),
     dict(mode=L.RNN_GRU, gate_order=(0, 1, 3)), dict(mode=L.RNN_GRU, reset_after=2, gate_order=(0, 1, 2)),
-    dict(ldx=8), dict(ldy=16),
+    dict(ldx=8), dict(ldy=16), dict(direction=2, ldy=48),
 ])
 def test_invalid_descriptors(bad):
     d = _desc(**bad)
@@ -152,3 +152,10 @@ def test_recompute_mode_is_lstm_only_and_drops_the_cell_sequence():
     assert n1 > 0 and n0 - n1 >= T * B * H * 4
     assert g.rnn_workspace_bytes(_desc(recompute=2)) == 0
     assert g.rnn_workspace_bytes(_desc(mode=L.RNN_GRU, gate_order=(0, 1, 2), recompute=1)) == 0
+
+
+def test_bidirectional_layer_workspace_is_two_halves():
+    single = g.rnn_workspace_bytes(_desc(direction=1, ldy=64))
+    both = g.rnn_workspace_bytes(_desc(direction=2))       # ldy 0 means 2H for both directions
+    assert single > 0 and both == 2 * single
+    assert g.rnn_workspace_bytes(_desc(direction=2, ldy=64)) == both

@@ -431,3 +431,70 @@ def test_lstm_recompute_with_final_state_gradients(direction):
     got, ref = _run(wl, inp, P, direction, None, dhT, dcT, lengths=np.array([9, 4, 0, 1, 8, 9], np.int32),
                     recompute=True)
     print(compare(got, ref, "f32", extra=f"dir{direction}"))
+
+
+# ------------------------------------------------ bidirectional layer ----
+
+@pytest.mark.parametrize("mode,ra,dtype", [("lstm", None, "f32"), ("gru", True, "f32"), ("gru", False, "f32"),
+                                           ("lstm", None, "bf16")])
+def test_bidirectional_layer_runs_both_directions(mode, ra, dtype):
+    """direction 2: [2, ...] stacked weights and states, y/dy halves in one
+    [T, B, 2H] tensor, dx summed over the directions; each direction against
+    the oracle with its own weights and initial and final states."""
+    import oracle as O
+    from gru_layer_fwd_amd.api import RnnLayer
+    from rnn_harness import dev, host
+    T, B, I, H = 9, 12, 64, 64
+    if dtype == "bf16":
+        T, B, I, H = 12, 24, 256, 256
+    rng = np.random.default_rng(81)
+    G = 4 if mode == "lstm" else 3
+    from gru_layer_fwd_amd.synth import round_to
+    rnd = lambda a: round_to(a, dtype)  # noqa: E731
+    k = 1 / np.sqrt(H)
+    W_ih, W_hh = rnd(rng.uniform(-k, k, (2, G * H, I))), rnd(rng.uniform(-k, k, (2, G * H, H)))
+    b_ih, b_hh = rnd(rng.uniform(-k, k, (2, G * H))), rnd(rng.uniform(-k, k, (2, G * H)))
+    x = rnd(rng.standard_normal((T, B, I)))
+    h0 = rnd(0.5 * rng.standard_normal((2, B, H)))
+    c0 = rnd(0.5 * rng.standard_normal((2, B, H))) if mode == "lstm" else None
+    g = rnd(rng.standard_normal((T, B, 2 * H)))
+    dhT = rnd(rng.standard_normal((2, B, H)))
+    dcT = rnd(rng.standard_normal((2, B, H))) if mode == "lstm" else None
+    L = _ragged_lengths(B, T, 83)
+    lens = torch.as_tensor(L, dtype=torch.int32).to("cuda")
+    lay = RnnLayer(mode, T, B, I, H, dtype, direction=2, reset_after=bool(ra), lengths=lens)
+    d_ = lambda a: dev(a, dtype)  # noqa: E731
+    tdt = lay.torch_dtype
+    y = torch.full((T, B, 2 * H), float("nan"), dtype=tdt, device="cuda")
+    hT = torch.empty(2, B, H, dtype=tdt, device="cuda")
+    cT = torch.empty(2, B, H, dtype=tdt, device="cuda") if mode == "lstm" else None
+    dx = torch.empty(T, B, I, dtype=tdt, device="cuda")
+    dh0 = torch.empty(2, B, H, dtype=tdt, device="cuda")
+    dc0 = torch.empty(2, B, H, dtype=tdt, device="cuda") if mode == "lstm" else None
+    grads = [torch.empty(a.shape, dtype=tdt, device="cuda") for a in (W_ih, W_hh, b_ih, b_hh)]
+    Wd = [d_(a) for a in (W_ih, W_hh, b_ih, b_hh)]
+    lay.fwd(d_(x), d_(h0), d_(c0), *Wd, y, hT, cT)
+    lay.bwd_data(Wd[0], Wd[1], d_(h0), d_(c0), y, d_(g), d_(dhT), d_(dcT), dx, dh0, dc0)
+    lay.bwd_weights(d_(x), d_(h0), y, *grads)
+    torch.cuda.synchronize()
+    assert lay.device_status() == 0
+    order = (0, 1, 2, 3) if mode == "lstm" else (0, 1, 2)
+    tol_f, tol_g = (1e-4, 1e-3) if dtype == "f32" else (2e-2, 2e-2)
+    dx_ref = 0
+    for dd in range(2):
+        P = Params(W_ih[dd], W_hh[dd], b_ih[dd], b_hh[dd])
+        fw = O.layer_forward(mode, x, h0[dd], None if c0 is None else c0[dd], P, order, reverse=bool(dd),
+                             reset_after=bool(ra), lengths=L)
+        gr = O.layer_backward(mode, fw, g[:, :, dd * H:(dd + 1) * H], dhT[dd], None if dcT is None else dcT[dd])
+        dx_ref = dx_ref + gr["dx"]
+        errs = {"y": O.rel_err(host(y)[:, :, dd * H:(dd + 1) * H], fw["y"]), "hT": O.rel_err(host(hT)[dd], fw["hT"]),
+                "dh0": O.rel_err(host(dh0)[dd], gr["dh0"])}
+        for name, t in zip(("dW_ih", "dW_hh", "db_ih", "db_hh"), grads):
+            errs[name] = O.rel_err(host(t)[dd], gr[name])
+        if mode == "lstm":
+            errs["cT"] = O.rel_err(host(cT)[dd], fw["cT"])
+            errs["dc0"] = O.rel_err(host(dc0)[dd], gr["dc0"])
+        print(dd, errs)
+        assert all(v <= (tol_f if k in ("y", "hT", "cT") else tol_g) for k, v in errs.items()), (dd, errs)
+    e = O.rel_err(host(dx), dx_ref)
+    assert e <= tol_g, e
