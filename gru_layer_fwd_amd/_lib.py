@@ -34,6 +34,7 @@ _SIGS = {
     "rnn_bwd_weights": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
     "rnn_last_device_status": (_c.c_int, [_P]),
     "rnn_status_string": (_c.c_char_p, [_c.c_int]),
+    "rnn_set_handshake_timeout": (_c.c_int, [_c.c_double]),
     "rnn_profile_enable": (_c.c_int, [_c.c_int]),
     "rnn_profile_read": (_c.c_int, [_P, _c.c_int, _c.c_int]),
 }
@@ -134,6 +135,11 @@ def rnn_last_device_status(workspace) -> int:
 
 def rnn_status_string(status: int) -> str:
     return lib().rnn_status_string(status).decode()
+
+
+def rnn_set_handshake_timeout(seconds: float) -> int:
+    """Handshake time-out for later calls (0: default; < 0: give up at once)."""
+    return lib().rnn_set_handshake_timeout(float(seconds))
 
 
 def rnn_profile_enable(on: bool) -> int:

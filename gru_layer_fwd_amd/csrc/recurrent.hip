@@ -53,6 +53,12 @@ constexpr int ST_TIMEOUT = -5;
 // later kernel reads (saved gates, cell states) always uses plain stores.
 __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout) {
   const int lane = threadIdx.x & 63;
+  if (timeout < 0) {
+    // a limit of no time at all (set from the host to exercise the error
+    // path): the wait gives up at once
+    if (lane == 0) __hip_atomic_store(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
   long long t0 = 0;
   for (int it = 0;; ++it) {
     bool ok = true;

@@ -149,8 +149,12 @@ void* at(void* p, long long elems, size_t es) { return p ? (char*)p + elems * (l
 
 struct DevInfo {
   int cu = 0;
-  long long ticks = 0;
+  long long ticks = 0;  // handshake time-out in wall-clock ticks (< 0: give up at once)
+  int rate_khz = 0;
 };
+
+// handshake time-out of the persistent kernels (seconds; < 0: no time at all)
+double g_timeout_s = TIMEOUT_S;
 
 int dev_info(DevInfo* out) {
   static DevInfo cache[64];
@@ -161,10 +165,11 @@ int dev_info(DevInfo* out) {
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return RNN_ERR_DEVICE;
     if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || rate_khz <= 0)
       rate_khz = 100000;
-    cache[dev].ticks = (long long)(TIMEOUT_S * rate_khz * 1000.0);
+    cache[dev].rate_khz = rate_khz;
     cache[dev].cu = cu;
   }
   *out = cache[dev];
+  out->ticks = g_timeout_s < 0 ? -1 : (long long)(g_timeout_s * out->rate_khz * 1000.0);
   return RNN_OK;
 }
 
@@ -860,6 +865,11 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
         return st;
     }
   }
+  return RNN_OK;
+}
+
+RNN_API int rnn_set_handshake_timeout(double seconds) {
+  g_timeout_s = seconds == 0 ? TIMEOUT_S : seconds;
   return RNN_OK;
 }
 

@@ -163,6 +163,13 @@ int rnn_last_device_status(const void* workspace);
 /* Static description of a status code. */
 const char* rnn_status_string(int status);
 
+/* Time-out of the cross-workgroup step handshake for the calls queued after
+ * this one, process-wide (the bounded waits of the persistent kernels;
+ * default 10 s). 0 restores the default; a negative value makes every wait
+ * give up at once, so a call completes with RNN_ERR_TIMEOUT in its device
+ * status and undefined outputs (a way to exercise the error path). */
+int rnn_set_handshake_timeout(double seconds);
+
 /* Optional kernel timing, for measurement tools (the tracing hook of the
  * layer API; off by default). While enabled, every kernel the library queues
  * is bracketed by two HIP events recorded on the call's stream, under a label

@@ -498,3 +498,38 @@ def test_bidirectional_layer_runs_both_directions(mode, ra, dtype):
         assert all(v <= (tol_f if k in ("y", "hT", "cT") else tol_g) for k, v in errs.items()), (dd, errs)
     e = O.rel_err(host(dx), dx_ref)
     assert e <= tol_g, e
+
+
+# ------------------------------------------------- failure detection ----
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_handshake_timeout_is_reported_and_recovers(bidir):
+    """A time-out forced from the host (every bounded wait gives up at once):
+    the kernels still run to the end and the workspace status word reports
+    RNN_ERR_TIMEOUT; with the default restored the same layer is exact again."""
+    from gru_layer_fwd_amd import _lib as Lb
+    wl, inp, P = _case("lstm_f32_t8_b2_i16_h32", T=6, B=5, I=16, H=32)
+    direction = 2 if bidir else 0
+    try:
+        Lb.rnn_set_handshake_timeout(-1.0)
+        lay_args = dict(direction=direction)
+        from gru_layer_fwd_amd.api import RnnLayer
+        from rnn_harness import dev
+        lay = RnnLayer("lstm", wl.T, wl.B, wl.I, wl.H, "f32", **lay_args)
+        dirs = 2 if bidir else 1
+        G = 4
+        W = [torch.stack([dev(a, "f32")] * dirs) if bidir else dev(a, "f32") for a in (P.W_ih, P.W_hh, P.b_ih, P.b_hh)]
+        x = dev(inp["x"], "f32")
+        y = torch.empty(wl.T, wl.B, wl.H * dirs, device="cuda")
+        g = torch.randn(wl.T, wl.B, wl.H * dirs, device="cuda")
+        dx = torch.empty_like(x)
+        lay.fwd(x, None, None, *W, y)
+        torch.cuda.synchronize()
+        assert lay.device_status() == Lb.RNN_ERR_TIMEOUT
+        lay.bwd_data(W[0], W[1], None, None, y, g, None, None, dx)
+        torch.cuda.synchronize()
+        assert lay.device_status() == Lb.RNN_ERR_TIMEOUT
+    finally:
+        Lb.rnn_set_handshake_timeout(0.0)
+    got, ref = _run(wl, inp, P)
+    print(compare(got, ref, "f32"))
