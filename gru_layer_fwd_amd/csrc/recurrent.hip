@@ -313,6 +313,22 @@ __device__ __forceinline__ void spill_acc(float* red, const f4 (&acc)[MB][NT], i
   }
 }
 
+// the same for four consecutive columns (col a multiple of 4), one 16-byte
+// LDS read per wave
+template <int NW, int BG, int NCOL>
+__device__ __forceinline__ float4 red_sum4(const float* red, int row, int col) {
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float4 v = *(const float4*)&red[(w * BG + row) * NCOL + col];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  return s;
+}
+
 template <int NW, int BG, int NCOL>
 __device__ __forceinline__ float red_sum(const float* red, int row, int col) {
   float s = 0.f;
@@ -400,7 +416,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
+  // LSTM columns are unit-major (column 4u+g: gate g of unit u), so that a
+  // unit's four gate sums sit in one 16-byte LDS word per wave; the GRU's
+  // three lanes are gate-major (column g*HS+u)
   load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, [&](int col) -> long long {
+    if constexpr (CELL == CELL_LSTM) return (long long)a.perm[col & 3] * H + J0 + (col >> 2);
     const int g = col / HS;
     return (long long)a.perm[g] * H + J0 + (col - g * HS);
   });
@@ -471,10 +491,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
       TS* yr = (TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j;
       float h;
       if constexpr (CELL == CELL_LSTM) {
-        const float zi = red_sum<NW, BG, NCOL>(red, bl, 0 * HS + j) + to_f(pz[u][0]);
-        const float zf = red_sum<NW, BG, NCOL>(red, bl, 1 * HS + j) + to_f(pz[u][1]);
-        const float zg = red_sum<NW, BG, NCOL>(red, bl, 2 * HS + j) + to_f(pz[u][2]);
-        const float zo = red_sum<NW, BG, NCOL>(red, bl, 3 * HS + j) + to_f(pz[u][3]);
+        const float4 zs = red_sum4<NW, BG, NCOL>(red, bl, 4 * j);
+        const float zi = zs.x + to_f(pz[u][0]);
+        const float zf = zs.y + to_f(pz[u][1]);
+        const float zg = zs.z + to_f(pz[u][2]);
+        const float zo = zs.w + to_f(pz[u][3]);
         const float ig = sigmoidf_(zi), fg = sigmoidf_(zf), gg = tanhf_(zg), og = sigmoidf_(zo);
         const float c = fg * cst[u] + ig * gg;
         const float hn = og * tanhf_(c);
