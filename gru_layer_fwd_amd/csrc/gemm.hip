@@ -94,9 +94,9 @@ __device__ __forceinline__ bool affine_rows(const RowMap& m, long long k0, int B
     return true;
   }
   if (m.kind == 1) {
-    const long long g = k0 / m.H;
-    if ((k0 + BK - 1) / m.H != g) return false;
-    base = p + ((long long)m.perm[g] - g) * m.H * m.ld;
+    const int g = (int)k0 / m.H;
+    if (((int)k0 + BK - 1) / m.H != g) return false;
+    base = p + (pick4(m.perm, g) - g) * m.H * m.ld;
     return true;
   }
   const long long f0 = (long long)(m.dir ? m.T - 1 : 0) * m.B;  // first step's rows
@@ -215,7 +215,7 @@ struct Waves {  // 256x256 tiles run 8 waves (2x4), smaller ones 4 (2x2)
   static constexpr int NT = 64 * 2 * WGN;
 };
 
-template <typename TS, bool AKO, bool BKO, int BM, int BN>
+template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT>
 __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   extern __shared__ __align__(16) char smem[];
   constexpr int NT = Waves<BM, BN>::NT, WGN = Waves<BM, BN>::WGN;
@@ -230,8 +230,11 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   const Tile tl = tile_of(nM, nN, g.ksplit);
   const long long m0 = (long long)tl.m * BM, n0 = (long long)tl.n * BN;
   // output part of this tile: B rows, first column and column count of the part
-  const bool sec = g.n_split > 0 && n0 >= g.n_split;
-  const RowMap& bmap = sec ? g.b2 : g.b;
+  // (two output parts only in the SPLIT instantiation). The map is copied:
+  // every field then stays in registers, where a reference into the kernel
+  // argument makes the compiler keep a private copy of the whole argument
+  const bool sec = SPLIT && n0 >= g.n_split;
+  const RowMap bmap = sec ? g.b2 : g.b;
   const long long nb0 = sec ? n0 - g.n_split : n0;
   const long long nend = g.n_split > 0 ? (sec ? g.N - g.n_split : g.n_split) : g.N;
   const long long kb = (long long)tl.kz * g.kslice;
@@ -350,7 +353,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     const long long n = n0 + wn * WN + j * 16 + r16;
     if (!part_out && g.bias1 && n < g.N) {
       const long long gg = n / g.H;
-      const long long src = (long long)g.perm[gg] * g.H + (n - gg * g.H);
+      const long long src = pick4(g.perm, gg) * g.H + (n - gg * g.H);
       colbias[j] = to_f(((const TS*)g.bias1)[src]);
       if (g.bias2 && gg != g.bias_skip_gate) colbias[j] += to_f(((const TS*)g.bias2)[src]);
     }
@@ -400,7 +403,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
           if (g.c_kind == 1) {
             const long long cm = g.c_row0 + m;
             const long long gg = cm / g.H;
-            row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
+            row = pick4(g.perm, gg) * g.H + (cm - gg * g.H);
           }
           uint4* cp = sec ? (uint4*)((TS*)g.c2 + row * g.ldc2 + nl) : (uint4*)((TS*)g.c + row * g.ldc + nl);
           uint4 o = v;
@@ -445,7 +448,7 @@ __global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
     for (int e = 0; e < V; ++e) {
       const long long nn = n + e;
       const long long gg = nn / g.H;
-      const long long src = (long long)g.perm[gg] * g.H + (nn - gg * g.H);
+      const long long src = pick4(g.perm, gg) * g.H + (nn - gg * g.H);
       v[e] += to_f(((const TS*)g.bias1)[src]);
       if (g.bias2 && gg != g.bias_skip_gate) v[e] += to_f(((const TS*)g.bias2)[src]);
     }
@@ -454,7 +457,7 @@ __global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
   if (g.c_kind == 1) {
     const long long cm = g.c_row0 + m;
     const long long gg = cm / g.H;
-    row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
+    row = pick4(g.perm, gg) * g.H + (cm - gg * g.H);
   }
   const bool sec = g.n_split > 0 && n >= g.n_split;
   TS* cp = sec ? (TS*)g.c2 + row * g.ldc2 + (n - g.n_split) : (TS*)g.c + row * g.ldc + n;
@@ -483,7 +486,7 @@ __global__ __launch_bounds__(256) void rowsum_finish(GemmArgs g) {
   for (int kz = 0; kz < g.ksplit; ++kz) v += g.rowsum[(long long)kz * g.M + m];
   const long long cm = g.c_row0 + m;
   const long long gg = cm / g.H;
-  const long long row = (long long)g.perm[gg] * g.H + (cm - gg * g.H);
+  const long long row = pick4(g.perm, gg) * g.H + (cm - gg * g.H);
   TS* o = (TS*)g.rowsum_out + row;
   float w = v;
   if (g.accumulate) w += to_f(*o);
@@ -600,9 +603,9 @@ __global__ void fill_i32(int* p, int v, long long n) {
   if (i < n) p[i] = v;
 }
 
-template <typename TS, bool AKO, bool BKO, int BM, int BN>
+template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
-  const void* f = (const void*)gemm_kernel<TS, AKO, BKO, BM, BN>;
+  const void* f = (const void*)gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT>;
   const int lds = 2 * (BM + BN) * ROWB;
   static bool attr = false;
   if (!attr) {
@@ -611,16 +614,25 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
     attr = true;
   }
   const long long nM = (g.M + BM - 1) / BM, nN = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<TS, AKO, BKO, BM, BN>), dim3((unsigned)(nM * nN * g.ksplit)),
+  hipLaunchKernelGGL((gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT>), dim3((unsigned)(nM * nN * g.ksplit)),
                      dim3(Waves<BM, BN>::NT), lds, s, g);
   return hipGetLastError();
 }
 
 template <typename TS, bool AKO, bool BKO>
 hipError_t launch_shape(const GemmArgs& g, int bm, int bn, hipStream_t s) {
-  if (bm == 256 && bn == 256) return launch_tile<TS, AKO, BKO, 256, 256>(g, s);
-  if (bm == 256 && bn == 128) return launch_tile<TS, AKO, BKO, 256, 128>(g, s);
-  return launch_tile<TS, AKO, BKO, 128, 128>(g, s);
+  if constexpr (AKO && BKO) {
+    if (g.n_split > 0) {
+      if (bm == 256 && bn == 256) return launch_tile<TS, AKO, BKO, 256, 256, true>(g, s);
+      if (bm == 256 && bn == 128) return launch_tile<TS, AKO, BKO, 256, 128, true>(g, s);
+      return launch_tile<TS, AKO, BKO, 128, 128, true>(g, s);
+    }
+  } else {
+    if (g.n_split > 0) return hipErrorInvalidValue;  // two output parts: weight-gradient products only
+  }
+  if (bm == 256 && bn == 256) return launch_tile<TS, AKO, BKO, 256, 256, false>(g, s);
+  if (bm == 256 && bn == 128) return launch_tile<TS, AKO, BKO, 256, 128, false>(g, s);
+  return launch_tile<TS, AKO, BKO, 128, 128, false>(g, s);
 }
 
 }  // namespace

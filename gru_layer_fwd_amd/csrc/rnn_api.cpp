@@ -68,6 +68,7 @@ bool shape_supported(const rnn_desc_t* d) {
   if (d->I % 8 || d->H % 16) return false;
   if (ldx_of(d) % 8 || ldy_of(d) % 8) return false;
   if ((long long)d->T * d->B > (1LL << 31) / 2) return false;
+  if (4LL * d->H > (1LL << 30)) return false;  // gate-row indices in 32 bits
   return true;
 }
 

@@ -75,16 +75,26 @@ struct RowMap {
   int B, T, dir;
 };
 
+// perm[g] for g in [0, 4) as selects rather than an indexed load, so that
+// the argument structs stay in registers (an indexed array would make the
+// compiler keep a private copy of the whole kernel argument in scratch)
+__device__ __forceinline__ long long pick4(const int (&p)[4], long long g) {
+  return g == 0 ? p[0] : g == 1 ? p[1] : g == 2 ? p[2] : p[3];
+}
+
 template <typename TS>
 __device__ __forceinline__ const TS* map_row(const RowMap& m, long long o) {
   const TS* p = (const TS*)m.ptr;
+  // row indices stay below 2^31 (the launcher checks T*B and G*H): 32-bit
+  // divisions, not the much longer 64-bit sequences
   if (m.kind == 1) {
-    long long g = o / m.H;
-    return p + ((long long)m.perm[g] * m.H + (o - g * m.H)) * m.ld;
+    const int oi = (int)o, g = oi / m.H;
+    return p + (pick4(m.perm, g) * m.H + (oi - g * m.H)) * m.ld;
   }
   if (m.kind == 2) {
-    int t = (int)(o / m.B);
-    int b = (int)(o - (long long)t * m.B);
+    const int oi = (int)o;
+    int t = oi / m.B;
+    int b = oi - t * m.B;
     int first = m.dir ? (m.T - 1) : 0;
     if (t == first) return m.h0 ? (const TS*)m.h0 + (long long)b * m.ld0 : nullptr;
     int tp = m.dir ? t + 1 : t - 1;
