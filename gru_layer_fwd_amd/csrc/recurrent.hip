@@ -63,7 +63,7 @@ __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int*
   for (int it = 0;; ++it) {
     bool ok = true;
     for (int i = lane; i < n; i += 64)
-      ok = ok && (__hip_atomic_load(f + i * FSTRIDE, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
+      ok = ok && (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
     if (__all(ok)) break;
     if ((it & 63) == 0) {
       if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
@@ -113,11 +113,11 @@ __device__ __forceinline__ bool group_is_local(int* myflag, const int* gflags, i
   int x;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
   x = (x & 15) + 1;
-  if (threadIdx.x == 0) __hip_atomic_store(myflag + 1, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_flags(gflags + 1, n, 1, status, timeout);
+  if (threadIdx.x == 0) __hip_atomic_store(myflag + FLAG_PLACE, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_flags(gflags + FLAG_PLACE, n, 1, status, timeout);
   bool same = true;
   for (int i = threadIdx.x & 63; i < n; i += 64)
-    same = same && (__hip_atomic_load(gflags + i * FSTRIDE + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == x);
+    same = same && (__hip_atomic_load(gflags + FLAG_PLACE + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == x);
   return __all(same);
 }
 
@@ -401,8 +401,8 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
-  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
@@ -557,8 +557,8 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
-  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
@@ -684,8 +684,8 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
-  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
@@ -887,8 +887,8 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + (grp * a.nSlices + sl) * FSTRIDE;
-  const int* gflags = a.flags + grp * a.nSlices * FSTRIDE;
+  int* myflag = a.flags + grp * a.nSlices + sl;
+  const int* gflags = a.flags + grp * a.nSlices;
   const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;

@@ -17,7 +17,6 @@ namespace {
 using rnn::bf16;
 
 constexpr size_t ALIGN = 256;
-constexpr int FLAG_SLOTS = 1024;   // per region; >= persistent workgroups (one counter line each)
 constexpr int MAX_CHUNKS = 64;     // bias-gradient partial sums
 constexpr double TIMEOUT_S = 10.0;
 
@@ -83,7 +82,7 @@ Layout layout(const rnn_desc_t* d) {
   L.status = off;
   off += ALIGN;
   L.flags = off;
-  off += up(2 * (size_t)FLAG_SLOTS * rnn::FSTRIDE * sizeof(int));
+  off += up(2 * (size_t)rnn::FLAG_PASS * sizeof(int));  // forward and backward passes
   L.partial = off;
   off += up((size_t)MAX_CHUNKS * 4 * H * sizeof(float));
   {
@@ -293,7 +292,7 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const Dev
                       const char* what) {
   const long long nwg = (long long)p.nGroups * p.nSlices;
   const long long grid = Lr.dual ? 2 * nwg : nwg;
-  if (nwg > FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;
+  if (nwg > rnn::FLAG_PLACE) return RNN_ERR_UNSUPPORTED;  // one step counter each
   const int occ = rnn::max_coresident(p);
   if (occ < 1 || grid > (long long)occ * di.cu) {
     if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, grid, occ, di.cu);
@@ -409,8 +408,8 @@ int fwd_begin(const rnn_desc_t* d, const FwdIO& io, char* ws, const rnn::RecPlan
   {
     // one fill from the status word through the last counter this launch uses
     ProfScope ps(L_FILL, s);
-    const long long n = (long long)(L.flags - L.status) / sizeof(int) +
-                        (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE;
+    const long long n = (long long)(L.flags - L.status) / sizeof(int) + rnn::FLAG_PLACE +
+                        (long long)plan.nGroups * plan.nSlices;
     if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
   }
 
@@ -514,13 +513,13 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
   const int cell = cell_of(d);
   int perm[4];
   inv_perm(d, perm);
-  int* flags = (int*)(ws + L.flags) + FLAG_SLOTS * rnn::FSTRIDE;
+  int* flags = (int*)(ws + L.flags) + rnn::FLAG_PASS;
   {
     // one fill from the status word through the last backward counter (the
     // forward counters in between are no longer read)
     ProfScope ps(L_FILL, s);
-    const long long n = (long long)(flags - (int*)(ws + L.status)) +
-                        (long long)plan.nGroups * plan.nSlices * rnn::FSTRIDE;
+    const long long n = (long long)(flags - (int*)(ws + L.status)) + rnn::FLAG_PLACE +
+                        (long long)plan.nGroups * plan.nSlices;
     if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
   }
 

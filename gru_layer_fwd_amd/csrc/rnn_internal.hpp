@@ -182,8 +182,11 @@ hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void*
 
 
 // ------------------------------------------------- persistent recurrences --
-// step counters sit on their own 128-byte lines (stride in ints)
-constexpr int FSTRIDE = 32;
+// Step counters of one pass: one int per workgroup, a batch group's counters
+// adjacent (a consumer reads all of its group's counters with one 128-byte
+// request per poll); the placement words (XCC id + 1) follow at FLAG_PLACE.
+constexpr int FLAG_PLACE = 1024;  // ints; also the most workgroups of a launch
+constexpr int FLAG_PASS = 2 * FLAG_PLACE;  // ints per pass (counters + placement words)
 
 struct RecArgs {
   int T, B, H, dir;
