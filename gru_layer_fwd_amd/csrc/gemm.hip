@@ -185,6 +185,39 @@ __device__ __forceinline__ void rowsum_ko(float (&s)[2 * R / NT][8], const uint4
     }
 }
 
+// ---- direct-to-LDS operand loads (k-contiguous operands, no split).
+// A wave instruction `buffer_load_dwordx4 ... lds` writes its 64 lanes' 16
+// bytes to 1 KiB of LDS in lane order: 8 tile rows of 128 bytes. The chunks
+// of a row are swizzled in LDS (lds_off), so the lane at physical chunk pc of
+// row r fetches logical chunk pc ^ ((r/2)%8) from memory; the fragment reads
+// are then the same as for the register-staged loads. Rows and chunks past
+// the operand's end read a record offset past the buffer, which returns 0.
+// The instruction is written as inline assembly: the compiler then does not
+// treat every later LDS read as a possible reader of the load in flight
+// (which would make it wait for the next stage before reading the current
+// one); the kernel orders the stages itself (wait + barrier).
+constexpr int DMA_OOB = 0x7FFFFFF0;  // record count of the buffers and the offset of an empty load
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// raw buffer descriptor: base, stride 0, DMA_OOB bytes, 32-bit data format
+__device__ __forceinline__ i32x4 dma_rsrc(const void* base) {
+  const unsigned long long a = (unsigned long long)base;
+  i32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  r.y = __builtin_amdgcn_readfirstlane((int)((unsigned)(a >> 32) & 0xFFFFu));
+  r.z = DMA_OOB;
+  r.w = 0x00020000;
+  return r;
+}
+
+// 64 lanes x 16 bytes from record offsets voff to LDS [lds, lds + 1 KiB)
+__device__ __forceinline__ void dma16(const char* lds, int voff, i32x4 rs) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  const int m0 = __builtin_amdgcn_readfirstlane((int)(unsigned)(unsigned long long)(lds_char*)lds);
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs), "{m0}"(m0) : "memory");
+}
+
 struct Tile {
   int m, n, kz;
 };
@@ -215,8 +248,9 @@ struct Waves {  // 256x256 tiles run 8 waves (2x4), smaller ones 4 (2x2)
   static constexpr int NT = 64 * 2 * WGN;
 };
 
-template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT>
+template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT, bool DMA>
 __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
+  static_assert(!DMA || (!AKO && !BKO && !SPLIT), "direct-to-LDS loads: k-contiguous operands");
   extern __shared__ __align__(16) char smem[];
   constexpr int NT = Waves<BM, BN>::NT, WGN = Waves<BM, BN>::WGN;
   constexpr int TILE_A = BM * ROWB, TILE_B = BN * ROWB;
@@ -254,46 +288,12 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 
   constexpr int RA = AKO ? 1 : BM * 8 / NT, RB = BKO ? 1 : BN * 8 / NT;
   constexpr int OA = AKO ? 2 * BM / NT : 1, OB = BKO ? 2 * BN / NT : 1;
-  uint4 ra_c[RA], rb_c[RB];
-  uint4 ra_o[OA][4], rb_o[OB][4];
   float rs[OA][8];
 #pragma unroll
   for (int i = 0; i < OA; ++i)
 #pragma unroll
     for (int e = 0; e < 8; ++e) rs[i][e] = 0.f;
-
-  const TS* pa[RA];
-  const TS* pb[RB];
-  if constexpr (!AKO) rows_kc<TS, BM, NT>(pa, g.a, m0, g.M);
-  if constexpr (!BKO) rows_kc<TS, BN, NT>(pb, bmap, nb0, nend);
-  auto gload = [&](int kt) {
-    const long long k0 = kb + (long long)kt * BK;
-    if constexpr (AKO) load_ko<TS, BM, NT>(ra_o, g.a, m0, g.M, k0, ke);
-    else load_kc<TS, BM, NT>(ra_c, pa, k0, ke);
-    if constexpr (BKO) load_ko<TS, BN, NT>(rb_o, bmap, nb0, nend, k0, ke);
-    else load_kc<TS, BN, NT>(rb_c, pb, k0, ke);
-  };
-  auto sstore = [&](int b) {
-    if constexpr (AKO) {
-      store_ko<TS, BM, NT>(sA(b), ra_o);
-      if (want_rows) rowsum_ko<TS, BM, NT>(rs, ra_o);
-    } else {
-      store_kc<BM, NT>(sA(b), ra_c);
-    }
-    if constexpr (BKO) store_ko<TS, BN, NT>(sB(b), rb_o);
-    else store_kc<BN, NT>(sB(b), rb_c);
-  };
-
-  if (nk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* A = sA(buf);
-    const char* Bp = sB(buf);
+  auto kstep = [&](const char* A, const char* Bp) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 a[FM], b[FN];
@@ -306,8 +306,111 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a[i], b[j]);
     }
-    if (kt + 1 < nk) sstore(buf ^ 1);
+  };
+
+  if constexpr (DMA) {
+    // Operand rows as 32-bit byte offsets from their buffer (the launcher
+    // checks that both operands span less than DMA_OOB bytes). Thread t feeds
+    // rows (i * NW + w) * 8 + lane / 8 of each tile, physical chunk lane % 8,
+    // whose logical chunk lc depends on the row only through (w, lane).
+    constexpr int NW = NT / 64, NI = BM * 8 / NT, KQ = Chunk<TS>::KQ;
+    static_assert(BM == BN && FM >= FN, "square tiles, B fragments read within the A rows");
+    const TS* abase = (const TS*)g.a.ptr;
+    const TS* bbase = (const TS*)bmap.ptr;
+    const int lrow = lane >> 3;
+    const int lc = (lane & 7) ^ ((4 * w + (lrow >> 1)) & 7);
+    int aoff[NI], boff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (i * NW + w) * 8 + lrow;
+      const long long am = m0 + row, bn = nb0 + row;
+      aoff[i] = am < g.M ? (int)(map_row<TS>(g.a, am) - abase) * (int)sizeof(TS) + lc * 16 : -1;
+      boff[i] = bn < nend ? (int)(map_row<TS>(bmap, bn) - bbase) * (int)sizeof(TS) + lc * 16 : -1;
+    }
+    const i32x4 rsa = dma_rsrc(abase), rsb = dma_rsrc(bbase);
+    const int kend = (int)ke;
+    auto issue = [&](int st, int kt) {
+      const int k0 = kt * BK;
+      const bool kin = k0 + lc * KQ < kend;
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        dma16(sA(st) + (i * NW + w) * 1024, (kin && aoff[i] >= 0) ? aoff[i] + k0 * (int)sizeof(TS) : DMA_OOB, rsa);
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        dma16(sB(st) + (i * NW + w) * 1024, (kin && boff[i] >= 0) ? boff[i] + k0 * (int)sizeof(TS) : DMA_OOB, rsb);
+    };
+    // two stages: the loads of k-tile kt+1 run while kt is multiplied; the
+    // wait and the barrier at the top of a k-tile make its stage complete for
+    // every wave and free the other stage (every wave is past k-tile kt-1)
+    // The fragments of the second k-step are read between the products of
+    // the first (one A and at most one B fragment per row of products), so
+    // their LDS latency hides behind MFMAs; the scheduling barriers keep the
+    // compiler from gathering the reads back into one block.
+    if (nk > 0) issue(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
+      const char* A = sA(kt & 1);
+      const char* Bp = sB(kt & 1);
+      uint4 a0[FM], b0[FN], a1[FM], b1[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) a0[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, q));
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b0[j] = *(const uint4*)(Bp + lds_off(wn * WN + j * 16 + r16, q));
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a0[i], b0[j]);
+        a1[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, 4 + q));
+        if (i < FN) b1[i] = *(const uint4*)(Bp + lds_off(wn * WN + i * 16 + r16, 4 + q));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a1[i], b1[j]);
+    }
     __syncthreads();
+  } else {
+    uint4 ra_c[RA], rb_c[RB];
+    uint4 ra_o[OA][4], rb_o[OB][4];
+
+    const TS* pa[RA];
+    const TS* pb[RB];
+    if constexpr (!AKO) rows_kc<TS, BM, NT>(pa, g.a, m0, g.M);
+    if constexpr (!BKO) rows_kc<TS, BN, NT>(pb, bmap, nb0, nend);
+    auto gload = [&](int kt) {
+      const long long k0 = kb + (long long)kt * BK;
+      if constexpr (AKO) load_ko<TS, BM, NT>(ra_o, g.a, m0, g.M, k0, ke);
+      else load_kc<TS, BM, NT>(ra_c, pa, k0, ke);
+      if constexpr (BKO) load_ko<TS, BN, NT>(rb_o, bmap, nb0, nend, k0, ke);
+      else load_kc<TS, BN, NT>(rb_c, pb, k0, ke);
+    };
+    auto sstore = [&](int b) {
+      if constexpr (AKO) {
+        store_ko<TS, BM, NT>(sA(b), ra_o);
+        if (want_rows) rowsum_ko<TS, BM, NT>(rs, ra_o);
+      } else {
+        store_kc<BM, NT>(sA(b), ra_c);
+      }
+      if constexpr (BKO) store_ko<TS, BN, NT>(sB(b), rb_o);
+      else store_kc<BN, NT>(sB(b), rb_c);
+    };
+
+    if (nk > 0) {
+      gload(0);
+      sstore(0);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int buf = kt & 1;
+      if (kt + 1 < nk) gload(kt + 1);
+      kstep(sA(buf), sB(buf));
+      if (kt + 1 < nk) sstore(buf ^ 1);
+      __syncthreads();
+    }
+
   }
 
   // bias-gradient partial sums of this tile's A rows (k-outer A only)
@@ -603,9 +706,9 @@ __global__ void fill_i32(int* p, int v, long long n) {
   if (i < n) p[i] = v;
 }
 
-template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT>
+template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT, bool DMA = false>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
-  const void* f = (const void*)gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT>;
+  const void* f = (const void*)gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT, DMA>;
   const int lds = 2 * (BM + BN) * ROWB;
   static bool attr = false;
   if (!attr) {
@@ -614,13 +717,33 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
     attr = true;
   }
   const long long nM = (g.M + BM - 1) / BM, nN = (g.N + BN - 1) / BN;
-  hipLaunchKernelGGL((gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT>), dim3((unsigned)(nM * nN * g.ksplit)),
+  hipLaunchKernelGGL((gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT, DMA>), dim3((unsigned)(nM * nN * g.ksplit)),
                      dim3(Waves<BM, BN>::NT), lds, s, g);
   return hipGetLastError();
 }
 
+// Direct-to-LDS operand loads apply to bf16 products with k-contiguous
+// operands in whole 256x256 tiles without a K split, whose operands each span
+// less than DMA_OOB bytes from their base (32-bit record offsets).
+template <typename TS>
+bool dma_eligible(const GemmArgs& g, int bm, int bn) {
+  if (!std::is_same<TS, bf16>::value || bm != 256 || bn != 256 || g.ksplit != 1 || g.n_split > 0) return false;
+  auto span_ok = [&](const RowMap& m, long long rows) {
+    if (m.kind != 0 && m.kind != 1) return false;
+    const long long bytes = (rows * m.ld + g.K) * (long long)sizeof(TS);
+    return ((uintptr_t)m.ptr % 16) == 0 && m.ld % 8 == 0 && bytes < DMA_OOB;
+  };
+  // kind 1 (gate-permuted) rows stay inside the first G*H rows of the buffer
+  const long long arows = g.a.kind == 1 ? ((g.M + g.a.H - 1) / g.a.H) * g.a.H : g.M;
+  const long long brows = g.b.kind == 1 ? ((g.N + g.b.H - 1) / g.b.H) * g.b.H : g.N;
+  return span_ok(g.a, arows) && span_ok(g.b, brows) && g.K % 8 == 0 && g.K < DMA_OOB / 2;
+}
+
 template <typename TS, bool AKO, bool BKO>
 hipError_t launch_shape(const GemmArgs& g, int bm, int bn, hipStream_t s) {
+  if constexpr (!AKO && !BKO && std::is_same<TS, bf16>::value) {
+    if (dma_eligible<TS>(g, bm, bn)) return launch_tile<TS, false, false, 256, 256, false, true>(g, s);
+  }
   if constexpr (AKO && BKO) {
     if (g.n_split > 0) {
       if (bm == 256 && bn == 256) return launch_tile<TS, AKO, BKO, 256, 256, true>(g, s);
