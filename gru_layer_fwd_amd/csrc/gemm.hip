@@ -701,6 +701,42 @@ __global__ __launch_bounds__(256) void att_reduce(const float* part, int nslices
   datt[i] = from_f<TS>(sum);
 }
 
+// 64 x 64 tiles through LDS (one padding element per row): 16-byte reads of
+// 64 W rows, 16-byte writes of 64 transposed rows.
+template <typename TS>
+__global__ __launch_bounds__(256) void weight_transpose(const TS* W, int G, int H, int I, Perm4 perm, TS* wt,
+                                                        long long ldt) {
+  constexpr int T = 64, KQ = Chunk<TS>::KQ, CPR = T / KQ;  // 16-byte chunks per tile row
+  __shared__ TS tile[T][T + 1];
+  const int k0 = blockIdx.y * T, i0 = blockIdx.x * T;
+  const int K = G * H;
+  for (int c = threadIdx.x; c < T * CPR; c += 256) {
+    const int r = c / CPR, q = c % CPR;
+    const int k = k0 + r, i = i0 + q * KQ;
+    TS v[KQ];
+    if (k < K && i < I) {
+      const int g = k / H;
+      const long long row = (long long)pick4(perm.p, g) * H + (k - g * H);
+      *(uint4*)v = *(const uint4*)(W + row * I + i);
+    } else {
+#pragma unroll
+      for (int e = 0; e < KQ; ++e) v[e] = from_f<TS>(0.f);
+    }
+#pragma unroll
+    for (int e = 0; e < KQ; ++e) tile[r][q * KQ + e] = v[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < T * CPR; c += 256) {
+    const int r = c / CPR, q = c % CPR;  // output row i0 + r, columns k0 + q*KQ ..
+    const int i = i0 + r, k = k0 + q * KQ;
+    if (i >= I || k >= K) continue;
+    TS v[KQ];
+#pragma unroll
+    for (int e = 0; e < KQ; ++e) v[e] = tile[q * KQ + e][r];
+    *(uint4*)(wt + (long long)i * ldt + k) = *(const uint4*)v;
+  }
+}
+
 __global__ void fill_i32(int* p, int v, long long n) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -910,6 +946,23 @@ hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void*
   return hipGetLastError();
 }
 
+template <typename TS>
+hipError_t launch_weight_transpose(const void* W, int G, int H, int I, const int perm[4], void* wt, long long ldt,
+                                   hipStream_t s) {
+  const long long K = (long long)G * H;
+  if (K <= 0 || I <= 0) return hipSuccess;
+  if (I % Chunk<TS>::KQ || K % Chunk<TS>::KQ || ldt % Chunk<TS>::KQ || ldt < K) return hipErrorInvalidValue;
+  Perm4 p4;
+  for (int i = 0; i < 4; ++i) p4.p[i] = i < G ? perm[i] : 0;
+  dim3 grid((unsigned)((I + 63) / 64), (unsigned)((K + 63) / 64));
+  hipLaunchKernelGGL((weight_transpose<TS>), grid, dim3(256), 0, s, (const TS*)W, G, H, I, p4, (TS*)wt, ldt);
+  return hipGetLastError();
+}
+
+template hipError_t launch_weight_transpose<float>(const void*, int, int, int, const int*, void*, long long,
+                                                   hipStream_t);
+template hipError_t launch_weight_transpose<bf16>(const void*, int, int, int, const int*, void*, long long,
+                                                  hipStream_t);
 template hipError_t launch_att_reduce<float>(const float*, int, long long, void*, int, hipStream_t);
 template hipError_t launch_att_reduce<bf16>(const float*, int, long long, void*, int, hipStream_t);
 template hipError_t launch_zero_inactive<float>(void*, long long, const int*, int, int, int, hipStream_t);

@@ -32,7 +32,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : (d->direction =
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -122,6 +122,10 @@ Layout layout(const rnn_desc_t* d) {
   // AUGRU: per hidden slice partial score gradients (slices hold >= 16 units)
   L.attp = off;
   if (d->att) off += up(TB * (H / 16) * sizeof(float));
+  // bf16: W_ih transposed to [I][G*H] for the input gradient (a k-contiguous
+  // operand, loaded straight into LDS)
+  L.wt = off;
+  if (d->dtype == RNN_BF16) off += up((size_t)d->I * gates(d) * H * s);
   L.total = off;
   return L;
 }
@@ -593,10 +597,18 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
     if ((st = hip_status(e))) return st;
   }
   if (io.dx) {
-    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]
+    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]; in bf16
+    // through W_ih transposed to [I][G*H] (both operands k-contiguous)
+    ProfScope ps(L_DX, s);
+    const bool wt = d->dtype == RNN_BF16;
+    if (wt) {
+      const hipError_t e =
+          rnn::launch_weight_transpose<bf16>(io.W_ih, G, d->H, d->I, perm, ws + L.wt, (long long)G * d->H, s);
+      if ((st = hip_status(e))) return st;
+    }
     rnn::GemmArgs g{};
     g.a = rows(ws + L.dg, (long long)L.GD * d->H);
-    g.b = perm_rows(io.W_ih, d->I, d->H, perm);
+    g.b = wt ? rows(ws + L.wt, (long long)G * d->H) : perm_rows(io.W_ih, d->I, d->H, perm);
     g.M = (long long)d->T * d->B;
     g.N = d->I;
     g.K = (long long)G * d->H;
@@ -606,8 +618,7 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
     g.accumulate = accumulate ? 1 : 0;
     g.part = (float*)(ws + L.gemm);
     g.ws_floats = (long long)L.gemm_floats;
-    ProfScope ps(L_DX, s);
-    if ((st = hip_status(gemm_dt(d->dtype, g, false, true, s)))) return st;
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, !wt, s)))) return st;
   }
   return RNN_OK;
 }

@@ -180,6 +180,13 @@ hipError_t launch_lstm_cell_scan(const void* z, long long ldz, const void* c0, c
 template <typename TS>
 hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void* datt, int accumulate, hipStream_t s);
 
+// Gate-row transpose of an input weight: wt[i*ldt + k] = W[row(k)*I + i] for
+// k < G*H (canonical gate order: row(k) = perm[k/H]*H + k%H) and i < I, so
+// that the input gradient reads W_ih as a k-contiguous operand.
+template <typename TS>
+hipError_t launch_weight_transpose(const void* W, int G, int H, int I, const int perm[4], void* wt, long long ldt,
+                                   hipStream_t s);
+
 
 // ------------------------------------------------- persistent recurrences --
 // Step counters of one pass: one int per workgroup, a batch group's counters
