@@ -250,7 +250,7 @@ struct Waves {  // 256x256 tiles run 8 waves (2x4), smaller ones 4 (2x2)
 
 template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT, bool DMA>
 __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
-  static_assert(!DMA || (!AKO && !BKO && !SPLIT), "direct-to-LDS loads: k-contiguous operands");
+  static_assert(!DMA || (!AKO && !BKO), "direct-to-LDS loads: k-contiguous operands");
   extern __shared__ __align__(16) char smem[];
   constexpr int NT = Waves<BM, BN>::NT, WGN = Waves<BM, BN>::WGN;
   constexpr int TILE_A = BM * ROWB, TILE_B = BN * ROWB;
@@ -330,7 +330,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     const i32x4 rsa = dma_rsrc(abase), rsb = dma_rsrc(bbase);
     const int kend = (int)ke;
     auto issue = [&](int st, int kt) {
-      const int k0 = kt * BK;
+      const int k0 = (int)kb + kt * BK;
       const bool kin = k0 + lc * KQ < kend;
 #pragma unroll
       for (int i = 0; i < NI; ++i)
@@ -346,6 +346,10 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     // the first (one A and at most one B fragment per row of products), so
     // their LDS latency hides behind MFMAs; the scheduling barriers keep the
     // compiler from gathering the reads back into one block.
+    // row sums: one thread per A row, N tiles below rsp = min(nN, 8) take part
+    const int rsp = nN < 8 ? nN : 8;
+    const bool rows_kc = g.rowsum != nullptr && tl.n < rsp && threadIdx.x < BM;
+    float rsum = 0.f;
     if (nk > 0) issue(0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -370,8 +374,57 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a1[i], b1[j]);
+      // A written out transposed: every k-tile, N tile n takes rows
+      // [n * rpw, (n+1) * rpw) of the tile in 8 x 8 blocks (8 rows, one
+      // 16-byte k chunk), transposed in registers; lanes with consecutive row
+      // blocks write adjacent 16-byte pieces of one output row
+      if (g.at != nullptr) {
+        const int rpw = nN >= 32 ? 8 : (BM / nN + 7) / 8 * 8;
+        const int nb = rpw / 8;
+        const int cb = threadIdx.x / nb, rb = threadIdx.x - cb * nb;
+        const int r = tl.n * rpw + rb * 8;
+        if (cb < 8 && r < BM) {
+          uint4 rw[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) rw[e] = *(const uint4*)(A + lds_off(r + e, cb));
+          const long long kc0 = kb + (long long)kt * BK + cb * 8;
+          TS* out = (TS*)g.at + m0 + r;
+#pragma unroll
+          for (int kq = 0; kq < 8; ++kq) {
+            const long long k = kc0 + kq;
+            if (k >= ke) break;
+            // element kq of rows 2w, 2w+1 -> word w of the output chunk
+            const int sel = (kq & 1) ? 0x07060302 : 0x05040100;
+            uint4 o;
+            o.x = __builtin_amdgcn_perm(((const unsigned*)&rw[1])[kq >> 1], ((const unsigned*)&rw[0])[kq >> 1], sel);
+            o.y = __builtin_amdgcn_perm(((const unsigned*)&rw[3])[kq >> 1], ((const unsigned*)&rw[2])[kq >> 1], sel);
+            o.z = __builtin_amdgcn_perm(((const unsigned*)&rw[5])[kq >> 1], ((const unsigned*)&rw[4])[kq >> 1], sel);
+            o.w = __builtin_amdgcn_perm(((const unsigned*)&rw[7])[kq >> 1], ((const unsigned*)&rw[6])[kq >> 1], sel);
+            TS* dst = out + k * g.ld_at;
+            if (m0 + r + 8 <= g.M) {
+              *(uint4*)dst = o;
+            } else {
+              const TS* ov = (const TS*)&o;
+              for (int e = 0; e < 8 && m0 + r + e < g.M; ++e) dst[e] = ov[e];
+            }
+          }
+        }
+      }
+      // bias-gradient row sums (k-contiguous A): N tile n < RSP sums the
+      // 16-byte chunks c == n (mod RSP) of every row of the k-tile
+      if (rows_kc) {
+        for (int c = tl.n; c < 8; c += rsp) {
+          const uint4 v = *(const uint4*)(A + lds_off(threadIdx.x, c));
+          const unsigned* w4 = (const unsigned*)&v;
+#pragma unroll
+          for (int d = 0; d < 4; ++d)
+            rsum += __uint_as_float(w4[d] << 16) + __uint_as_float(w4[d] & 0xFFFF0000u);
+        }
+      }
     }
     __syncthreads();
+    if (rows_kc && m0 + threadIdx.x < g.M)
+      g.rowsum[((long long)tl.kz * g.rs_parts + tl.n) * g.M + m0 + threadIdx.x] = rsum;
   } else {
     uint4 ra_c[RA], rb_c[RB];
     uint4 ra_o[OA][4], rb_o[OB][4];
@@ -586,7 +639,7 @@ __global__ __launch_bounds__(256) void rowsum_finish(GemmArgs g) {
   const long long m = (long long)blockIdx.x * 256 + threadIdx.x;
   if (m >= g.M) return;
   float v = 0.f;
-  for (int kz = 0; kz < g.ksplit; ++kz) v += g.rowsum[(long long)kz * g.M + m];
+  for (int q = 0; q < g.rs_slots; ++q) v += g.rowsum[(long long)q * g.M + m];
   const long long cm = g.c_row0 + m;
   const long long gg = cm / g.H;
   const long long row = pick4(g.perm, gg) * g.H + (cm - gg * g.H);
@@ -737,6 +790,65 @@ __global__ __launch_bounds__(256) void weight_transpose(const TS* W, int G, int 
   }
 }
 
+// 64 rows x 64 elements per block: rows read as 16-byte chunks, transposed
+// through LDS, written as 16-byte chunks of 8 consecutive columns.
+template <typename TS>
+__global__ __launch_bounds__(256) void gather_transpose(RowMap src, int R, int T, int B, TS* out) {
+  constexpr int TL = 64, KQ = Chunk<TS>::KQ, CPR = TL / KQ;
+  __shared__ TS tile[TL][TL + 1];
+  const long long TB = (long long)T * B;
+  const long long c0 = (long long)blockIdx.y * TL;
+  const int r0 = blockIdx.x * TL;
+  for (int c = threadIdx.x; c < TL * CPR; c += 256) {
+    const int kc = c / CPR, q = c % CPR;
+    const long long col = c0 + kc;
+    const int r = r0 + q * KQ;
+    TS v[KQ];
+#pragma unroll
+    for (int e = 0; e < KQ; ++e) v[e] = from_f<TS>(0.f);
+    if (col < TB && r < R) {
+      const TS* p = map_row<TS>(src, col);
+      if (p) *(uint4*)v = *(const uint4*)(p + r);
+    }
+#pragma unroll
+    for (int e = 0; e < KQ; ++e) tile[kc][q * KQ + e] = v[e];
+  }
+  __syncthreads();
+  for (int c = threadIdx.x; c < TL * CPR; c += 256) {
+    const int rr = c / CPR, q = c % CPR;  // output row r0 + rr, columns c0 + q*KQ ..
+    const int r = r0 + rr;
+    const long long col = c0 + q * KQ;
+    if (r >= R || col >= TB) continue;
+    TS v[KQ];
+#pragma unroll
+    for (int e = 0; e < KQ; ++e) v[e] = tile[q * KQ + e][rr];
+    *(uint4*)(out + (long long)r * TB + col) = *(const uint4*)v;
+  }
+}
+
+// Row sums of a k-contiguous operand, one block per row (strided 16-byte
+// chunks per thread, then a fixed-order reduction): out[m] = sum_k A(m, k).
+template <typename TS>
+__global__ __launch_bounds__(256) void rowsum_rows(RowMap a, long long K, float* out) {
+  constexpr int KQ = Chunk<TS>::KQ;
+  __shared__ float part[256];
+  const TS* row = map_row<TS>(a, blockIdx.x);
+  float v = 0.f;
+  for (long long k = (long long)threadIdx.x * KQ; k < K; k += 256LL * KQ) {
+    TS e[KQ];
+    *(uint4*)e = *(const uint4*)(row + k);
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) v += to_f(e[i]);
+  }
+  part[threadIdx.x] = v;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = part[0];
+}
+
 __global__ void fill_i32(int* p, int v, long long n) {
   long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -763,24 +875,28 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
 // less than DMA_OOB bytes from their base (32-bit record offsets).
 template <typename TS>
 bool dma_eligible(const GemmArgs& g, int bm, int bn) {
-  if (!std::is_same<TS, bf16>::value || bm != 256 || bn != 256 || g.ksplit != 1 || g.n_split > 0) return false;
+  if (!std::is_same<TS, bf16>::value || bm != 256 || bn != 256) return false;
   auto span_ok = [&](const RowMap& m, long long rows) {
     if (m.kind != 0 && m.kind != 1) return false;
     const long long bytes = (rows * m.ld + g.K) * (long long)sizeof(TS);
     return ((uintptr_t)m.ptr % 16) == 0 && m.ld % 8 == 0 && bytes < DMA_OOB;
   };
   // kind 1 (gate-permuted) rows stay inside the first G*H rows of the buffer
-  const long long arows = g.a.kind == 1 ? ((g.M + g.a.H - 1) / g.a.H) * g.a.H : g.M;
-  const long long brows = g.b.kind == 1 ? ((g.N + g.b.H - 1) / g.b.H) * g.b.H : g.N;
-  return span_ok(g.a, arows) && span_ok(g.b, brows) && g.K % 8 == 0 && g.K < DMA_OOB / 2;
+  auto rows_of = [&](const RowMap& m, long long n) { return m.kind == 1 ? (n + m.H - 1) / m.H * m.H : n; };
+  const long long nb = g.n_split > 0 ? g.n_split : g.N;
+  if (g.n_split > 0 && !span_ok(g.b2, rows_of(g.b2, g.N - nb))) return false;
+  return span_ok(g.a, rows_of(g.a, g.M)) && span_ok(g.b, rows_of(g.b, nb)) && g.K % 8 == 0 && g.K < DMA_OOB / 2;
 }
 
 template <typename TS, bool AKO, bool BKO>
 hipError_t launch_shape(const GemmArgs& g, int bm, int bn, hipStream_t s) {
   if constexpr (!AKO && !BKO && std::is_same<TS, bf16>::value) {
-    if (dma_eligible<TS>(g, bm, bn)) return launch_tile<TS, false, false, 256, 256, false, true>(g, s);
+    if (dma_eligible<TS>(g, bm, bn)) {
+      if (g.n_split > 0) return launch_tile<TS, false, false, 256, 256, true, true>(g, s);
+      return launch_tile<TS, false, false, 256, 256, false, true>(g, s);
+    }
   }
-  if constexpr (AKO && BKO) {
+  if constexpr (AKO == BKO) {
     if (g.n_split > 0) {
       if (bm == 256 && bn == 256) return launch_tile<TS, AKO, BKO, 256, 256, true>(g, s);
       if (bm == 256 && bn == 128) return launch_tile<TS, AKO, BKO, 256, 128, true>(g, s);
@@ -845,7 +961,7 @@ GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long lon
 
 size_t gemm_workspace_floats(long long M, long long N, long long K, int cu_count) {
   const GemmPlan p = plan_gemm(M, N, K, cu_count, 1LL << 62);
-  return (size_t)p.ksplit * (size_t)(M * N + M);
+  return (size_t)p.ksplit * (size_t)(M * N + 8 * M);  // partial tiles, row-sum partials
 }
 
 template <typename TS>
@@ -856,18 +972,44 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
   g.ksplit = p.ksplit;
   g.kslice = (g.ksplit == 1) ? g.K : p.kslice;
   if (g.ksplit > 1 && !g.part) return hipErrorInvalidValue;
-  // row sums go to the per-slice buffer after the partial tiles
+  // Row sums (bias gradients) go to the per-slice buffer after the partial
+  // tiles: from the register-staged k-outer A (one part per slice) or from
+  // the k-contiguous A tiles of the direct-load kernel (one part per N tile,
+  // at most 8). Other products take no row sums, and only the direct-load
+  // kernel writes A out transposed.
+  const bool dma = !a_kouter && !b_kouter && dma_eligible<TS>(g, p.bm, p.bn);
+  const long long nN = (g.N + p.bn - 1) / p.bn;
+  // k-contiguous A without the direct-load kernel: row sums by a pass of
+  // their own (one slot), the transposed A by the gather transpose
+  const bool rows_pass = g.rowsum_out && !a_kouter && !dma;
+  void* const at = g.at;
+  if (at && a_kouter) return hipErrorInvalidValue;
+  if (!dma) g.at = nullptr;
+  g.rs_parts = (g.rowsum_out && dma) ? (int)(nN < 8 ? nN : 8) : 1;
+  g.rs_slots = rows_pass ? 1 : g.ksplit * g.rs_parts;
   g.rowsum = (g.rowsum_out && g.part) ? g.part + (long long)g.ksplit * g.M * g.N : nullptr;
   if (g.rowsum_out && !g.rowsum) return hipErrorInvalidValue;
   if (g.n_split > 0 && (g.bias1 || g.n_split >= g.N || g.n_split % p.bn != 0)) return hipErrorInvalidValue;
-  if (g.part && (long long)g.ksplit * (g.M * g.N + g.M) > g.ws_floats && (g.ksplit > 1 || g.rowsum_out))
+  if (g.part && (long long)g.ksplit * (g.M * g.N + g.M * g.rs_parts) > g.ws_floats && (g.ksplit > 1 || g.rowsum_out))
     return hipErrorInvalidValue;
+  GemmArgs gk = g;
+  if (rows_pass) gk.rowsum = nullptr;  // the product kernel takes none
   hipError_t e;
-  if (!a_kouter && !b_kouter) e = launch_shape<TS, false, false>(g, p.bm, p.bn, s);
-  else if (!a_kouter && b_kouter) e = launch_shape<TS, false, true>(g, p.bm, p.bn, s);
-  else if (a_kouter && b_kouter) e = launch_shape<TS, true, true>(g, p.bm, p.bn, s);
+  if (!a_kouter && !b_kouter) e = launch_shape<TS, false, false>(gk, p.bm, p.bn, s);
+  else if (!a_kouter && b_kouter) e = launch_shape<TS, false, true>(gk, p.bm, p.bn, s);
+  else if (a_kouter && b_kouter) e = launch_shape<TS, true, true>(gk, p.bm, p.bn, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
+  if (at && !dma) {
+    // A rows are M vectors of K: transposed to at[k * M + m]
+    if (g.ld_at != g.M || g.M > 0x7fffffff) return hipErrorInvalidValue;
+    if ((e = launch_gather_transpose<TS>(g.a, (int)g.K, 1, (int)g.M, at, s)) != hipSuccess) return e;
+  }
+  if (rows_pass) {
+    if (g.M > 0x7fffffff || g.K % Chunk<TS>::KQ) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((rowsum_rows<TS>), dim3((unsigned)g.M), dim3(256), 0, s, g.a, g.K, g.rowsum);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (g.ksplit > 1) {
     const long long n = g.M * g.N;
     if (g.N % 8 != 0 || g.ldc % 8 != 0 || (g.n_split > 0 && (g.ldc2 % 8 != 0 || g.n_split % 8 != 0)))
@@ -963,6 +1105,20 @@ template hipError_t launch_weight_transpose<float>(const void*, int, int, int, c
                                                    hipStream_t);
 template hipError_t launch_weight_transpose<bf16>(const void*, int, int, int, const int*, void*, long long,
                                                   hipStream_t);
+template <typename TS>
+hipError_t launch_gather_transpose(const RowMap& src, int R, int T, int B, void* out, hipStream_t s) {
+  const long long TB = (long long)T * B;
+  if (R <= 0 || TB <= 0) return hipSuccess;
+  // 16-byte chunks along both the rows and the columns
+  if (R % Chunk<TS>::KQ || TB % Chunk<TS>::KQ || src.ld % Chunk<TS>::KQ) return hipErrorInvalidValue;
+  if ((TB + 63) / 64 > 0x7fffffff) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((R + 63) / 64), (unsigned)((TB + 63) / 64));
+  hipLaunchKernelGGL((gather_transpose<TS>), grid, dim3(256), 0, s, src, R, T, B, (TS*)out);
+  return hipGetLastError();
+}
+
+template hipError_t launch_gather_transpose<float>(const RowMap&, int, int, int, void*, hipStream_t);
+template hipError_t launch_gather_transpose<bf16>(const RowMap&, int, int, int, void*, hipStream_t);
 template hipError_t launch_att_reduce<float>(const float*, int, long long, void*, int, hipStream_t);
 template hipError_t launch_att_reduce<bf16>(const float*, int, long long, void*, int, hipStream_t);
 template hipError_t launch_zero_inactive<float>(void*, long long, const int*, int, int, int, hipStream_t);

@@ -32,7 +32,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : (d->direction =
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, dgt, xt, ht, total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -69,6 +69,12 @@ bool shape_supported(const rnn_desc_t* d) {
   if ((long long)d->T * d->B > (1LL << 31) / 2) return false;
   if (4LL * d->H > (1LL << 30)) return false;  // gate-row indices in 32 bits
   return true;
+}
+
+// bf16 LSTM layers run the weight gradients as one product over k-contiguous
+// (transposed) operands; T*B is then a whole number of 16-byte chunks
+bool nt_weight_grads(const rnn_desc_t* d) {
+  return d->mode == RNN_LSTM && d->dtype == RNN_BF16 && ((long long)d->T * d->B) % 8 == 0;
 }
 
 Layout layout(const rnn_desc_t* d) {
@@ -126,6 +132,17 @@ Layout layout(const rnn_desc_t* d) {
   // operand, loaded straight into LDS)
   L.wt = off;
   if (d->dtype == RNN_BF16) off += up((size_t)d->I * gates(d) * H * s);
+  // bf16 LSTM: the weight-gradient product as a k-contiguous one: the gate
+  // gradients, x and h_{t-1} transposed to [.][T*B]
+  L.dgt = L.xt = L.ht = off;
+  if (nt_weight_grads(d)) {
+    L.dgt = off;
+    off += up(TB * 4 * H * s);
+    L.xt = off;
+    off += up(TB * (size_t)d->I * s);
+    L.ht = off;
+    off += up(TB * H * s);
+  }
   L.total = off;
   return L;
 }
@@ -618,7 +635,18 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
     g.accumulate = accumulate ? 1 : 0;
     g.part = (float*)(ws + L.gemm);
     g.ws_floats = (long long)L.gemm_floats;
+    if (nt_weight_grads(d)) {
+      // the gate gradients transposed for the weight gradients, written
+      // from the product's own A tiles
+      g.at = ws + L.dgt;
+      g.ld_at = g.M;
+    }
     if ((st = hip_status(gemm_dt(d->dtype, g, false, !wt, s)))) return st;
+  } else if (nt_weight_grads(d)) {
+    ProfScope ps(L_AUX, s);
+    const hipError_t e = rnn::launch_gather_transpose<bf16>(rows(ws + L.dg, (long long)L.GD * d->H), 4 * d->H, d->T,
+                                                            d->B, ws + L.dgt, s);
+    if ((st = hip_status(e))) return st;
   }
   return RNN_OK;
 }
@@ -785,7 +813,37 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   // output parts (dG is read once, one split-K finish); the bias gradients
   // (equal for the two biases) come from its row sums
   const bool merged = cell == rnn::CELL_LSTM && dW_ih && dW_hh && d->I % 256 == 0;
-  if (merged) {
+  if (merged && nt_weight_grads(d)) {
+    // the same product with k-contiguous operands: dG^T (written by the
+    // input-gradient product) against x^T and h_{t-1}^T; the bias gradients
+    // from its row sums
+    ProfScope ps(L_DW, s);
+    rnn::GemmArgs g{};
+    hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
+    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(hprev, H, d->T, d->B, ws + L.ht, s);
+    if ((st = hip_status(e))) return st;
+    g.a = rows(ws + L.dgt, TB);
+    g.b = rows(ws + L.xt, TB);
+    g.b2 = rows(ws + L.ht, TB);
+    g.n_split = d->I;
+    g.M = (long long)G * H;
+    g.N = (long long)d->I + H;
+    g.K = TB;
+    g.c = dW_ih;
+    g.ldc = d->I;
+    g.c2 = dW_hh;
+    g.ldc2 = H;
+    g.c_kind = 1;
+    g.c_row0 = 0;
+    g.H = H;
+    for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+    g.accumulate = acc;
+    g.part = (float*)(ws + L.gemm);
+    g.ws_floats = (long long)L.gemm_floats;
+    g.rowsum_out = db_ih ? db_ih : db_hh;
+    g.rowsum_out2 = db_ih ? db_hh : nullptr;
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+  } else if (merged) {
     rnn::GemmArgs g{};
     g.a = rows(dg, GDH);
     g.b = rows(x, ldx_of(d));

@@ -120,7 +120,7 @@ struct GemmArgs {
   const void* bias1;  // optional: bias1[perm-mapped n] (+ bias2 unless gate == skip)
   const void* bias2;
   int bias_skip_gate;
-  // fp32 scratch: split-K partial tiles [ksplit][M][N], then row sums [ksplit][M]
+  // fp32 scratch: split-K partial tiles [ksplit][M][N], then row-sum partials
   float* part;
   long long ws_floats;
   // optional bias gradients = row sums of a k-outer A over k, written like
@@ -134,10 +134,16 @@ struct GemmArgs {
   RowMap b2;
   void* c2;
   long long ldc2;
+  // optional (direct-load products with a k-contiguous A): A written out
+  // transposed as well, at[k * ld_at + m] for every (m, k) of the product
+  void* at;
+  long long ld_at;
   // set by the launcher
   int ksplit;
   long long kslice;
-  float* rowsum;
+  float* rowsum;   // row-sum partials [rs_slots][M]: slice kz, part p at kz * rs_parts + p
+  int rs_parts;
+  int rs_slots;
 };
 
 struct GemmPlan {
@@ -179,6 +185,11 @@ hipError_t launch_lstm_cell_scan(const void* z, long long ldz, const void* c0, c
 
 template <typename TS>
 hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void* datt, int accumulate, hipStream_t s);
+
+// Operand transpose for the weight gradients: out[r * T*B + i] = row i of
+// `src` (i = t*B + b), element r (zero where the map has no row), r < R.
+template <typename TS>
+hipError_t launch_gather_transpose(const RowMap& src, int R, int T, int B, void* out, hipStream_t s);
 
 // Gate-row transpose of an input weight: wt[i*ldt + k] = W[row(k)*I + i] for
 // k < G*H (canonical gate order: row(k) = perm[k/H]*H + k%H) and i < I, so

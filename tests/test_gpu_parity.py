@@ -95,6 +95,17 @@ def test_accumulate_and_skip_dx():
         np.testing.assert_array_equal(nodx[k], once[k])
 
 
+def test_bf16_lstm_weight_gradients_without_dx():
+    # bf16 LSTM weight gradients run over transposed gate gradients, written
+    # by the input-gradient product or, when dx is not requested, by a
+    # transpose of their own: both give the same values
+    wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=16, B=32, I=256, H=256, h0_std=0.3, c0_std=0.3)
+    once = gpu_layer("lstm", "bf16", P, inp["x"], inp["h0"], inp["c0"], inp["g"])
+    nodx = gpu_layer("lstm", "bf16", P, inp["x"], inp["h0"], inp["c0"], inp["g"], want_dx=False)
+    for k in ("dW_ih", "dW_hh", "db_ih", "db_hh", "dh0", "dc0", "y"):
+        np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
+
+
 @pytest.mark.parametrize("name", ["gru_f32_t64_b16_i256_h256", "grura_f32_t64_b16_i256_h256"])
 def test_gru_f32_full(name):
     wl, inp, P = _case(name)
