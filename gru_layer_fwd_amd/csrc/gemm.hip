@@ -639,7 +639,14 @@ __global__ __launch_bounds__(256) void rowsum_finish(GemmArgs g) {
   const long long m = (long long)blockIdx.x * 256 + threadIdx.x;
   if (m >= g.M) return;
   float v = 0.f;
-  for (int q = 0; q < g.rs_slots; ++q) v += g.rowsum[(long long)q * g.M + m];
+  // slots loaded 8 at a time, then added in order
+  for (int q0 = 0; q0 < g.rs_slots; q0 += 8) {
+    float p[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) p[i] = q0 + i < g.rs_slots ? g.rowsum[(long long)(q0 + i) * g.M + m] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v += p[i];
+  }
   const long long cm = g.c_row0 + m;
   const long long gg = cm / g.H;
   const long long row = pick4(g.perm, gg) * g.H + (cm - gg * g.H);

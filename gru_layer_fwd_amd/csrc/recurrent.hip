@@ -51,7 +51,8 @@ constexpr int ST_TIMEOUT = -5;
 // plain stores when the whole batch group shares one XCD's L2 (`local`) and
 // device-scope stores otherwise. Data that only the owning workgroup or a
 // later kernel reads (saved gates, cell states) always uses plain stores.
-__device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout) {
+__device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout,
+                                           int stride = 1, bool pipe = false) {
   const int lane = threadIdx.x & 63;
   if (timeout < 0) {
     // a limit of no time at all (set from the host to exercise the error
@@ -60,10 +61,51 @@ __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int*
     return;
   }
   long long t0 = 0;
+  if (pipe && n <= 64) {
+    // One counter per lane, two polls in flight: a new poll is issued as
+    // soon as the older one has been checked, so a counter set while one
+    // poll is on its way is seen by the next about half an L2 round trip
+    // later rather than a whole one. The status word and the time-out are
+    // looked at only once a wait has lasted over 20 us (never in a normal
+    // step), so that the loop carries no other load.
+    const int* p = f + (lane < n ? lane : 0) * stride;
+    int v0 = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_sleep(4);
+    int v1 = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    t0 = (long long)wall_clock64();
+    // runs of polls in straight-line code (the compiler then tracks the two
+    // loads in flight exactly), the first one ahead of the loop; the
+    // time-out between runs
+    auto run = [&]() {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (__all(v0 >= target)) return true;
+        v0 = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all(v1 >= target)) return true;
+        v1 = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      return false;
+    };
+    bool done = run();
+    while (!done) {
+      done = run();
+      if (done) break;
+      const long long now = (long long)wall_clock64();
+      if (now - t0 > (timeout >> 19)) {
+        if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+        if (now - t0 > timeout) {
+          if (lane == 0) __hip_atomic_store(status, ST_TIMEOUT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    asm volatile("" ::: "memory");
+    return;
+  }
   for (int it = 0;; ++it) {
     bool ok = true;
     for (int i = lane; i < n; i += 64)
-      ok = ok && (__hip_atomic_load(f + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
+      ok = ok && (__hip_atomic_load(f + i * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target);
     if (__all(ok)) break;
     if ((it & 63) == 0) {
       if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
@@ -108,16 +150,16 @@ __device__ __forceinline__ void xstore(bf16* p, float v, bool local) {
 // second word of its counter line with a device-scope store, waits (device
 // scope) until all members of its batch group have done so and compares.
 // Every wave reads the same published values, so the whole group agrees.
-__device__ __forceinline__ bool group_is_local(int* myflag, const int* gflags, int n, int* status,
-                                               long long timeout) {
+__device__ __forceinline__ bool group_is_local(int* myflag, const int* gflags, int n, int stride, int place_off,
+                                               int* status, long long timeout) {
   int x;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
   x = (x & 15) + 1;
-  if (threadIdx.x == 0) __hip_atomic_store(myflag + FLAG_PLACE, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_flags(gflags + FLAG_PLACE, n, 1, status, timeout);
+  if (threadIdx.x == 0) __hip_atomic_store(myflag + place_off, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_flags(gflags + place_off, n, 1, status, timeout, stride);
   bool same = true;
   for (int i = threadIdx.x & 63; i < n; i += 64)
-    same = same && (__hip_atomic_load(gflags + FLAG_PLACE + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == x);
+    same = same && (__hip_atomic_load(gflags + place_off + i * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == x);
   return __all(same);
 }
 
@@ -401,9 +443,13 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
-  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
+  // groups of 64 or more rows always span several XCDs (one counter line
+  // each); a constant stride keeps their register-bound code lean
+  const int fstride = MB >= 4 ? FLAG_LINE : a.fstride;
+  const int place_off = MB >= 4 ? 1 : a.place_off;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * fstride;
+  const int* gflags = a.flags + grp * a.nSlices * fstride;
+  const bool local = group_is_local(myflag, gflags, a.nSlices, fstride, place_off, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -465,7 +511,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
         pa[u] = *ap;
       }
     }
-    if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks);
+    if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks, fstride, MB < 4 && local);
     f4 acc[MB][NT];
     zero_acc(acc);
     if (tiled && s > 0) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
@@ -557,9 +603,10 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
-  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
+  int* myflag = a.flags + (grp * a.nSlices + sl) * a.fstride;
+  const int* gflags = a.flags + grp * a.nSlices * a.fstride;
+  const bool local =
+      group_is_local(myflag, gflags, a.nSlices, a.fstride, a.place_off, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -602,7 +649,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
       pa[u] = *ap;  // AUGRU attention score of this step and row
     }
     // phase A: r, u
-    if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks);
+    if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks, a.fstride, local);
     {
       f4 acc[MB][NTA];
       zero_acc(acc);
@@ -627,7 +674,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
     }
     publish(myflag, 2 * s + 1, local);
     // phase B: candidate and new state
-    wait_flags(gflags, a.nSlices, 2 * s + 1, a.status, a.timeout_ticks);
+    wait_flags(gflags, a.nSlices, 2 * s + 1, a.status, a.timeout_ticks, a.fstride, local);
     {
       f4 acc[MB][NTB];
       zero_acc(acc);
@@ -684,9 +731,13 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
-  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
+  // groups of 64 or more rows always span several XCDs (one counter line
+  // each); a constant stride keeps their register-bound code lean
+  const int fstride = MB >= 4 ? FLAG_LINE : a.fstride;
+  const int place_off = MB >= 4 ? 1 : a.place_off;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * fstride;
+  const int* gflags = a.flags + grp * a.nSlices * fstride;
+  const bool local = group_is_local(myflag, gflags, a.nSlices, fstride, place_off, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -768,7 +819,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
     f4 acc[MB][NT];
     zero_acc(acc);
     if (n > 0) {
-      wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks);
+      wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks, fstride, CELL == CELL_LSTM && MB < 4 && local);
       if (tiled) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
       if (!tiled) {
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
@@ -887,9 +938,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
-  int* myflag = a.flags + grp * a.nSlices + sl;
-  const int* gflags = a.flags + grp * a.nSlices;
-  const bool local = group_is_local(myflag, gflags, a.nSlices, a.status, a.timeout_ticks);
+  int* myflag = a.flags + (grp * a.nSlices + sl) * a.fstride;
+  const int* gflags = a.flags + grp * a.nSlices * a.fstride;
+  const bool local =
+      group_is_local(myflag, gflags, a.nSlices, a.fstride, a.place_off, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -943,7 +995,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
       f4 acc[MB][NT];
       zero_acc(acc);
       if (n > 0) {
-        wait_flags(gflags, a.nSlices, 2 * n, a.status, a.timeout_ticks);
+        wait_flags(gflags, a.nSlices, 2 * n, a.status, a.timeout_ticks, a.fstride);
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);
         contract<TS, MB, NT, KIA>(acc, WA, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, 2 * H, 1 << 30,
                                   0);
@@ -987,7 +1039,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
     }
     publish(myflag, 2 * n + 1, local);
     if (a.att) att_rows<HS>(attl, a.datt_part, t, B, b0, bend, a.nSlices, sl);
-    wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks);
+    wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks, a.fstride);
     {
       f4 acc[MB][NT];
       zero_acc(acc);
@@ -1131,7 +1183,8 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, 
       const double cost = step_cost(e, bg, groups, slices, K, kstep, esize, ring, xcds);
       if (cost < best) {
         best = cost;
-        *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e)};
+        *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e),
+                     xcd_span(nwg, slices, xcds)};
         found = true;
       }
     }

@@ -5,6 +5,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <vector>
 
 #include "../../include/rnn.h"
@@ -75,6 +76,22 @@ bool shape_supported(const rnn_desc_t* d) {
 // (transposed) operands; T*B is then a whole number of 16-byte chunks
 bool nt_weight_grads(const rnn_desc_t* d) {
   return d->mode == RNN_LSTM && d->dtype == RNN_BF16 && ((long long)d->T * d->B) % 8 == 0;
+}
+
+// Step-counter layout of a plan (see FLAG_LINE): adjacent counters for a
+// batch group on one XCD, one line each otherwise; and the count of ints
+// from the first counter through the last placement word of nwg workgroups.
+void counter_layout(const rnn::RecPlan& plan, int* stride, int* place_off) {
+  // (the kernels of 64-row tiles assume one line per counter)
+  const bool packed = plan.xcd_span <= 1 && plan.mb < 4;
+  *stride = packed ? 1 : rnn::FLAG_LINE;
+  *place_off = packed ? rnn::FLAG_SLOTS : 1;
+}
+long long counter_ints(const rnn::RecPlan& plan) {
+  int stride, place;
+  counter_layout(plan, &stride, &place);
+  const long long nwg = (long long)plan.nGroups * plan.nSlices;
+  return std::max((long long)place + nwg, nwg * stride);
 }
 
 Layout layout(const rnn_desc_t* d) {
@@ -313,7 +330,7 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const Dev
                       const char* what) {
   const long long nwg = (long long)p.nGroups * p.nSlices;
   const long long grid = Lr.dual ? 2 * nwg : nwg;
-  if (nwg > rnn::FLAG_PLACE) return RNN_ERR_UNSUPPORTED;  // one step counter each
+  if (nwg > rnn::FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;  // one step counter each
   const int occ = rnn::max_coresident(p);
   if (occ < 1 || grid > (long long)occ * di.cu) {
     if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, grid, occ, di.cu);
@@ -323,9 +340,9 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const Dev
   if (log_on())
     fprintf(stderr,
             "[rnn] %s: %s%d groups of %d rows x %d slices (%d units), %d waves, mb=%d nt=%d ki=%d, lds=%zu, "
-            "ring=%s, model %.2f us/step\n",
+            "ring=%s, counters every %d ints, model %.2f us/step\n",
             what, Lr.dual ? "2 directions x " : "", p.nGroups, p.bg, p.nSlices, p.Hs, p.nw, p.mb, p.nt, p.ki,
-            p.lds_bytes, a.xbuf ? (a.xpacked ? "packed" : "tiled") : "off", p.cost_us);
+            p.lds_bytes, a.xbuf ? (a.xpacked ? "packed" : "tiled") : "off", a.fstride, p.cost_us);
   hipError_t e = rnn::launch_rec(p, Lr, s);
   if (e != hipSuccess) {
     if (log_on()) fprintf(stderr, "[rnn] %s: launch failed: %s\n", what, hipGetErrorString(e));
@@ -429,8 +446,7 @@ int fwd_begin(const rnn_desc_t* d, const FwdIO& io, char* ws, const rnn::RecPlan
   {
     // one fill from the status word through the last counter this launch uses
     ProfScope ps(L_FILL, s);
-    const long long n = (long long)(L.flags - L.status) / sizeof(int) + rnn::FLAG_PLACE +
-                        (long long)plan.nGroups * plan.nSlices;
+    const long long n = (long long)(L.flags - L.status) / sizeof(int) + counter_ints(plan);
     if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
   }
 
@@ -481,6 +497,7 @@ int fwd_begin(const rnn_desc_t* d, const FwdIO& io, char* ws, const rnn::RecPlan
   a.cT = (d->mode == RNN_LSTM) ? io.cT : nullptr;
   a.GD = L.GD;
   a.flags = (int*)(ws + L.flags);
+  counter_layout(plan, &a.fstride, &a.place_off);
   a.status = status;
   a.timeout_ticks = di.ticks;
   a.lengths = d->lengths;
@@ -539,8 +556,7 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
     // one fill from the status word through the last backward counter (the
     // forward counters in between are no longer read)
     ProfScope ps(L_FILL, s);
-    const long long n = (long long)(flags - (int*)(ws + L.status)) + rnn::FLAG_PLACE +
-                        (long long)plan.nGroups * plan.nSlices;
+    const long long n = (long long)(flags - (int*)(ws + L.status)) + counter_ints(plan);
     if ((st = hip_status(rnn::launch_fill_i32((int*)(ws + L.status), 0, n, s)))) return st;
   }
 
@@ -587,6 +603,7 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
   a.dh0 = io.dh0;
   a.dc0 = (d->mode == RNN_LSTM) ? io.dc0 : nullptr;
   a.flags = flags;
+  counter_layout(plan, &a.fstride, &a.place_off);
   a.status = status;
   a.timeout_ticks = di.ticks;
   a.lengths = d->lengths;

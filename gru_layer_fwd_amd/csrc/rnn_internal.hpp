@@ -200,11 +200,15 @@ hipError_t launch_weight_transpose(const void* W, int G, int H, int I, const int
 
 
 // ------------------------------------------------- persistent recurrences --
-// Step counters of one pass: one int per workgroup, a batch group's counters
-// adjacent (a consumer reads all of its group's counters with one 128-byte
-// request per poll); the placement words (XCC id + 1) follow at FLAG_PLACE.
-constexpr int FLAG_PLACE = 1024;  // ints; also the most workgroups of a launch
-constexpr int FLAG_PASS = 2 * FLAG_PLACE;  // ints per pass (counters + placement words)
+// Step counters of one pass: one per workgroup, `fstride` ints apart. A
+// batch group held by one XCD keeps its counters adjacent (stride 1: a
+// consumer reads them all with one 128-byte request per poll); groups spread
+// over several XCDs give every counter its own 128-byte line (stride 32), as
+// device-scope writes from several XCDs into one line are slow. The
+// placement word (XCC id + 1) of a counter sits `place_off` ints after it.
+constexpr int FLAG_SLOTS = 1024;               // most workgroups of a launch
+constexpr int FLAG_LINE = 32;                  // ints per 128-byte line
+constexpr int FLAG_PASS = FLAG_SLOTS * FLAG_LINE;  // ints per pass
 
 struct RecArgs {
   int T, B, H, dir;
@@ -233,6 +237,7 @@ struct RecArgs {
   void* dh0;
   void* dc0;
   int* flags;
+  int fstride, place_off;  // counter stride and placement-word offset (ints)
   int* status;
   long long timeout_ticks;
   // exchange ring in the MFMA operand layout (NULL: the vector is read from
@@ -261,6 +266,7 @@ struct RecPlan {
   double cost_us;       // modelled time per step
   const void* func;
   size_t lds_bytes;
+  int xcd_span;         // XCDs a batch group covers (under the launch's block placement)
 };
 
 // Choose a plan and report it; returns false when no instantiated plan fits.
