@@ -1,11 +1,11 @@
 """Summarise rocprofv3 output of bench.py runs into short text files.
 
     python -m gru_layer_fwd_amd.prof_summary --workload NAME \
-        --stats DIR/bench_kernel_stats.csv \
+        --trace DIR/bench_kernel_trace.csv \
         [--fetch DIR/bench_counter_collection.csv --write DIR/bench_counter_collection.csv \
          --copy-bytes N] --command "..." --out profiles/NAME.md
 
-Writes a markdown table of per-kernel durations (kernel-trace --stats) and,
+Writes a markdown table of per-kernel durations (from the kernel trace) and,
 when the two counter passes are given, HBM bytes per launch from FETCH_SIZE
 and WRITE_SIZE (KiB per dispatch), each scaled by the factor that makes the
 reading of the calibration copy (the largest __amd_rocclr_copyBuffer
@@ -13,6 +13,13 @@ dispatch, `copy-bytes` read and as many written) equal to its true size. The
 per-launch bytes of every layer kernel are also merged into
 profiles/traffic.json under the current kernel-source hash, which bench.py
 reports only while the sources are unchanged.
+
+One GEMM kernel can serve several steps of the layer (the input projection
+and the input gradient share an instantiation), so each dispatch is given
+the step it performs from its place in the dispatch order: GEMMs before the
+forward recurrence are the projection; after the backward recurrence the
+first GEMM is the input gradient and the later ones the weight gradients;
+transposes and finishing passes go with the GEMM they serve.
 """
 from __future__ import annotations
 
@@ -23,18 +30,38 @@ import json
 import os
 import sys
 
-LABELS = (("rec_fwd", "rec_fwd"), ("rec_bwd", "rec_bwd"), ("gemm_kernelIDF16bLb0ELb0E", "proj_gemm"),
-          ("gemm_kernelIfLb0ELb0E", "proj_gemm"), ("gemm_kernelIDF16bLb0ELb1E", "dx_gemm"),
-          ("gemm_kernelIfLb0ELb1E", "dx_gemm"), ("gemm_kernel<bool", "dw_gemm"), ("gemm_kernelIDF16bLb1ELb1E", "dw_gemm"),
-          ("gemm_kernelIfLb1ELb1E", "dw_gemm"), ("colsum", "db_colsum"), ("fill", "fill"),
-          ("lstm_cell_scan", "aux"), ("zero_inactive", "aux"), ("gather_first_rows", "aux"), ("att_reduce", "aux"))
-
-
-def label_of(name: str) -> str:
-    for key, lab in LABELS:
-        if key in name:
-            return lab
-    return "other"
+def step_labels(names):
+    """Step of every dispatch, from the kernel names in dispatch order."""
+    out, phase, gemms_after_bwd = [], "start", 0
+    for n in names:
+        if "rec_fwd" in n:
+            lab, phase = "rec_fwd", "after_fwd"
+        elif "rec_bwd" in n:
+            lab, phase, gemms_after_bwd = "rec_bwd", "after_bwd", 0
+        elif "fill_i32" in n:
+            lab = "fill"
+            if phase == "after_bwd":
+                phase = "start"
+        elif "gemm_kernel" in n:
+            if phase == "after_bwd":
+                lab = "dx_gemm" if gemms_after_bwd == 0 else "dw_gemm"
+                gemms_after_bwd += 1
+            else:
+                lab = "proj_gemm"
+        elif "weight_transpose" in n:
+            lab = "dx_gemm (W_ih transpose)"
+        elif "gather_transpose" in n:
+            lab = "dw_gemm (transposes)" if phase == "after_bwd" else "aux"
+        elif "splitk_finish" in n or "rowsum_finish" in n or "rowsum_rows" in n:
+            lab = "dw_gemm (finish)" if phase == "after_bwd" else "proj_gemm (finish)"
+        elif "colsum" in n:
+            lab = "db_colsum"
+        elif "copyBuffer" in n or "fillBuffer" in n:
+            lab = "other"
+        else:
+            lab = "aux"
+        out.append(lab)
+    return out
 
 
 def short(name: str) -> str:
@@ -42,21 +69,22 @@ def short(name: str) -> str:
 
 
 def read_counters(path):
-    rows = list(csv.DictReader(open(path)))
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+    labs = step_labels([r["Kernel_Name"] for r in rows])
     per = collections.defaultdict(list)
     copies = []
-    for r in rows:
+    for r, lab in zip(rows, labs):
         v = float(r["Counter_Value"])
         if "copyBuffer" in r["Kernel_Name"]:
             copies.append(v)
-        per[r["Kernel_Name"]].append(v)
+        per[(r["Kernel_Name"], lab)].append(v)
     return per, (max(copies) if copies else None)
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
-    ap.add_argument("--stats", required=True)
+    ap.add_argument("--trace", required=True, help="kernel_trace.csv of a --kernel-trace run")
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--copy-bytes", type=int, default=0)
@@ -65,13 +93,17 @@ def main(argv=None):
     ap.add_argument("--traffic-json", default=None)
     a = ap.parse_args(argv)
 
-    stats = list(csv.DictReader(open(a.stats)))
+    rows = sorted(csv.DictReader(open(a.trace)), key=lambda r: int(r["Dispatch_Id"]))
+    labs = step_labels([r["Kernel_Name"] for r in rows])
+    dur = collections.defaultdict(list)
+    for r, lab in zip(rows, labs):
+        dur[(r["Kernel_Name"], lab)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    total = sum(sum(v) for v in dur.values())
     lines = [f"# rocprofv3 kernel summary: {a.workload}", "", "Produced by:", "", "```"]
     lines += a.command.strip().splitlines() + ["```", ""]
     lines += ["| kernel | step | calls | avg us | total % |", "|---|---|---|---|---|"]
-    for r in stats:
-        lines.append(f"| `{short(r['Name'])}` | {label_of(r['Name'])} | {r['Calls']} | "
-                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['Percentage']):.2f} |")
+    for (name, lab), v in sorted(dur.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{short(name)}` | {lab} | {len(v)} | {sum(v) / len(v):.1f} | {100 * sum(v) / total:.2f} |")
     traffic = {}
     if a.fetch and a.write and a.copy_bytes:
         fetch, cf = read_counters(a.fetch)
@@ -82,13 +114,13 @@ def main(argv=None):
                   f"the {a.copy_bytes >> 20} MiB calibration copy read and write exactly its size):", "",
                   "| kernel | step | read MiB | write MiB | total MiB |", "|---|---|---|---|---|"]
         for k in fetch:
-            if "copyBuffer" in k or k not in write:
+            name, lab = k
+            if "copyBuffer" in name or k not in write:
                 continue
             fr = sum(fetch[k]) / len(fetch[k]) * f_scale * 1024
             wr = sum(write[k]) / len(write[k]) * w_scale * 1024
-            lab = label_of(k)
-            lines.append(f"| `{short(k)}` | {lab} | {fr / 2**20:.1f} | {wr / 2**20:.1f} | {(fr + wr) / 2**20:.1f} |")
-            if lab in ("rec_fwd", "rec_bwd", "proj_gemm", "dx_gemm"):
+            lines.append(f"| `{short(name)}` | {lab} | {fr / 2**20:.1f} | {wr / 2**20:.1f} | {(fr + wr) / 2**20:.1f} |")
+            if lab in ("rec_fwd", "rec_bwd", "proj_gemm", "dx_gemm", "dw_gemm"):
                 traffic[lab] = fr + wr
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out, "w") as fh:
