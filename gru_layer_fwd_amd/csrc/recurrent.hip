@@ -123,6 +123,29 @@ __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int*
   asm volatile("" ::: "memory");
 }
 
+// The slices a wave's share of the contraction depends on: contraction rows
+// [k0, k1) read the exchanged values of units k % H, which slice u / HS
+// produces. A range covering H units or wrapping past H depends on every
+// slice; an empty one on none. The waves of a workgroup together cover the
+// whole contraction, so after the barrier that follows the contraction the
+// workgroup has waited for every slice (which the reuse of exchange slots
+// two steps later relies on).
+__device__ __forceinline__ void wave_slices(int k0, int k1, int H, int HS, int nS, int& s0, int& n) {
+  if (k1 <= k0) {
+    s0 = 0;
+    n = 0;
+    return;
+  }
+  const int u0 = k0 % H, u1 = (k1 - 1) % H;
+  if (k1 - k0 >= H || u1 < u0) {
+    s0 = 0;
+    n = nS;
+    return;
+  }
+  s0 = u0 / HS;
+  n = u1 / HS + 1 - s0;
+}
+
 // Every wave waits for its stores of the exchanged vector to be
 // acknowledged, the workgroup meets, then one thread publishes the step
 // counter.
@@ -453,6 +476,13 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
+  // this wave's contraction rows and the slices producing them
+  int ws0, wsn;
+  {
+    constexpr int KSTEP = 4 * Chunk<TS>::KQ;
+    const int w = tid >> 6, k0 = w * KI * KSTEP;
+    wave_slices(k0, min(H, k0 + KI * KSTEP), H, HS, a.nSlices, ws0, wsn);
+  }
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
   // exchange ring (single row-tile plans)
@@ -511,7 +541,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
         pa[u] = *ap;
       }
     }
-    if (s > 0) wait_flags(gflags, a.nSlices, s, a.status, a.timeout_ticks, fstride, MB < 4 && local);
+    if (s > 0) wait_flags(gflags + ws0 * fstride, wsn, s, a.status, a.timeout_ticks, fstride, MB < 4 && local);
     f4 acc[MB][NT];
     zero_acc(acc);
     if (tiled && s > 0) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
@@ -744,6 +774,13 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
   const int K = GK * H;
+  // this wave's contraction rows and the slices producing them
+  int ws0, wsn;
+  {
+    constexpr int KSTEP = 4 * Chunk<TS>::KQ;
+    const int k0 = (tid >> 6) * KI * KSTEP;
+    wave_slices(k0, min(K, k0 + KI * KSTEP), H, HS, a.nSlices, ws0, wsn);
+  }
   // GRU: lanes r, u, then the recurrent candidate lane d_c*r stored in lane 3
   const int kshift = (CELL == CELL_LSTM) ? (1 << 30) : 2 * H;
   const int kskip = (CELL == CELL_LSTM) ? 0 : H;
@@ -819,7 +856,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
     f4 acc[MB][NT];
     zero_acc(acc);
     if (n > 0) {
-      wait_flags(gflags, a.nSlices, n, a.status, a.timeout_ticks, fstride, CELL == CELL_LSTM && MB < 4 && local);
+      wait_flags(gflags + ws0 * fstride, wsn, n, a.status, a.timeout_ticks, fstride, CELL == CELL_LSTM && MB < 4 && local);
       if (tiled) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
       if (!tiled) {
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
