@@ -427,7 +427,7 @@ __device__ __forceinline__ void load_w_rows(uint4 (&Wr)[NT][KI], const TS* W, in
 // kb + [0, K): W_hh[perm[g]*H + k%H][J0+col] with g = k/H).
 template <typename TS, int NT, int KI, typename Perm>
 __device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, int H, const Perm& perm, int J0,
-                                            int gate0, int K) {
+                                            int gate0, int K, bool unit_major = false) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
@@ -441,10 +441,16 @@ __device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, in
 #pragma unroll
       for (int i = 0; i < KQ; ++i) e[i] = from_f<TS>(0.f);
       if (k < K) {
-        const int g = gate0 + k / H;
-        const int kk = k % H;
+        if (unit_major) {
+          // contraction row 4u + g: gate g of unit u (four gates)
 #pragma unroll
-        for (int i = 0; i < KQ; ++i) e[i] = W[((long long)perm[g] * H + kk + i) * H + col];
+          for (int i = 0; i < KQ; ++i) e[i] = W[((long long)perm[(k + i) & 3] * H + ((k + i) >> 2)) * H + col];
+        } else {
+          const int g = gate0 + k / H;
+          const int kk = k % H;
+#pragma unroll
+          for (int i = 0; i < KQ; ++i) e[i] = W[((long long)perm[g] * H + kk + i) * H + col];
+        }
       }
       Wr[nt][ks] = *(const uint4*)e;
     }
@@ -774,12 +780,22 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
   const int K = GK * H;
+  // bf16 LSTM through the exchange ring: contraction rows unit-major (row
+  // 4u + g: gate g of unit u), so that a wave's rows come from few slices
+  // and a producer stores a unit's four gradients as one 8-byte piece (not
+  // for the register-bound 64-row tiles, whose spill code it upsets)
+  const bool umaj = CELL == CELL_LSTM && sizeof(TS) == 2 && MB < 4 && a.xbuf != nullptr;
   // this wave's contraction rows and the slices producing them
   int ws0, wsn;
   {
     constexpr int KSTEP = 4 * Chunk<TS>::KQ;
-    const int k0 = (tid >> 6) * KI * KSTEP;
-    wave_slices(k0, min(K, k0 + KI * KSTEP), H, HS, a.nSlices, ws0, wsn);
+    const int k0 = (tid >> 6) * KI * KSTEP, k1 = min(K, k0 + KI * KSTEP);
+    if (umaj && k1 > k0) {
+      ws0 = (k0 >> 2) / HS;
+      wsn = ((k1 - 1) >> 2) / HS + 1 - ws0;
+    } else {
+      wave_slices(k0, k1, H, HS, a.nSlices, ws0, wsn);
+    }
   }
   // GRU: lanes r, u, then the recurrent candidate lane d_c*r stored in lane 3
   const int kshift = (CELL == CELL_LSTM) ? (1 << 30) : 2 * H;
@@ -791,7 +807,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
-  load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K);
+  load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K, umaj);
 
   float dcar[UPT], hcar[UPT];
   bool live[UPT];
@@ -903,7 +919,19 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         dv[u][1] = d_f;
         dv[u][2] = d_g;
         dv[u][3] = d_o;
-        if (tiled) {
+        if (umaj) {
+          // the unit's four gradients: rows 4jj..4jj+3, adjacent in the tile
+          char* xs = xslot(n);
+          const int jj = J0 + j_[u];
+          const unsigned lo = (unsigned)__builtin_bit_cast(unsigned short, (bf16)d_i) |
+                              ((unsigned)__builtin_bit_cast(unsigned short, (bf16)d_f) << 16);
+          const unsigned hi = (unsigned)__builtin_bit_cast(unsigned short, (bf16)d_g) |
+                              ((unsigned)__builtin_bit_cast(unsigned short, (bf16)d_o) << 16);
+          unsigned long long* p8 = (unsigned long long*)(xs + xoff<TS>(bl_[u], 4 * jj, packed, MB));
+          const unsigned long long v8 = (unsigned long long)lo | ((unsigned long long)hi << 32);
+          if (local) *p8 = v8;
+          else __hip_atomic_store(p8, v8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else if (tiled) {
           char* xs = xslot(n);
           const int jj = J0 + j_[u];
           xstore((TS*)(xs + xoff<TS>(bl_[u], jj, packed, MB)), d_i, local);
