@@ -402,7 +402,9 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
             o.w = __builtin_amdgcn_perm(((const unsigned*)&rw[7])[kq >> 1], ((const unsigned*)&rw[6])[kq >> 1], sel);
             TS* dst = out + k * g.ld_at;
             if (m0 + r + 8 <= g.M) {
-              *(uint4*)dst = o;
+              // streamed past the L2 that holds this product's operand tiles
+              typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+              __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), (u32x4*)dst);
             } else {
               const TS* ov = (const TS*)&o;
               for (int e = 0; e < 8 && m0 + r + e < g.M; ++e) dst[e] = ov[e];
