@@ -767,7 +767,7 @@ __global__ __launch_bounds__(256) void att_reduce(const float* part, int nslices
 // 64 W rows, 16-byte writes of 64 transposed rows.
 template <typename TS>
 __global__ __launch_bounds__(256) void weight_transpose(const TS* W, int G, int H, int I, Perm4 perm, TS* wt,
-                                                        long long ldt) {
+                                                        long long ldt, int umaj) {
   constexpr int T = 64, KQ = Chunk<TS>::KQ, CPR = T / KQ;  // 16-byte chunks per tile row
   __shared__ TS tile[T][T + 1];
   const int k0 = blockIdx.y * T, i0 = blockIdx.x * T;
@@ -777,8 +777,9 @@ __global__ __launch_bounds__(256) void weight_transpose(const TS* W, int G, int 
     const int k = k0 + r, i = i0 + q * KQ;
     TS v[KQ];
     if (k < K && i < I) {
-      const int g = k / H;
-      const long long row = (long long)pick4(perm.p, g) * H + (k - g * H);
+      // column k: gate-major (g*H + u) or unit-major (4u + g, four gates)
+      const int g = umaj ? (k & 3) : k / H;
+      const long long row = (long long)pick4(perm.p, g) * H + (umaj ? (k >> 2) : k - g * H);
       *(uint4*)v = *(const uint4*)(W + row * I + i);
     } else {
 #pragma unroll
@@ -1099,21 +1100,23 @@ hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void*
 
 template <typename TS>
 hipError_t launch_weight_transpose(const void* W, int G, int H, int I, const int perm[4], void* wt, long long ldt,
-                                   hipStream_t s) {
+                                   hipStream_t s, bool unit_major) {
   const long long K = (long long)G * H;
   if (K <= 0 || I <= 0) return hipSuccess;
   if (I % Chunk<TS>::KQ || K % Chunk<TS>::KQ || ldt % Chunk<TS>::KQ || ldt < K) return hipErrorInvalidValue;
+  if (unit_major && G != 4) return hipErrorInvalidValue;
   Perm4 p4;
   for (int i = 0; i < 4; ++i) p4.p[i] = i < G ? perm[i] : 0;
   dim3 grid((unsigned)((I + 63) / 64), (unsigned)((K + 63) / 64));
-  hipLaunchKernelGGL((weight_transpose<TS>), grid, dim3(256), 0, s, (const TS*)W, G, H, I, p4, (TS*)wt, ldt);
+  hipLaunchKernelGGL((weight_transpose<TS>), grid, dim3(256), 0, s, (const TS*)W, G, H, I, p4, (TS*)wt, ldt,
+                     unit_major ? 1 : 0);
   return hipGetLastError();
 }
 
 template hipError_t launch_weight_transpose<float>(const void*, int, int, int, const int*, void*, long long,
-                                                   hipStream_t);
+                                                   hipStream_t, bool);
 template hipError_t launch_weight_transpose<bf16>(const void*, int, int, int, const int*, void*, long long,
-                                                  hipStream_t);
+                                                  hipStream_t, bool);
 template <typename TS>
 hipError_t launch_gather_transpose(const RowMap& src, int R, int T, int B, void* out, hipStream_t s) {
   const long long TB = (long long)T * B;

@@ -807,7 +807,13 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
   uint4 Wr[NT][KI];
-  load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K, umaj);
+  // with W_hh transposed into the contraction order, the operands are rows
+  // (one 16-byte load each, as in the forward); reading W_hh columns takes
+  // one load per element from eight W rows
+  bool wrows = false;
+  if constexpr (MB < 4) wrows = a.W_hhT != nullptr;
+  if (wrows) load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hhT, K, [&](int col) -> long long { return J0 + col; });
+  else load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K, umaj);
 
   float dcar[UPT], hcar[UPT];
   bool live[UPT];

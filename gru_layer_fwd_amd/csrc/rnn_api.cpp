@@ -33,7 +33,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : (d->direction =
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, dgt, xt, ht, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, wht, dgt, xt, ht, total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -149,6 +149,9 @@ Layout layout(const rnn_desc_t* d) {
   // operand, loaded straight into LDS)
   L.wt = off;
   if (d->dtype == RNN_BF16) off += up((size_t)d->I * gates(d) * H * s);
+  // W_hh transposed to [H][G*H] in the BPTT kernel's contraction order
+  L.wht = off;
+  if (cell_of(d) != rnn::CELL_GRU_BASIC) off += up((size_t)H * gates(d) * H * s);
   // bf16 LSTM: the weight-gradient product as a k-contiguous one: the gate
   // gradients, x and h_{t-1} transposed to [.][T*B]
   L.dgt = L.xt = L.ht = off;
@@ -610,6 +613,27 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
   a.att = d->att;
   a.datt_part = (float*)(ws + L.attp);
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
+  // W_hh transposed into the contraction order of the BPTT kernel (unit-major
+  // rows for the bf16 LSTM ring, gate-major otherwise), so that the kernel
+  // loads its operands as rows instead of one element per load. Measured: at
+  // 8 MiB of W_hh the kernel's start-up falls by 13-17 us for an 8 us
+  // transpose; at 4 MiB and below the transpose costs more than it saves.
+  // The 64-row-tile kernels read W_hh itself.
+  a.W_hhT = nullptr;
+  const int kq = 16 / (int)esz(d);
+  const size_t whh_bytes = (size_t)gates(d) * d->H * d->H * esz(d);
+  if (cell != rnn::CELL_GRU_BASIC && plan.mb < 4 && d->H % kq == 0 && whh_bytes >= ((size_t)8 << 20)) {
+    const bool umaj = cell == rnn::CELL_LSTM && d->dtype == RNN_BF16 && a.xbuf != nullptr;
+    const int G = gates(d);
+    ProfScope ps(L_AUX, s);
+    const hipError_t e =
+        d->dtype == RNN_BF16
+            ? rnn::launch_weight_transpose<bf16>(io.W_hh, G, d->H, d->H, perm, ws + L.wht, (long long)G * d->H, s, umaj)
+            : rnn::launch_weight_transpose<float>(io.W_hh, G, d->H, d->H, perm, ws + L.wht, (long long)G * d->H, s,
+                                                  umaj);
+    if ((st = hip_status(e))) return st;
+    a.W_hhT = ws + L.wht;
+  }
   return RNN_OK;
 }
 

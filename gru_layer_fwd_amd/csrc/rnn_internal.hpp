@@ -191,12 +191,13 @@ hipError_t launch_att_reduce(const float* part, int nslices, long long TB, void*
 template <typename TS>
 hipError_t launch_gather_transpose(const RowMap& src, int R, int T, int B, void* out, hipStream_t s);
 
-// Gate-row transpose of an input weight: wt[i*ldt + k] = W[row(k)*I + i] for
-// k < G*H (canonical gate order: row(k) = perm[k/H]*H + k%H) and i < I, so
-// that the input gradient reads W_ih as a k-contiguous operand.
+// Gate-row transpose of a weight: wt[i*ldt + k] = W[row(k)*I + i] for
+// k < G*H and i < I, with row(k) = perm[k/H]*H + k%H (canonical gate order)
+// or, unit_major (G = 4), perm[k%4]*H + k/4. The input gradient reads W_ih
+// this way as a k-contiguous operand, the BPTT kernels W_hh.
 template <typename TS>
 hipError_t launch_weight_transpose(const void* W, int G, int H, int I, const int perm[4], void* wt, long long ldt,
-                                   hipStream_t s);
+                                   hipStream_t s, bool unit_major = false);
 
 
 // ------------------------------------------------- persistent recurrences --
@@ -234,6 +235,7 @@ struct RecArgs {
   const void* dcT;
   void* dg;         // gate gradients
   int GD;           // lanes of dg rows
+  const void* W_hhT;  // W_hh transposed to [H][K] in the contraction order (NULL: read W_hh columns)
   void* dh0;
   void* dc0;
   int* flags;

@@ -106,6 +106,17 @@ def test_bf16_lstm_weight_gradients_without_dx():
         np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
 
 
+@pytest.mark.parametrize("order,direction", [((1, 0, 2, 3), 0), ((3, 2, 0, 1), 1)])
+def test_bptt_transposed_recurrent_weights(order, direction):
+    # bf16 LSTM, H = 1024 (8 MiB of W_hh), small batch: the BPTT kernel reads
+    # W_hh from a copy transposed into its unit-major contraction order, gate
+    # permutation included (fp32 has no forward plan with that much W_hh)
+    wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=4, B=8, I=32, H=1024, h0_std=0.3, c0_std=0.3)
+    P = _permute_params(P, order, wl.H)
+    got, ref = _run(wl, inp, P, direction, order)
+    print(compare(got, ref, "bf16", extra=f"order={order} dir={direction}"))
+
+
 @pytest.mark.parametrize("name", ["gru_f32_t64_b16_i256_h256", "grura_f32_t64_b16_i256_h256"])
 def test_gru_f32_full(name):
     wl, inp, P = _case(name)
