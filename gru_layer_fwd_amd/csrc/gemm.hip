@@ -375,38 +375,43 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a1[i], b1[j]);
       // A written out transposed: every k-tile, N tile n takes rows
-      // [n * rpw, (n+1) * rpw) of the tile in 8 x 8 blocks (8 rows, one
-      // 16-byte k chunk), transposed in registers; lanes with consecutive row
-      // blocks write adjacent 16-byte pieces of one output row
+      // [n * rpw, (n+1) * rpw) of the tile in blocks of 8 rows x 2 k (one
+      // dword per row from LDS, two output chunks built by byte permutes),
+      // spread over the first waves so that no wave carries it alone; lanes
+      // with consecutive row blocks write adjacent 16-byte pieces of one
+      // output row
       if (g.at != nullptr) {
         const int rpw = nN >= 32 ? 8 : (BM / nN + 7) / 8 * 8;
         const int nb = rpw / 8;
-        const int cb = threadIdx.x / nb, rb = threadIdx.x - cb * nb;
-        const int r = tl.n * rpw + rb * 8;
-        if (cb < 8 && r < BM) {
-          uint4 rw[8];
+        for (int it = threadIdx.x; it < nb * (BK / 2); it += NT) {
+          const int kp = it / nb, rb = it - kp * nb;
+          const int r = tl.n * rpw + rb * 8;
+          const long long k = kb + (long long)kt * BK + 2 * kp;
+          if (r >= BM || k >= ke) continue;
+          unsigned d[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) rw[e] = *(const uint4*)(A + lds_off(r + e, cb));
-          const long long kc0 = kb + (long long)kt * BK + cb * 8;
+          for (int e = 0; e < 8; ++e) d[e] = *(const unsigned*)(A + lds_off(r + e, kp >> 2) + (kp & 3) * 4);
+          // element 2kp (low halves) and 2kp+1 (high halves) of rows r..r+7
+          uint4 o[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int sel = h ? 0x07060302 : 0x05040100;
+            o[h].x = __builtin_amdgcn_perm(d[1], d[0], sel);
+            o[h].y = __builtin_amdgcn_perm(d[3], d[2], sel);
+            o[h].z = __builtin_amdgcn_perm(d[5], d[4], sel);
+            o[h].w = __builtin_amdgcn_perm(d[7], d[6], sel);
+          }
           TS* out = (TS*)g.at + m0 + r;
 #pragma unroll
-          for (int kq = 0; kq < 8; ++kq) {
-            const long long k = kc0 + kq;
-            if (k >= ke) break;
-            // element kq of rows 2w, 2w+1 -> word w of the output chunk
-            const int sel = (kq & 1) ? 0x07060302 : 0x05040100;
-            uint4 o;
-            o.x = __builtin_amdgcn_perm(((const unsigned*)&rw[1])[kq >> 1], ((const unsigned*)&rw[0])[kq >> 1], sel);
-            o.y = __builtin_amdgcn_perm(((const unsigned*)&rw[3])[kq >> 1], ((const unsigned*)&rw[2])[kq >> 1], sel);
-            o.z = __builtin_amdgcn_perm(((const unsigned*)&rw[5])[kq >> 1], ((const unsigned*)&rw[4])[kq >> 1], sel);
-            o.w = __builtin_amdgcn_perm(((const unsigned*)&rw[7])[kq >> 1], ((const unsigned*)&rw[6])[kq >> 1], sel);
-            TS* dst = out + k * g.ld_at;
+          for (int h = 0; h < 2; ++h) {
+            if (k + h >= ke) break;
+            TS* dst = out + (k + h) * g.ld_at;
             if (m0 + r + 8 <= g.M) {
               // streamed past the L2 that holds this product's operand tiles
               typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-              __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o), (u32x4*)dst);
+              __builtin_nontemporal_store(__builtin_bit_cast(u32x4, o[h]), (u32x4*)dst);
             } else {
-              const TS* ov = (const TS*)&o;
+              const TS* ov = (const TS*)&o[h];
               for (int e = 0; e < 8 && m0 + r + e < g.M; ++e) dst[e] = ov[e];
             }
           }
