@@ -19,7 +19,8 @@ and the input gradient share an instantiation), so each dispatch is given
 the step it performs from its place in the dispatch order: GEMMs before the
 forward recurrence are the projection; after the backward recurrence the
 first GEMM is the input gradient and the later ones the weight gradients;
-transposes and finishing passes go with the GEMM they serve.
+transposes and finishing passes go with the step they serve (a weight
+transpose before the backward recurrence is W_hh's, one after it W_ih's).
 """
 from __future__ import annotations
 
@@ -49,7 +50,7 @@ def step_labels(names):
             else:
                 lab = "proj_gemm"
         elif "weight_transpose" in n:
-            lab = "dx_gemm (W_ih transpose)"
+            lab = "dx_gemm (W_ih transpose)" if phase == "after_bwd" else "rec_bwd (W_hh transpose)"
         elif "gather_transpose" in n:
             lab = "dw_gemm (transposes)" if phase == "after_bwd" else "aux"
         elif "splitk_finish" in n or "rowsum_finish" in n or "rowsum_rows" in n:
