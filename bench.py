@@ -9,8 +9,9 @@ workload is the single-layer bf16 LSTM at T=256, B=64, I=H=1024.
 Prints one JSON line: the throughput in timestep*batch/s, the algorithmic
 TFLOP/s, a roofline entry for the kernel that takes the most time per step
 (timed live with HIP events on the library's stream through the
-rnn_profile_* hook), and the CPU oracle timed on a bounded sample of the same
-workload on the host cores.
+rnn_profile_* hook, in a second pass over the same K steps so that the
+event records stay out of the throughput), and the CPU oracle timed on a
+bounded sample of the same workload on the host cores.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME]
 """
@@ -224,20 +225,34 @@ def main():
     torch.cuda.synchronize()
     if status() != 0:
         raise SystemExit(f"device status {status()} after warm-up")
-    L.rnn_profile_read(reset=True)
-    L.rnn_profile_enable(True)
+    # The K steps are timed twice: once as they run (the throughput), then
+    # once more with a HIP event pair around every library step on its
+    # stream (per-kernel durations, the roofline). The event records cost
+    # about 60 us per layer step at the headline shape, so they stay out of
+    # the throughput figure.
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    if status() != 0:
+        raise SystemExit(f"device status {status()} in the timed region")
+    L.rnn_profile_read(reset=True)
+    L.rnn_profile_enable(True)
+    torch.cuda.synchronize()
+    tp0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    tp1 = time.perf_counter()
     L.rnn_profile_enable(False)
     prof = L.rnn_profile_read(reset=True)
     if status() != 0:
         raise SystemExit(f"device status {status()} in the timed region")
 
     ms = (t1 - t0) * 1e3 / args.steps
+    ms_timed = (tp1 - tp0) * 1e3 / args.steps
     units = wl.T * wl.B
     value = units / (ms / 1e3)
     tflops = wl.flops_gemm() / (ms / 1e3) / 1e12
@@ -294,6 +309,7 @@ def main():
         "roofline": roof,
         "recurrent_us_per_step": rec,
         "kernels": kern,
+        "kernels_pass_ms_per_step": ms_timed,
     }
     if args.copy_mib:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
