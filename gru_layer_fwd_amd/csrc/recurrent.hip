@@ -810,8 +810,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   // with W_hh transposed into the contraction order, the operands are rows
   // (one 16-byte load each, as in the forward); reading W_hh columns takes
   // one load per element from eight W rows
-  bool wrows = false;
-  if constexpr (MB < 4) wrows = a.W_hhT != nullptr;
+  const bool wrows = a.W_hhT != nullptr;
   if (wrows) load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hhT, K, [&](int col) -> long long { return J0 + col; });
   else load_w_cols<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, a.perm, J0, 0, K, umaj);
 

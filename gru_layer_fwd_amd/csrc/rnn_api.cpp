@@ -618,12 +618,11 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
   // loads its operands as rows instead of one element per load. Measured: at
   // 8 MiB of W_hh the kernel's start-up falls by 13-17 us for an 8 us
   // transpose; at 4 MiB and below the transpose costs more than it saves.
-  // The 64-row-tile kernels read W_hh itself.
   a.W_hhT = nullptr;
   const int kq = 16 / (int)esz(d);
   const size_t whh_bytes = (size_t)gates(d) * d->H * d->H * esz(d);
-  if (cell != rnn::CELL_GRU_BASIC && plan.mb < 4 && d->H % kq == 0 && whh_bytes >= ((size_t)8 << 20)) {
-    const bool umaj = cell == rnn::CELL_LSTM && d->dtype == RNN_BF16 && a.xbuf != nullptr;
+  if (cell != rnn::CELL_GRU_BASIC && d->H % kq == 0 && whh_bytes >= ((size_t)8 << 20)) {
+    const bool umaj = cell == rnn::CELL_LSTM && d->dtype == RNN_BF16 && plan.mb < 4 && a.xbuf != nullptr;
     const int G = gates(d);
     ProfScope ps(L_AUX, s);
     const hipError_t e =
