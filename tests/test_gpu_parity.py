@@ -457,18 +457,21 @@ def test_lstm_recompute_with_final_state_gradients(direction):
 
 # ------------------------------------------------ bidirectional layer ----
 
-@pytest.mark.parametrize("mode,ra,dtype", [("lstm", None, "f32"), ("gru", True, "f32"), ("gru", False, "f32"),
-                                           ("lstm", None, "bf16")])
-def test_bidirectional_layer_runs_both_directions(mode, ra, dtype):
+@pytest.mark.parametrize("mode,ra,dtype,big", [("lstm", None, "f32", False), ("gru", True, "f32", False),
+                                               ("gru", False, "f32", False), ("lstm", None, "bf16", False),
+                                               ("lstm", None, "bf16", True)])
+def test_bidirectional_layer_runs_both_directions(mode, ra, dtype, big):
     """direction 2: [2, ...] stacked weights and states, y/dy halves in one
     [T, B, 2H] tensor, dx summed over the directions; each direction against
-    the oracle with its own weights and initial and final states."""
+    the oracle with its own weights and initial and final states. `big`:
+    H = 1024, so that each direction's BPTT reads its own transposed copy of
+    its W_hh (8 MiB)."""
     import oracle as O
     from gru_layer_fwd_amd.api import RnnLayer
     from rnn_harness import dev, host
     T, B, I, H = 9, 12, 64, 64
     if dtype == "bf16":
-        T, B, I, H = 12, 24, 256, 256
+        T, B, I, H = (6, 8, 32, 1024) if big else (12, 24, 256, 256)
     rng = np.random.default_rng(81)
     G = 4 if mode == "lstm" else 3
     from gru_layer_fwd_amd.synth import round_to
