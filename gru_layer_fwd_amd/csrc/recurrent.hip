@@ -460,7 +460,13 @@ __device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, in
 // ------------------------------------------------------ forward kernels --
 // LSTM (GL = 4 gate lanes) and reset-after GRU (GL = 3: r, u and the
 // recurrent candidate term n_h = h W_hc^T + b_hc, kept apart).
-template <int CELL, typename TS, int NW, int MB, int NT, int KI>
+// RING: the exchange ring carries the vector (h0 too: each workgroup writes
+// its units of h0 into the slot step 0 reads before the placement
+// rendezvous, which then orders them before every read); otherwise every
+// step reads h0 / y rows directly. Two variants, so that the ring kernels
+// carry no code of the row path (in the register-bound 64- and 128-row
+// tiles that code alone made the compiler spill).
+template <int CELL, typename TS, int NW, int MB, int NT, int KI, bool RING>
 __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, NCOL = NT * 16;
   constexpr int GL = (CELL == CELL_LSTM) ? 4 : 3;
@@ -478,7 +484,6 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   const int place_off = MB >= 4 ? 1 : a.place_off;
   int* myflag = a.flags + (grp * a.nSlices + sl) * fstride;
   const int* gflags = a.flags + grp * a.nSlices * fstride;
-  const bool local = group_is_local(myflag, gflags, a.nSlices, fstride, place_off, a.status, a.timeout_ticks);
   const int tid = threadIdx.x;
   const int H = a.H, B = a.B, T = a.T;
   const int J0 = sl * HS, b0 = grp * a.bg;
@@ -492,20 +497,10 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
   // exchange ring (single row-tile plans)
-  const bool tiled = a.xbuf != nullptr;
+  constexpr bool tiled = RING;
   const bool packed = a.xpacked != 0;
   const int xbytes = H * (packed ? 8 : 16 * MB) * (int)sizeof(TS);
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
-
-  uint4 Wr[NT][KI];
-  // LSTM columns are unit-major (column 4u+g: gate g of unit u), so that a
-  // unit's four gate sums sit in one 16-byte LDS word per wave; the GRU's
-  // three lanes are gate-major (column g*HS+u)
-  load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, [&](int col) -> long long {
-    if constexpr (CELL == CELL_LSTM) return (long long)a.perm[col & 3] * H + J0 + (col >> 2);
-    const int g = col / HS;
-    return (long long)a.perm[g] * H + J0 + (col - g * HS);
-  });
 
   // per-unit state; unit = (batch row bl, hidden unit j) of this workgroup
   float cst[UPT], hst[UPT], bhc[UPT];
@@ -527,6 +522,27 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
       if (CELL == CELL_GRU_RA) bhc[u] = to_f(((const TS*)a.b_hh)[(long long)a.perm[2] * H + J0 + j_[u]]);
     }
   }
+  if constexpr (RING) {
+    // h0 into the slot step 0 reads (device scope: the placement is not known
+    // yet), acknowledged before the rendezvous publishes this workgroup
+#pragma unroll
+    for (int u = 0; u < UPT; ++u)
+      if (live[u]) xstore((TS*)(xslot(-1) + xoff<TS>(bl_[u], J0 + j_[u], packed, MB)), hst[u], false);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  const bool local = group_is_local(myflag, gflags, a.nSlices, fstride, place_off, a.status, a.timeout_ticks);
+
+  uint4 Wr[NT][KI];
+  // LSTM columns are unit-major (column 4u+g: gate g of unit u), so that a
+  // unit's four gate sums sit in one 16-byte LDS word per wave; the GRU's
+  // three lanes are gate-major (column g*HS+u)
+  load_w_rows<TS, NT, KI>(Wr, (const TS*)a.W_hh, H, [&](int col) -> long long {
+    if constexpr (CELL == CELL_LSTM) return (long long)a.perm[col & 3] * H + J0 + (col >> 2);
+    const int g = col / HS;
+    return (long long)a.perm[g] * H + J0 + (col - g * HS);
+  });
+
 
   for (int s = 0; s < T; ++s) {
     const int t = a.dir ? T - 1 - s : s;
@@ -550,8 +566,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
     if (s > 0) wait_flags(gflags + ws0 * fstride, wsn, s, a.status, a.timeout_ticks, fstride, MB < 4 && local);
     f4 acc[MB][NT];
     zero_acc(acc);
-    if (tiled && s > 0) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
-    if (!tiled || s == 0) {
+    if constexpr (RING) {
+      contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
+    } else {
       const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
       const long long ld = (s == 0) ? H : a.ldy;
       contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, bend, H, 1 << 30, 0);
@@ -1136,10 +1153,13 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
 struct Entry {
   int cell, dtype, fwd, nw, mb, nt, ki, kib;
   const void* func;
+  const void* func_plain;  // forward without an exchange ring (NULL for the others)
 };
 
-#define F_LSTM(TS, NW, MB, NT, KI) (const void*)rec_fwd<CELL_LSTM, TS, NW, MB, NT, KI>
-#define F_GRA(TS, NW, MB, NT, KI) (const void*)rec_fwd<CELL_GRU_RA, TS, NW, MB, NT, KI>
+#define F_LSTM(TS, NW, MB, NT, KI) \
+  (const void*)rec_fwd<CELL_LSTM, TS, NW, MB, NT, KI, true>, (const void*)rec_fwd<CELL_LSTM, TS, NW, MB, NT, KI, false>
+#define F_GRA(TS, NW, MB, NT, KI) \
+  (const void*)rec_fwd<CELL_GRU_RA, TS, NW, MB, NT, KI, true>, (const void*)rec_fwd<CELL_GRU_RA, TS, NW, MB, NT, KI, false>
 #define B_LSTM(TS, NW, MB, NT, KI) (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI>
 #define B_GRA(TS, NW, MB, NT, KI) (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI>
 
@@ -1254,7 +1274,7 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, 
       if (cost < best) {
         best = cost;
         *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e),
-                     xcd_span(nwg, slices, xcds)};
+                     xcd_span(nwg, slices, xcds), e.func_plain};
         found = true;
       }
     }
@@ -1278,14 +1298,15 @@ int max_coresident(const RecPlan& p) {
 }
 
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute(p.func, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
+  // forward kernels come in a ring and a row-read variant
+  const void* f = (p.func_plain && L.d[0].xbuf == nullptr) ? p.func_plain : p.func;
+  hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
   if (e != hipSuccess) return e;
   const int n = p.nGroups * p.nSlices;
   if (L.dual && n % 4 != 0) return hipErrorInvalidValue;
   RecLaunch args = L;
   void* kargs[] = {&args};
-  return hipLaunchCooperativeKernel(p.func, dim3(L.dual ? 2 * n : n), dim3(p.nw * 64), kargs, (unsigned)p.lds_bytes,
-                                    s);
+  return hipLaunchCooperativeKernel(f, dim3(L.dual ? 2 * n : n), dim3(p.nw * 64), kargs, (unsigned)p.lds_bytes, s);
 }
 
 }  // namespace rnn
