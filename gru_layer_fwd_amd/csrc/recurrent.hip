@@ -773,7 +773,9 @@ __device__ __forceinline__ void att_rows(const float* attl, float* part, int t, 
 // dG'_{t+1} W_hh (dG' = [di,df,dg,do], or [d_r, d_u, d_c*r] for the GRU),
 // contracted over all gate rows; the workgroup holds the W_hh columns of its
 // HS units. Steps are processed in the reverse of the forward order.
-template <int CELL, typename TS, int NW, int MB, int NT, int KI>
+// RING as for the forward kernels: the ring variant carries no code of the
+// row-read path.
+template <int CELL, typename TS, int NW, int MB, int NT, int KI, bool RING>
 __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, HS = NT * 16;
   constexpr int GK = (CELL == CELL_LSTM) ? 4 : 3;
@@ -801,7 +803,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   // 4u + g: gate g of unit u), so that a wave's rows come from few slices
   // and a producer stores a unit's four gradients as one 8-byte piece (not
   // for the register-bound 64-row tiles, whose spill code it upsets)
-  const bool umaj = CELL == CELL_LSTM && sizeof(TS) == 2 && MB < 4 && a.xbuf != nullptr;
+  const bool umaj = CELL == CELL_LSTM && sizeof(TS) == 2 && MB < 4 && RING;
   // this wave's contraction rows and the slices producing them
   int ws0, wsn;
   {
@@ -818,7 +820,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   const int kshift = (CELL == CELL_LSTM) ? (1 << 30) : 2 * H;
   const int kskip = (CELL == CELL_LSTM) ? 0 : H;
   // exchange ring (single row-tile plans): the contracted lanes only
-  const bool tiled = a.xbuf != nullptr;
+  constexpr bool tiled = RING;
   const bool packed = a.xpacked != 0;
   const int xbytes = K * (packed ? 8 : 16 * MB) * (int)sizeof(TS);
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
@@ -895,8 +897,8 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
     zero_acc(acc);
     if (n > 0) {
       wait_flags(gflags + ws0 * fstride, wsn, n, a.status, a.timeout_ticks, fstride, CELL == CELL_LSTM && MB < 4 && local);
-      if (tiled) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
-      if (!tiled) {
+      if constexpr (RING) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
+      if constexpr (!RING) {
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
         contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
                                  kskip);
@@ -1153,15 +1155,17 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
 struct Entry {
   int cell, dtype, fwd, nw, mb, nt, ki, kib;
   const void* func;
-  const void* func_plain;  // forward without an exchange ring (NULL for the others)
+  const void* func_plain;  // variant without an exchange ring (NULL: basic GRU, func serves both)
 };
 
 #define F_LSTM(TS, NW, MB, NT, KI) \
   (const void*)rec_fwd<CELL_LSTM, TS, NW, MB, NT, KI, true>, (const void*)rec_fwd<CELL_LSTM, TS, NW, MB, NT, KI, false>
 #define F_GRA(TS, NW, MB, NT, KI) \
   (const void*)rec_fwd<CELL_GRU_RA, TS, NW, MB, NT, KI, true>, (const void*)rec_fwd<CELL_GRU_RA, TS, NW, MB, NT, KI, false>
-#define B_LSTM(TS, NW, MB, NT, KI) (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI>
-#define B_GRA(TS, NW, MB, NT, KI) (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI>
+#define B_LSTM(TS, NW, MB, NT, KI) \
+  (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI, true>, (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI, false>
+#define B_GRA(TS, NW, MB, NT, KI) \
+  (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI, true>, (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI, false>
 
 // dtype 0 = fp32, 1 = bf16
 const Entry kTable[] = {
@@ -1298,7 +1302,7 @@ int max_coresident(const RecPlan& p) {
 }
 
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {
-  // forward kernels come in a ring and a row-read variant
+  // LSTM and reset-after GRU kernels come in a ring and a row-read variant
   const void* f = (p.func_plain && L.d[0].xbuf == nullptr) ? p.func_plain : p.func;
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
   if (e != hipSuccess) return e;

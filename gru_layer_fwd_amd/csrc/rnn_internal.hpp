@@ -269,7 +269,7 @@ struct RecPlan {
   const void* func;
   size_t lds_bytes;
   int xcd_span;         // XCDs a batch group covers (under the launch's block placement)
-  const void* func_plain;  // forward: the variant without an exchange ring (NULL: func serves both)
+  const void* func_plain;  // the variant without an exchange ring (NULL: func serves both)
 };
 
 // Choose a plan and report it; returns false when no instantiated plan fits.
