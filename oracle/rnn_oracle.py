@@ -341,11 +341,39 @@ def stack_backward(mode, recs, dy):
 
 
 def rel_err(got, ref):
-    """max_i |got_i - ref_i| / max_i |ref_i| (0 when both are all-zero)."""
+    """max_i |got_i - ref_i| / max_i |ref_i| over one tensor (0 when both are
+    all-zero; the plain max|got - ref| when only the reference is).
+
+    The tolerance metric of the parity tests (the pages give none; tanh
+    outputs cross zero, so an element-wise relative error is not used).
+    Shapes must match exactly (no broadcasting), and a NaN or infinity in
+    either operand gives NaN, so that a comparison `err <= tol` fails."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.max(np.abs(ref)) if ref.size else 0.0
-    num = np.max(np.abs(got - ref)) if ref.size else 0.0
+    if got.shape != ref.shape:
+        raise ValueError(f"rel_err: shape {got.shape} != reference shape {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    if not (np.all(np.isfinite(got)) and np.all(np.isfinite(ref))):
+        return float("nan")
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(got - ref)))
     if den == 0.0:
-        return float(num)
-    return float(num / den)
+        return num
+    return num / den
+
+
+def rel_err_l2(got, ref):
+    """Norm-wise companion of rel_err: ||got - ref||_2 / ||ref||_2 (same
+    shape rule, NaN for non-finite input)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if got.shape != ref.shape:
+        raise ValueError(f"rel_err_l2: shape {got.shape} != reference shape {ref.shape}")
+    if ref.size == 0:
+        return 0.0
+    if not (np.all(np.isfinite(got)) and np.all(np.isfinite(ref))):
+        return float("nan")
+    den = float(np.linalg.norm(ref.ravel()))
+    num = float(np.linalg.norm((got - ref).ravel()))
+    return num if den == 0.0 else num / den

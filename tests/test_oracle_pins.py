@@ -624,3 +624,41 @@ def test_augru_finite_differences(ra, rev, lengths):
         T = x.shape[0]
         for b, Lb in enumerate(lengths):
             np.testing.assert_array_equal(gr["datt"][Lb:T, b], 0.0)
+
+
+# ------------------------------------------------ the tolerance metric ----
+# rel_err is max_i |got_i - ref_i| / max_i |ref_i| per tensor; every parity
+# assertion rests on it, so it is pinned by values worked out by hand.
+
+def test_rel_err_hand_values():
+    # |got - ref| = (0.5, 0, 0.25), max = 0.5; max |ref| = 4 -> 0.125
+    assert O.rel_err([1.5, -2.0, 4.25], [1.0, -2.0, 4.0]) == 0.125
+    # the denominator takes the absolute value: max |ref| = |-8| = 8
+    assert O.rel_err([0.0, -7.0], [1.0, -8.0]) == 1.0 / 8.0
+    # a sign flip of the largest element counts twice its size: |-4 - 4| / 4
+    assert O.rel_err([1.0, -4.0], [1.0, 4.0]) == 2.0
+    # exact agreement
+    assert O.rel_err(np.arange(6.0).reshape(2, 3), np.arange(6.0).reshape(2, 3)) == 0.0
+    # a zero reference: the absolute difference (0.5), and 0 when both are zero
+    assert O.rel_err([0.5, -0.25], [0.0, 0.0]) == 0.5
+    assert O.rel_err(np.zeros(4), np.zeros(4)) == 0.0
+    # norm-wise companion: ||(3, 4)|| / ||(6, 8)|| = 5 / 10
+    assert O.rel_err_l2([3.0, 4.0], [0.0, 0.0]) == 5.0
+    assert O.rel_err_l2([9.0, 12.0], [6.0, 8.0]) == 0.5
+
+
+def test_rel_err_fails_on_nan_and_infinity():
+    for bad in ([1.0, np.nan, 2.0], [np.inf, 0.0, 0.0], [1.0, 1.0, -np.inf]):
+        e = O.rel_err(bad, [1.0, 1.0, 2.0])
+        assert np.isnan(e) and not (e <= 1e-3)
+        assert np.isnan(O.rel_err([1.0, 1.0, 2.0], bad))
+        assert np.isnan(O.rel_err_l2(bad, [1.0, 1.0, 2.0]))
+
+
+def test_rel_err_rejects_shape_mismatch():
+    with pytest.raises(ValueError):
+        O.rel_err(np.ones((3, 4)), np.ones(4))
+    with pytest.raises(ValueError):
+        O.rel_err(np.ones((2, 3)), np.ones((3, 2)))
+    with pytest.raises(ValueError):
+        O.rel_err_l2(np.ones(5), np.ones(4))
