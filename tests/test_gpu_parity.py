@@ -1,10 +1,7 @@
 """GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
 
-Small and medium cases compare every output element; the full-size
-workloads compare sampled batch rows, computed by the oracle on those rows
-alone (batch rows never interact), with the upstream gradient set to zero on
-all other rows so that the weight and bias gradients are the sums over the
-sampled rows only and can be compared in full.
+Small and medium cases (several MFMA tiles and ragged tails); every output
+element is compared. The full-size workloads are in test_gpu_full_size.py.
 """
 import numpy as np
 import pytest
@@ -144,70 +141,6 @@ def test_bf16_medium(name, changes):
     print(compare(got, ref, "bf16", extra=name))
 
 
-# ------------------------------------------------------- full sizes -------
-
-def _sampled(name, rows, direction=0, lengths=None, att=None, recompute=False):
-    wl = W[name]
-    inp = synth.make_inputs(wl)
-    p = inp["params"][0][0]
-    P = Params(p.W_ih, p.W_hh, p.b_ih, p.b_hh)
-    g = inp["g"].copy()
-    mask = np.zeros(wl.B, dtype=bool)
-    mask[rows] = True
-    g[:, ~mask] = 0.0
-    got = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], g, None, None, direction,
-                    wl.reset_after, lengths=lengths, att=att, recompute=recompute)
-    sub = lambda a: None if a is None else a[rows]  # noqa: E731
-    ref = oracle_layer(wl.mode, P, inp["x"][:, rows], sub(inp["h0"]), sub(inp["c0"]), g[:, rows], None, None,
-                       direction, wl.reset_after, lengths=sub(lengths), att=None if att is None else att[:, rows])
-    return wl, got, ref
-
-
-@pytest.mark.parametrize("direction", [0, 1])
-def test_headline_lstm_bf16_full_size_sampled_rows(direction):
-    rows = [0, 17, 63]
-    wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction)
-    print(compare(got, ref, "bf16", rows=rows))
-
-
-@pytest.mark.parametrize("name", ["lstm_bf16_t128_b128_i2048_h2048", "grura_bf16_t128_b128_i2048_h2048"])
-def test_large_bf16_full_size_sampled_rows(name):
-    rows = [5, 127]
-    wl, got, ref = _sampled(name, rows)
-    print(compare(got, ref, "bf16", rows=rows))
-
-
-def test_bidir_two_layer_stack_full_size_sampled_rows():
-    import oracle as O
-    from gru_layer_fwd_amd.api import RnnStack
-    from rnn_harness import dev, host
-    wl = W["bilstm2_f32_t512_b32_i512_h512"]
-    inp = synth.make_inputs(wl)
-    rows = [3, 30]
-    g = inp["g"].copy()
-    mask = np.zeros(wl.B, dtype=bool)
-    mask[rows] = True
-    g[:, ~mask] = 0.0
-    st = RnnStack("lstm", wl.T, wl.B, wl.I, wl.H, "f32", wl.layers, wl.bidir)
-    params = [[tuple(dev(a, "f32") for a in (p.W_ih, p.W_hh, p.b_ih, p.b_hh)) for p in per] for per in inp["params"]]
-    grads = [[tuple(torch.zeros_like(t) for t in pd) for pd in per] for per in params]
-    x = dev(inp["x"], "f32")
-    dx = torch.empty_like(x)
-    y = st.fwd(x, params)
-    st.bwd(x, params, dev(g, "f32"), dx, grads)
-    torch.cuda.synchronize()
-    recs, y_ref = O.stack_forward("lstm", inp["x"][:, rows], inp["params"], (0, 1, 2, 3), True)
-    gr_ref, dx_ref = O.stack_backward("lstm", recs, g[:, rows])
-    errs = {"y": O.rel_err(host(y)[:, rows], y_ref), "dx": O.rel_err(host(dx)[:, rows], dx_ref)}
-    for li in range(2):
-        for d in range(2):
-            for k, t in zip(("dW_ih", "dW_hh", "db_ih", "db_hh"), grads[li][d]):
-                errs[f"L{li}d{d}.{k}"] = O.rel_err(host(t), gr_ref[li][d][k])
-    print(errs)
-    assert errs["y"] <= 1e-4, errs
-    assert all(v <= 1e-3 for k, v in errs.items() if k != "y"), errs
-
-
 # ------------------------------------------------- variable lengths -------
 
 def _ragged_lengths(B, T, seed):
@@ -243,15 +176,6 @@ def test_variable_lengths_bf16_medium(cell, H, direction):
     L = _ragged_lengths(wl.B, wl.T, 11 + direction)
     got, ref = _run(wl, inp, P, direction, lengths=L)
     print(compare(got, ref, "bf16", extra=f"{cell} H{H} dir{direction}"))
-
-
-@pytest.mark.parametrize("direction", [0, 1])
-def test_headline_lstm_bf16_variable_lengths_sampled_rows(direction):
-    wl = W["lstm_bf16_t256_b64_i1024_h1024"]
-    L = _ragged_lengths(wl.B, wl.T, 3)
-    rows = [int(np.argmin(L)), int(np.argmax(L)), 17, 40]
-    wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction, lengths=L)
-    print(compare(got, ref, "bf16", rows=rows))
 
 
 @pytest.mark.parametrize("mode", ["lstm", "gru"])
@@ -324,17 +248,6 @@ def test_augru_bf16_medium(ra, H):
     print(compare(got, ref, "bf16", extra=f"augru ra={ra} H{H}"))
 
 
-@pytest.mark.parametrize("direction", [0, 1])
-def test_augru_bf16_full_size_sampled_rows(direction):
-    wl = W["grura_bf16_t128_b128_i2048_h2048"]
-    att = _scores(wl.T, wl.B, 51, "bf16")
-    L = _ragged_lengths(wl.B, wl.T, 23)
-    rows = [int(np.argmin(L)), int(np.argmax(L)), 77]
-    wl, got, ref = _sampled("grura_bf16_t128_b128_i2048_h2048", rows, direction, lengths=L, att=att)
-    print(compare(got, ref, "bf16", rows=rows))
-
-
-
 # ---------------------------------------- LSTM cell-state recomputation ----
 
 @pytest.mark.parametrize("direction", [0, 1])
@@ -356,13 +269,6 @@ def test_lstm_recompute_bf16_medium(H):
     wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=14, B=24, I=64, H=H, h0_std=0.3, c0_std=0.3)
     got, ref = _run(wl, inp, P, 1, lengths=_ragged_lengths(wl.B, wl.T, 37), recompute=True)
     print(compare(got, ref, "bf16", extra=f"recompute H{H}"))
-
-
-@pytest.mark.parametrize("direction", [0, 1])
-def test_headline_lstm_recompute_sampled_rows(direction):
-    rows = [0, 33, 63]
-    wl, got, ref = _sampled("lstm_bf16_t256_b64_i1024_h1024", rows, direction, recompute=True)
-    print(compare(got, ref, "bf16", rows=rows))
 
 
 # ------------------------------------------- more ring configurations -----
