@@ -121,9 +121,27 @@ def cpu_baseline(wl, inp, rows: int):
     dt = time.perf_counter() - t0
     units = wl.T * rows
     return {"value": units / dt, "unit": "timestep*batch/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, fwd+bwd_data+bwd_weights over all T={wl.T} steps on {rows} of "
-                      f"{wl.B} batch rows ({dt:.2f} s on {threads} threads)",
-            "seconds": dt, "np": np.__version__}
+            "sample": f"fp64 numpy oracle (library matmul, BLAS threads = cores), fwd+bwd_data+bwd_weights "
+                      f"over all T={wl.T} steps on {rows} of {wl.B} batch rows ({dt:.2f} s)",
+            "seconds": dt, "np": np.__version__, "host": host_cpu()}
+
+
+def host_cpu():
+    """CPU model, logical CPUs of the host and those this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"model": model, "logical_cpus": os.cpu_count(), "usable_cpus": usable}
 
 
 def main():
@@ -320,6 +338,13 @@ def main():
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_rows or wl.B, wl.B))
     print(json.dumps(out), flush=True)
+    # explicit teardown before the interpreter exits: every queued kernel
+    # done, the library's profiling events released (profiling is off and
+    # read), torch's cached device memory returned
+    torch.cuda.synchronize()
+    del step
+    torch.cuda.empty_cache()
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":

@@ -35,6 +35,7 @@ _SIGS = {
     "rnn_last_device_status": (_c.c_int, [_P]),
     "rnn_status_string": (_c.c_char_p, [_c.c_int]),
     "rnn_set_handshake_timeout": (_c.c_int, [_c.c_double]),
+    "rnn_plan_query": (_c.c_int, [_P, _c.c_int, _c.c_int, _c.c_int, _P]),
     "rnn_profile_enable": (_c.c_int, [_c.c_int]),
     "rnn_profile_read": (_c.c_int, [_P, _c.c_int, _c.c_int]),
 }
@@ -56,6 +57,21 @@ class RnnDesc(ctypes.Structure):
         ("lengths", ctypes.c_void_p),
         ("att", ctypes.c_void_p),
         ("recompute", ctypes.c_int),
+    ]
+
+
+class RnnPlan(ctypes.Structure):
+    _fields_ = [
+        ("groups", ctypes.c_int),
+        ("rows", ctypes.c_int),
+        ("slices", ctypes.c_int),
+        ("units", ctypes.c_int),
+        ("waves", ctypes.c_int),
+        ("workgroups", ctypes.c_int),
+        ("dual", ctypes.c_int),
+        ("ring", ctypes.c_int),
+        ("xcd_span", ctypes.c_int),
+        ("model_us_per_step", ctypes.c_double),
     ]
 
 
@@ -140,6 +156,15 @@ def rnn_status_string(status: int) -> str:
 def rnn_set_handshake_timeout(seconds: float) -> int:
     """Handshake time-out for later calls (0: default; < 0: give up at once)."""
     return lib().rnn_set_handshake_timeout(float(seconds))
+
+
+def rnn_plan_query(desc, pass_: int, cu_count: int = 0, wg_per_cu: int = 0):
+    """(status, RnnPlan) of the persistent kernel of pass 0 (forward) or 1
+    (backward); cu_count/wg_per_cu > 0 inject the device's CU count and the
+    kernel's co-resident workgroups per CU (then no device is touched)."""
+    out = RnnPlan()
+    st = lib().rnn_plan_query(ctypes.byref(desc), int(pass_), int(cu_count), int(wg_per_cu), ctypes.byref(out))
+    return st, out
 
 
 def rnn_profile_enable(on: bool) -> int:

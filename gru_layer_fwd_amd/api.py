@@ -137,32 +137,53 @@ class RnnStack:
             return t
         return torch.stack([t, t])
 
+    @staticmethod
+    def _on(stream):
+        """Context that makes `stream` torch's current stream: the stacked
+        temporaries and copy-backs of a bidirectional layer are then ordered
+        with the library's kernels on it (a raw stream handle is refused,
+        since torch could not order its own work with it)."""
+        import contextlib
+        if stream is None:
+            return contextlib.nullcontext()
+        if not isinstance(stream, torch.cuda.Stream):
+            raise TypeError("RnnStack takes a torch.cuda.Stream (or None for the current stream)")
+        return torch.cuda.stream(stream)
+
     def fwd(self, x, params, h0=None, c0=None, stream=None):
-        inp = x
-        h0s, c0s = self._state(h0), self._state(c0)
-        for li, lay in enumerate(self.layers):
-            W_ih, W_hh, b_ih, b_hh = self._layer_params(li, params)
-            lay.fwd(inp, h0s, c0s, W_ih, W_hh, b_ih, b_hh, self.ys[li], stream=stream)
-            inp = self.ys[li]
-        return self.ys[-1]
+        with self._on(stream):
+            return self._fwd(x, params, h0, c0)
 
     def bwd(self, x, params, dy, dx=None, grads=None, h0=None, c0=None, stream=None):
         """dy: gradient of the last layer's output. grads[l][d] = (dW_ih, dW_hh, db_ih, db_hh)
         (or None to skip the weight gradients)."""
+        with self._on(stream):
+            return self._bwd(x, params, dy, dx, grads, h0, c0)
+
+    def _fwd(self, x, params, h0, c0):
+        inp = x
+        h0s, c0s = self._state(h0), self._state(c0)
+        for li, lay in enumerate(self.layers):
+            W_ih, W_hh, b_ih, b_hh = self._layer_params(li, params)
+            lay.fwd(inp, h0s, c0s, W_ih, W_hh, b_ih, b_hh, self.ys[li])
+            inp = self.ys[li]
+        return self.ys[-1]
+
+    def _bwd(self, x, params, dy, dx, grads, h0, c0):
         d_out = dy
         h0s, c0s = self._state(h0), self._state(c0)
         for li in range(len(self.layers) - 1, -1, -1):
             lay = self.layers[li]
             d_in = dx if li == 0 else self.dxs[li]
             W_ih, W_hh, _, _ = self._layer_params(li, params)
-            lay.bwd_data(W_ih, W_hh, h0s, c0s, self.ys[li], d_out, None, None, d_in, stream=stream)
+            lay.bwd_data(W_ih, W_hh, h0s, c0s, self.ys[li], d_out, None, None, d_in)
             if grads is not None:
                 inp = x if li == 0 else self.ys[li - 1]
                 if self.dirs == 1:
-                    lay.bwd_weights(inp, h0s, self.ys[li], *grads[li][0], stream=stream)
+                    lay.bwd_weights(inp, h0s, self.ys[li], *grads[li][0])
                 else:
                     pairs = [self._pair(grads[li][0][i], grads[li][1][i]) for i in range(4)]
-                    lay.bwd_weights(inp, h0s, self.ys[li], *(t for t, _ in pairs), stream=stream)
+                    lay.bwd_weights(inp, h0s, self.ys[li], *(t for t, _ in pairs))
                     for i, (t, view) in enumerate(pairs):
                         if not view:
                             grads[li][0][i].copy_(t[0])

@@ -1228,13 +1228,15 @@ int xcd_span(long long nwg, int slices, int xcds) {
   return slices < 8 ? slices : 8;
 }
 
-// Modelled time of one step (us), from measurements on MI355X: a step
-// handshake costs ~1 us when a batch group shares one XCD and ~2 us across
-// XCDs; a 16x16x32 bf16 MFMA issues every ~3.7 ns per SIMD with two or more
-// waves per SIMD and every ~10.8 ns with one (fp32: four 16x16x4 per k-step,
-// taken as ~2.5x the bf16 time); every CU reads the whole exchanged vector
-// of its group per step, ~150 GB/s from the tiled ring and ~75 GB/s from row
-// layout; the gate epilogue costs ~0.2 us per unit a thread carries.
+// Modelled time of one step (us): a step handshake costs ~1 us when a
+// batch group shares one XCD and ~2 us across XCDs (measured); a 16x16x32
+// bf16 MFMA occupies its SIMD for 16 cycles (6.67 ns at 2.4 GHz: the
+// published 2.5 PFLOP/s dense peak over 1024 SIMDs), and a wave alone on its
+// SIMD was measured to issue one every ~10.8 ns; a fp32 k-step is four
+// 16x16x4 fp32 MFMAs of 32 cycles each (the published 157.3 TFLOP/s), 8x the
+// bf16 k-step; every CU reads the whole exchanged vector of its group per
+// step, ~150 GB/s from the tiled ring and ~75 GB/s from row layout
+// (measured); the gate epilogue costs ~0.2 us per unit a thread carries.
 double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize, bool ring,
                  int xcds) {
   const int span = xcd_span((long long)groups * slices, slices, xcds);
@@ -1242,7 +1244,8 @@ double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kste
   const int phases = (e.cell == CELL_GRU_BASIC) ? 2 : 1;
   const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
   const double wps = e.nw / 4.0;  // waves per SIMD
-  const double t_inst = (wps >= 2 ? 3.7e-3 : 10.8e-3) * (kstep == 32 ? 1.0 : 2.5);
+  // us per k-step per SIMD; a wave alone on its SIMD issues at 6.67/10.8 of the rate
+  const double t_inst = (kstep == 32 ? 16.0 / 2.4e3 : 8.0 * 16.0 / 2.4e3) * (wps >= 2 ? 1.0 : 10.8 / 6.67);
   const double mfma = wps * e.mb * e.nt * kused * t_inst;
   const double data = (double)bg * K * esize / (ring ? 150e3 : 75e3);
   const int units = e.mb * 16 * units_per_wg(e);

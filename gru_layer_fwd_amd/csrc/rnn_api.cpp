@@ -267,6 +267,13 @@ hipEvent_t take_event() {
   if (hipEventCreate(&e) != hipSuccess) return nullptr;
   return e;
 }
+// Destroys the pooled events (none may be pending): done whenever profiling
+// is off and every recorded pair has been read, so that no HIP event of the
+// library outlives its use (a process then tears down with none alive).
+void release_pool(Prof& p) {
+  for (hipEvent_t e : p.pool) (void)hipEventDestroy(e);
+  p.pool.clear();
+}
 // Brackets the kernels queued during its lifetime with two events.
 struct ProfScope {
   int label;
@@ -329,13 +336,22 @@ void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws,
   a.xbuf = ws + L.xb;
 }
 
+// A persistent grid is launched only when every workgroup can be resident at
+// once (each waits for the others every step): at most one step counter per
+// workgroup, and grid <= (workgroups per CU) x CUs.
+int coresidency(long long nwg, bool dual, int occ, int cu) {
+  const long long grid = dual ? 2 * nwg : nwg;
+  if (nwg > rnn::FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;
+  if (occ < 1 || cu < 1 || grid > (long long)occ * cu) return RNN_ERR_UNSUPPORTED;
+  return RNN_OK;
+}
+
 int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const DevInfo& di, hipStream_t s,
                       const char* what) {
   const long long nwg = (long long)p.nGroups * p.nSlices;
   const long long grid = Lr.dual ? 2 * nwg : nwg;
-  if (nwg > rnn::FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;  // one step counter each
   const int occ = rnn::max_coresident(p);
-  if (occ < 1 || grid > (long long)occ * di.cu) {
+  if (coresidency(nwg, Lr.dual != 0, occ, di.cu) != RNN_OK) {
     if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, grid, occ, di.cu);
     return RNN_ERR_UNSUPPORTED;
   }
@@ -977,13 +993,55 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   return RNN_OK;
 }
 
+RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_per_cu, rnn_plan_t* out) {
+  if (!desc_ok(d) || !out || (pass != 0 && pass != 1) || cu_count < 0 || wg_per_cu < 0) return RNN_ERR_INVALID_ARG;
+  if (!shape_supported(d)) return RNN_ERR_UNSUPPORTED;
+  memset(out, 0, sizeof(*out));
+  DevInfo di;
+  if (cu_count > 0) {
+    di.cu = cu_count;
+  } else {
+    if (int st = dev_info(&di)) return st;
+  }
+  const int cell = cell_of(d);
+  rnn::RecPlan plan;
+  bool dual;
+  auto planner = [&](int cu, int xcds, rnn::RecPlan* p) {
+    return pass == 0 ? rnn::plan_fwd(cell, d->dtype, d->B, d->H, cu, xcds, p)
+                     : rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p);
+  };
+  if (!choose_plan(planner, d->direction == 2, di, &plan, &dual)) return RNN_ERR_UNSUPPORTED;
+  const long long nwg = (long long)plan.nGroups * plan.nSlices;
+  out->groups = plan.nGroups;
+  out->rows = plan.bg;
+  out->slices = plan.nSlices;
+  out->units = plan.Hs;
+  out->waves = plan.nw;
+  out->workgroups = (int)(dual ? 2 * nwg : nwg);
+  out->dual = dual ? 1 : 0;
+  out->xcd_span = plan.xcd_span;
+  out->model_us_per_step = plan.cost_us;
+  {
+    const rnn_desc_t h = half_desc(d, 0);
+    const Layout L = layout(&h);
+    rnn::RecArgs a{};
+    const long long K = pass == 0 ? d->H : (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H;
+    if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, nullptr, K, esz(d));
+    out->ring = a.xg_bytes ? (a.xpacked ? 2 : 1) : 0;
+  }
+  const int occ = wg_per_cu > 0 ? wg_per_cu : rnn::max_coresident(plan);
+  return coresidency(nwg, dual, occ, di.cu);
+}
+
 RNN_API int rnn_set_handshake_timeout(double seconds) {
   g_timeout_s = seconds == 0 ? TIMEOUT_S : seconds;
   return RNN_OK;
 }
 
 RNN_API int rnn_profile_enable(int on) {
-  prof().on = on != 0;
+  Prof& p = prof();
+  p.on = on != 0;
+  if (!p.on && p.pending.empty()) release_pool(p);
   return RNN_OK;
 }
 
@@ -999,6 +1057,7 @@ RNN_API int rnn_profile_read(rnn_kernel_time_t* out, int max, int reset) {
     p.pool.push_back(e.b);
   }
   p.pending.clear();
+  if (!p.on) release_pool(p);
   if (st != RNN_OK) return st;
   int n = 0;
   for (int l = 0; l < L_COUNT; ++l) {

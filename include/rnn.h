@@ -122,53 +122,120 @@ typedef struct rnn_desc {
                         elements for one extra elementwise pass. */
 } rnn_desc_t;
 
-/* Bytes of workspace the three calls need for this descriptor (0 if invalid). */
+/* Bytes of workspace the three calls need for this descriptor (0 if the
+ * descriptor is invalid). The workspace plays the role of the reserve space
+ * that the SystemDS LibMatrixCuDNN page sizes through its RNN algorithm
+ * object and hands to the forward-training, backward-data and
+ * backward-weights calls ("lstm" / "lstmBackward"): it holds the saved
+ * per-step activations, the gate gradients, step counters and scratch.
+ * Pure host computation; needs no device. */
 size_t rnn_workspace_bytes(const rnn_desc_t* desc);
 
-/* Forward over the sequence: y (every step), hT/cT (final state), and the
- * per-step activations the backward calls read, kept in the workspace.
+/* Forward over the sequence (popnn Lstm.cpp "lstmFwd" / Gru.cpp "gruFwd",
+ * one "basicLstmCellForwardPass" / "basicGruCellForwardPass" per step, the
+ * input-weight product hoisted over all steps as "calcSequenceWeightedInputs"
+ * does; the forward-training call of the SystemDS page's
+ * "singleLayerUnidirectionalRNNForward"): y [T][B][H] (every step), hT and cT
+ * [B][H] (the state after the last processed step), and the per-step
+ * activations that the backward calls read, kept in the workspace.
+ * Required: x, W_ih, W_hh, b_ih, b_hh, y; h0/c0 NULL = zero initial state
+ * (the CUDA fragment page's `cx == NULL` test); hT/cT NULL = not written.
+ * Returns RNN_ERR_INVALID_ARG for a bad descriptor, a NULL required pointer
+ * or a pointer that is not 16-byte aligned, RNN_ERR_WORKSPACE_TOO_SMALL,
+ * RNN_ERR_UNSUPPORTED for a shape the kernels do not handle, RNN_ERR_DEVICE
+ * if a launch fails; nothing is queued when an error is returned.
  * Queues: the input projection GEMM, then one persistent recurrent kernel. */
 int rnn_fwd(const rnn_desc_t* desc, const void* x, const void* h0, const void* c0,
             const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
             void* y, void* hT, void* cT, void* workspace, size_t ws_bytes, void* stream);
 
-/* Backward through time for the data gradients: dx (overwritten, or added to
- * when accumulate != 0), dh0, dc0, from dy at every step and dhT/dcT.
+/* Backward through time for the data gradients (popnn Lstm.cpp
+ * "backwardStepImpl" and Gru.cpp "backwardStepImpl" /
+ * "backwardStepImplResetAfter" per step, in reverse step order; the
+ * persistent backward-data kernel of the CUDA fragment page; the
+ * backward-data call of the SystemDS page's "lstmBackward"):
+ * dx [T][B][I] (overwritten, or added to when accumulate != 0), dh0, dc0
+ * [B][H], from dy at every step and the final-state gradients dhT/dcT.
  * With attention scores (desc->att), datt [T][B] (storage type; NULL = not
  * written) receives their gradient, minus the sum over hidden units of the
  * scaled update gate's gradient times the unscaled gate, zero past a row's
  * length; it follows the same overwrite / accumulate rule as dx.
- * y, h0 and c0 are the values given to / produced by rnn_fwd. The per-step
- * gate gradients are kept in the workspace for rnn_bwd_weights.
- * Queues: one persistent reverse-time kernel, the score-gradient sum (with
- * datt), then the dx GEMM. */
+ * Required: W_ih, W_hh, y, dy; y, h0 and c0 are the values given to /
+ * produced by rnn_fwd with this workspace. dhT/dcT NULL = zero; dh0/dc0 NULL
+ * = not written (the CUDA fragment page's `dhx != NULL`, `dcx != NULL`
+ * tests); dx NULL skips the input-gradient product. The per-step gate
+ * gradients are kept in the workspace for rnn_bwd_weights. Errors as for
+ * rnn_fwd. Queues: one persistent reverse-time kernel, the score-gradient
+ * sum (with datt), then the dx GEMM. */
 int rnn_bwd_data(const rnn_desc_t* desc, const void* W_ih, const void* W_hh,
                  const void* h0, const void* c0, const void* y, const void* dy,
                  const void* dhT, const void* dcT, void* dx, void* dh0, void* dc0,
                  void* datt, int accumulate, void* workspace, size_t ws_bytes, void* stream);
 
-/* Weight gradients summed over every (t, b): dW_ih = sum dG^T x,
- * dW_hh = sum dG_h^T h_{t-1} (h_{-1} = h0), db_ih, db_hh (popnn
- * "basicLstmParamUpdate", "basicGruParamUpdate"). accumulate != 0 adds to the
- * existing contents, otherwise they are overwritten. Any of the four outputs
- * may be NULL to skip it. Queues: the dW GEMMs and the bias reductions. */
+/* Weight gradients summed over every (t, b) (popnn Lstm.cpp
+ * "basicLstmParamUpdate", Gru.cpp "basicGruParamUpdate"; the
+ * backward-weights call of the SystemDS page's "lstmBackward"):
+ * dW_ih = sum dG^T x, dW_hh = sum dG_h^T h_{t-1} (h_{-1} = h0), db_ih,
+ * db_hh, in the weights' shapes and gate order. accumulate != 0 adds to the
+ * existing contents (popnn zeroes its accumulators and then adds), otherwise
+ * they are overwritten. Any of the four outputs may be NULL to skip it.
+ * Required: x, y (rnn_fwd's); the workspace written by rnn_fwd and then
+ * rnn_bwd_data. Errors as for rnn_fwd. Queues: the dW GEMMs and the bias
+ * reductions. */
 int rnn_bwd_weights(const rnn_desc_t* desc, const void* x, const void* h0, const void* y,
                     void* dW_ih, void* dW_hh, void* db_ih, void* db_hh, int accumulate,
                     void* workspace, size_t ws_bytes, void* stream);
 
 /* Device status word of the workspace (RNN_OK or RNN_ERR_TIMEOUT) after the
- * caller has synchronised the stream of the last call. Reads 4 bytes. */
+ * caller has synchronised the stream of the last call; the device-side
+ * counterpart of the status checks that the SystemDS page's "checkStatus"
+ * performs on every library call. Reads 4 bytes with a blocking copy;
+ * RNN_ERR_INVALID_ARG for a NULL workspace, RNN_ERR_DEVICE if the copy
+ * fails. */
 int rnn_last_device_status(const void* workspace);
 
-/* Static description of a status code. */
+/* Static description of a status code (never NULL; "unknown status" for a
+ * value that is not an rnn_status), as the SystemDS page's "checkStatus"
+ * turns a library status into its message. */
 const char* rnn_status_string(int status);
 
 /* Time-out of the cross-workgroup step handshake for the calls queued after
  * this one, process-wide (the bounded waits of the persistent kernels;
- * default 10 s). 0 restores the default; a negative value makes every wait
- * give up at once, so a call completes with RNN_ERR_TIMEOUT in its device
- * status and undefined outputs (a way to exercise the error path). */
+ * default 10 s). The CUDA fragment page's persistent kernel spins on its
+ * step data with no bound; here every wait is bounded and reports
+ * RNN_ERR_TIMEOUT through rnn_last_device_status. 0 restores the default; a
+ * negative value makes every wait give up at once, so a call completes with
+ * RNN_ERR_TIMEOUT in its device status and undefined outputs (a way to
+ * exercise the error path). Returns RNN_OK. */
 int rnn_set_handshake_timeout(double seconds);
+
+/* Plan of the persistent recurrent kernel of one pass (0 = forward,
+ * 1 = backward through time) for this descriptor: how the batch rows and
+ * hidden units are split over workgroups, which the CUDA fragment page's
+ * persistent kernel fixes at compile time (its block and batch tiling) and
+ * the popnn pages leave to the IPU planner. A persistent grid only runs when
+ * all its workgroups are resident at once, since every workgroup waits for
+ * the others at every step: the plan is refused (RNN_ERR_UNSUPPORTED) when
+ * no instantiated kernel fits `cu_count` compute units with `wg_per_cu`
+ * workgroups co-resident per CU. cu_count = 0 queries the current device,
+ * wg_per_cu = 0 asks the HIP runtime for the kernel's occupancy (both need
+ * a GPU); with both given the call is pure host computation, the same
+ * decision rnn_fwd / rnn_bwd_data take before launching.
+ * Returns RNN_OK with *out filled, RNN_ERR_INVALID_ARG (bad descriptor,
+ * pass, counts or NULL out), RNN_ERR_UNSUPPORTED, or RNN_ERR_DEVICE. */
+typedef struct rnn_plan {
+  int groups;       /* batch groups (each runs its own recurrence) */
+  int rows;         /* batch rows per group */
+  int slices;       /* hidden slices per group (workgroups of a group) */
+  int units;        /* hidden units per slice */
+  int waves;        /* 64-wide waves per workgroup */
+  int workgroups;   /* grid of the launch (both directions when dual) */
+  int dual;         /* 1: the two directions of a bidirectional layer share one launch */
+  int ring;         /* exchange of the step vector: 0 rows of y / dG, 1 tiled ring, 2 packed ring */
+  int xcd_span;     /* XCDs one batch group covers */
+  double model_us_per_step; /* the planner's modelled time per step */
+} rnn_plan_t;
+int rnn_plan_query(const rnn_desc_t* desc, int pass, int cu_count, int wg_per_cu, rnn_plan_t* out);
 
 /* Optional kernel timing, for measurement tools (the tracing hook of the
  * layer API; off by default). While enabled, every kernel the library queues
@@ -183,7 +250,9 @@ typedef struct rnn_kernel_time {
   double total_ms;
 } rnn_kernel_time_t;
 
-/* on != 0 starts recording, 0 stops. Returns RNN_OK. */
+/* on != 0 starts recording, 0 stops. The library's HIP events are destroyed
+ * once recording is off and every recorded pair has been read, so none is
+ * alive at process exit. Returns RNN_OK. */
 int rnn_profile_enable(int on);
 
 /* Waits for every recorded event, folds the durations into per-label totals

@@ -21,7 +21,7 @@ def _declared():
 
 def test_header_declares_the_abi():
     assert _declared() == sorted(["rnn_workspace_bytes", "rnn_fwd", "rnn_bwd_data", "rnn_bwd_weights",
-                                  "rnn_last_device_status", "rnn_status_string", "rnn_set_handshake_timeout",
+                                  "rnn_last_device_status", "rnn_status_string", "rnn_set_handshake_timeout", "rnn_plan_query",
                                   "rnn_profile_enable", "rnn_profile_read"])
 
 
@@ -159,3 +159,53 @@ def test_bidirectional_layer_workspace_is_two_halves():
     both = g.rnn_workspace_bytes(_desc(direction=2))       # ldy 0 means 2H for both directions
     assert single > 0 and both == 2 * single
     assert g.rnn_workspace_bytes(_desc(direction=2, ldy=64)) == both
+
+
+# ------------------------------------------- plans and co-residency ----
+# rnn_plan_query with an injected CU count and occupancy is the same host
+# decision rnn_fwd / rnn_bwd_data take before a persistent launch, made
+# without a device.
+
+def _plan(desc, pass_, cu=256, occ=1):
+    return L.rnn_plan_query(desc, pass_, cu, occ)
+
+
+def test_headline_plan_one_batch_group_per_xcd():
+    d = g.make_desc(L.RNN_LSTM, 256, 64, 1024, 1024, L.RNN_BF16)
+    for p in (0, 1):
+        st, pl = _plan(d, p)
+        assert st == L.RNN_OK
+        # 8 groups of 8 rows, each over the 32 CUs of one XCD (32 slices of 32 units)
+        assert (pl.groups, pl.rows, pl.slices, pl.units, pl.waves) == (8, 8, 32, 32, 8)
+        assert pl.workgroups == 256 and pl.xcd_span == 1 and pl.ring == 2 and pl.dual == 0
+        assert 0 < pl.model_us_per_step < 10
+
+
+def test_coresidency_refusal_with_injected_cu_count():
+    d = g.make_desc(L.RNN_LSTM, 256, 64, 1024, 1024, L.RNN_BF16)
+    # half the chip: the planner still finds a grid that fits (16-row groups)
+    st, pl = _plan(d, 0, cu=128)
+    assert st == L.RNN_OK and pl.workgroups <= 128
+    # 16 CUs cannot hold W_hh (8 MiB) in the registers of a co-resident grid
+    for cu in (16, 31):
+        st, _ = _plan(d, 0, cu=cu)
+        assert st == L.RNN_ERR_UNSUPPORTED, cu
+        st, _ = _plan(d, 1, cu=cu)
+        assert st == L.RNN_ERR_UNSUPPORTED, cu
+
+
+def test_bidirectional_layer_shares_one_launch():
+    d = g.make_desc(L.RNN_LSTM, 512, 32, 512, 512, L.RNN_F32, direction=2)
+    for p in (0, 1):
+        st, pl = _plan(d, p)
+        assert st == L.RNN_OK and pl.dual == 1
+        assert pl.workgroups == 2 * pl.groups * pl.slices <= 256
+
+
+def test_plan_query_argument_errors():
+    d = g.make_desc(L.RNN_LSTM, 8, 2, 16, 32, L.RNN_F32)
+    assert L.rnn_plan_query(d, 2, 256, 1)[0] == L.RNN_ERR_INVALID_ARG
+    assert L.rnn_plan_query(d, 0, -1, 1)[0] == L.RNN_ERR_INVALID_ARG
+    assert L.rnn_plan_query(d, 0, 256, -1)[0] == L.RNN_ERR_INVALID_ARG
+    assert L.lib().rnn_plan_query(ctypes.byref(d), 0, 256, 1, None) == L.RNN_ERR_INVALID_ARG
+    assert L.rnn_plan_query(_desc(H=40), 0, 256, 1)[0] == L.RNN_ERR_UNSUPPORTED
