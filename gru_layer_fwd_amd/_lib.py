@@ -29,6 +29,7 @@ _P = _c.c_void_p
 _SIGS = {
     "rnn_workspace_bytes": (_c.c_size_t, [_P]),
     "rnn_fwd": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_size_t, _P]),
+    "rnn_fwd_noalloc": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "rnn_bwd_data": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t,
                                 _P]),
     "rnn_bwd_weights": (_c.c_int, [_P, _P, _P, _P, _P, _P, _P, _P, _c.c_int, _P, _c.c_size_t, _P]),
@@ -131,6 +132,13 @@ def rnn_workspace_bytes(desc: RnnDesc) -> int:
 def rnn_fwd(desc, x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, workspace, ws_bytes, stream) -> int:
     return lib().rnn_fwd(ctypes.byref(desc), x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT,
                          workspace, ws_bytes, stream)
+
+
+RNN_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def rnn_fwd_noalloc(desc, x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, stream) -> int:
+    return lib().rnn_fwd_noalloc(ctypes.byref(desc), x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, stream)
 
 
 def rnn_bwd_data(desc, W_ih, W_hh, h0, c0, y, dy, dhT, dcT, dx, dh0, dc0, datt, accumulate,

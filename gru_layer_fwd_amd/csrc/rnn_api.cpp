@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "../../include/rnn.h"
@@ -745,6 +746,45 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   for (int k = 0; k < halves; ++k)
     if ((st = fwd_end(&hd[k], args[k], s))) return st;
   return RNN_OK;
+}
+
+// ---- forward with no allocation and no workspace argument ----
+// The workspace of rnn_fwd_noalloc is this array. In host code its name is
+// a host-side stand-in: the device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is
+// ever passed to kernels. Every call on a device shares that device's copy;
+// each call starts by zeroing its status word and step counters with a fill
+// kernel, as rnn_fwd does, and calls that overlap in time on one device race.
+static __device__ __align__(256) unsigned char scratch[RNN_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RNN_ERR_DEVICE;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return RNN_ERR_DEVICE;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return RNN_OK;
+}
+}  // namespace
+
+RNN_API int rnn_fwd_noalloc(const rnn_desc_t* d, const void* x, const void* h0, const void* c0, const void* W_ih,
+                            const void* W_hh, const void* b_ih, const void* b_hh, void* y, void* hT, void* cT,
+                            void* stream) {
+  // size checks first: a descriptor beyond the array is refused on the host
+  if (!desc_ok(d)) return RNN_ERR_INVALID_ARG;
+  if (ws_total(d) > (size_t)RNN_NOALLOC_SCRATCH_BYTES) return RNN_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (int st = scratch_ptr(&ws)) return st;
+  return rnn_fwd(d, x, h0, c0, W_ih, W_hh, b_ih, b_hh, y, hT, cT, ws, (size_t)RNN_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh, const void* h0, const void* c0,

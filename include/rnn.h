@@ -149,6 +149,25 @@ int rnn_fwd(const rnn_desc_t* desc, const void* x, const void* h0, const void* c
             const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
             void* y, void* hT, void* cT, void* workspace, size_t ws_bytes, void* stream);
 
+/* Forward over the sequence with no allocation and no workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): rnn_fwd,
+ * same arguments, outputs and errors, with its workspace in a static device
+ * array of RNN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it
+ * runs on until the process ends. A descriptor whose rnn_workspace_bytes()
+ * exceeds that size is refused with RNN_ERR_WORKSPACE_TOO_SMALL before any
+ * device work. The call allocates nothing (no hipMalloc, no library
+ * allocation). All calls on one GPU share that GPU's array, which keeps the
+ * last call's contents: calls that overlap in time on one GPU race, and the
+ * saved activations it leaves are not meant for the backward calls (they
+ * take a caller-owned workspace written by rnn_fwd). The first call on a
+ * device looks up the array's device address (RNN_ERR_DEVICE if that
+ * fails). */
+#define RNN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int rnn_fwd_noalloc(const rnn_desc_t* desc, const void* x, const void* h0, const void* c0,
+                    const void* W_ih, const void* W_hh, const void* b_ih, const void* b_hh,
+                    void* y, void* hT, void* cT, void* stream);
+
 /* Backward through time for the data gradients (popnn Lstm.cpp
  * "backwardStepImpl" and Gru.cpp "backwardStepImpl" /
  * "backwardStepImplResetAfter" per step, in reverse step order; the
