@@ -329,6 +329,26 @@ def main():
         "kernels": kern,
         "kernels_pass_ms_per_step": ms_timed,
     }
+    # the exchange alone on the persistent kernels' own grids: the floor the
+    # step handshake puts under a step (rnn_handshake_probe)
+    floor = {}
+    probe_lay = lay if (wl.layers == 1 and not wl.bidir) else st.layers[0]
+    cs = torch.cuda.current_stream()
+    for pass_, label in ((0, "rec_fwd"), (1, "rec_bwd")):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        e0.record(cs)
+        rc = 0
+        for _ in range(reps):
+            rc = L.rnn_handshake_probe(probe_lay.desc, pass_, probe_lay.workspace.data_ptr(), probe_lay.ws_bytes,
+                                       cs.cuda_stream)
+            if rc != 0:
+                break
+        e1.record(cs)
+        torch.cuda.synchronize()
+        if rc == 0 and probe_lay.device_status() == 0:
+            floor[label] = e0.elapsed_time(e1) * 1e3 / (reps * wl.T)
+    out["handshake_floor_us_per_step"] = floor or None
     if args.copy_mib:
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -37,6 +37,7 @@ _SIGS = {
     "rnn_status_string": (_c.c_char_p, [_c.c_int]),
     "rnn_set_handshake_timeout": (_c.c_int, [_c.c_double]),
     "rnn_plan_query": (_c.c_int, [_P, _c.c_int, _c.c_int, _c.c_int, _P]),
+    "rnn_handshake_probe": (_c.c_int, [_P, _c.c_int, _P, _c.c_size_t, _P]),
     "rnn_profile_enable": (_c.c_int, [_c.c_int]),
     "rnn_profile_read": (_c.c_int, [_P, _c.c_int, _c.c_int]),
 }
@@ -81,6 +82,15 @@ class RnnKernelTime(ctypes.Structure):
 
 
 _lib = None
+
+
+def select(path: str):
+    """Load another build of the library (e.g. the step-timer debug build)
+    instead of librnn.so; only before the first call into the library."""
+    global LIB_PATH
+    if _lib is not None and os.path.abspath(path) != os.path.abspath(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is already loaded")
+    LIB_PATH = path
 
 
 def lib():
@@ -173,6 +183,10 @@ def rnn_plan_query(desc, pass_: int, cu_count: int = 0, wg_per_cu: int = 0):
     out = RnnPlan()
     st = lib().rnn_plan_query(ctypes.byref(desc), int(pass_), int(cu_count), int(wg_per_cu), ctypes.byref(out))
     return st, out
+
+
+def rnn_handshake_probe(desc, pass_: int, workspace, ws_bytes, stream) -> int:
+    return lib().rnn_handshake_probe(ctypes.byref(desc), int(pass_), workspace, ws_bytes, stream)
 
 
 def rnn_profile_enable(on: bool) -> int:

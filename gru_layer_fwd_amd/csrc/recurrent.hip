@@ -38,9 +38,49 @@
 // "backwardStepImpl"; GRU popnn Gru.cpp "basicGruCellForwardPass",
 // "gruCellForwardPassCalcUnitsResetAfter", "backwardStepImpl" and
 // "backwardStepImplResetAfter".
+#include <type_traits>
+
 #include "rnn_internal.hpp"
 
 namespace rnn {
+
+#ifdef RNN_STEP_TIMERS
+// Thread 0 keeps the step's clock readings in LDS (no vector-memory store
+// inside the loop, which would join the memory counters the kernel waits
+// on) and copies them out when the kernel ends.
+static __device__ unsigned long long g_step_timers[TIMER_WGS * TIMER_STEPS * TIMER_PHASES];
+static __device__ unsigned long long g_step_cal[TIMER_WGS * 4];
+#define STEP_TIMER_DECL __shared__ unsigned step_tl_[TIMER_STEPS * TIMER_PHASES]
+#define STEP_TIMER(step, phase)                                                   \
+  do {                                                                            \
+    if (threadIdx.x == 0 && (step) >= 0 && (step) < TIMER_STEPS)                  \
+      step_tl_[(step) * TIMER_PHASES + (phase)] = (unsigned)__builtin_amdgcn_s_memtime(); \
+  } while (0)
+#define STEP_TIMER_CAL(which)                                                                 \
+  do {                                                                                        \
+    if (threadIdx.x == 0 && blockIdx.x < TIMER_WGS) {                                         \
+      g_step_cal[blockIdx.x * 4 + 2 * (which)] = __builtin_amdgcn_s_memtime();                \
+      g_step_cal[blockIdx.x * 4 + 2 * (which) + 1] = __builtin_amdgcn_s_memrealtime();        \
+    }                                                                                         \
+  } while (0)
+#define STEP_TIMER_FLUSH(nsteps)                                                              \
+  do {                                                                                        \
+    __syncthreads();                                                                          \
+    if (blockIdx.x < TIMER_WGS)                                                               \
+      for (int i_ = threadIdx.x; i_ < min((nsteps), TIMER_STEPS) * TIMER_PHASES; i_ += blockDim.x) \
+        g_step_timers[(size_t)blockIdx.x * TIMER_STEPS * TIMER_PHASES + i_] = step_tl_[i_];   \
+  } while (0)
+hipError_t read_step_timers(unsigned long long* timers, unsigned long long* cal) {
+  hipError_t e = hipMemcpyFromSymbol(timers, HIP_SYMBOL(g_step_timers), sizeof(g_step_timers));
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(cal, HIP_SYMBOL(g_step_cal), sizeof(g_step_cal));
+  return e;
+}
+#else
+#define STEP_TIMER_DECL
+#define STEP_TIMER(step, phase) ((void)0)
+#define STEP_TIMER_CAL(which) ((void)0)
+#define STEP_TIMER_FLUSH(nsteps) ((void)0)
+#endif
 
 namespace {
 
@@ -188,6 +228,23 @@ __device__ __forceinline__ bool group_is_local(int* myflag, const int* gflags, i
 
 constexpr int BUF_RSRC_W3 = 0x00020000;  // buffer resource word 3 for the gfx9 family
 constexpr int CPOL_SC1 = 16;             // device scope
+constexpr int BUF_SKIP = 0x40000000;     // an offset past every buffer below: the access is dropped
+
+// One storage element through a buffer resource: an offset at or past the
+// resource's size is dropped by the hardware, so a store can be issued
+// unconditionally (no branch), which keeps the count of memory operations a
+// wave has in flight the same on every path.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, long long bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)(bytes < 0x7FFFFFFF ? bytes : 0x7FFFFFFF),
+                                           BUF_RSRC_W3);
+}
+template <typename TS>
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t rs, int off, float v) {
+  if constexpr (sizeof(TS) == 2)
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), rs, off, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, 0);
+}
 
 // Workgroup -> (group, slice). Workgroups are dispatched round-robin over the
 // 8 XCDs; consecutive workgroups of one batch group are placed on the same
@@ -248,9 +305,15 @@ __device__ __forceinline__ uint4 rot8(const uint4& v) { return make_uint4(rot8(v
 // acc[mb][nt] += (previous step's vector, k-steps [w*KI, w*KI+KI)) . Wr[nt][.]
 // from the exchange ring tiles `xb` of this group (nbytes valid; loads past
 // it return zero). Unpacked tiles are ordered (k-step, row tile).
-template <typename TS, int MB, int NT, int KI>
+// `mid` runs once the ring loads (the first batch of them) are issued and
+// before any product waits for them: memory operations it issues queue
+// behind the ring loads, so the products do not wait for them.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+template <typename TS, int MB, int NT, int KI, typename Mid = NoMid>
 __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const char* xb, int nbytes,
-                                           bool packed) {
+                                           bool packed, Mid mid = Mid()) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, nbytes, BUF_RSRC_W3);
   if constexpr (MB == 1 && KI % 2 == 0) {
@@ -263,6 +326,10 @@ __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[
         v[i] = make_uint4(r[0], r[1], r[2], r[3]);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!std::is_same<Mid, NoMid>::value) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint4 odd = rot8(v[i]);
@@ -290,6 +357,12 @@ __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[
         v[i][mb] = make_uint4(r[0], r[1], r[2], r[3]);
       }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!std::is_same<Mid, NoMid>::value) {
+      if (k0 == 0) {
+        mid();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < KB; ++i) {
       if (k0 + i >= KI) break;
@@ -475,6 +548,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
+  STEP_TIMER_DECL;
 
   int grp, sl;
   RecArgsK& a = launch_slot(L, grp, sl);
@@ -544,46 +618,112 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   });
 
 
-  for (int s = 0; s < T; ++s) {
-    const int t = a.dir ? T - 1 - s : s;
-    const int tp = a.dir ? t + 1 : t - 1;
-    // projected inputs of this step do not depend on the exchange: their
-    // loads are issued before the wait and land while it polls
-    // (unconditional loads from a valid address: a branch per load would
-    // make the compiler wait for each one on the spot)
-    TS pz[UPT][GL], pa[UPT];
+  // Pipelined ring kernels (one row tile): the operands of step s+1 are
+  // loaded, and the stores of step s-1 issued, while step s's exchange loads
+  // are in flight. Loads and stores share one in-order completion counter:
+  // issued just before the wait for the step counters they would hold up
+  // every poll until they complete, and stores still pending at the top of
+  // a step make the compiler wait for them there.
+  constexpr bool PIPE = RING && MB < 4;
+  auto prefetch = [&](int ps, TS (&qz)[UPT][GL], TS (&qa)[UPT]) {
+    const int pt = a.dir ? T - 1 - ps : ps;
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const TS* zr = (const TS*)a.z + (live[u] ? ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
+      // unconditional loads from a valid address: a branch per load would
+      // make the compiler wait for each one on the spot
+      const TS* zr = (const TS*)a.z + (live[u] ? ((long long)pt * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
 #pragma unroll
-      for (int g = 0; g < GL; ++g) pz[u][g] = zr[g * H];
+      for (int g = 0; g < GL; ++g) qz[u][g] = zr[g * H];
       // AUGRU attention score of this step and row
       if constexpr (CELL == CELL_GRU_RA) {
-        const TS* ap = a.att ? (const TS*)a.att + (live[u] ? (long long)t * B + b0 + bl_[u] : 0) : zr;
-        pa[u] = *ap;
+        const TS* ap = a.att ? (const TS*)a.att + (live[u] ? (long long)pt * B + b0 + bl_[u] : 0) : zr;
+        qa[u] = *ap;
       }
     }
+  };
+  // what only later kernels read: y (when the ring carries the exchange),
+  // the saved gates and the cell states of processing step ps; with `on`
+  // false (no step to store) every store is dropped. Branch-free: the
+  // products that wait for the exchange loads issued before these stores
+  // then wait for exactly those loads.
+  auto post_stores = [&](int ps, bool on, const float (&qsv)[UPT][4], const float (&qhv)[UPT],
+                         const float (&qcv)[UPT]) {
+    const int pt = a.dir ? T - 1 - ps : ps;
+    constexpr int SZ = (int)sizeof(TS);
+    const auto rz = rsrc((const TS*)a.z + (long long)pt * B * GZH, (long long)B * GZH * SZ);
+    const auto ry = rsrc((const TS*)a.y + (long long)pt * B * a.ldy, (long long)B * a.ldy * SZ);
+    const bool cb = CELL == CELL_LSTM && a.cbuf != nullptr;
+    const auto rc = rsrc(cb ? (const TS*)a.cbuf + (long long)pt * B * a.ldc : (const TS*)a.z, cb ? (long long)B * a.ldc * SZ : 0);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const bool ok = on && live[u];
+      const int b = b0 + bl_[u], jj = J0 + j_[u];
+      const int oz = ok ? (b * (int)GZH + jj) * SZ : BUF_SKIP;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bstore<TS>(rz, oz + g * H * SZ, qsv[u][g]);
+      bstore<TS>(ry, ok ? (b * (int)a.ldy + jj) * SZ : BUF_SKIP, qhv[u]);
+      if constexpr (CELL == CELL_LSTM) bstore<TS>(rc, ok ? (b * (int)a.ldc + jj) * SZ : BUF_SKIP, qcv[u]);
+    }
+  };
+  TS pz[UPT][GL], pa[UPT];                  // operands of the current step
+  float dsv[UPT][4], dhv[UPT], dcv[UPT];    // the previous step's deferred stores (PIPE)
+  if constexpr (PIPE) prefetch(0, pz, pa);
+
+  STEP_TIMER_CAL(0);
+  for (int s = 0; s < T; ++s) {
+    STEP_TIMER(s, 0);
+    const int t = a.dir ? T - 1 - s : s;
+    const int tp = a.dir ? t + 1 : t - 1;
+    // without the pipeline, the projected inputs of this step are loaded
+    // before the wait and land while it polls
+    if constexpr (!PIPE) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        const TS* zr = (const TS*)a.z + (live[u] ? ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u] : 0);
+#pragma unroll
+        for (int g = 0; g < GL; ++g) pz[u][g] = zr[g * H];
+        if constexpr (CELL == CELL_GRU_RA) {
+          const TS* ap = a.att ? (const TS*)a.att + (live[u] ? (long long)t * B + b0 + bl_[u] : 0) : zr;
+          pa[u] = *ap;
+        }
+      }
+    }
+    TS pzn[UPT][GL], pan[UPT];  // the next step's operands (PIPE)
     if (s > 0) wait_flags(gflags + ws0 * fstride, wsn, s, a.status, a.timeout_ticks, fstride, MB < 4 && local);
+    STEP_TIMER(s, 1);
     f4 acc[MB][NT];
     zero_acc(acc);
     if constexpr (RING) {
-      contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
+      if constexpr (PIPE) {
+        auto mid = [&]() {
+          prefetch(s + 1 < T ? s + 1 : s, pzn, pan);
+          post_stores(s > 0 ? s - 1 : 0, s > 0, dsv, dhv, dcv);
+        };
+        contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed, mid);
+      } else {
+        contract_x<TS, MB, NT, KI>(acc, Wr, xslot(s - 1), xbytes, packed);
+      }
     } else {
       const TS* src = (s == 0) ? (const TS*)a.h0 : (const TS*)a.y + (long long)tp * B * a.ldy;
       const long long ld = (s == 0) ? H : a.ldy;
       contract<TS, MB, NT, KI>(acc, Wr, src, ld, b0, bend, H, 1 << 30, 0);
     }
+    STEP_TIMER(s, 2);
     spill_acc(red, acc, bend - b0);
+    STEP_TIMER(s, 3);
     __syncthreads();
+    STEP_TIMER(s, 4);
     // the exchanged vector is stored first; what only later kernels read
     // (y when the ring carries the exchange, saved gates, cell states) is
     // kept in registers and stored after the step counter is published
+    // (pipelined: during the next step's exchange loads)
     // A step past a row's length (variable lengths) keeps the state, saves
     // zero gates and outputs zero; the exchange still carries the kept state
     // (without the ring, y carries it and is zeroed by a later pass).
     float sv[UPT][4], hv[UPT], cv[UPT];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
+      if constexpr (PIPE) sv[u][0] = sv[u][1] = sv[u][2] = sv[u][3] = hv[u] = cv[u] = 0.f;
       if (!live[u]) continue;
       const int bl = bl_[u], j = j_[u], b = b0 + bl;
       const bool act = t < len_[u];
@@ -625,22 +765,50 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
       if (tiled) xstore((TS*)(xslot(s) + xoff<TS>(bl, J0 + j, packed, MB)), h, local);
       else xstore(yr, h, local);
     }
+    STEP_TIMER(s, 5);
     publish(myflag, s + 1, local);
+    STEP_TIMER(s, 6);
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) dsv[u][g] = sv[u][g];
+        dhv[u] = hv[u];
+        dcv[u] = cv[u];
+#pragma unroll
+        for (int g = 0; g < GL; ++g) pz[u][g] = pzn[u][g];
+        pa[u] = pan[u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+        if (!live[u]) continue;
+        const int bl = bl_[u], j = j_[u], b = b0 + bl;
+        TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
+        if (tiled) ((TS*)a.y)[((long long)t * B + b) * a.ldy + J0 + j] = from_f<TS>(hv[u]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) zr[g * H] = from_f<TS>(sv[u][g]);
+        if constexpr (CELL == CELL_LSTM) {
+          if (a.cbuf) ((TS*)a.cbuf)[((long long)t * B + b) * a.ldc + J0 + j] = from_f<TS>(cv[u]);
+          if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(cst[u]);
+        }
+        if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hst[u]);
+      }
+    }
+    STEP_TIMER(s, 7);
+  }
+  if constexpr (PIPE) {
+    post_stores(T - 1, true, dsv, dhv, dcv);
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
-      const int bl = bl_[u], j = j_[u], b = b0 + bl;
-      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
-      if (tiled) ((TS*)a.y)[((long long)t * B + b) * a.ldy + J0 + j] = from_f<TS>(hv[u]);
-#pragma unroll
-      for (int g = 0; g < 4; ++g) zr[g * H] = from_f<TS>(sv[u][g]);
-      if constexpr (CELL == CELL_LSTM) {
-        if (a.cbuf) ((TS*)a.cbuf)[((long long)t * B + b) * a.ldc + J0 + j] = from_f<TS>(cv[u]);
-        if (s == T - 1 && a.cT) ((TS*)a.cT)[(long long)b * H + J0 + j] = from_f<TS>(cst[u]);
-      }
-      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hst[u]);
+      const long long o = (long long)(b0 + bl_[u]) * H + J0 + j_[u];
+      if (CELL == CELL_LSTM && a.cT) ((TS*)a.cT)[o] = from_f<TS>(cst[u]);
+      if (a.hT) ((TS*)a.hT)[o] = from_f<TS>(hst[u]);
     }
   }
+  STEP_TIMER_CAL(1);
+  STEP_TIMER_FLUSH(T);
 }
 
 // Basic GRU: the candidate contracts r*h_{t-1} over all hidden units, so a
@@ -782,6 +950,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
+  STEP_TIMER_DECL;
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
@@ -852,60 +1021,108 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
     }
   }
 
-  for (int n = 0; n <= T; ++n) {
-    const int s = T - 1 - n;  // processing index of this step (-1: the final dh0 contraction)
-    const int t = a.dir ? T - 1 - s : s;
-    const int tp = a.dir ? t + 1 : t - 1;
-    // own-unit operands of the step (independent of the exchange), loaded
-    // ahead of the wait: dy, saved gates, cell states / previous output
-    // (unconditional loads from valid addresses; `on` selects at use)
-    TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT], pa[UPT];
-    bool pvalid[UPT];
+  // Pipelined ring kernels (one row tile), as in the forward: the own-unit
+  // operands of step n+1 are loaded, and step n-1's gate gradients (and
+  // AUGRU score partials) stored, while step n's exchange loads are in
+  // flight, so that neither holds up the poll of the step counters. The
+  // cell-state lane rebuilt into dG (recomputation) is read two steps before
+  // the deferred store that overwrites it.
+  constexpr bool PIPE = RING && MB < 4;
+  auto prefetch = [&](int pn, TS (&qdy)[UPT], TS (&qz)[UPT][4], TS (&qc)[UPT], TS (&qprev)[UPT], TS (&qa)[UPT],
+                      bool (&qvalid)[UPT]) {
+    const int ps = T - 1 - pn;
+    const int pt = a.dir ? T - 1 - ps : ps;
+    const int ptp = a.dir ? pt + 1 : pt - 1;
+    // own-unit operands of the step (independent of the exchange): dy,
+    // saved gates, cell states / previous output (unconditional loads from
+    // valid addresses; `on` selects at use)
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
-      const bool on = live[u] && n < T;
-      const long long row = on ? (long long)t * B + b0 + bl_[u] : 0;
+      const bool on = live[u] && pn < T;
+      const long long row = on ? (long long)pt * B + b0 + bl_[u] : 0;
       const long long o = on ? (long long)(b0 + bl_[u]) * H + J0 + j_[u] : 0;
       const int jj = on ? J0 + j_[u] : 0;
       const TS* zr = (const TS*)a.z + row * GZH + jj;
-      pdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
+      qdy[u] = ((const TS*)a.dy)[row * a.ldy + jj];
       if constexpr (CELL == CELL_GRU_RA) {
         const TS* ap = a.att ? (const TS*)a.att + row : (const TS*)a.dy;
-        pa[u] = *ap;
+        qa[u] = *ap;
       }
 #pragma unroll
-      for (int g = 0; g < 4; ++g) pz[u][g] = zr[g * H];
+      for (int g = 0; g < 4; ++g) qz[u][g] = zr[g * H];
       // the row's first processed step takes its previous state from h0/c0
       // (direction 1 with variable lengths: the row's own last step)
-      const bool first = a.dir ? (t == len_[u] - 1) : (t == 0);
-      const bool inseq = tp >= 0 && tp < T;
+      const bool first = a.dir ? (pt == len_[u] - 1) : (pt == 0);
+      const bool inseq = ptp >= 0 && ptp < T;
       if constexpr (CELL == CELL_LSTM) {
-        pc[u] = ((const TS*)a.cbuf)[row * a.ldc + jj];
-        pvalid[u] = on && (!first || a.c0);
+        qc[u] = ((const TS*)a.cbuf)[row * a.ldc + jj];
+        qvalid[u] = on && (!first || a.c0);
         const TS* cprev = (first && a.c0) ? (const TS*)a.c0 + o
-                        : (const TS*)a.cbuf + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldc + jj);
-        pprev[u] = *cprev;
+                        : (const TS*)a.cbuf + (first || !on || !inseq ? 0 : ((long long)ptp * B + b0 + bl_[u]) * a.ldc + jj);
+        qprev[u] = *cprev;
       } else {
-        pc[u] = from_f<TS>(0.f);
-        pvalid[u] = on && (!first || a.h0);
+        qc[u] = from_f<TS>(0.f);
+        qvalid[u] = on && (!first || a.h0);
         const TS* hprev = (first && a.h0) ? (const TS*)a.h0 + o
-                        : (const TS*)a.y + (first || !on || !inseq ? 0 : ((long long)tp * B + b0 + bl_[u]) * a.ldy + jj);
-        pprev[u] = *hprev;
+                        : (const TS*)a.y + (first || !on || !inseq ? 0 : ((long long)ptp * B + b0 + bl_[u]) * a.ldy + jj);
+        qprev[u] = *hprev;
       }
     }
+  };
+  // gate gradients of processing step pn for the later kernels (the ring
+  // carried the exchange); branch-free as in the forward (`on` false: every
+  // store dropped)
+  auto post_stores = [&](int pn, bool on, const float (&qdv)[UPT][4]) {
+    const int ps = T - 1 - pn;
+    const int pt = a.dir ? T - 1 - ps : ps;
+    constexpr int SZ = (int)sizeof(TS);
+    const auto rg = rsrc((const TS*)a.dg + (long long)pt * B * GDH, (long long)B * GDH * SZ);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int og = (on && live[u]) ? ((b0 + bl_[u]) * (int)GDH + J0 + j_[u]) * SZ : BUF_SKIP;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) bstore<TS>(rg, og + g * H * SZ, qdv[u][g]);
+    }
+  };
+  TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT], pa[UPT];  // operands of the current step
+  bool pvalid[UPT];
+  float ddv[UPT][4];  // the previous step's deferred gate gradients (PIPE)
+  if constexpr (PIPE) prefetch(0, pdy, pz, pc, pprev, pa, pvalid);
+
+  STEP_TIMER_CAL(0);
+  for (int n = 0; n <= T; ++n) {
+    STEP_TIMER(n, 0);
+    const int s = T - 1 - n;  // processing index of this step (-1: the final dh0 contraction)
+    const int t = a.dir ? T - 1 - s : s;
+    if constexpr (!PIPE) prefetch(n, pdy, pz, pc, pprev, pa, pvalid);
+    TS ndy[UPT], nz[UPT][4], nc[UPT], nprev[UPT], na[UPT];  // the next step's operands (PIPE)
+    bool nvalid[UPT];
+    auto mid = [&]() {
+      if constexpr (PIPE) {
+        prefetch(n + 1 < T ? n + 1 : T - 1, ndy, nz, nc, nprev, na, nvalid);
+        post_stores(n > 0 ? n - 1 : 0, n > 0, ddv);
+      }
+    };
     f4 acc[MB][NT];
     zero_acc(acc);
     if (n > 0) {
       wait_flags(gflags + ws0 * fstride, wsn, n, a.status, a.timeout_ticks, fstride, CELL == CELL_LSTM && MB < 4 && local);
-      if constexpr (RING) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
+      STEP_TIMER(n, 1);
+      if constexpr (PIPE) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed, mid);
+      else if constexpr (RING) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
       if constexpr (!RING) {
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
         contract<TS, MB, NT, KI>(acc, Wr, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, K, kshift,
                                  kskip);
       }
+    } else if constexpr (PIPE) {
+      mid();
     }
+    STEP_TIMER(n, 2);
     spill_acc(red, acc, bend - b0);
+    STEP_TIMER(n, 3);
     __syncthreads();
+    STEP_TIMER(n, 4);
     if (n == T) {
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
@@ -920,6 +1137,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
     float dv[UPT][4];
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
+      if constexpr (PIPE) dv[u][0] = dv[u][1] = dv[u][2] = dv[u][3] = 0.f;
       if (!live[u]) continue;
       const long long row = (long long)t * B + b0 + bl_[u];
       // a step past the row's length has zero gate gradients; the gradient
@@ -999,9 +1217,25 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         }
       }
     }
+    STEP_TIMER(n, 5);
     publish(myflag, n + 1, local);
+    STEP_TIMER(n, 6);
     if (CELL == CELL_GRU_RA && a.att) att_rows<HS>(attl, a.datt_part, t, B, b0, bend, a.nSlices, sl);
-    if (tiled) {
+    if constexpr (PIPE) {
+#pragma unroll
+      for (int u = 0; u < UPT; ++u) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          ddv[u][g] = dv[u][g];
+          pz[u][g] = nz[u][g];
+        }
+        pdy[u] = ndy[u];
+        pc[u] = nc[u];
+        pprev[u] = nprev[u];
+        pa[u] = na[u];
+        pvalid[u] = nvalid[u];
+      }
+    } else if (tiled) {
       // gate gradients for the later kernels (the ring carried the exchange)
 #pragma unroll
       for (int u = 0; u < UPT; ++u) {
@@ -1011,7 +1245,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         for (int g = 0; g < 4; ++g) gr[g * H] = from_f<TS>(dv[u][g]);
       }
     }
+    STEP_TIMER(n, 7);
   }
+  STEP_TIMER_CAL(1);
+  STEP_TIMER_FLUSH(T + 1);
 }
 
 // Basic GRU backward: phase A contracts [d_r, d_u]_{t+1} with W_h{r,u} and
@@ -1149,6 +1386,75 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
     }
     publish(myflag, 2 * n + 2, local);
   }
+}
+
+// ------------------------------------------------- exchange-only probe --
+// The step exchange of a plan with nothing else: the same grid, placement
+// check, counters, per-wave waits and exchange-ring layout as the ring
+// kernels above, and per step the same loads (this wave's k-steps of the
+// previous step's vector) and stores (each unit's gk values, one 8-byte piece
+// when unit-major), but no contraction and no gate arithmetic. Its time per
+// step is the floor that the exchange protocol alone puts under a step. A
+// measurement probe: rnn_handshake_probe launches it, the layer calls never.
+template <typename TS, int NW>
+__global__ __launch_bounds__(NW * 64) void rec_exchange_probe(RecLaunch L, int K, int ki, int gk, int umaj) {
+  constexpr int NTH = NW * 64;
+  constexpr int KSTEP = 4 * Chunk<TS>::KQ;
+  int grp, sl;
+  RecArgsK& a = launch_slot(L, grp, sl);
+  const int fstride = a.fstride, place_off = a.place_off;
+  int* myflag = a.flags + (grp * a.nSlices + sl) * fstride;
+  const int* gflags = a.flags + grp * a.nSlices * fstride;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int H = a.H, T = a.T, HS = a.Hs;
+  const int J0 = sl * HS, b0 = grp * a.bg;
+  const int bend = min(a.B, b0 + a.bg);
+  const bool packed = a.xpacked != 0;
+  const int xbytes = K * (packed ? 8 : 16) * (int)sizeof(TS);
+  auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
+  int ws0, wsn;
+  {
+    const int k0 = w * ki * KSTEP, k1 = min(K, k0 + ki * KSTEP);
+    if (umaj && k1 > k0) {
+      ws0 = (k0 >> 2) / HS;
+      wsn = ((k1 - 1) >> 2) / HS + 1 - ws0;
+    } else {
+      wave_slices(k0, k1, H, HS, a.nSlices, ws0, wsn);
+    }
+  }
+  const bool local = group_is_local(myflag, gflags, a.nSlices, fstride, place_off, a.status, a.timeout_ticks);
+  const int units = (bend - b0) * HS;
+  unsigned keep = 0;
+  for (int s = 0; s < T; ++s) {
+    if (s > 0) {
+      wait_flags(gflags + ws0 * fstride, wsn, s, a.status, a.timeout_ticks, fstride, a.bg <= 16 && local);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)xslot(s - 1), (short)0, xbytes, BUF_RSRC_W3);
+      const int nl = packed ? ki / 2 : ki;
+      const int base = packed ? (w * ki) / 2 : w * ki;
+      for (int i = 0; i < nl; ++i) {
+        const auto r = __builtin_amdgcn_raw_buffer_load_b128(rs, (base + i) * 1024 + lane * 16, 0, CPOL_SC1);
+        keep ^= r[0] ^ r[1] ^ r[2] ^ r[3];
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    __syncthreads();
+    // values that depend on the loads (zero), so that they stay live
+    const float v = (float)(keep & 0u);
+    for (int unit = tid; unit < units; unit += NTH) {
+      const int bl = unit / HS, j = unit - bl * HS, jj = J0 + j;
+      char* xs = xslot(s);
+      if (umaj) {
+        unsigned long long* p8 = (unsigned long long*)(xs + xoff<TS>(bl, 4 * jj, packed, 1));
+        if (local) *p8 = (unsigned long long)__float_as_uint(v);
+        else __hip_atomic_store(p8, (unsigned long long)__float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        for (int g = 0; g < gk; ++g) xstore((TS*)(xs + xoff<TS>(bl, g * H + jj, packed, 1)), v, local);
+      }
+    }
+    publish(myflag, s + 1, local);
+  }
+  asm volatile("" ::"v"(keep));
 }
 
 // ------------------------------------------------------------ plans ------
@@ -1302,6 +1608,20 @@ int max_coresident(const RecPlan& p) {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, p.func, p.nw * 64, p.lds_bytes) != hipSuccess) return 0;
   return n;
+}
+
+hipError_t launch_exchange_probe(const RecPlan& p, const RecLaunch& L, int dtype, int K, int gk, int umaj,
+                                 hipStream_t s) {
+  const void* f = nullptr;
+  if (p.nw == 4) f = dtype ? (const void*)rec_exchange_probe<bf16, 4> : (const void*)rec_exchange_probe<float, 4>;
+  if (p.nw == 8) f = dtype ? (const void*)rec_exchange_probe<bf16, 8> : (const void*)rec_exchange_probe<float, 8>;
+  if (f == nullptr || p.mb != 1 || L.d[0].xbuf == nullptr) return hipErrorInvalidValue;
+  const int n = p.nGroups * p.nSlices;
+  if (L.dual && n % 4 != 0) return hipErrorInvalidValue;
+  RecLaunch args = L;
+  int ki = p.ki;
+  void* kargs[] = {&args, &K, &ki, &gk, &umaj};
+  return hipLaunchCooperativeKernel(f, dim3(L.dual ? 2 * n : n), dim3(p.nw * 64), kargs, 0, s);
 }
 
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {

@@ -198,10 +198,22 @@ struct DevInfo {
 // handshake time-out of the persistent kernels (seconds; < 0: no time at all)
 double g_timeout_s = TIMEOUT_S;
 
+bool log_on() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("RNN_LOG");
+    v = (e && *e && *e != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
 int dev_info(DevInfo* out) {
   static DevInfo cache[64];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return RNN_ERR_DEVICE;
+  if (const hipError_t e = hipGetDevice(&dev); e != hipSuccess || dev < 0 || dev >= 64) {
+    if (log_on()) fprintf(stderr, "[rnn] hipGetDevice: %s (device %d)\n", hipGetErrorString(e), dev);
+    return RNN_ERR_DEVICE;
+  }
   if (cache[dev].cu == 0) {
     int cu = 0, rate_khz = 0;
     if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return RNN_ERR_DEVICE;
@@ -215,14 +227,6 @@ int dev_info(DevInfo* out) {
   return RNN_OK;
 }
 
-bool log_on() {
-  static int v = -1;
-  if (v < 0) {
-    const char* e = getenv("RNN_LOG");
-    v = (e && *e && *e != '0') ? 1 : 0;
-  }
-  return v == 1;
-}
 
 void inv_perm(const rnn_desc_t* d, int perm[4]) {
   for (int k = 0; k < 4; ++k) perm[k] = 0;
@@ -237,7 +241,12 @@ int check_common(const rnn_desc_t* d, const void* ws, size_t ws_bytes) {
   return RNN_OK;
 }
 
-int hip_status(hipError_t e) { return e == hipSuccess ? RNN_OK : RNN_ERR_DEVICE; }
+int hip_status_at(hipError_t e, int line) {
+  if (e == hipSuccess) return RNN_OK;
+  if (log_on()) fprintf(stderr, "[rnn] HIP error %d (%s) at rnn_api.cpp:%d\n", (int)e, hipGetErrorString(e), line);
+  return RNN_ERR_DEVICE;
+}
+#define hip_status(e) hip_status_at((e), __LINE__)
 
 // ---- optional kernel timing (rnn_profile_*) ----
 enum Label { L_FILL, L_PROJ, L_RFWD, L_RBWD, L_DX, L_DW, L_DB, L_AUX, L_COUNT };
@@ -1072,6 +1081,94 @@ RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_p
   const int occ = wg_per_cu > 0 ? wg_per_cu : rnn::max_coresident(plan);
   return coresidency(nwg, dual, occ, di.cu);
 }
+
+RNN_API int rnn_handshake_probe(const rnn_desc_t* d, int pass, void* workspace, size_t ws_bytes, void* stream) {
+  int st = check_common(d, workspace, ws_bytes);
+  if (st) return st;
+  if (pass != 0 && pass != 1) return RNN_ERR_INVALID_ARG;
+  const int cell = cell_of(d);
+  if (cell == rnn::CELL_GRU_BASIC) return RNN_ERR_UNSUPPORTED;  // no exchange ring
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  g_cu_count = di.cu;
+  const bool bidir = d->direction == 2;
+  const int halves = bidir ? 2 : 1;
+  rnn::RecPlan plan;
+  bool dual;
+  auto planner = [&](int cu, int xcds, rnn::RecPlan* p) {
+    return pass == 0 ? rnn::plan_fwd(cell, d->dtype, d->B, d->H, cu, xcds, p)
+                     : rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p);
+  };
+  if (!choose_plan(planner, bidir, di, &plan, &dual)) return RNN_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  const rnn_desc_t hd[2] = {half_desc(d, 0), half_desc(d, 1)};
+  const size_t half_bytes = layout(&hd[0]).total;
+  int* status = (int*)(ws + layout(&hd[0]).status);
+  const int G = (cell == rnn::CELL_LSTM) ? 4 : 3;
+  const long long K = pass == 0 ? d->H : (long long)G * d->H;
+  rnn::RecArgs args[2]{};
+  for (int k = 0; k < halves; ++k) {
+    char* w = ws + k * half_bytes;
+    const Layout L = layout(&hd[k]);
+    int* flags = (int*)(w + L.flags) + (pass ? rnn::FLAG_PASS : 0);
+    {
+      const long long n = (long long)(flags - (int*)(w + L.status)) + counter_ints(plan);
+      if ((st = hip_status(rnn::launch_fill_i32((int*)(w + L.status), 0, n, s)))) return st;
+    }
+    rnn::RecArgs& a = args[k];
+    a.T = d->T;
+    a.B = d->B;
+    a.H = d->H;
+    a.dir = hd[k].direction;
+    a.nGroups = plan.nGroups;
+    a.nSlices = plan.nSlices;
+    a.Hs = plan.Hs;
+    a.bg = plan.bg;
+    a.flags = flags;
+    counter_layout(plan, &a.fstride, &a.place_off);
+    a.status = status;
+    a.timeout_ticks = di.ticks;
+    set_xbuf(a, plan, L, w, K, esz(d));
+    if (!a.xbuf || plan.mb != 1) return RNN_ERR_UNSUPPORTED;
+  }
+  const int umaj = (pass == 1 && cell == rnn::CELL_LSTM && d->dtype == RNN_BF16) ? 1 : 0;
+  const int gk = pass == 0 ? 1 : G;
+  auto go = [&](const rnn::RecLaunch& Lr) -> int {
+    const long long nwg = (long long)plan.nGroups * plan.nSlices;
+    if (coresidency(nwg, Lr.dual != 0, rnn::max_coresident(plan), di.cu) != RNN_OK) return RNN_ERR_UNSUPPORTED;
+    return hip_status(rnn::launch_exchange_probe(plan, Lr, d->dtype, (int)K, gk, umaj, s));
+  };
+  if (dual) {
+    rnn::RecLaunch Lr{};
+    Lr.d[0] = args[0];
+    Lr.d[1] = args[1];
+    Lr.dual = 1;
+    return go(Lr);
+  }
+  for (int k = 0; k < halves; ++k) {
+    rnn::RecLaunch Lr{};
+    Lr.d[0] = args[k];
+    if ((st = go(Lr))) return st;
+  }
+  return RNN_OK;
+}
+
+#ifdef RNN_STEP_TIMERS
+// Debug build only (include/rnn_debug.h): the per-step timers of the last
+// persistent kernel(s), after the caller has synchronised.
+RNN_API int rnn_step_timers_read(unsigned long long* timers, unsigned long long* cal) {
+  if (!timers || !cal) return RNN_ERR_INVALID_ARG;
+  return hip_status(rnn::read_step_timers(timers, cal));
+}
+RNN_API int rnn_step_timers_shape(int* wgs, int* steps, int* phases) {
+  if (!wgs || !steps || !phases) return RNN_ERR_INVALID_ARG;
+  *wgs = rnn::TIMER_WGS;
+  *steps = rnn::TIMER_STEPS;
+  *phases = rnn::TIMER_PHASES;
+  return RNN_OK;
+}
+#endif
 
 RNN_API int rnn_set_handshake_timeout(double seconds) {
   g_timeout_s = seconds == 0 ? TIMEOUT_S : seconds;

@@ -200,6 +200,20 @@ hipError_t launch_weight_transpose(const void* W, int G, int H, int I, const int
                                    hipStream_t s, bool unit_major = false);
 
 
+// ----------------------------------------------------- per-step timers --
+// Debug build only (RNN_STEP_TIMERS defined): thread 0 of every workgroup of
+// a persistent kernel writes the shader clock (s_memtime) at fixed points of
+// every step into a device array, and the pair (s_memtime, s_memrealtime)
+// when the kernel starts and ends, so that a host tool can turn the ticks
+// into nanoseconds and report where a step's time goes. In the normal build
+// the macros are empty.
+constexpr int TIMER_WGS = 512, TIMER_STEPS = 512, TIMER_PHASES = 8;
+#ifdef RNN_STEP_TIMERS
+// copies the timers (TIMER_WGS x TIMER_STEPS x TIMER_PHASES uint64) and the
+// calibration pairs (TIMER_WGS x 4 uint64) to host memory (recurrent.hip)
+hipError_t read_step_timers(unsigned long long* timers, unsigned long long* cal);
+#endif
+
 // ------------------------------------------------- persistent recurrences --
 // Step counters of one pass: one per workgroup, `fstride` ints apart. A
 // batch group held by one XCD keeps its counters adjacent (stride 1: a
@@ -277,6 +291,11 @@ struct RecPlan {
 bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p);
 bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p);
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s);
+// The exchange-only probe on plan p's grid (single 16-row tile ring plans):
+// K = length of the exchanged vector, gk values stored per unit (one 8-byte
+// piece when umaj), dtype 0 = fp32, 1 = bf16.
+hipError_t launch_exchange_probe(const RecPlan& p, const RecLaunch& L, int dtype, int K, int gk, int umaj,
+                                 hipStream_t s);
 int max_coresident(const RecPlan& p);
 
 }  // namespace rnn

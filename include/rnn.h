@@ -256,6 +256,20 @@ typedef struct rnn_plan {
 } rnn_plan_t;
 int rnn_plan_query(const rnn_desc_t* desc, int pass, int cu_count, int wg_per_cu, rnn_plan_t* out);
 
+/* Measurement probe of the step exchange (the per-step wait of the CUDA
+ * fragment page's persistent kernel, here the step counters and exchange
+ * ring): queues, for pass 0 (forward) or 1 (backward through time), a
+ * persistent kernel on exactly the grid that rnn_fwd / rnn_bwd_data would
+ * launch for this descriptor, which runs the T steps of the exchange alone:
+ * the same placement check, counters, per-wave waits, exchange-ring loads and
+ * stores, with no contraction and no gate arithmetic. Its time divided by T
+ * is the floor that the exchange puts under a step. Takes a workspace as
+ * rnn_fwd does (its status word and counters are overwritten; nothing else
+ * the layer calls keep there is touched beyond the exchange ring). Returns
+ * RNN_ERR_UNSUPPORTED for the basic GRU and plans without an exchange ring,
+ * else as rnn_fwd. */
+int rnn_handshake_probe(const rnn_desc_t* desc, int pass, void* workspace, size_t ws_bytes, void* stream);
+
 /* Optional kernel timing, for measurement tools (the tracing hook of the
  * layer API; off by default). While enabled, every kernel the library queues
  * is bracketed by two HIP events recorded on the call's stream, under a label

@@ -22,7 +22,7 @@ def _declared():
 def test_header_declares_the_abi():
     assert _declared() == sorted(["rnn_workspace_bytes", "rnn_fwd", "rnn_bwd_data", "rnn_bwd_weights",
                                   "rnn_last_device_status", "rnn_status_string", "rnn_set_handshake_timeout", "rnn_plan_query",
-                                  "rnn_fwd_noalloc",
+                                  "rnn_fwd_noalloc", "rnn_handshake_probe",
                                   "rnn_profile_enable", "rnn_profile_read"])
 
 
