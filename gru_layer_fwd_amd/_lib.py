@@ -74,6 +74,7 @@ class RnnPlan(ctypes.Structure):
         ("ring", ctypes.c_int),
         ("xcd_span", ctypes.c_int),
         ("model_us_per_step", ctypes.c_double),
+        ("blocks", ctypes.c_int),
     ]
 
 

@@ -38,6 +38,7 @@
 // "backwardStepImpl"; GRU popnn Gru.cpp "basicGruCellForwardPass",
 // "gruCellForwardPassCalcUnitsResetAfter", "backwardStepImpl" and
 // "backwardStepImplResetAfter".
+#include <algorithm>
 #include <type_traits>
 
 #include "rnn_internal.hpp"
@@ -70,6 +71,10 @@ static __device__ unsigned long long g_step_cal[TIMER_WGS * 4];
       for (int i_ = threadIdx.x; i_ < min((nsteps), TIMER_STEPS) * TIMER_PHASES; i_ += blockDim.x) \
         g_step_timers[(size_t)blockIdx.x * TIMER_STEPS * TIMER_PHASES + i_] = step_tl_[i_];   \
   } while (0)
+hipError_t reset_step_timers() {
+  static unsigned long long zeros[TIMER_WGS * 4] = {};
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_step_cal), zeros, sizeof(zeros));
+}
 hipError_t read_step_timers(unsigned long long* timers, unsigned long long* cal) {
   hipError_t e = hipMemcpyFromSymbol(timers, HIP_SYMBOL(g_step_timers), sizeof(g_step_timers));
   if (e == hipSuccess) e = hipMemcpyFromSymbol(cal, HIP_SYMBOL(g_step_cal), sizeof(g_step_cal));
@@ -259,16 +264,25 @@ __device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t rs, int off, float
 typedef const __attribute__((address_space(4))) RecArgs RecArgsK;
 static_assert(offsetof(RecLaunch, d) == 0, "RecLaunch.d leads the kernel arguments");
 
-__device__ __forceinline__ RecArgsK& launch_slot(const RecLaunch& L, int& grp, int& sl) {
+// Padded placement (per_xcd > 0): each XCD of a direction holds per_xcd
+// consecutive logical indices (whole batch groups), so that a group of
+// fewer workgroups than fit an XCD, but more than n / 8, still shares one
+// L2; the launch has xcds * per_xcd blocks per direction and those past the
+// plan's n workgroups return at once (`idle`).
+__device__ __forceinline__ RecArgsK& launch_slot(const RecLaunch& L, int& grp, int& sl, bool& idle) {
   const int b = blockIdx.x;
   const int n = L.d[0].nGroups * L.d[0].nSlices;
+  const int P = L.per_xcd;
   int d = 0, lw;
   if (!L.dual) {
-    lw = ((n & 7) == 0) ? (b & 7) * (n >> 3) + (b >> 3) : b;
+    if (P > 0) lw = (b & 7) * P + (b >> 3);
+    else lw = ((n & 7) == 0) ? (b & 7) * (n >> 3) + (b >> 3) : b;
   } else {
     d = (b & 7) >> 2;
-    lw = (b & 3) * (n >> 2) + (b >> 3);
+    lw = (b & 3) * (P > 0 ? P : (n >> 2)) + (b >> 3);
   }
+  idle = lw >= n;
+  if (idle) lw = 0;
   RecArgsK& a = ((RecArgsK*)__builtin_amdgcn_kernarg_segment_ptr())[d];
   grp = lw / a.nSlices;
   sl = lw - grp * a.nSlices;
@@ -551,7 +565,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   STEP_TIMER_DECL;
 
   int grp, sl;
-  RecArgsK& a = launch_slot(L, grp, sl);
+  bool idle;
+  RecArgsK& a = launch_slot(L, grp, sl, idle);
+  if (idle) return;
   // groups of 64 or more rows always span several XCDs (one counter line
   // each); a constant stride keeps their register-bound code lean
   const int fstride = MB >= 4 ? FLAG_LINE : a.fstride;
@@ -823,7 +839,9 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
   extern __shared__ float red[];
 
   int grp, sl;
-  RecArgsK& a = launch_slot(L, grp, sl);
+  bool idle;
+  RecArgsK& a = launch_slot(L, grp, sl, idle);
+  if (idle) return;
   int* myflag = a.flags + (grp * a.nSlices + sl) * a.fstride;
   const int* gflags = a.flags + grp * a.nSlices * a.fstride;
   const bool local =
@@ -954,7 +972,9 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
-  RecArgsK& a = launch_slot(L, grp, sl);
+  bool idle;
+  RecArgsK& a = launch_slot(L, grp, sl, idle);
+  if (idle) return;
   // groups of 64 or more rows always span several XCDs (one counter line
   // each); a constant stride keeps their register-bound code lean
   const int fstride = MB >= 4 ? FLAG_LINE : a.fstride;
@@ -1263,7 +1283,9 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
-  RecArgsK& a = launch_slot(L, grp, sl);
+  bool idle;
+  RecArgsK& a = launch_slot(L, grp, sl, idle);
+  if (idle) return;
   int* myflag = a.flags + (grp * a.nSlices + sl) * a.fstride;
   const int* gflags = a.flags + grp * a.nSlices * a.fstride;
   const bool local =
@@ -1401,7 +1423,9 @@ __global__ __launch_bounds__(NW * 64) void rec_exchange_probe(RecLaunch L, int K
   constexpr int NTH = NW * 64;
   constexpr int KSTEP = 4 * Chunk<TS>::KQ;
   int grp, sl;
-  RecArgsK& a = launch_slot(L, grp, sl);
+  bool idle;
+  RecArgsK& a = launch_slot(L, grp, sl, idle);
+  if (idle) return;
   const int fstride = a.fstride, place_off = a.place_off;
   int* myflag = a.flags + (grp * a.nSlices + sl) * fstride;
   const int* gflags = a.flags + grp * a.nSlices * fstride;
@@ -1489,23 +1513,30 @@ const Entry kTable[] = {
     {CELL_GRU_RA, 1, 1, 8, 1, 6, 4, 0, F_GRA(bf16, 8, 1, 6, 4)},
     {CELL_GRU_RA, 1, 1, 8, 4, 3, 8, 0, F_GRA(bf16, 8, 4, 3, 8)},
     {CELL_GRU_RA, 0, 1, 4, 1, 3, 8, 0, F_GRA(float, 4, 1, 3, 8)},
+    {CELL_GRU_RA, 0, 1, 4, 1, 3, 4, 0, F_GRA(float, 4, 1, 3, 4)},
+    {CELL_GRU_RA, 0, 1, 8, 1, 3, 2, 0, F_GRA(float, 8, 1, 3, 2)},
     // forward basic GRU (nt = candidate tiles)
     {CELL_GRU_BASIC, 1, 1, 4, 1, 1, 8, 0, (const void*)rec_fwd_grub<bf16, 4, 1, 1, 8>},
     {CELL_GRU_BASIC, 0, 1, 4, 1, 1, 8, 0, (const void*)rec_fwd_grub<float, 4, 1, 1, 8>},
+    {CELL_GRU_BASIC, 0, 1, 4, 1, 1, 4, 0, (const void*)rec_fwd_grub<float, 4, 1, 1, 4>},
     // backward LSTM
     {CELL_LSTM, 1, 0, 4, 1, 1, 32, 0, B_LSTM(bf16, 4, 1, 1, 32)},
     {CELL_LSTM, 1, 0, 8, 1, 2, 16, 0, B_LSTM(bf16, 8, 1, 2, 16)},
     {CELL_LSTM, 1, 0, 8, 4, 1, 32, 0, B_LSTM(bf16, 8, 4, 1, 32)},
     {CELL_LSTM, 0, 0, 4, 1, 1, 32, 0, B_LSTM(float, 4, 1, 1, 32)},
     {CELL_LSTM, 0, 0, 8, 1, 1, 16, 0, B_LSTM(float, 8, 1, 1, 16)},
+    {CELL_LSTM, 0, 0, 4, 1, 1, 8, 0, B_LSTM(float, 4, 1, 1, 8)},
     // backward reset-after GRU
     {CELL_GRU_RA, 1, 0, 4, 1, 1, 32, 0, B_GRA(bf16, 4, 1, 1, 32)},
     {CELL_GRU_RA, 1, 0, 8, 1, 2, 16, 0, B_GRA(bf16, 8, 1, 2, 16)},
     {CELL_GRU_RA, 1, 0, 4, 4, 1, 48, 0, B_GRA(bf16, 4, 4, 1, 48)},
     {CELL_GRU_RA, 0, 0, 4, 1, 1, 32, 0, B_GRA(float, 4, 1, 1, 32)},
+    {CELL_GRU_RA, 0, 0, 4, 1, 1, 12, 0, B_GRA(float, 4, 1, 1, 12)},
+    {CELL_GRU_RA, 0, 0, 8, 1, 1, 6, 0, B_GRA(float, 8, 1, 1, 6)},
     // backward basic GRU (ki = phase A k-steps, kib = phase B)
     {CELL_GRU_BASIC, 1, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<bf16, 4, 1, 1, 16, 8>},
     {CELL_GRU_BASIC, 0, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<float, 4, 1, 1, 16, 8>},
+    {CELL_GRU_BASIC, 0, 0, 4, 1, 1, 8, 4, (const void*)rec_bwd_grub<float, 4, 1, 1, 8, 4>},
 };
 
 int units_per_wg(const Entry& e) {
@@ -1534,6 +1565,20 @@ int xcd_span(long long nwg, int slices, int xcds) {
   return slices < 8 ? slices : 8;
 }
 
+// Padded placement for groups that would span XCDs under the natural one:
+// whole groups per XCD (as few per XCD as the groups allow, spread over all
+// of the direction's XCDs). Returns per_xcd, or 0 when it does not apply
+// (groups already local, a group larger than an XCD, or more blocks than CUs).
+int padded_per_xcd(int groups, int slices, int xcds, int cu_count) {
+  const long long nwg = (long long)groups * slices;
+  if (xcd_span(nwg, slices, xcds) <= 1) return 0;
+  const int cu_per_xcd = cu_count / xcds;
+  const int gpx = (groups + xcds - 1) / xcds;
+  const int per = gpx * slices;
+  if (per > cu_per_xcd) return 0;
+  return per;
+}
+
 // Modelled time of one step (us): a step handshake costs ~1 us when a
 // batch group shares one XCD and ~2 us across XCDs (measured); a 16x16x32
 // bf16 MFMA occupies its SIMD for 16 cycles (6.67 ns at 2.4 GHz: the
@@ -1543,20 +1588,44 @@ int xcd_span(long long nwg, int slices, int xcds) {
 // bf16 k-step; every CU reads the whole exchanged vector of its group per
 // step, ~150 GB/s from the tiled ring and ~75 GB/s from row layout
 // (measured); the gate epilogue costs ~0.2 us per unit a thread carries.
-double step_cost(const Entry& e, int bg, int groups, int slices, int K, int kstep, int esize, bool ring,
-                 int xcds) {
-  const int span = xcd_span((long long)groups * slices, slices, xcds);
+//
+// Contraction time of one product: wave w owns k-steps [w*ki, w*ki+ki) of
+// the ksteps the contraction has (waves past the end have none) and waves
+// w, w+4 share SIMD w%4, so the busiest SIMD sets the time.
+double contraction_us(int nw, int ki, int ntiles, int K, int kstep) {
+  const int ks = (K + kstep - 1) / kstep;
+  int worst = 0, busy_worst = 0;
+  for (int sm = 0; sm < 4; ++sm) {
+    int sum = 0, busy = 0;
+    for (int w = sm; w < nw; w += 4) {
+      const int kw = std::min(ki, std::max(0, ks - w * ki));
+      sum += kw;
+      busy += kw > 0;
+    }
+    if (sum > worst) {
+      worst = sum;
+      busy_worst = busy;
+    }
+  }
+  const double t_k = (kstep == 32 ? 16.0 : 8.0 * 16.0) / 2.4e3;  // us per 16x16 k-step on a SIMD
+  return worst * ntiles * t_k * (busy_worst >= 2 ? 1.0 : 10.8 / 6.67);
+}
+
+double step_cost(const Entry& e, int bg, int span, int H, int K, int kstep, int esize, bool ring) {
   const double hand = span <= 1 ? 1.0 : 2.0;
-  const int phases = (e.cell == CELL_GRU_BASIC) ? 2 : 1;
-  const int kused = (K + e.nw * kstep - 1) / (e.nw * kstep);
-  const double wps = e.nw / 4.0;  // waves per SIMD
-  // us per k-step per SIMD; a wave alone on its SIMD issues at 6.67/10.8 of the rate
-  const double t_inst = (kstep == 32 ? 16.0 / 2.4e3 : 8.0 * 16.0 / 2.4e3) * (wps >= 2 ? 1.0 : 10.8 / 6.67);
-  const double mfma = wps * e.mb * e.nt * kused * t_inst;
-  const double data = (double)bg * K * esize / (ring ? 150e3 : 75e3);
+  double mfma, data;
+  if (e.cell == CELL_GRU_BASIC) {
+    // two products per step, each behind its own exchange
+    if (e.fwd) mfma = contraction_us(e.nw, e.ki, 2 * e.nt * e.mb, H, kstep) + contraction_us(e.nw, e.ki, e.nt * e.mb, H, kstep);
+    else mfma = contraction_us(e.nw, e.ki, e.nt * e.mb, 2 * H, kstep) + contraction_us(e.nw, e.kib, e.nt * e.mb, H, kstep);
+    data = (double)bg * (e.fwd ? 2 * H : 3 * H) * esize / 75e3;
+    return 2 * hand + mfma + data + 0.2 * 2;
+  }
+  mfma = contraction_us(e.nw, e.ki, e.nt * e.mb, K, kstep);
+  data = (double)bg * K * esize / (ring ? 150e3 : 75e3);
   const int units = e.mb * 16 * units_per_wg(e);
   const int upt = (units + e.nw * 64 - 1) / (e.nw * 64);
-  return phases * hand + mfma + data + 0.2 * upt;
+  return hand + mfma + data + 0.2 * upt;
 }
 
 bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, RecPlan* p) {
@@ -1583,11 +1652,13 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, 
       const long long nwg = (long long)groups * slices;
       if (nwg > cu_count) continue;  // at most one persistent workgroup per CU
       const bool ring = (cell != CELL_GRU_BASIC) && ((long long)K * esize) % 64 == 0 && bg <= 16 * e.mb;
-      const double cost = step_cost(e, bg, groups, slices, K, kstep, esize, ring, xcds);
+      const int per_xcd = padded_per_xcd(groups, slices, xcds, cu_count);
+      const int span = per_xcd > 0 ? 1 : xcd_span(nwg, slices, xcds);
+      const double cost = step_cost(e, bg, span, H, K, kstep, esize, ring);
       if (cost < best) {
         best = cost;
-        *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e),
-                     xcd_span(nwg, slices, xcds), e.func_plain};
+        *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e), span, e.func_plain,
+                     per_xcd, xcds};
         found = true;
       }
     }
@@ -1604,6 +1675,11 @@ bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan
   return choose(cell, dtype, 0, B, H, cu_count, xcds, p);
 }
 
+long long launch_blocks(const RecPlan& p, bool dual) {
+  const long long per_dir = p.per_xcd > 0 ? (long long)p.xcds * p.per_xcd : (long long)p.nGroups * p.nSlices;
+  return dual ? 2 * per_dir : per_dir;
+}
+
 int max_coresident(const RecPlan& p) {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, p.func, p.nw * 64, p.lds_bytes) != hipSuccess) return 0;
@@ -1617,11 +1693,12 @@ hipError_t launch_exchange_probe(const RecPlan& p, const RecLaunch& L, int dtype
   if (p.nw == 8) f = dtype ? (const void*)rec_exchange_probe<bf16, 8> : (const void*)rec_exchange_probe<float, 8>;
   if (f == nullptr || p.mb != 1 || L.d[0].xbuf == nullptr) return hipErrorInvalidValue;
   const int n = p.nGroups * p.nSlices;
-  if (L.dual && n % 4 != 0) return hipErrorInvalidValue;
+  if (L.dual && n % 4 != 0 && p.per_xcd == 0) return hipErrorInvalidValue;
   RecLaunch args = L;
+  args.per_xcd = p.per_xcd;
   int ki = p.ki;
   void* kargs[] = {&args, &K, &ki, &gk, &umaj};
-  return hipLaunchCooperativeKernel(f, dim3(L.dual ? 2 * n : n), dim3(p.nw * 64), kargs, 0, s);
+  return hipLaunchCooperativeKernel(f, dim3(launch_blocks(p, L.dual != 0)), dim3(p.nw * 64), kargs, 0, s);
 }
 
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {
@@ -1630,10 +1707,12 @@ hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
   if (e != hipSuccess) return e;
   const int n = p.nGroups * p.nSlices;
-  if (L.dual && n % 4 != 0) return hipErrorInvalidValue;
+  if (L.dual && n % 4 != 0 && p.per_xcd == 0) return hipErrorInvalidValue;
   RecLaunch args = L;
+  args.per_xcd = p.per_xcd;
   void* kargs[] = {&args};
-  return hipLaunchCooperativeKernel(f, dim3(L.dual ? 2 * n : n), dim3(p.nw * 64), kargs, (unsigned)p.lds_bytes, s);
+  return hipLaunchCooperativeKernel(f, dim3(launch_blocks(p, L.dual != 0)), dim3(p.nw * 64), kargs,
+                                    (unsigned)p.lds_bytes, s);
 }
 
 }  // namespace rnn

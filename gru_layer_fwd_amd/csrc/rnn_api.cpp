@@ -349,8 +349,9 @@ void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws,
 // A persistent grid is launched only when every workgroup can be resident at
 // once (each waits for the others every step): at most one step counter per
 // workgroup, and grid <= (workgroups per CU) x CUs.
-int coresidency(long long nwg, bool dual, int occ, int cu) {
-  const long long grid = dual ? 2 * nwg : nwg;
+int coresidency(const rnn::RecPlan& p, bool dual, int occ, int cu) {
+  const long long nwg = (long long)p.nGroups * p.nSlices;
+  const long long grid = rnn::launch_blocks(p, dual);
   if (nwg > rnn::FLAG_SLOTS) return RNN_ERR_UNSUPPORTED;
   if (occ < 1 || cu < 1 || grid > (long long)occ * cu) return RNN_ERR_UNSUPPORTED;
   return RNN_OK;
@@ -358,10 +359,9 @@ int coresidency(long long nwg, bool dual, int occ, int cu) {
 
 int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const DevInfo& di, hipStream_t s,
                       const char* what) {
-  const long long nwg = (long long)p.nGroups * p.nSlices;
-  const long long grid = Lr.dual ? 2 * nwg : nwg;
+  const long long grid = rnn::launch_blocks(p, Lr.dual != 0);
   const int occ = rnn::max_coresident(p);
-  if (coresidency(nwg, Lr.dual != 0, occ, di.cu) != RNN_OK) {
+  if (coresidency(p, Lr.dual != 0, occ, di.cu) != RNN_OK) {
     if (log_on()) fprintf(stderr, "[rnn] %s: grid %lld not co-resident (occupancy %d x %d CUs)\n", what, grid, occ, di.cu);
     return RNN_ERR_UNSUPPORTED;
   }
@@ -386,7 +386,7 @@ int launch_persistent(const rnn::RecPlan& p, const rnn::RecLaunch& Lr, const Dev
 template <typename F>
 bool choose_plan(F planner, bool bidir, const DevInfo& di, rnn::RecPlan* plan, bool* dual) {
   *dual = false;
-  if (bidir && planner(di.cu / 2, 4, plan) && (plan->nGroups * plan->nSlices) % 4 == 0) {
+  if (bidir && planner(di.cu / 2, 4, plan) && ((plan->nGroups * plan->nSlices) % 4 == 0 || plan->per_xcd > 0)) {
     *dual = true;
     return true;
   }
@@ -1067,6 +1067,7 @@ RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_p
   out->units = plan.Hs;
   out->waves = plan.nw;
   out->workgroups = (int)(dual ? 2 * nwg : nwg);
+  out->blocks = (int)rnn::launch_blocks(plan, dual);
   out->dual = dual ? 1 : 0;
   out->xcd_span = plan.xcd_span;
   out->model_us_per_step = plan.cost_us;
@@ -1079,7 +1080,7 @@ RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_p
     out->ring = a.xg_bytes ? (a.xpacked ? 2 : 1) : 0;
   }
   const int occ = wg_per_cu > 0 ? wg_per_cu : rnn::max_coresident(plan);
-  return coresidency(nwg, dual, occ, di.cu);
+  return coresidency(plan, dual, occ, di.cu);
 }
 
 RNN_API int rnn_handshake_probe(const rnn_desc_t* d, int pass, void* workspace, size_t ws_bytes, void* stream) {
@@ -1136,7 +1137,7 @@ RNN_API int rnn_handshake_probe(const rnn_desc_t* d, int pass, void* workspace, 
   const int gk = pass == 0 ? 1 : G;
   auto go = [&](const rnn::RecLaunch& Lr) -> int {
     const long long nwg = (long long)plan.nGroups * plan.nSlices;
-    if (coresidency(nwg, Lr.dual != 0, rnn::max_coresident(plan), di.cu) != RNN_OK) return RNN_ERR_UNSUPPORTED;
+    if (coresidency(plan, Lr.dual != 0, rnn::max_coresident(plan), di.cu) != RNN_OK) return RNN_ERR_UNSUPPORTED;
     return hip_status(rnn::launch_exchange_probe(plan, Lr, d->dtype, (int)K, gk, umaj, s));
   };
   if (dual) {
@@ -1161,6 +1162,7 @@ RNN_API int rnn_step_timers_read(unsigned long long* timers, unsigned long long*
   if (!timers || !cal) return RNN_ERR_INVALID_ARG;
   return hip_status(rnn::read_step_timers(timers, cal));
 }
+RNN_API int rnn_step_timers_reset(void) { return hip_status(rnn::reset_step_timers()); }
 RNN_API int rnn_step_timers_shape(int* wgs, int* steps, int* phases) {
   if (!wgs || !steps || !phases) return RNN_ERR_INVALID_ARG;
   *wgs = rnn::TIMER_WGS;

@@ -212,6 +212,8 @@ constexpr int TIMER_WGS = 512, TIMER_STEPS = 512, TIMER_PHASES = 8;
 // copies the timers (TIMER_WGS x TIMER_STEPS x TIMER_PHASES uint64) and the
 // calibration pairs (TIMER_WGS x 4 uint64) to host memory (recurrent.hip)
 hipError_t read_step_timers(unsigned long long* timers, unsigned long long* cal);
+// zeroes the calibration pairs (a workgroup that records none did not run)
+hipError_t reset_step_timers();
 #endif
 
 // ------------------------------------------------- persistent recurrences --
@@ -273,6 +275,9 @@ struct RecArgs {
 struct RecLaunch {
   RecArgs d[2];
   int dual;
+  int per_xcd;      // > 0: padded placement, per_xcd logical workgroups on each XCD of a
+                    // direction (the launch has xcds * per_xcd blocks per direction, the
+                    // ones past the plan's workgroups return at once); 0: n / xcds each
 };
 
 struct RecPlan {
@@ -284,6 +289,8 @@ struct RecPlan {
   size_t lds_bytes;
   int xcd_span;         // XCDs a batch group covers (under the launch's block placement)
   const void* func_plain;  // the variant without an exchange ring (NULL: func serves both)
+  int per_xcd;          // padded placement (RecLaunch::per_xcd), 0 = natural
+  int xcds;             // XCDs one direction is spread over (8, or 4 in a dual launch)
 };
 
 // Choose a plan and report it; returns false when no instantiated plan fits.
@@ -291,6 +298,8 @@ struct RecPlan {
 bool plan_fwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p);
 bool plan_bwd(int cell, int dtype, int B, int H, int cu_count, int xcds, RecPlan* p);
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s);
+// blocks of a persistent launch of plan p (both directions when dual)
+long long launch_blocks(const RecPlan& p, bool dual);
 // The exchange-only probe on plan p's grid (single 16-row tile ring plans):
 // K = length of the exchanged vector, gk values stored per unit (one 8-byte
 // piece when umaj), dtype 0 = fp32, 1 = bf16.

@@ -51,11 +51,14 @@ def _timers(lib):
     return flat.reshape(t.shape), c.reshape(w.value, 4).astype(np.int64)
 
 
-def analyse(t, cal, nwg, nsteps, skip=8):
-    """Per-phase means (ns) over workgroups [0, nwg) and steps [skip, nsteps - skip)."""
-    nwg = min(nwg, t.shape[0])
+def analyse(t, cal, nblocks, nsteps, skip=8):
+    """Per-phase means (ns) over the blocks among [0, nblocks) that ran (nonzero
+    calibration pairs) and steps [skip, nsteps - skip)."""
+    nblocks = min(nblocks, t.shape[0])
     nsteps = min(nsteps, t.shape[1])
-    t, cal = t[:nwg, :nsteps], cal[:nwg]
+    ran = np.nonzero(cal[:nblocks, 0] != 0)[0]
+    t, cal = t[ran, :nsteps], cal[ran]
+    nwg = len(ran)
     # s_memtime ticks per ns from each workgroup's start/end pairs (s_memrealtime: 100 MHz)
     ticks_per_ns = float(np.median((cal[:, 2] - cal[:, 0]) / ((cal[:, 3] - cal[:, 1]) * 10.0)))
     lo, hi = skip, max(skip + 1, nsteps - skip)
@@ -87,7 +90,7 @@ def main():
     from . import synth
     L.select(os.path.join(os.path.dirname(os.path.abspath(__file__)), "librnn_timers.so"))
     lib = L.lib()
-    for name in ("rnn_step_timers_shape", "rnn_step_timers_read"):
+    for name in ("rnn_step_timers_shape", "rnn_step_timers_read", "rnn_step_timers_reset"):
         getattr(lib, name).restype = ctypes.c_int
 
     from .api import RnnLayer
@@ -113,6 +116,8 @@ def main():
     torch.cuda.synchronize()
     res = {"workload": name}
     for pass_, label in ((0, "forward"), (1, "backward")):
+        torch.cuda.synchronize()
+        assert lib.rnn_step_timers_reset() == 0
         if pass_ == 0:
             lay.fwd(x, h0, c0, *W, y)
         else:
@@ -122,7 +127,7 @@ def main():
         st, plan = L.rnn_plan_query(lay.desc, pass_)
         assert st == 0
         t, cal = _timers(lib)
-        res[label] = analyse(t, cal, plan.workgroups, wl.T + pass_)
+        res[label] = analyse(t, cal, plan.blocks, wl.T + pass_)
         res[label]["plan"] = {k: getattr(plan, k) for k, _ in plan._fields_}
         # the exchange alone on the same grid
         s = torch.cuda.current_stream()

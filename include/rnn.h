@@ -248,11 +248,13 @@ typedef struct rnn_plan {
   int slices;       /* hidden slices per group (workgroups of a group) */
   int units;        /* hidden units per slice */
   int waves;        /* 64-wide waves per workgroup */
-  int workgroups;   /* grid of the launch (both directions when dual) */
+  int workgroups;   /* working workgroups of the launch (both directions when dual) */
   int dual;         /* 1: the two directions of a bidirectional layer share one launch */
   int ring;         /* exchange of the step vector: 0 rows of y / dG, 1 tiled ring, 2 packed ring */
   int xcd_span;     /* XCDs one batch group covers */
   double model_us_per_step; /* the planner's modelled time per step */
+  int blocks;       /* blocks launched: workgroups, or more when groups are padded to whole
+                       XCDs (the extra blocks return at once) */
 } rnn_plan_t;
 int rnn_plan_query(const rnn_desc_t* desc, int pass, int cu_count, int wg_per_cu, rnn_plan_t* out);
 

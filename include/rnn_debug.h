@@ -12,7 +12,7 @@
  *   3 partial sums written to LDS, 4 past the workgroup barrier,
  *   5 gate epilogue done (exchange stores issued), 6 step counter published,
  *   7 stores for later kernels issued.
- * Records cover workgroups [0, wgs) (launch order) and steps [0, steps)
+ * Records cover blocks [0, wgs) (launch order) and steps [0, steps)
  * (processing order); each kernel launch overwrites what it reaches.
  */
 #ifndef RNN_DEBUG_H_
@@ -21,6 +21,11 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Zeroes the per-workgroup calibration pairs: after the next launch, a
+ * block whose pairs are still zero did no work (padded placements launch
+ * blocks that return at once). RNN_ERR_DEVICE if the copy fails. */
+int rnn_step_timers_reset(void);
 
 /* Dimensions of the timer array: wgs x steps x phases 64-bit ticks. */
 int rnn_step_timers_shape(int* wgs, int* steps, int* phases);
