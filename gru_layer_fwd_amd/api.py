@@ -34,12 +34,14 @@ class RnnLayer:
 
     def __init__(self, mode: str, T: int, B: int, I: int, H: int, dtype: str, direction: int = 0,
                  reset_after: bool = True, gate_order=None, ldx: int = 0, ldy: int = 0, device="cuda",
-                 lengths=None, att=None, recompute=False):
+                 lengths=None, att=None, recompute=False, dw_hh_mode=0):
         """`lengths`: optional int32 device tensor [B] of per-row sequence
         lengths; `att`: optional [T, B] device tensor of AUGRU attention
         scores in the layer's dtype (GRU only). Both are kept referenced by
         the layer; the three calls read them. `recompute` (LSTM): keep only
-        the gates between the forward and backward calls."""
+        the gates between the forward and backward calls. `dw_hh_mode` 1:
+        the recurrent-weight gradient from the separate product, never
+        accumulated inside the BPTT kernel."""
         self.mode, self.dtype = mode, dtype
         self.T, self.B, self.I, self.H = T, B, I, H
         if lengths is not None:
@@ -52,7 +54,7 @@ class RnnLayer:
         self.lengths, self.att = lengths, att
         self.desc = L.make_desc(MODE_OF[mode], T, B, I, H, DT_OF[dtype], direction,
                                 int(bool(reset_after)), gate_order, ldx, ldy, _p(lengths), _p(att),
-                                int(bool(recompute)))
+                                int(bool(recompute)), int(dw_hh_mode))
         self.ws_bytes = L.rnn_workspace_bytes(self.desc)
         if self.ws_bytes == 0:
             raise L.RnnError(L.RNN_ERR_INVALID_ARG, "rnn_workspace_bytes")

@@ -679,6 +679,7 @@ __global__ __launch_bounds__(256) void colsum_partial(const TS* src, long long l
   long long r1 = r0 + rows_per;
   if (r1 > M) r1 = M;
   float s = 0.f;
+#pragma unroll 8
   for (long long r = r0; r < r1; ++r) s += to_f(src[r * lds + col0 + n]);
   partial[(long long)blockIdx.y * ncols + n] = s;
 }
@@ -693,6 +694,7 @@ __global__ __launch_bounds__(256) void colsum_final(const float* partial, int nc
   const int n = blockIdx.x * 256 + threadIdx.x;
   if (n >= ncols) return;
   float s = 0.f;
+#pragma unroll 8
   for (int c = 0; c < nchunks; ++c) s += partial[(long long)c * ncols + n];
   const int r = out_row0 + n;
   const int gg = r / H;
@@ -710,6 +712,37 @@ __device__ __forceinline__ int clamp_len(const int* lengths, int b, int T) {
 }
 
 // one-dimensional grids: block = (row, block of 256 columns)
+// Recurrent-weight and bias gradients from the per-group partials the BPTT
+// kernel accumulated (fused dW): out[perm row of k][c] (+)= sum over groups
+// g, in order, of part[(g*K + k)*H + c], and db[perm row of k] (+)= sum of
+// part[groups*K*H + g*K + k]; k runs over the canonical gate rows. Either
+// output may be NULL.
+template <typename TS>
+__global__ __launch_bounds__(256) void dw_partials_finish(const float* __restrict__ part, int groups, int K, int H,
+                                                          Perm4 perm, TS* out, TS* db, int accumulate) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (long long)K * H) return;
+  if (out) {
+    const int k = (int)(i / H), c = (int)(i - (long long)k * H);
+    float s = 0.f;
+    for (int g = 0; g < groups; ++g) s += part[((long long)g * K + k) * H + c];
+    const int gg = k / H;
+    TS* o = out + ((long long)perm.p[gg] * H + (k - gg * H)) * H + c;
+    if (accumulate) s += to_f(*o);
+    *o = from_f<TS>(s);
+  }
+  if (db && i < K) {
+    const int k = (int)i;
+    const float* pb = part + (long long)groups * K * H;
+    float s = 0.f;
+    for (int g = 0; g < groups; ++g) s += pb[(long long)g * K + k];
+    const int gg = k / H;
+    TS* o = db + perm.p[gg] * H + (k - gg * H);
+    if (accumulate) s += to_f(*o);
+    *o = from_f<TS>(s);
+  }
+}
+
 template <typename TS>
 __global__ __launch_bounds__(256) void zero_inactive(TS* y, long long ldy, const int* lengths, int T, int B, int H) {
   const int ncb = (H + 255) / 256;
@@ -949,11 +982,11 @@ GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long lon
     p.bm = p.bn = 128;
   } else if (K < 2048) {
     // few 128x128 tiles and a moderate contraction: split it into slices of
-    // at least 256 so that more CUs take part
+    // at least 128 so that more CUs take part
     p.bm = p.bn = 128;
     long long ks = (cu_count + t128 - 1) / t128;
-    if (ks > K / 256) ks = K / 256;
-    if (ks > 8) ks = 8;
+    if (ks > K / 128) ks = K / 128;
+    if (ks > 16) ks = 16;
     while (ks > 1 && ks * (M * N + M) > ws_floats) --ks;
     p.ksplit = (int)(ks < 1 ? 1 : ks);
   } else {
@@ -1043,7 +1076,9 @@ template <typename TS>
 hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, int ncols, void* out, int out_row0,
                          int H, const int perm[4], int accumulate, float* partial, int max_chunks, hipStream_t s) {
   if (ncols <= 0) return hipSuccess;
-  long long nch = (M + 255) / 256;
+  // chunks of >= 16 rows: enough blocks that the loads of a column are in
+  // flight together rather than one after another
+  long long nch = (M + 15) / 16;
   if (nch > max_chunks) nch = max_chunks;
   if (nch < 1) nch = 1;
   const long long rows_per = (M + nch - 1) / nch;
@@ -1144,6 +1179,22 @@ template hipError_t launch_gather_first_rows<float>(const void*, long long, int,
                                                     hipStream_t);
 template hipError_t launch_gather_first_rows<bf16>(const void*, long long, int, int, const int*, int, int, void*,
                                                    hipStream_t);
+
+template <typename TS>
+hipError_t launch_dw_partials_finish(const float* part, int groups, int K, int H, const int perm[4], void* out,
+                                     void* db, int accumulate, hipStream_t s) {
+  const long long n = (long long)K * H;
+  if (n <= 0 || (!out && !db)) return hipSuccess;
+  Perm4 p4;
+  for (int i = 0; i < 4; ++i) p4.p[i] = perm[i];
+  hipLaunchKernelGGL((dw_partials_finish<TS>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, groups, K,
+                     H, p4, (TS*)out, (TS*)db, accumulate);
+  return hipGetLastError();
+}
+template hipError_t launch_dw_partials_finish<float>(const float*, int, int, int, const int*, void*, void*, int,
+                                                     hipStream_t);
+template hipError_t launch_dw_partials_finish<bf16>(const float*, int, int, int, const int*, void*, void*, int,
+                                                    hipStream_t);
 
 hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s) {
   if (n <= 0) return hipSuccess;

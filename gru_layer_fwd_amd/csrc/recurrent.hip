@@ -96,8 +96,15 @@ constexpr int ST_TIMEOUT = -5;
 // plain stores when the whole batch group shares one XCD's L2 (`local`) and
 // device-scope stores otherwise. Data that only the owning workgroup or a
 // later kernel reads (saved gates, cell states) always uses plain stores.
+// `idle` (optional) is work that does not depend on the counters: it runs
+// once, while the first poll is in flight.
+struct NoIdle {
+  __device__ void operator()() const {}
+};
+template <typename Idle = NoIdle>
 __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int* status, long long timeout,
-                                           int stride = 1, bool pipe = false) {
+                                           int stride = 1, bool pipe = false, Idle idle = Idle()) {
+  constexpr bool HOOK = !std::is_same<Idle, NoIdle>::value;
   const int lane = threadIdx.x & 63;
   if (timeout < 0) {
     // a limit of no time at all (set from the host to exercise the error
@@ -106,6 +113,17 @@ __device__ __forceinline__ void wait_flags(const int* f, int n, int target, int*
     return;
   }
   long long t0 = 0;
+  if constexpr (HOOK) {
+    // one poll (lanes past n read counter 0) in flight while `idle` runs
+    const int v = __hip_atomic_load(f + (lane < n ? lane : 0) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_sched_barrier(0);
+    idle();
+    __builtin_amdgcn_sched_barrier(0);
+    if (n <= 64 && __all(v >= target)) {
+      asm volatile("" ::: "memory");
+      return;
+    }
+  }
   if (pipe && n <= 64) {
     // One counter per lane, two polls in flight: a new poll is issued as
     // soon as the older one has been checked, so a counter set while one
@@ -325,9 +343,16 @@ __device__ __forceinline__ uint4 rot8(const uint4& v) { return make_uint4(rot8(v
 struct NoMid {
   __device__ void operator()() const {}
 };
-template <typename TS, int MB, int NT, int KI, typename Mid = NoMid>
+// `after` (packed tiles only) runs once the products are issued, with this
+// wave's tiles: tile i holds k-step 2i in lanes 0-7 of each 16 and 2i+1 in
+// lanes 8-15
+struct NoAfter {
+  template <typename V>
+  __device__ void operator()(const V&) const {}
+};
+template <typename TS, int MB, int NT, int KI, typename Mid = NoMid, typename After = NoAfter>
 __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const char* xb, int nbytes,
-                                           bool packed, Mid mid = Mid()) {
+                                           bool packed, Mid mid = Mid(), After after = After()) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, nbytes, BUF_RSRC_W3);
   if constexpr (MB == 1 && KI % 2 == 0) {
@@ -352,6 +377,7 @@ __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], odd, Wr[nt][2 * i + 1]);
       }
+      after(v);
       return;
     }
   }
@@ -961,13 +987,31 @@ __device__ __forceinline__ void att_rows(const float* attl, float* part, int t, 
 // HS units. Steps are processed in the reverse of the forward order.
 // RING as for the forward kernels: the ring variant carries no code of the
 // row-read path.
-template <int CELL, typename TS, int NW, int MB, int NT, int KI, bool RING>
+// FDW (fp32, packed ring of one row tile): the kernel also accumulates the
+// recurrent-weight gradient dW_hh[k][J] += sum_b dG'_{t+1}[b][k] h_t[b][J]
+// for its own units J over all contraction rows k, one 16x16x4 fp32 MFMA per
+// 16 rows of k, 16 units and 4 batch rows. dG' is the ring tile the wave has
+// just contracted, kept in LDS transposed to batch-major lanes (one 16-byte
+// write per lane); h_t is the previous state each unit's epilogue used,
+// kept in LDS per step parity. The products for the tiles of one step run
+// two steps later, while the first poll of that step's wait is in flight;
+// the last step's right after its contraction. The
+// recurrent bias gradient (the same dG' summed over rows and steps) is
+// summed per unit in registers. Both go to a.dwp as per-group partials at
+// the end: [nGroups][K][H] then [nGroups][K].
+template <int CELL, typename TS, int NW, int MB, int NT, int KI, bool RING, bool FDW = false>
 __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   constexpr int NTH = NW * 64, BG = MB * 16, HS = NT * 16;
   constexpr int GK = (CELL == CELL_LSTM) ? 4 : 3;
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
+  static_assert(!FDW || (RING && MB == 1 && sizeof(TS) == 4 && KI % 2 == 0 && NW >= GK),
+                "fused dW: fp32 packed ring (and LDS for the bias partials)");
   extern __shared__ float red[];
+  // fused dW: h_{t-1} of the units per step parity, and per wave its ring
+  // tiles of the last contraction as [16 rows: batch row + 8 * k-step parity][16 k]
+  __shared__ float hbuf[FDW ? 2 * BG * HS : 1];
+  __shared__ float xtr[FDW ? NW * (KI / 2) * 256 : 1];
   STEP_TIMER_DECL;
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
@@ -1048,8 +1092,9 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   // cell-state lane rebuilt into dG (recomputation) is read two steps before
   // the deferred store that overwrites it.
   constexpr bool PIPE = RING && MB < 4;
+  constexpr bool HH = FDW && CELL == CELL_LSTM;  // the LSTM's h_{t-1} for the fused dW
   auto prefetch = [&](int pn, TS (&qdy)[UPT], TS (&qz)[UPT][4], TS (&qc)[UPT], TS (&qprev)[UPT], TS (&qa)[UPT],
-                      bool (&qvalid)[UPT]) {
+                      bool (&qvalid)[UPT], TS (&qhh)[UPT], bool (&qhv)[UPT]) {
     const int ps = T - 1 - pn;
     const int pt = a.dir ? T - 1 - ps : ps;
     const int ptp = a.dir ? pt + 1 : pt - 1;
@@ -1080,6 +1125,12 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         const TS* cprev = (first && a.c0) ? (const TS*)a.c0 + o
                         : (const TS*)a.cbuf + (first || !on || !inseq ? 0 : ((long long)ptp * B + b0 + bl_[u]) * a.ldc + jj);
         qprev[u] = *cprev;
+        if constexpr (HH) {
+          qhv[u] = on && (!first || a.h0);
+          const TS* hprev = (first && a.h0) ? (const TS*)a.h0 + o
+                          : (const TS*)a.y + (first || !on || !inseq ? 0 : ((long long)ptp * B + b0 + bl_[u]) * a.ldy + jj);
+          qhh[u] = *hprev;
+        }
       } else {
         qc[u] = from_f<TS>(0.f);
         qvalid[u] = on && (!first || a.h0);
@@ -1104,31 +1155,106 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
       for (int g = 0; g < 4; ++g) bstore<TS>(rg, og + g * H * SZ, qdv[u][g]);
     }
   };
-  TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT], pa[UPT];  // operands of the current step
-  bool pvalid[UPT];
+  TS pdy[UPT], pz[UPT][4], pc[UPT], pprev[UPT], pa[UPT], phh[UPT];  // operands of the current step
+  bool pvalid[UPT], phv[UPT];
   float ddv[UPT][4];  // the previous step's deferred gate gradients (PIPE)
-  if constexpr (PIPE) prefetch(0, pdy, pz, pc, pprev, pa, pvalid);
+  if constexpr (PIPE) prefetch(0, pdy, pz, pc, pprev, pa, pvalid, phh, phv);
+  // fused dW: this wave's accumulators (k-step kl of its range, unit tile nt)
+  f4 dw[FDW ? KI : 1][FDW ? NT : 1];
+  float* xw = xtr + (FDW ? (tid >> 6) * (KI / 2) * 256 : 0);
+  float dbacc[UPT][FDW ? 4 : 1];  // fused db_hh: this thread's units, summed over steps
+#pragma unroll
+  for (int u = 0; u < UPT; ++u)
+#pragma unroll
+    for (int g = 0; g < (FDW ? 4 : 1); ++g) dbacc[u][g] = 0.f;
+  if constexpr (FDW) {
+#pragma unroll
+    for (int i = 0; i < KI; ++i)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) dw[i][nt] = f4{0.f, 0.f, 0.f, 0.f};
+    // rows past the group stay zero (the first step's barrier orders this
+    // before any epilogue writes)
+    for (int i = tid; i < 2 * BG * HS; i += NTH) hbuf[i] = 0.f;
+  }
+  // keep this wave's ring tiles: ring lane L holds row L%8 of k-step parity
+  // (L/8)%2, k = 4(L/16)..+3 of the 16 in the k-step
+  auto keep_tiles = [&](const auto& v) {
+    if constexpr (FDW) {
+      const int lane = tid & 63;
+#pragma unroll
+      for (int i = 0; i < KI / 2; ++i) *(uint4*)(xw + i * 256 + (lane & 15) * 16 + 4 * (lane >> 4)) = v[i];
+    }
+  };
+  // dW_hh[k][J] += sum_b dG'[b][k] h[b][J] over the kept tiles, with h from hb:
+  // A[m = k][kk = b] and B[kk = b][n = unit], 4 batch rows per product (one
+  // set of products for groups of 4 rows, two for 8). Straight-line code:
+  // every LDS read is issued before the first product waits.
+  auto dw_rows = [&](const float* hb, auto nhq) {
+    constexpr int NHQ = decltype(nhq)::value;
+    const int lane = tid & 63, rowsg = bend - b0;
+    float hv[NHQ][NT], av[KI][NHQ];
+#pragma unroll
+    for (int hq = 0; hq < NHQ; ++hq)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) hv[hq][nt] = hb[((lane >> 4) + 4 * hq) * HS + nt * 16 + (lane & 15)];
+#pragma unroll
+    for (int i = 0; i < KI / 2; ++i)
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int hq = 0; hq < NHQ; ++hq) {
+          const int bb = (lane >> 4) + 4 * hq;
+          const float x = xw[i * 256 + (bb + 8 * half) * 16 + (lane & 15)];
+          av[2 * i + half][hq] = bb < rowsg ? x : 0.f;  // ring rows past the group hold stale data
+        }
+#pragma unroll
+    for (int hq = 0; hq < NHQ; ++hq)
+#pragma unroll
+      for (int kl = 0; kl < KI; ++kl)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          dw[kl][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kl][hq], hv[hq][nt], dw[kl][nt], 0, 0, 0);
+  };
+  auto dw_accumulate = [&](const float* hb) {
+    if constexpr (FDW) {
+      if (a.bg > 4) dw_rows(hb, std::integral_constant<int, 2>());
+      else dw_rows(hb, std::integral_constant<int, 1>());
+    }
+  };
 
   STEP_TIMER_CAL(0);
   for (int n = 0; n <= T; ++n) {
     STEP_TIMER(n, 0);
     const int s = T - 1 - n;  // processing index of this step (-1: the final dh0 contraction)
     const int t = a.dir ? T - 1 - s : s;
-    if constexpr (!PIPE) prefetch(n, pdy, pz, pc, pprev, pa, pvalid);
-    TS ndy[UPT], nz[UPT][4], nc[UPT], nprev[UPT], na[UPT];  // the next step's operands (PIPE)
-    bool nvalid[UPT];
+    if constexpr (!PIPE) prefetch(n, pdy, pz, pc, pprev, pa, pvalid, phh, phv);
+    TS ndy[UPT], nz[UPT][4], nc[UPT], nprev[UPT], na[UPT], nhh[UPT];  // the next step's operands (PIPE)
+    bool nvalid[UPT], nhv[UPT];
     auto mid = [&]() {
       if constexpr (PIPE) {
-        prefetch(n + 1 < T ? n + 1 : T - 1, ndy, nz, nc, nprev, na, nvalid);
+        prefetch(n + 1 < T ? n + 1 : T - 1, ndy, nz, nc, nprev, na, nvalid, nhh, nhv);
         post_stores(n > 0 ? n - 1 : 0, n > 0, ddv);
       }
     };
     f4 acc[MB][NT];
     zero_acc(acc);
     if (n > 0) {
-      wait_flags(gflags + ws0 * fstride, wsn, n, a.status, a.timeout_ticks, fstride, CELL == CELL_LSTM && MB < 4 && local);
+      // fused dW: the tiles the last contraction kept (dG' of step n-2) with
+      // the state that step followed, while the first poll is in flight
+      auto idle = [&]() {
+        if constexpr (FDW) {
+          if (n >= 2) dw_accumulate(hbuf + (n & 1) * BG * HS);
+        }
+      };
+      if constexpr (FDW)
+        wait_flags(gflags + ws0 * fstride, wsn, n, a.status, a.timeout_ticks, fstride,
+                   CELL == CELL_LSTM && MB < 4 && local, idle);
+      else
+        wait_flags(gflags + ws0 * fstride, wsn, n, a.status, a.timeout_ticks, fstride,
+                   CELL == CELL_LSTM && MB < 4 && local);
       STEP_TIMER(n, 1);
-      if constexpr (PIPE) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed, mid);
+      if constexpr (FDW) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed, mid, keep_tiles);
+      else if constexpr (PIPE) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed, mid);
       else if constexpr (RING) contract_x<TS, MB, NT, KI>(acc, Wr, xslot(n - 1), xbytes, packed);
       if constexpr (!RING) {
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);  // step whose dG feeds this one
@@ -1152,6 +1278,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         if (a.dh0) ((TS*)a.dh0)[o] = from_f<TS>(dh0);
         if (CELL == CELL_LSTM && a.dc0) ((TS*)a.dc0)[o] = from_f<TS>(dcar[u]);
       }
+      if constexpr (FDW) dw_accumulate(hbuf + ((T - 1) & 1) * BG * HS);
       break;
     }
     float dv[UPT][4];
@@ -1177,10 +1304,17 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         const float d_g = act ? dc * ig * (1.f - gg * gg) : 0.f;
         dcar[u] = act ? dc * fg : dcar[u];
         hcar[u] = act ? 0.f : dh_in;
+        if constexpr (HH) hbuf[(n & 1) * BG * HS + bl_[u] * HS + j_[u]] = phv[u] ? to_f(phh[u]) : 0.f;
         dv[u][0] = d_i;
         dv[u][1] = d_f;
         dv[u][2] = d_g;
         dv[u][3] = d_o;
+        if constexpr (FDW) {
+          dbacc[u][0] += d_i;
+          dbacc[u][1] += d_f;
+          dbacc[u][2] += d_g;
+          dbacc[u][3] += d_o;
+        }
         if (umaj) {
           // the unit's four gradients: rows 4jj..4jj+3, adjacent in the tile
           char* xs = xslot(n);
@@ -1209,6 +1343,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
       } else {
         const float r = to_f(pz[u][0]), uu = to_f(pz[u][1]), c = to_f(pz[u][2]), nh = to_f(pz[u][3]);
         const float hp = pvalid[u] ? to_f(pprev[u]) : 0.f;
+        if constexpr (FDW) hbuf[(n & 1) * BG * HS + bl_[u] * HS + j_[u]] = hp;
         // AUGRU: the state update uses the scaled gate us = (1 - att) * uu
         const float sa = a.att ? 1.f - to_f(pa[u]) : 1.f;
         const float us = sa * uu;
@@ -1223,6 +1358,11 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         dv[u][1] = d_u;
         dv[u][2] = d_c;  // input side only: read by later kernels
         dv[u][3] = d_c * r;
+        if constexpr (FDW) {
+          dbacc[u][0] += d_r;
+          dbacc[u][1] += d_u;
+          dbacc[u][2] += d_c * r;  // the recurrent candidate row's gradient
+        }
         if (!tiled) gr[2 * H] = from_f<TS>(d_c);
         if (tiled) {
           char* xs = xslot(n);
@@ -1254,6 +1394,10 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
         pprev[u] = nprev[u];
         pa[u] = na[u];
         pvalid[u] = nvalid[u];
+        if constexpr (HH) {
+          phh[u] = nhh[u];
+          phv[u] = nhv[u];
+        }
       }
     } else if (tiled) {
       // gate gradients for the later kernels (the ring carried the exchange)
@@ -1266,6 +1410,42 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
       }
     }
     STEP_TIMER(n, 7);
+  }
+  if constexpr (FDW) {
+    // this group's partial dW_hh: rows of the wave's k-steps, the slice's units
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int kl = 0; kl < KI; ++kl) {
+      const int k = (w * KI + kl) * 16 + 4 * (lane >> 4);
+      if (k >= K) break;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int c = J0 + nt * 16 + (lane & 15);
+        float* o = a.dwp + ((long long)grp * K + k) * H + c;
+        if (c < H) {
+          o[0] = dw[kl][nt].x;
+          o[H] = dw[kl][nt].y;
+          o[2 * H] = dw[kl][nt].z;
+          o[3 * H] = dw[kl][nt].w;
+        }
+      }
+    }
+    // bias partial: the units' sums over the group's rows, in row order
+    __syncthreads();  // the last step's reads of red are done
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      const int unit = tid + u * NTH;
+      if (unit < UNITS)
+#pragma unroll
+        for (int g = 0; g < GK; ++g) red[(g * BG + bl_[u]) * HS + j_[u]] = dbacc[u][g];
+    }
+    __syncthreads();
+    for (int i = tid; i < GK * HS; i += NTH) {
+      const int g = i / HS, j = i - g * HS;
+      float sum = 0.f;
+      for (int r = 0; r < BG; ++r) sum += red[(g * BG + r) * HS + j];
+      if (J0 + j < H) a.dwp[(long long)a.nGroups * K * H + (long long)grp * K + g * H + J0 + j] = sum;
+    }
   }
   STEP_TIMER_CAL(1);
   STEP_TIMER_FLUSH(T + 1);
@@ -1486,6 +1666,7 @@ struct Entry {
   int cell, dtype, fwd, nw, mb, nt, ki, kib;
   const void* func;
   const void* func_plain;  // variant without an exchange ring (NULL: basic GRU, func serves both)
+  const void* func_fdw;    // backward ring variant with the fused dW_hh (NULL: none)
 };
 
 #define F_LSTM(TS, NW, MB, NT, KI) \
@@ -1496,6 +1677,9 @@ struct Entry {
   (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI, true>, (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI, false>
 #define B_GRA(TS, NW, MB, NT, KI) \
   (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI, true>, (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI, false>
+#define B_LSTM_FDW(TS, NW, MB, NT, KI) B_LSTM(TS, NW, MB, NT, KI), (const void*)rec_bwd<CELL_LSTM, TS, NW, MB, NT, KI, true, true>
+#define B_GRA_FDW(TS, NW, MB, NT, KI) \
+  B_GRA(TS, NW, MB, NT, KI), (const void*)rec_bwd<CELL_GRU_RA, TS, NW, MB, NT, KI, true, true>
 
 // dtype 0 = fp32, 1 = bf16
 const Entry kTable[] = {
@@ -1525,14 +1709,14 @@ const Entry kTable[] = {
     {CELL_LSTM, 1, 0, 8, 4, 1, 32, 0, B_LSTM(bf16, 8, 4, 1, 32)},
     {CELL_LSTM, 0, 0, 4, 1, 1, 32, 0, B_LSTM(float, 4, 1, 1, 32)},
     {CELL_LSTM, 0, 0, 8, 1, 1, 16, 0, B_LSTM(float, 8, 1, 1, 16)},
-    {CELL_LSTM, 0, 0, 4, 1, 1, 8, 0, B_LSTM(float, 4, 1, 1, 8)},
+    {CELL_LSTM, 0, 0, 4, 1, 1, 8, 0, B_LSTM_FDW(float, 4, 1, 1, 8)},
     // backward reset-after GRU
     {CELL_GRU_RA, 1, 0, 4, 1, 1, 32, 0, B_GRA(bf16, 4, 1, 1, 32)},
     {CELL_GRU_RA, 1, 0, 8, 1, 2, 16, 0, B_GRA(bf16, 8, 1, 2, 16)},
     {CELL_GRU_RA, 1, 0, 4, 4, 1, 48, 0, B_GRA(bf16, 4, 4, 1, 48)},
     {CELL_GRU_RA, 0, 0, 4, 1, 1, 32, 0, B_GRA(float, 4, 1, 1, 32)},
-    {CELL_GRU_RA, 0, 0, 4, 1, 1, 12, 0, B_GRA(float, 4, 1, 1, 12)},
-    {CELL_GRU_RA, 0, 0, 8, 1, 1, 6, 0, B_GRA(float, 8, 1, 1, 6)},
+    {CELL_GRU_RA, 0, 0, 4, 1, 1, 12, 0, B_GRA_FDW(float, 4, 1, 1, 12)},
+    {CELL_GRU_RA, 0, 0, 8, 1, 1, 6, 0, B_GRA_FDW(float, 8, 1, 1, 6)},
     // backward basic GRU (ki = phase A k-steps, kib = phase B)
     {CELL_GRU_BASIC, 1, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<bf16, 4, 1, 1, 16, 8>},
     {CELL_GRU_BASIC, 0, 0, 4, 1, 1, 16, 8, (const void*)rec_bwd_grub<float, 4, 1, 1, 16, 8>},
@@ -1628,6 +1812,23 @@ double step_cost(const Entry& e, int bg, int span, int H, int K, int kstep, int 
   return hand + mfma + data + 0.2 * upt;
 }
 
+// Fused dW_hh (fp32): each wave adds one 16x16x4 MFMA (32 cycles) per
+// k-step, unit tile and 4 batch rows per step; they run while the workgroup
+// waits for the next step, so only what exceeds the modelled step time
+// outside the contraction shows.
+double fused_dw_us(const Entry& e, int bg, int K, double step_us, int kstep) {
+  const int ks = (K + kstep - 1) / kstep;
+  int worst = 0;
+  for (int sm = 0; sm < 4; ++sm) {
+    int sum = 0;
+    for (int w = sm; w < e.nw; w += 4) sum += std::min(e.ki, std::max(0, ks - w * e.ki));
+    worst = std::max(worst, sum);
+  }
+  const double dw = worst * e.nt * ((bg + 3) / 4) * 32.0 / 2.4e3;
+  const double slack = step_us - contraction_us(e.nw, e.ki, e.nt * e.mb, K, kstep);
+  return std::max(0.0, dw - slack);
+}
+
 bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, RecPlan* p) {
   const int kstep = dtype ? 32 : 16;
   const int esize = dtype ? 2 : 4;
@@ -1655,10 +1856,12 @@ bool choose(int cell, int dtype, int fwd, int B, int H, int cu_count, int xcds, 
       const int per_xcd = padded_per_xcd(groups, slices, xcds, cu_count);
       const int span = per_xcd > 0 ? 1 : xcd_span(nwg, slices, xcds);
       const double cost = step_cost(e, bg, span, H, K, kstep, esize, ring);
-      if (cost < best) {
+      // on a tie, the entry with the fused dW_hh variant
+      const bool fdw = e.func_fdw && ring && bg <= 8;
+      if (cost < best - 1e-9 || (found && cost < best + 1e-9 && fdw && !p->func_fdw)) {
         best = cost;
         *p = RecPlan{e.nw, e.mb, e.nt, e.ki, hs, groups, slices, bg, cost, e.func, lds_of(e), span, e.func_plain,
-                     per_xcd, xcds};
+                     per_xcd, fdw ? e.func_fdw : nullptr, fdw ? fused_dw_us(e, bg, K, cost, kstep) : 0.0, xcds};
         found = true;
       }
     }
@@ -1681,8 +1884,14 @@ long long launch_blocks(const RecPlan& p, bool dual) {
 }
 
 int max_coresident(const RecPlan& p) {
+  // the least of the variants a launch of the plan may run
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, p.func, p.nw * 64, p.lds_bytes) != hipSuccess) return 0;
+  for (const void* f : {p.func, p.func_plain, p.func_fdw}) {
+    if (!f) continue;
+    int m = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&m, f, p.nw * 64, p.lds_bytes) != hipSuccess) return 0;
+    n = (f == p.func) ? m : std::min(n, m);
+  }
   return n;
 }
 
@@ -1704,6 +1913,13 @@ hipError_t launch_exchange_probe(const RecPlan& p, const RecLaunch& L, int dtype
 hipError_t launch_rec(const RecPlan& p, const RecLaunch& L, hipStream_t s) {
   // LSTM and reset-after GRU kernels come in a ring and a row-read variant
   const void* f = (p.func_plain && L.d[0].xbuf == nullptr) ? p.func_plain : p.func;
+  // fused dW_hh: the plan's variant, packed ring tiles, in every direction
+  const bool fdw = L.d[0].dwp != nullptr;
+  if (fdw || (L.dual && L.d[1].dwp != nullptr)) {
+    if (!p.func_fdw || L.d[0].xbuf == nullptr || !L.d[0].xpacked || (L.dual && (L.d[1].dwp == nullptr || !L.d[1].xpacked)))
+      return hipErrorInvalidValue;
+    f = p.func_fdw;
+  }
   hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds_bytes);
   if (e != hipSuccess) return e;
   const int n = p.nGroups * p.nSlices;

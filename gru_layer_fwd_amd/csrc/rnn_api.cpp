@@ -34,7 +34,8 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : (d->direction =
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, wht, dgt, xt, ht, total;
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, wht, dgt, xt, ht, dwp, dwp_bytes,
+      total;
   size_t gemm_floats;
   int GZ, GD;
 };
@@ -51,6 +52,7 @@ bool desc_ok(const rnn_desc_t* d) {
   if (d->mode == RNN_GRU && d->reset_after != 0 && d->reset_after != 1) return false;
   if (d->att && d->mode != RNN_GRU) return false;  // attention scores scale the GRU update gate
   if (d->recompute != 0 && !(d->recompute == 1 && d->mode == RNN_LSTM)) return false;
+  if (d->dw_hh_mode != 0 && d->dw_hh_mode != 1) return false;
   if (d->T < 1 || d->B < 1 || d->I < 1 || d->H < 1) return false;
   const int G = gates(d);
   int seen = 0;
@@ -93,6 +95,15 @@ long long counter_ints(const rnn::RecPlan& plan) {
   counter_layout(plan, &stride, &place);
   const long long nwg = (long long)plan.nGroups * plan.nSlices;
   return std::max((long long)place + nwg, nwg * stride);
+}
+
+// shapes whose backward plans can carry the fused dW_hh variant (the fp32
+// plans of 4 waves with 8 or 12 k-steps each, and 8 waves with 6: there the
+// accumulators fit beside the resident W_hh without spilling)
+bool fused_dw_shape(const rnn_desc_t* d) {
+  if (d->dtype != RNN_F32 || d->dw_hh_mode != 0) return false;
+  const int cell = cell_of(d);
+  return (cell == rnn::CELL_LSTM && d->H <= 128) || (cell == rnn::CELL_GRU_RA && d->H <= 256);
 }
 
 Layout layout(const rnn_desc_t* d) {
@@ -163,6 +174,14 @@ Layout layout(const rnn_desc_t* d) {
     off += up(TB * (size_t)d->I * s);
     L.ht = off;
     off += up(TB * H * s);
+  }
+  // fp32 reset-after GRU (H <= 256) and LSTM (H <= 128): per batch group
+  // (>= 4 rows) partial recurrent-weight gradients of the fused BPTT kernel
+  L.dwp = off;
+  L.dwp_bytes = 0;
+  if (fused_dw_shape(d)) {
+    L.dwp_bytes = (size_t)((d->B + 3) / 4) * (cell == rnn::CELL_LSTM ? 4 : 3) * H * (H + 1) * sizeof(float);
+    off += up(L.dwp_bytes);
   }
   L.total = off;
   return L;
@@ -332,18 +351,38 @@ hipError_t colsum_dt(int dtype, const void* src, long long lds, long long M, int
 
 // Exchange ring for single row-tile plans; K = contraction length of the
 // exchanged vector. Pairs of k-steps share a tile when groups have <= 8 rows.
-void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws, long long K, size_t esize) {
-  a.xbuf = nullptr;
-  a.xg_bytes = 0;
-  a.xpacked = 0;
-  if (p.bg > 16 * p.mb) return;
-  if ((K * (long long)esize) % 64 != 0) return;  // whole k-steps only
+// Returns 0 (no ring: the kernels read rows of y / dG), 1 (tiled) or 2 (packed).
+int ring_kind(const rnn::RecPlan& p, const Layout& L, long long K, size_t esize) {
+  if (p.bg > 16 * p.mb) return 0;
+  if ((K * (long long)esize) % 64 != 0) return 0;  // whole k-steps only
   const long long gbytes = K * 16 * (long long)p.mb * (long long)esize;  // a 1 KiB tile per (k-step, row tile)
-  if ((size_t)(2 * p.nGroups * gbytes) > L.xb_bytes) return;
+  if ((size_t)(2 * p.nGroups * gbytes) > L.xb_bytes) return 0;
   const long long ksteps = K * (long long)esize / 64;
-  a.xpacked = (p.mb == 1 && p.bg <= 8 && ksteps % 2 == 0 && p.ki % 2 == 0) ? 1 : 0;
-  a.xg_bytes = gbytes;
-  a.xbuf = ws + L.xb;
+  return (p.mb == 1 && p.bg <= 8 && ksteps % 2 == 0 && p.ki % 2 == 0) ? 2 : 1;
+}
+void set_xbuf(rnn::RecArgs& a, const rnn::RecPlan& p, const Layout& L, char* ws, long long K, size_t esize) {
+  const int kind = ring_kind(p, L, K, esize);
+  a.xbuf = kind ? ws + L.xb : nullptr;
+  a.xg_bytes = kind ? K * 16 * (long long)p.mb * (long long)esize : 0;
+  a.xpacked = kind == 2 ? 1 : 0;
+}
+
+// Whether the BPTT kernel of backward plan p accumulates dW_hh for (half)
+// descriptor d: a plan with the fused variant on a packed ring, room for the
+// partials, and the modelled cost of the extra per-step products (what the
+// wait does not hide, plus the partial sums) below that of the separate
+// product it replaces (~15 us per launch it saves, at ~50 TFLOP/s).
+bool fused_dw(const rnn_desc_t* d, const rnn::RecPlan& p) {
+  if (!fused_dw_shape(d) || !p.func_fdw) return false;
+  const Layout L = layout(d);
+  const long long K = (long long)(cell_of(d) == rnn::CELL_LSTM ? 4 : 3) * d->H;
+  if (ring_kind(p, L, K, esz(d)) != 2) return false;
+  const double part = (double)p.nGroups * K * (d->H + 1) * sizeof(float);
+  if (part > (double)L.dwp_bytes) return false;
+  const int launches = cell_of(d) == rnn::CELL_LSTM ? (d->I % 256 == 0 ? 0 : 1) : 2;
+  const double saved = 15.0 * launches + 2.0 * K * d->H * (double)d->T * d->B / 50e6;
+  const double cost = d->T * p.fdw_us + 5.0 + part / 4e6;
+  return cost < saved;
 }
 
 // A persistent grid is launched only when every workgroup can be resident at
@@ -391,6 +430,15 @@ bool choose_plan(F planner, bool bidir, const DevInfo& di, rnn::RecPlan* plan, b
     return true;
   }
   return planner(di.cu, 8, plan);
+}
+
+// The backward plan of d (both calls of the backward pass choose it here).
+int bwd_plan(const rnn_desc_t* d, const DevInfo& di, rnn::RecPlan* plan, bool* dual) {
+  const int cell = cell_of(d);
+  if (!choose_plan([&](int cu, int xcds, rnn::RecPlan* p) { return rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p); },
+                   d->direction == 2, di, plan, dual))
+    return RNN_ERR_UNSUPPORTED;
+  return RNN_OK;
 }
 
 int run_persistent(const rnn::RecPlan& plan, bool dual, int halves, const rnn::RecArgs (&args)[2],
@@ -639,6 +687,7 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
   a.att = d->att;
   a.datt_part = (float*)(ws + L.attp);
   if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, ws, (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H, esz(d));
+  a.dwp = fused_dw(d, plan) ? (float*)(ws + L.dwp) : nullptr;
   // W_hh transposed into the contraction order of the BPTT kernel (unit-major
   // rows for the bf16 LSTM ring, gate-major otherwise), so that the kernel
   // loads its operands as rows instead of one element per load. Measured: at
@@ -814,9 +863,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   const int halves = bidir ? 2 : 1;
   rnn::RecPlan plan;
   bool dual;
-  if (!choose_plan([&](int cu, int xcds, rnn::RecPlan* p) { return rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p); },
-                   bidir, di, &plan, &dual))
-    return RNN_ERR_UNSUPPORTED;
+  if ((st = bwd_plan(d, di, &plan, &dual))) return st;
   // the score-gradient shares of a workgroup's units sit after its reduction buffer
   if (d->att) plan.lds_bytes += (size_t)plan.mb * 16 * plan.Hs * sizeof(float);
   hipStream_t s = (hipStream_t)stream;
@@ -839,32 +886,12 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   return RNN_OK;
 }
 
-RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, const void* y, void* dW_ih,
-                            void* dW_hh, void* db_ih, void* db_hh, int accumulate, void* workspace,
-                            size_t ws_bytes, void* stream) {
-  int st = check_common(d, workspace, ws_bytes);
-  if (st) return st;
-  if (!x || !y) return RNN_ERR_INVALID_ARG;
-  const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh, d->lengths};
-  for (const void* p : ptrs)
-    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
-  if (d->direction == 2) {
-    // the two halves in turn, each over its own workspace half and [2][...] slice
-    const size_t es = esz(d);
-    const long long G = gates(d), H = d->H, BH = (long long)d->B * d->H;
-    for (int k = 0; k < 2; ++k) {
-      const rnn_desc_t h = half_desc(d, k);
-      const size_t hb = layout(&h).total;
-      if ((st = rnn_bwd_weights(&h, x, at(h0, k * BH, es), at(y, k * H, es), at(dW_ih, k * G * H * d->I, es),
-                                at(dW_hh, k * G * H * H, es), at(db_ih, k * G * H, es), at(db_hh, k * G * H, es),
-                                accumulate, (char*)workspace + k * hb, hb, stream)))
-        return st;
-    }
-    return RNN_OK;
-  }
-  DevInfo di;
-  if ((st = dev_info(&di))) return st;
-  g_cu_count = di.cu;
+namespace {
+// Weight gradients of one direction. fused_groups > 0: the BPTT kernel left
+// that many per-group dW_hh partials in the workspace.
+int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const void* y, void* dW_ih, void* dW_hh,
+                    void* db_ih, void* db_hh, int accumulate, void* workspace, void* stream, int fused_groups) {
+  int st;
   const Layout L = layout(d);
   const int cell = cell_of(d);
   hipStream_t s = (hipStream_t)stream;
@@ -917,7 +944,8 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   // LSTM with both weight gradients: one product over [x | h_{t-1}] with two
   // output parts (dG is read once, one split-K finish); the bias gradients
   // (equal for the two biases) come from its row sums
-  const bool merged = cell == rnn::CELL_LSTM && dW_ih && dW_hh && d->I % 256 == 0;
+  const bool fused = fused_groups > 0;
+  const bool merged = cell == rnn::CELL_LSTM && dW_ih && dW_hh && d->I % 256 == 0 && !fused;
   if (merged && nt_weight_grads(d)) {
     // the same product with k-contiguous operands: dG^T (written by the
     // input-gradient product) against x^T and h_{t-1}^T; the bias gradients
@@ -979,7 +1007,16 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   }
   // recurrent side: lanes of dG_h (LSTM: all; GRU: r,u, then the candidate rows)
   const int ccol = (cell == rnn::CELL_GRU_RA) ? 3 * H : 2 * H;  // candidate lane of dG_h
-  if (dW_hh) {
+  if ((dW_hh || db_hh) && fused) {
+    // the per-group partials of the BPTT kernel, summed in group order (the
+    // kernel used each row's own h_{t-1}, so no direction-1 correction)
+    ProfScope ps(L_DW, s);
+    const int K = (cell == rnn::CELL_LSTM ? 4 : 3) * H;
+    if ((st = hip_status(rnn::launch_dw_partials_finish<float>((const float*)(ws + L.dwp), fused_groups, K, H, perm,
+                                                               dW_hh, db_hh, acc, s))))
+      return st;
+  }
+  if (dW_hh && !fused) {
     if (merged) {
       // done above
     } else if (cell == rnn::CELL_LSTM) {
@@ -1030,7 +1067,8 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
         if (cell == rnn::CELL_GRU_RA && (st = hip_status(corr(2LL * H, H, ccol)))) return st;
       }
     }
-  } else if (db_hh) {
+  }
+  if (db_hh && !dW_hh && !fused) {
     if (cell == rnn::CELL_LSTM) {
       if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, 0, 4 * H, db_hh, 0, H, perm, acc, partial, s)))) return st;
     } else {
@@ -1038,6 +1076,43 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
       if ((st = hip_status(colsum_dt(d->dtype, dg, GDH, TB, ccol, H, db_hh, 2 * H, H, perm, acc, partial, s))))
         return st;
     }
+  }
+  return RNN_OK;
+}
+}  // namespace
+
+RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, const void* y, void* dW_ih,
+                            void* dW_hh, void* db_ih, void* db_hh, int accumulate, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  int st = check_common(d, workspace, ws_bytes);
+  if (st) return st;
+  if (!x || !y) return RNN_ERR_INVALID_ARG;
+  const void* ptrs[] = {x, h0, y, dW_ih, dW_hh, db_ih, db_hh, d->lengths};
+  for (const void* p : ptrs)
+    if (p && !aligned(p)) return RNN_ERR_INVALID_ARG;
+  DevInfo di;
+  if ((st = dev_info(&di))) return st;
+  g_cu_count = di.cu;
+  const rnn_desc_t h0d = half_desc(d, 0);
+  int fused_groups = 0;
+  if (fused_dw_shape(&h0d)) {
+    rnn::RecPlan plan;
+    bool dual;
+    if ((st = bwd_plan(d, di, &plan, &dual))) return st;
+    if (fused_dw(&h0d, plan)) fused_groups = plan.nGroups;
+  }
+  if (d->direction != 2)
+    return bwd_weights_dir(d, x, h0, y, dW_ih, dW_hh, db_ih, db_hh, accumulate, workspace, stream, fused_groups);
+  // the two halves in turn, each over its own workspace half and [2][...] slice
+  const size_t es = esz(d);
+  const long long G = gates(d), H = d->H, BH = (long long)d->B * d->H;
+  for (int k = 0; k < 2; ++k) {
+    const rnn_desc_t h = half_desc(d, k);
+    const size_t hb = layout(&h).total;
+    if ((st = bwd_weights_dir(&h, x, at(h0, k * BH, es), at(y, k * H, es), at(dW_ih, k * G * H * d->I, es),
+                              at(dW_hh, k * G * H * H, es), at(db_ih, k * G * H, es), at(db_hh, k * G * H, es),
+                              accumulate, (char*)workspace + k * hb, stream, fused_groups)))
+      return st;
   }
   return RNN_OK;
 }
@@ -1078,6 +1153,7 @@ RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_p
     const long long K = pass == 0 ? d->H : (long long)(cell == rnn::CELL_LSTM ? 4 : 3) * d->H;
     if (cell != rnn::CELL_GRU_BASIC) set_xbuf(a, plan, L, nullptr, K, esz(d));
     out->ring = a.xg_bytes ? (a.xpacked ? 2 : 1) : 0;
+    out->fused_dw = pass == 1 && fused_dw(&h, plan) ? 1 : 0;
   }
   const int occ = wg_per_cu > 0 ? wg_per_cu : rnn::max_coresident(plan);
   return coresidency(plan, dual, occ, di.cu);

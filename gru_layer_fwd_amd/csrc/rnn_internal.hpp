@@ -165,6 +165,13 @@ hipError_t launch_colsum(const void* src, long long lds, long long M, int col0, 
 
 hipError_t launch_fill_i32(int* p, int v, long long n, hipStream_t s);
 
+// dW_hh[perm row of k][c] (+)= sum over g < groups of part[(g*K + k)*H + c],
+// db_hh[perm row of k] (+)= sum of part[groups*K*H + g*K + k] (the BPTT
+// kernel's fused partials; k canonical gate rows; out or db may be NULL)
+template <typename TS>
+hipError_t launch_dw_partials_finish(const float* part, int groups, int K, int H, const int perm[4], void* out,
+                                     void* db, int accumulate, hipStream_t s);
+
 // y[t][b][0..H) = 0 for every step t >= lengths[b] (clamped to [0, T]).
 template <typename TS>
 hipError_t launch_zero_inactive(void* y, long long ldy, const int* lengths, int T, int B, int H, hipStream_t s);
@@ -266,6 +273,7 @@ struct RecArgs {
   const int* lengths;  // per batch row step count (NULL: T); clamped to [0, T]
   const void* att;     // GRU only: AUGRU attention scores [T][B] (NULL: plain GRU)
   float* datt_part;    // backward with att: per-slice partial score gradients [T][B][nSlices]
+  float* dwp;          // backward: fused partials, dW_hh [nGroups][K][H] then db_hh [nGroups][K], fp32 (NULL: not fused)
 };
 
 // Kernel argument of the persistent kernels: one direction (dual = 0), or
@@ -290,6 +298,8 @@ struct RecPlan {
   int xcd_span;         // XCDs a batch group covers (under the launch's block placement)
   const void* func_plain;  // the variant without an exchange ring (NULL: func serves both)
   int per_xcd;          // padded placement (RecLaunch::per_xcd), 0 = natural
+  const void* func_fdw;    // backward ring variant that also accumulates dW_hh (NULL: none)
+  double fdw_us;        // modelled time per step the fused dW_hh products add (not hidden in the wait)
   int xcds;             // XCDs one direction is spread over (8, or 4 in a dual launch)
 };
 

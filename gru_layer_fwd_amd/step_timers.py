@@ -42,9 +42,14 @@ def _timers(lib):
     c = np.zeros(w.value * 4, dtype=np.uint64)
     st = lib.rnn_step_timers_read(t.ctypes.data_as(ctypes.c_void_p), c.ctypes.data_as(ctypes.c_void_p))
     assert st == 0, st
-    # the kernels keep the low 32 bits of the clock per step: unwrap them
+    # the kernels keep the low 32 bits of the clock per step: unwrap them;
+    # points a step does not pass (zero: e.g. the wait of the backward's
+    # first step) take the previous point's time first
     t = t.reshape(w.value, s.value, p.value).astype(np.int64)
     flat = t.reshape(w.value, -1)
+    idx = np.where(flat != 0, np.arange(flat.shape[1])[None, :], 0)
+    np.maximum.accumulate(idx, axis=1, out=idx)
+    flat = np.take_along_axis(flat, idx, axis=1)
     d = np.diff(flat, axis=1)
     d[d < -(1 << 31)] += 1 << 32
     flat[:, 1:] = flat[:, :1] + np.cumsum(d, axis=1)
@@ -56,6 +61,7 @@ def analyse(t, cal, nblocks, nsteps, skip=8):
     calibration pairs) and steps [skip, nsteps - skip)."""
     nblocks = min(nblocks, t.shape[0])
     nsteps = min(nsteps, t.shape[1])
+    skip = min(skip, max(1, nsteps // 4))  # short sequences: fewer steps left out at the ends
     ran = np.nonzero(cal[:nblocks, 0] != 0)[0]
     t, cal = t[ran, :nsteps], cal[ran]
     nwg = len(ran)
@@ -72,6 +78,7 @@ def analyse(t, cal, nblocks, nsteps, skip=8):
     out["first_step"] = float(np.mean(t[:, 1, 0] - t[:, 0, 0])) / ticks_per_ns
     out["clock_ghz"] = ticks_per_ns
     out["steps_averaged"] = int(hi - lo)
+    out["steps_skipped"] = int(skip)
     out["workgroups"] = int(nwg)
     return out
 
@@ -81,6 +88,8 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--out", default=None, help="write the markdown table here as well")
     ap.add_argument("--json", default=None, help="write the numbers as JSON here")
+    ap.add_argument("--separate-dw", action="store_true",
+                    help="dW_hh from the separate product (dw_hh_mode 1), not accumulated in the BPTT kernel")
     args = ap.parse_args()
 
     # torch first: the library then binds to the HIP runtime torch has loaded
@@ -105,7 +114,7 @@ def main():
     W = [dev(getattr(p, k)) for k in ("W_ih", "W_hh", "b_ih", "b_hh")]
     x, g, h0, c0 = dev(inp["x"]), dev(inp["g"]), dev(inp["h0"]), dev(inp["c0"])
     lay = RnnLayer(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, reset_after=wl.reset_after,
-                   gate_order=wl.gate_order())
+                   gate_order=wl.gate_order(), dw_hh_mode=int(args.separate_dw))
     y = torch.empty(wl.T, wl.B, wl.H, dtype=dt, device="cuda")
     dx = torch.empty_like(x)
     grads = [torch.empty_like(w) for w in W]
@@ -114,7 +123,7 @@ def main():
         lay.bwd_data(W[0], W[1], h0, c0, y, g, None, None, dx)
         lay.bwd_weights(x, h0, y, *grads)
     torch.cuda.synchronize()
-    res = {"workload": name}
+    res = {"workload": name, "dw_hh_mode": int(args.separate_dw)}
     for pass_, label in ((0, "forward"), (1, "backward")):
         torch.cuda.synchronize()
         assert lib.rnn_step_timers_reset() == 0
@@ -142,8 +151,10 @@ def main():
         torch.cuda.synchronize()
         if st == 0 and lay.device_status() == 0:
             res[label]["exchange_only_us_per_step"] = e0.elapsed_time(e1) * 1e3 / (reps * wl.T)
-    lines = [f"Per-step phases of the persistent kernels, {name} (debug build with step timers; "
-             f"ns, mean over workgroups and steps {8}..T-8)", "",
+    lines = [f"Per-step phases of the persistent kernels, {name}"
+             + (", dW_hh by the separate product" if args.separate_dw else "")
+             + " (debug build with step timers; ns, mean over workgroups and over the steps away from both"
+             " ends of the sequence)", "",
              "| pass | " + " | ".join(PHASES) + " | step | first step | start-up | exchange only |",
              "|---" * (len(PHASES) + 5) + "|"]
     for label in ("forward", "backward"):

@@ -120,6 +120,15 @@ typedef struct rnn_desc {
                         from them and c0 before BPTT (popnn Lstm.cpp,
                         "cellAndTanh" recomputation): T*B*H fewer workspace
                         elements for one extra elementwise pass. */
+  int dw_hh_mode;     /* 0 = the recurrent-weight gradient is accumulated inside
+                        the BPTT kernel of rnn_bwd_data where its plan allows
+                        (fp32, reset-after GRU or LSTM, batch groups of <= 8
+                        rows; rnn_plan_t.fused_dw) and rnn_bwd_weights only
+                        sums the per-group partials, the weight update folded
+                        into the backward steps as the popnn LSTM/GRU pages'
+                        backward-with-weight-update does; 1 = dW_hh always
+                        from the separate product over the saved gate
+                        gradients. Same value for both backward calls. */
 } rnn_desc_t;
 
 /* Bytes of workspace the three calls need for this descriptor (0 if the
@@ -255,6 +264,9 @@ typedef struct rnn_plan {
   double model_us_per_step; /* the planner's modelled time per step */
   int blocks;       /* blocks launched: workgroups, or more when groups are padded to whole
                        XCDs (the extra blocks return at once) */
+  int fused_dw;     /* pass 1: the BPTT kernel accumulates dW_hh itself (dw_hh_mode 0, a
+                       plan with the fused variant, and the planner's model finding that
+                       its extra per-step products cost less than the separate product) */
 } rnn_plan_t;
 int rnn_plan_query(const rnn_desc_t* desc, int pass, int cu_count, int wg_per_cu, rnn_plan_t* out);
 

@@ -210,3 +210,35 @@ def test_plan_query_argument_errors():
     assert L.rnn_plan_query(d, 0, 256, -1)[0] == L.RNN_ERR_INVALID_ARG
     assert L.lib().rnn_plan_query(ctypes.byref(d), 0, 256, 1, None) == L.RNN_ERR_INVALID_ARG
     assert L.rnn_plan_query(_desc(H=40), 0, 256, 1)[0] == L.RNN_ERR_UNSUPPORTED
+
+
+def test_fused_weight_gradient_plans():
+    """The BPTT kernel accumulates dW_hh for the small fp32 layers (both
+    reset-after GRU and LSTM shapes), not for bf16, the basic GRU or when
+    the descriptor asks for the separate product; the workspace holds the
+    per-group partials only where the fusion can apply."""
+    cases = [
+        # (mode, reset_after, T, B, I, H, dtype, fused)
+        (L.RNN_LSTM, 1, 8, 2, 16, 32, L.RNN_F32, 1),
+        (L.RNN_GRU, 1, 64, 16, 256, 256, L.RNN_F32, 1),
+        (L.RNN_GRU, 0, 64, 16, 256, 256, L.RNN_F32, 0),
+        (L.RNN_LSTM, 1, 256, 64, 1024, 1024, L.RNN_BF16, 0),
+        (L.RNN_LSTM, 1, 512, 32, 512, 512, L.RNN_F32, 0),
+    ]
+    for mode, ra, T, B, I, H, dt, fused in cases:
+        d = g.make_desc(mode, T, B, I, H, dt, reset_after=ra)
+        st, pl = _plan(d, 1)
+        assert st == L.RNN_OK
+        assert pl.fused_dw == fused, (mode, ra, H, dt)
+        st, pl = _plan(d, 0)
+        assert st == L.RNN_OK and pl.fused_dw == 0
+        sep = g.make_desc(mode, T, B, I, H, dt, reset_after=ra, dw_hh_mode=1)
+        st, pl = _plan(sep, 1)
+        assert st == L.RNN_OK and pl.fused_dw == 0
+        n_auto, n_sep = g.rnn_workspace_bytes(d), g.rnn_workspace_bytes(sep)
+        if fused:
+            # ceil(B / 4) groups of K x (H + 1) fp32 partials (dW_hh and db_hh) at most
+            K = (4 if mode == L.RNN_LSTM else 3) * H
+            assert n_sep < n_auto <= n_sep + ((B + 3) // 4) * K * (H + 1) * 4 + 4096
+        bad = g.make_desc(mode, T, B, I, H, dt, reset_after=ra, dw_hh_mode=2)
+        assert g.rnn_workspace_bytes(bad) == 0

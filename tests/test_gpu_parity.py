@@ -464,3 +464,31 @@ def test_handshake_timeout_is_reported_and_recovers(bidir):
         Lb.rnn_set_handshake_timeout(0.0)
     got, ref = _run(wl, inp, P)
     print(compare(got, ref, "f32"))
+
+
+# ------------------------------------------- fused weight gradient -----
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("cell,B,H", [("lstm", 197, 128), ("lstm", 13, 64), ("gru_ra", 83, 256), ("gru_ra", 13, 96)])
+def test_fused_recurrent_weight_gradient(cell, B, H, direction):
+    """dW_hh accumulated inside the BPTT kernel (batch groups of 4 and of 8
+    rows, a ragged last group, rows of length 0, 1, T-1 and T) and dW_hh
+    from the separate product both match the oracle; the plan reports the
+    fused path for these shapes."""
+    from gru_layer_fwd_amd import _lib as L
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    wl, inp, P = _case(name, T=16, B=B, I=64, H=H, w_scale=0.1, h0_std=0.5, c0_std=0.5)
+    d = L.make_desc(L.RNN_LSTM if cell == "lstm" else L.RNN_GRU, wl.T, B, wl.I, H, L.RNN_F32, direction, 1)
+    st, plan = L.rnn_plan_query(d, 1)
+    assert st == 0 and plan.fused_dw == 1 and plan.rows in (4, 8)
+    lens = _ragged_lengths(B, wl.T, 11 + direction)
+    print(f"[fused dW] {cell} B={B} H={H} dir={direction} rows={plan.rows} groups={plan.groups}", flush=True)
+    got, ref = _run(wl, inp, P, direction, lengths=lens, acc=(direction == 1))
+    e_fused = compare(got, ref, "f32", extra=f"fused {cell} B={B} H={H} dir{direction}")
+    sep = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], inp["g"], None, None, direction,
+                    wl.reset_after, None, lengths=lens, dw_hh_mode=1)
+    e_sep = compare(sep, ref, "f32", extra=f"separate {cell} B={B} H={H} dir{direction}")
+    print(f"dW_hh rel err fused {e_fused['dW_hh']:.2e} separate {e_sep['dW_hh']:.2e}")
+    # the rest of the backward pass does not depend on where dW_hh is formed
+    for k in ("dx", "dh0", "dW_ih", "db_ih"):
+        np.testing.assert_array_equal(got[k], sep[k], err_msg=k)
