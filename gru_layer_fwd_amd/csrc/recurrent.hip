@@ -863,6 +863,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
+  STEP_TIMER_DECL;
 
   int grp, sl;
   bool idle;
@@ -900,8 +901,20 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
     if (live[u] && a.lengths) len_[u] = min(max(a.lengths[b0 + bl_[u]], 0), T);
     if (live[u] && a.h0) hst[u] = to_f(((const TS*)a.h0)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
+  // both products contract over H: this wave's rows and the slices producing
+  // them (each wave waits for its own producers only; every step has its own
+  // rows of y and r*h, so nothing is rewritten while a slow wave reads it)
+  int ws0, wsn;
+  {
+    constexpr int KSTEP = 4 * Chunk<TS>::KQ;
+    const int k0 = (tid >> 6) * KI * KSTEP, k1 = min(H, k0 + KI * KSTEP);
+    wave_slices(k0, k1, H, HS, a.nSlices, ws0, wsn);
+  }
+  float sr[UPT], su[UPT], sc[UPT];  // gates stored after the step's counter
 
+  STEP_TIMER_CAL(0);
   for (int s = 0; s < T; ++s) {
+    STEP_TIMER(s, 0);
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
     TS pz[UPT][3], pa[UPT];
@@ -914,7 +927,8 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
       pa[u] = *ap;  // AUGRU attention score of this step and row
     }
     // phase A: r, u
-    if (s > 0) wait_flags(gflags, a.nSlices, 2 * s, a.status, a.timeout_ticks, a.fstride, local);
+    if (s > 0) wait_flags(gflags + ws0 * a.fstride, wsn, 2 * s, a.status, a.timeout_ticks, a.fstride, local);
+    STEP_TIMER(s, 1);
     {
       f4 acc[MB][NTA];
       zero_acc(acc);
@@ -923,6 +937,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
       contract<TS, MB, NTA, KI>(acc, WA, src, ld, b0, bend, H, 1 << 30, 0);
       spill_acc(red, acc, bend - b0);
     }
+    STEP_TIMER(s, 2);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
@@ -934,12 +949,22 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
       const bool act = t < len_[u];
       ust[u] = a.att ? (1.f - to_f(pa[u])) * uu : uu;  // AUGRU: scaled update gate
       xstore((TS*)a.rh + ((long long)t * B + b) * H + J0 + j, r * hst[u], local);
-      zr[0] = from_f<TS>(act ? r : 0.f);
-      zr[H] = from_f<TS>(act ? uu : 0.f);
+      sr[u] = act ? r : 0.f;
+      su[u] = act ? uu : 0.f;
     }
+    STEP_TIMER(s, 3);
     publish(myflag, 2 * s + 1, local);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      if (!live[u]) continue;
+      TS* zr = (TS*)a.z + ((long long)t * B + b0 + bl_[u]) * GZH + J0 + j_[u];
+      zr[0] = from_f<TS>(sr[u]);
+      zr[H] = from_f<TS>(su[u]);
+    }
     // phase B: candidate and new state
-    wait_flags(gflags, a.nSlices, 2 * s + 1, a.status, a.timeout_ticks, a.fstride, local);
+    STEP_TIMER(s, 4);
+    wait_flags(gflags + ws0 * a.fstride, wsn, 2 * s + 1, a.status, a.timeout_ticks, a.fstride, local);
+    STEP_TIMER(s, 5);
     {
       f4 acc[MB][NTB];
       zero_acc(acc);
@@ -947,11 +972,11 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
       spill_acc(red, acc, bend - b0);
     }
     __syncthreads();
+    STEP_TIMER(s, 6);
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
       const int bl = bl_[u], j = j_[u], b = b0 + bl;
-      TS* zr = (TS*)a.z + ((long long)t * B + b) * GZH + J0 + j;
       const float c = tanhf_(red_sum<NW, BG, HS>(red, bl, j) + to_f(pz[u][2]));
       const bool act = t < len_[u];
       // past a row's length the state is kept (and carried through y, which a
@@ -959,11 +984,20 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
       const float h = act ? ust[u] * hst[u] + (1.f - ust[u]) * c : hst[u];
       hst[u] = h;
       xstore((TS*)a.y + ((long long)t * B + b) * a.ldy + J0 + j, h, local);
-      zr[2 * H] = from_f<TS>(act ? c : 0.f);
-      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(h);
+      sc[u] = act ? c : 0.f;
     }
+    STEP_TIMER(s, 7);
     publish(myflag, 2 * s + 2, local);
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      if (!live[u]) continue;
+      const int b = b0 + bl_[u], j = j_[u];
+      ((TS*)a.z + ((long long)t * B + b) * GZH + J0 + j)[2 * H] = from_f<TS>(sc[u]);
+      if (s == T - 1 && a.hT) ((TS*)a.hT)[(long long)b * H + J0 + j] = from_f<TS>(hst[u]);
+    }
   }
+  STEP_TIMER_CAL(1);
+  STEP_TIMER_FLUSH(T);
 }
 
 // AUGRU score gradient: sum the per-unit shares of each batch row (in LDS,
@@ -1460,6 +1494,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
   constexpr int UNITS = BG * HS;
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
+  STEP_TIMER_DECL;
   float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
@@ -1483,6 +1518,16 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
   float hcar[UPT], dhs[UPT], rs[UPT], us[UPT], hps[UPT];
   bool live[UPT];
   int bl_[UPT], j_[UPT], len_[UPT];
+  // this wave's rows of the two products ([d_r | d_u] over 2H, d_c over H)
+  // and the slices producing them: each wave waits for those only
+  int wa0, wan, wb0, wbn;
+  {
+    constexpr int KSTEP = 4 * Chunk<TS>::KQ;
+    const int w = tid >> 6;
+    const int ka = w * KIA * KSTEP, kb = w * KIB * KSTEP;
+    wave_slices(ka, min(2 * H, ka + KIA * KSTEP), H, HS, a.nSlices, wa0, wan);
+    wave_slices(kb, min(H, kb + KIB * KSTEP), H, HS, a.nSlices, wb0, wbn);
+  }
 #pragma unroll
   for (int u = 0; u < UPT; ++u) {
     const int unit = tid + u * NTH;
@@ -1495,7 +1540,9 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
     if (live[u] && a.dhT) hcar[u] = to_f(((const TS*)a.dhT)[(long long)(b0 + bl_[u]) * H + J0 + j_[u]]);
   }
 
+  STEP_TIMER_CAL(0);
   for (int n = 0; n <= T; ++n) {
+    STEP_TIMER(n, 0);
     const int s = T - 1 - n;
     const int t = a.dir ? T - 1 - s : s;
     const int tp = a.dir ? t + 1 : t - 1;
@@ -1523,13 +1570,15 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
       f4 acc[MB][NT];
       zero_acc(acc);
       if (n > 0) {
-        wait_flags(gflags, a.nSlices, 2 * n, a.status, a.timeout_ticks, a.fstride);
+        wait_flags(gflags + wa0 * a.fstride, wan, 2 * n, a.status, a.timeout_ticks, a.fstride, local);
+        STEP_TIMER(n, 1);
         const int tn = a.dir ? T - 1 - (s + 1) : (s + 1);
         contract<TS, MB, NT, KIA>(acc, WA, (const TS*)a.dg + (long long)tn * B * GDH, GDH, b0, bend, 2 * H, 1 << 30,
                                   0);
       }
       spill_acc(red, acc, bend - b0);
     }
+    STEP_TIMER(n, 2);
     __syncthreads();
     if (n == T) {
 #pragma unroll
@@ -1565,9 +1614,12 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
       us[u] = sa * uu;
       hps[u] = hp;
     }
+    STEP_TIMER(n, 3);
     publish(myflag, 2 * n + 1, local);
     if (a.att) att_rows<HS>(attl, a.datt_part, t, B, b0, bend, a.nSlices, sl);
-    wait_flags(gflags, a.nSlices, 2 * n + 1, a.status, a.timeout_ticks, a.fstride);
+    STEP_TIMER(n, 4);
+    wait_flags(gflags + wb0 * a.fstride, wbn, 2 * n + 1, a.status, a.timeout_ticks, a.fstride, local);
+    STEP_TIMER(n, 5);
     {
       f4 acc[MB][NT];
       zero_acc(acc);
@@ -1576,6 +1628,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
       spill_acc(red, acc, bend - b0);
     }
     __syncthreads();
+    STEP_TIMER(n, 6);
 #pragma unroll
     for (int u = 0; u < UPT; ++u) {
       if (!live[u]) continue;
@@ -1586,8 +1639,11 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
       xstore((TS*)a.dg + row * GDH + J0 + j_[u], d_r, local);
       hcar[u] = act ? d_rh * rs[u] + dhs[u] * us[u] : dhs[u];
     }
+    STEP_TIMER(n, 7);
     publish(myflag, 2 * n + 2, local);
   }
+  STEP_TIMER_CAL(1);
+  STEP_TIMER_FLUSH(T + 1);
 }
 
 // ------------------------------------------------- exchange-only probe --

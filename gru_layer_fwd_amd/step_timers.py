@@ -33,6 +33,9 @@ import sys
 import numpy as np
 
 PHASES = ("wait", "contract", "spill", "barrier", "epilogue", "publish", "stores", "loop")
+# basic GRU: two exchanges per step (A: r, u from h_{t-1}; B: the candidate
+# from r*h_{t-1}; backward: A the carried gradient, B the one through r*h)
+PHASES_GRUB = ("waitA", "contractA", "epilogueA", "publishA", "waitB", "contractB", "epilogueB", "publishB")
 
 
 def _timers(lib):
@@ -56,7 +59,7 @@ def _timers(lib):
     return flat.reshape(t.shape), c.reshape(w.value, 4).astype(np.int64)
 
 
-def analyse(t, cal, nblocks, nsteps, skip=8):
+def analyse(t, cal, nblocks, nsteps, skip=8, phases=PHASES):
     """Per-phase means (ns) over the blocks among [0, nblocks) that ran (nonzero
     calibration pairs) and steps [skip, nsteps - skip)."""
     nblocks = min(nblocks, t.shape[0])
@@ -71,8 +74,8 @@ def analyse(t, cal, nblocks, nsteps, skip=8):
     seg = t[:, lo:hi + 1]
     out = {}
     for p in range(7):
-        out[PHASES[p]] = float(np.mean(seg[:, :-1, p + 1] - seg[:, :-1, p])) / ticks_per_ns
-    out["loop"] = float(np.mean(seg[:, 1:, 0] - seg[:, :-1, 7])) / ticks_per_ns
+        out[phases[p]] = float(np.mean(seg[:, :-1, p + 1] - seg[:, :-1, p])) / ticks_per_ns
+    out[phases[7]] = float(np.mean(seg[:, 1:, 0] - seg[:, :-1, 7])) / ticks_per_ns
     out["step"] = float(np.mean(seg[:, 1:, 0] - seg[:, :-1, 0])) / ticks_per_ns
     out["startup"] = float(np.mean((t[:, 0, 0] - (cal[:, 0] & 0xFFFFFFFF)) % (1 << 32))) / ticks_per_ns
     out["first_step"] = float(np.mean(t[:, 1, 0] - t[:, 0, 0])) / ticks_per_ns
@@ -124,6 +127,7 @@ def main():
         lay.bwd_weights(x, h0, y, *grads)
     torch.cuda.synchronize()
     res = {"workload": name, "dw_hh_mode": int(args.separate_dw)}
+    phases = PHASES_GRUB if (wl.mode == "gru" and not wl.reset_after) else PHASES
     for pass_, label in ((0, "forward"), (1, "backward")):
         torch.cuda.synchronize()
         assert lib.rnn_step_timers_reset() == 0
@@ -136,7 +140,7 @@ def main():
         st, plan = L.rnn_plan_query(lay.desc, pass_)
         assert st == 0
         t, cal = _timers(lib)
-        res[label] = analyse(t, cal, plan.blocks, wl.T + pass_)
+        res[label] = analyse(t, cal, plan.blocks, wl.T + pass_, phases=phases)
         res[label]["plan"] = {k: getattr(plan, k) for k, _ in plan._fields_}
         # the exchange alone on the same grid
         s = torch.cuda.current_stream()
@@ -155,12 +159,12 @@ def main():
              + (", dW_hh by the separate product" if args.separate_dw else "")
              + " (debug build with step timers; ns, mean over workgroups and over the steps away from both"
              " ends of the sequence)", "",
-             "| pass | " + " | ".join(PHASES) + " | step | first step | start-up | exchange only |",
-             "|---" * (len(PHASES) + 5) + "|"]
+             "| pass | " + " | ".join(phases) + " | step | first step | start-up | exchange only |",
+             "|---" * (len(phases) + 5) + "|"]
     for label in ("forward", "backward"):
         r = res[label]
         ex = r.get("exchange_only_us_per_step")
-        lines.append(f"| {label} | " + " | ".join(f"{r[k]:.0f}" for k in PHASES)
+        lines.append(f"| {label} | " + " | ".join(f"{r[k]:.0f}" for k in phases)
                      + f" | {r['step']:.0f} | {r['first_step']:.0f} | {r['startup']:.0f} | "
                      + (f"{ex * 1e3:.0f}" if ex is not None else "-") + " |")
     text = "\n".join(lines)
