@@ -57,8 +57,14 @@ static __device__ unsigned long long g_step_cal[TIMER_WGS * 4];
     if (threadIdx.x == 0 && (step) >= 0 && (step) < TIMER_STEPS)                  \
       step_tl_[(step) * TIMER_PHASES + (phase)] = (unsigned)__builtin_amdgcn_s_memtime(); \
   } while (0)
+// (which 0, at the start of the step loop: also clears the LDS buffer, so
+// that a point a step does not pass reads as zero)
 #define STEP_TIMER_CAL(which)                                                                 \
   do {                                                                                        \
+    if ((which) == 0) {                                                                       \
+      for (int i_ = threadIdx.x; i_ < TIMER_STEPS * TIMER_PHASES; i_ += blockDim.x) step_tl_[i_] = 0u; \
+      __syncthreads();                                                                        \
+    }                                                                                         \
     if (threadIdx.x == 0 && blockIdx.x < TIMER_WGS) {                                         \
       g_step_cal[blockIdx.x * 4 + 2 * (which)] = __builtin_amdgcn_s_memtime();                \
       g_step_cal[blockIdx.x * 4 + 2 * (which) + 1] = __builtin_amdgcn_s_memrealtime();        \
@@ -475,10 +481,15 @@ __device__ __forceinline__ void zero_acc(f4 (&acc)[MB][NT]) {
 
 // Partial products of every wave to LDS: red[w][row][col], row < BG, col < NCOL
 // (rows at or past `rows`, the padding of a batch group smaller than the
-// MFMA tile, are not written: nothing reads them).
+// MFMA tile, are not written: nothing reads them). Rows are RSTRIDE(NCOL)
+// floats apart: a store instruction writes 16 columns of rows 4q + e (q =
+// lane / 16), and with a row stride of 4 mod 8 floats those four rows fall
+// in different quarters of the LDS banks (a stride that is a multiple of 32
+// put them on the same banks).
+constexpr int rstride(int ncol) { return ncol + 4; }
 template <int MB, int NT>
 __device__ __forceinline__ void spill_acc(float* red, const f4 (&acc)[MB][NT], int rows) {
-  constexpr int BG = MB * 16, NCOL = NT * 16;
+  constexpr int BG = MB * 16, S = rstride(NT * 16);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
@@ -487,7 +498,7 @@ __device__ __forceinline__ void spill_acc(float* red, const f4 (&acc)[MB][NT], i
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) red[(w * BG + mb * 16 + q * 4 + e) * NCOL + nt * 16 + r16] = acc[mb][nt][e];
+      for (int e = 0; e < 4; ++e) red[(w * BG + mb * 16 + q * 4 + e) * S + nt * 16 + r16] = acc[mb][nt][e];
   }
 }
 
@@ -498,7 +509,7 @@ __device__ __forceinline__ float4 red_sum4(const float* red, int row, int col) {
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int w = 0; w < NW; ++w) {
-    const float4 v = *(const float4*)&red[(w * BG + row) * NCOL + col];
+    const float4 v = *(const float4*)&red[(w * BG + row) * rstride(NCOL) + col];
     s.x += v.x;
     s.y += v.y;
     s.z += v.z;
@@ -511,7 +522,7 @@ template <int NW, int BG, int NCOL>
 __device__ __forceinline__ float red_sum(const float* red, int row, int col) {
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < NW; ++w) s += red[(w * BG + row) * NCOL + col];
+  for (int w = 0; w < NW; ++w) s += red[(w * BG + row) * rstride(NCOL) + col];
   return s;
 }
 
@@ -1047,7 +1058,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   __shared__ float hbuf[FDW ? 2 * BG * HS : 1];
   __shared__ float xtr[FDW ? NW * (KI / 2) * 256 : 1];
   STEP_TIMER_DECL;
-  float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
+  float* attl = red + NW * BG * rstride(HS);  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
   bool idle;
@@ -1495,7 +1506,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
   constexpr int UPT = (UNITS + NTH - 1) / NTH;
   extern __shared__ float red[];
   STEP_TIMER_DECL;
-  float* attl = red + NW * BG * HS;  // AUGRU score-gradient shares (LDS sized for them when used)
+  float* attl = red + NW * BG * rstride(HS);  // AUGRU score-gradient shares (LDS sized for them when used)
 
   int grp, sl;
   bool idle;
@@ -1790,7 +1801,7 @@ size_t lds_of(const Entry& e) {
   int ncol;
   if (e.fwd) ncol = (e.cell == CELL_GRU_BASIC) ? 2 * e.nt * 16 : e.nt * 16;
   else ncol = e.nt * 16;
-  return (size_t)e.nw * e.mb * 16 * ncol * sizeof(float);
+  return (size_t)e.nw * e.mb * 16 * rstride(ncol) * sizeof(float);
 }
 
 // XCDs a batch group of `slices` workgroups covers under launch_slot, for a

@@ -3,7 +3,7 @@
     python -m gru_layer_fwd_amd.prof_summary --workload NAME \
         --trace DIR/bench_kernel_trace.csv \
         [--fetch DIR/bench_counter_collection.csv --write DIR/bench_counter_collection.csv \
-         --copy-bytes N] --command "..." --out profiles/NAME.md
+         --copy-bytes N] [--counters DIR/bench_counter_collection.csv ...] --command "..." --out profiles/NAME.md
 
 Writes a markdown table of per-kernel durations (from the kernel trace) and,
 when the two counter passes are given, HBM bytes per launch from FETCH_SIZE
@@ -82,6 +82,72 @@ def read_counters(path):
     return per, (max(copies) if copies else None)
 
 
+def read_counter_set(path):
+    """{(kernel, step): {counter: mean per dispatch}} from one --pmc pass with
+    several counters (one row per dispatch and counter)."""
+    by_disp = collections.OrderedDict()
+    for r in sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"])):
+        d = by_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {}})
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    names = [d["name"] for d in by_disp.values()]
+    labs = step_labels(names)
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for d, lab in zip(by_disp.values(), labs):
+        for c, v in d["c"].items():
+            acc[(d["name"], lab)][c].append(v)
+    return {k: {c: sum(v) / len(v) for c, v in cs.items()} for k, cs in acc.items()}
+
+
+def algorithmic_flops(workload):
+    """Algorithmic FLOPs per launch of each layer step of a workload (the
+    GEMM products; the persistent kernels' recurrent products)."""
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    from gru_layer_fwd_amd import synth
+    wl = synth.WORKLOADS[workload]
+    G = 4 if wl.mode == "lstm" else 3
+    TB, GH = wl.T * wl.B, G * wl.H
+    return {"proj_gemm": 2.0 * TB * GH * wl.I, "dx_gemm": 2.0 * TB * GH * wl.I,
+            "rec_fwd": 2.0 * TB * GH * wl.H, "rec_bwd": 2.0 * TB * GH * wl.H}
+
+
+def counter_lines(sets, workload, cus=256, simds=4, xcds=8):
+    """Markdown for the MFMA and LDS counter passes. GRBM_GUI_ACTIVE counts
+    the dispatch's cycles once per XCD (its sum over a dispatch is the
+    duration times the clock times the XCD count); SQ_VALU_MFMA_BUSY_CYCLES
+    sums the busy cycles of every SIMD (16 per 16x16x32 bf16 MFMA)."""
+    lines = []
+    alg = algorithmic_flops(workload)
+    for path in sets:
+        cs = read_counter_set(path)
+        counters = sorted({c for v in cs.values() for c in v})
+        mops = [c for c in counters if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
+        lines += ["", f"Counters per dispatch ({', '.join(counters)}), mean over the dispatches of each kernel and step:", ""]
+        head = ["kernel", "step"] + counters
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in counters and "GRBM_GUI_ACTIVE" in counters:
+            head.append(f"MFMA busy % (busy / (GUI_ACTIVE / {xcds} XCDs x {cus} CUs x {simds} SIMDs))")
+        if mops:
+            head += ["MFMA FLOPs issued (512 x MOPS)", "algorithmic FLOPs", "issued / algorithmic"]
+        if "SQ_LDS_BANK_CONFLICT" in counters and "SQ_ACTIVE_INST_LDS" in counters:
+            head.append("LDS bank-conflict cycles / LDS active cycles")
+        lines += ["| " + " | ".join(head) + " |", "|---" * len(head) + "|"]
+        for (name, lab), v in sorted(cs.items(), key=lambda kv: kv[0][1]):
+            if "copyBuffer" in name or "fillBuffer" in name:
+                continue
+            row = [f"`{short(name)}`", lab] + [f"{v.get(c, 0):.4g}" for c in counters]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in counters and "GRBM_GUI_ACTIVE" in counters:
+                g = v.get("GRBM_GUI_ACTIVE", 0)
+                row.append(f"{100 * v.get('SQ_VALU_MFMA_BUSY_CYCLES', 0) / (g / xcds * cus * simds):.1f}" if g else "-")
+            if mops:
+                issued = 512.0 * sum(v.get(c, 0) for c in mops)
+                a = alg.get(lab)
+                row += [f"{issued:.4g}", f"{a:.4g}" if a else "-", f"{issued / a:.2f}" if a else "-"]
+            if "SQ_LDS_BANK_CONFLICT" in counters and "SQ_ACTIVE_INST_LDS" in counters:
+                act = v.get("SQ_ACTIVE_INST_LDS", 0)
+                row.append(f"{v.get('SQ_LDS_BANK_CONFLICT', 0) / act:.3f}" if act else "-")
+            lines.append("| " + " | ".join(row) + " |")
+    return lines
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--workload", required=True)
@@ -89,6 +155,8 @@ def main(argv=None):
     ap.add_argument("--fetch")
     ap.add_argument("--write")
     ap.add_argument("--copy-bytes", type=int, default=0)
+    ap.add_argument("--counters", action="append", default=[],
+                    help="counter_collection.csv of a --pmc pass with several counters (MFMA, LDS); repeatable")
     ap.add_argument("--command", required=True, help="the command lines that produced the inputs")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json", default=None)
@@ -123,6 +191,8 @@ def main(argv=None):
             lines.append(f"| `{short(name)}` | {lab} | {fr / 2**20:.1f} | {wr / 2**20:.1f} | {(fr + wr) / 2**20:.1f} |")
             if lab in ("rec_fwd", "rec_bwd", "proj_gemm", "dx_gemm", "dw_gemm"):
                 traffic[lab] = fr + wr
+    if a.counters:
+        lines += counter_lines(a.counters, a.workload)
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
