@@ -60,6 +60,7 @@ class RnnDesc(ctypes.Structure):
         ("att", ctypes.c_void_p),
         ("recompute", ctypes.c_int),
         ("dw_hh_mode", ctypes.c_int),
+        ("stepwise", ctypes.c_int),
     ]
 
 
@@ -77,6 +78,7 @@ class RnnPlan(ctypes.Structure):
         ("model_us_per_step", ctypes.c_double),
         ("blocks", ctypes.c_int),
         ("fused_dw", ctypes.c_int),
+        ("stepwise", ctypes.c_int),
     ]
 
 
@@ -120,11 +122,12 @@ class RnnError(RuntimeError):
 
 def make_desc(mode: int, T: int, B: int, I: int, H: int, dtype: int, direction: int = 0,
               reset_after: int = 1, gate_order=None, ldx: int = 0, ldy: int = 0, lengths: int = 0,
-              att: int = 0, recompute: int = 0, dw_hh_mode: int = 0) -> RnnDesc:
+              att: int = 0, recompute: int = 0, dw_hh_mode: int = 0, stepwise: int = 0) -> RnnDesc:
     """`lengths`: device address of int32[B] sequence lengths (0 = all T);
     `att`: device address of the [T][B] AUGRU attention scores (0 = none);
     `recompute`: 1 = LSTM cell states rebuilt in the backward pass;
-    `dw_hh_mode`: 1 = dW_hh from the separate product, never fused into BPTT."""
+    `dw_hh_mode`: 1 = dW_hh from the separate product, never fused into BPTT;
+    `stepwise`: 1 = the per-step recurrence even where a persistent plan fits."""
     d = RnnDesc()
     d.mode, d.direction, d.reset_after, d.dtype = mode, direction, reset_after, dtype
     d.T, d.B, d.I, d.H, d.ldx, d.ldy = T, B, I, H, ldx, ldy
@@ -132,6 +135,7 @@ def make_desc(mode: int, T: int, B: int, I: int, H: int, dtype: int, direction: 
     d.att = att or None
     d.recompute = recompute
     d.dw_hh_mode = dw_hh_mode
+    d.stepwise = stepwise
     if gate_order is None:
         gate_order = (0, 1, 2, 3) if mode == RNN_LSTM else (0, 1, 2)
     order = list(gate_order) + [0] * (4 - len(gate_order))

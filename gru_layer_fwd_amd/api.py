@@ -34,14 +34,15 @@ class RnnLayer:
 
     def __init__(self, mode: str, T: int, B: int, I: int, H: int, dtype: str, direction: int = 0,
                  reset_after: bool = True, gate_order=None, ldx: int = 0, ldy: int = 0, device="cuda",
-                 lengths=None, att=None, recompute=False, dw_hh_mode=0):
+                 lengths=None, att=None, recompute=False, dw_hh_mode=0, stepwise=False):
         """`lengths`: optional int32 device tensor [B] of per-row sequence
         lengths; `att`: optional [T, B] device tensor of AUGRU attention
         scores in the layer's dtype (GRU only). Both are kept referenced by
         the layer; the three calls read them. `recompute` (LSTM): keep only
         the gates between the forward and backward calls. `dw_hh_mode` 1:
         the recurrent-weight gradient from the separate product, never
-        accumulated inside the BPTT kernel."""
+        accumulated inside the BPTT kernel. `stepwise`: the per-step
+        recurrence even where a persistent plan fits."""
         self.mode, self.dtype = mode, dtype
         self.T, self.B, self.I, self.H = T, B, I, H
         if lengths is not None:
@@ -54,7 +55,7 @@ class RnnLayer:
         self.lengths, self.att = lengths, att
         self.desc = L.make_desc(MODE_OF[mode], T, B, I, H, DT_OF[dtype], direction,
                                 int(bool(reset_after)), gate_order, ldx, ldy, _p(lengths), _p(att),
-                                int(bool(recompute)), int(dw_hh_mode))
+                                int(bool(recompute)), int(dw_hh_mode), int(bool(stepwise)))
         self.ws_bytes = L.rnn_workspace_bytes(self.desc)
         if self.ws_bytes == 0:
             raise L.RnnError(L.RNN_ERR_INVALID_ARG, "rnn_workspace_bytes")
@@ -104,7 +105,7 @@ class RnnStack:
     """
 
     def __init__(self, mode, T, B, I, H, dtype, layers, bidir, reset_after=True, gate_order=None,
-                 device="cuda", lengths=None):
+                 device="cuda", lengths=None, stepwise=False):
         self.dirs = 2 if bidir else 1
         self.T, self.B, self.I, self.H = T, B, I, H
         self.layers = []
@@ -112,7 +113,8 @@ class RnnStack:
             Il = I if layer == 0 else H * self.dirs
             self.layers.append(RnnLayer(mode, T, B, Il, H, dtype, direction=2 if bidir else 0,
                                         reset_after=reset_after, gate_order=gate_order, ldx=Il,
-                                        ldy=H * self.dirs, device=device, lengths=lengths))
+                                        ldy=H * self.dirs, device=device, lengths=lengths,
+                                        stepwise=stepwise))
         dt = self.layers[0].torch_dtype
         self.ys = [torch.empty(T, B, H * self.dirs, dtype=dt, device=device) for _ in range(layers)]
         # input gradients of layers 1.. (the output gradients of the layer below)

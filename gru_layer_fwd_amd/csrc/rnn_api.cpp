@@ -53,6 +53,7 @@ bool desc_ok(const rnn_desc_t* d) {
   if (d->att && d->mode != RNN_GRU) return false;  // attention scores scale the GRU update gate
   if (d->recompute != 0 && !(d->recompute == 1 && d->mode == RNN_LSTM)) return false;
   if (d->dw_hh_mode != 0 && d->dw_hh_mode != 1) return false;
+  if (d->stepwise != 0 && d->stepwise != 1) return false;
   if (d->T < 1 || d->B < 1 || d->I < 1 || d->H < 1) return false;
   const int G = gates(d);
   int seen = 0;
@@ -101,7 +102,7 @@ long long counter_ints(const rnn::RecPlan& plan) {
 // plans of 4 waves with 8 or 12 k-steps each, and 8 waves with 6: there the
 // accumulators fit beside the resident W_hh without spilling)
 bool fused_dw_shape(const rnn_desc_t* d) {
-  if (d->dtype != RNN_F32 || d->dw_hh_mode != 0) return false;
+  if (d->dtype != RNN_F32 || d->dw_hh_mode != 0 || d->stepwise) return false;
   const int cell = cell_of(d);
   return (cell == rnn::CELL_LSTM && d->H <= 128) || (cell == rnn::CELL_GRU_RA && d->H <= 256);
 }
@@ -132,6 +133,9 @@ Layout layout(const rnn_desc_t* d) {
     if (f2 > f) f = f2;
     if (f3 > f) f = f3;
     if (cell == rnn::CELL_LSTM && f4 > f) f = f4;
+    // the per-step recurrence keeps its carried state here between launches
+    const size_t f5 = rnn::stepwise_scratch_floats(cell, d->B, d->H);
+    if (f5 > f) f = f5;
     L.gemm = off;
     L.gemm_floats = f;
     off += up(f * sizeof(float));
@@ -353,7 +357,7 @@ hipError_t colsum_dt(int dtype, const void* src, long long lds, long long M, int
 // exchanged vector. Pairs of k-steps share a tile when groups have <= 8 rows.
 // Returns 0 (no ring: the kernels read rows of y / dG), 1 (tiled) or 2 (packed).
 int ring_kind(const rnn::RecPlan& p, const Layout& L, long long K, size_t esize) {
-  if (p.bg > 16 * p.mb) return 0;
+  if (p.nw == 0 || p.bg > 16 * p.mb) return 0;  // (nw 0: the per-step path)
   if ((K * (long long)esize) % 64 != 0) return 0;  // whole k-steps only
   const long long gbytes = K * 16 * (long long)p.mb * (long long)esize;  // a 1 KiB tile per (k-step, row tile)
   if ((size_t)(2 * p.nGroups * gbytes) > L.xb_bytes) return 0;
@@ -432,12 +436,45 @@ bool choose_plan(F planner, bool bidir, const DevInfo& di, rnn::RecPlan* plan, b
   return planner(di.cu, 8, plan);
 }
 
-// The backward plan of d (both calls of the backward pass choose it here).
-int bwd_plan(const rnn_desc_t* d, const DevInfo& di, rnn::RecPlan* plan, bool* dual) {
+// The plan of pass 0 (forward) or 1 (backward through time) for d: a
+// persistent plan when one fits with a co-resident grid (occ > 0: that many
+// workgroups per CU, else the device's occupancy) and d does not ask for the
+// per-step path; otherwise the per-step plan (nw = 0, one slice, no ring).
+// Both backward calls decide here, so they agree.
+bool persistent_plan(const rnn_desc_t* d, int pass, const DevInfo& di, int occ, rnn::RecPlan* plan, bool* dual) {
   const int cell = cell_of(d);
-  if (!choose_plan([&](int cu, int xcds, rnn::RecPlan* p) { return rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p); },
-                   d->direction == 2, di, plan, dual))
-    return RNN_ERR_UNSUPPORTED;
+  *dual = false;
+  if (!d->stepwise) {
+    auto planner = [&](int cu, int xcds, rnn::RecPlan* p) {
+      return pass == 0 ? rnn::plan_fwd(cell, d->dtype, d->B, d->H, cu, xcds, p)
+                       : rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p);
+    };
+    if (choose_plan(planner, d->direction == 2, di, plan, dual) &&
+        coresidency(*plan, *dual, occ > 0 ? occ : rnn::max_coresident(*plan), di.cu) == RNN_OK)
+      return true;
+  }
+  *plan = rnn::RecPlan{};
+  plan->nGroups = plan->nSlices = 1;
+  plan->Hs = d->H;
+  plan->bg = d->B;
+  plan->xcd_span = 1;
+  *dual = false;
+  return false;
+}
+
+// The per-step recurrence of every half of a layer (scratch: each half's
+// GEMM region, free between the products around it).
+int run_stepwise(const rnn_desc_t* d, int pass, int halves, const rnn::RecArgs (&args)[2], char* ws, size_t half_bytes,
+                 hipStream_t s) {
+  const rnn_desc_t h = half_desc(d, 0);
+  const Layout L = layout(&h);
+  for (int k = 0; k < halves; ++k) {
+    float* scratch = (float*)(ws + k * half_bytes + L.gemm);
+    const hipError_t e = pass == 0 ? rnn::stepwise_fwd(cell_of(d), d->dtype == RNN_BF16, args[k], scratch, s)
+                                   : rnn::stepwise_bwd(cell_of(d), d->dtype == RNN_BF16, args[k], scratch, s);
+    if (int st = hip_status(e)) return st;
+  }
+  if (log_on()) fprintf(stderr, "[rnn] %s: per-step path, %d steps\n", pass ? "bwd" : "fwd", d->T);
   return RNN_OK;
 }
 
@@ -696,7 +733,7 @@ int bwd_begin(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan
   a.W_hhT = nullptr;
   const int kq = 16 / (int)esz(d);
   const size_t whh_bytes = (size_t)gates(d) * d->H * d->H * esz(d);
-  if (cell != rnn::CELL_GRU_BASIC && d->H % kq == 0 && whh_bytes >= ((size_t)8 << 20)) {
+  if (plan.nw > 0 && cell != rnn::CELL_GRU_BASIC && d->H % kq == 0 && whh_bytes >= ((size_t)8 << 20)) {
     const bool umaj = cell == rnn::CELL_LSTM && d->dtype == RNN_BF16 && plan.mb < 4 && a.xbuf != nullptr;
     const int G = gates(d);
     ProfScope ps(L_AUX, s);
@@ -785,9 +822,7 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
   const int halves = bidir ? 2 : 1;
   rnn::RecPlan plan;
   bool dual;
-  if (!choose_plan([&](int cu, int xcds, rnn::RecPlan* p) { return rnn::plan_fwd(cell, d->dtype, d->B, d->H, cu, xcds, p); },
-                   bidir, di, &plan, &dual))
-    return RNN_ERR_UNSUPPORTED;
+  const bool pers = persistent_plan(d, 0, di, 0, &plan, &dual);
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   const rnn_desc_t hd[2] = {half_desc(d, 0), half_desc(d, 1)};
@@ -799,7 +834,9 @@ RNN_API int rnn_fwd(const rnn_desc_t* d, const void* x, const void* h0, const vo
     if ((st = fwd_begin(&hd[k], fwd_half(d, io, k), ws + k * half_bytes, plan, di, status, s, args[k]))) return st;
   {
     ProfScope ps(L_RFWD, s);
-    if ((st = run_persistent(plan, dual, halves, args, di, s, "fwd"))) return st;
+    if (pers) st = run_persistent(plan, dual, halves, args, di, s, "fwd");
+    else st = run_stepwise(d, 0, halves, args, ws, half_bytes, s);
+    if (st) return st;
   }
   for (int k = 0; k < halves; ++k)
     if ((st = fwd_end(&hd[k], args[k], s))) return st;
@@ -863,7 +900,7 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
   const int halves = bidir ? 2 : 1;
   rnn::RecPlan plan;
   bool dual;
-  if ((st = bwd_plan(d, di, &plan, &dual))) return st;
+  const bool pers = persistent_plan(d, 1, di, 0, &plan, &dual);
   // the score-gradient shares of a workgroup's units sit after its reduction buffer
   if (d->att) plan.lds_bytes += (size_t)plan.mb * 16 * plan.Hs * sizeof(float);
   hipStream_t s = (hipStream_t)stream;
@@ -877,7 +914,9 @@ RNN_API int rnn_bwd_data(const rnn_desc_t* d, const void* W_ih, const void* W_hh
     if ((st = bwd_begin(&hd[k], bwd_half(d, io, k), ws + k * half_bytes, plan, di, status, s, args[k]))) return st;
   {
     ProfScope ps(L_RBWD, s);
-    if ((st = run_persistent(plan, dual, halves, args, di, s, "bwd"))) return st;
+    if (pers) st = run_persistent(plan, dual, halves, args, di, s, "bwd");
+    else st = run_stepwise(d, 1, halves, args, ws, half_bytes, s);
+    if (st) return st;
   }
   // the second half of a bidirectional layer adds its dx and score gradient
   for (int k = 0; k < halves; ++k)
@@ -1098,8 +1137,7 @@ RNN_API int rnn_bwd_weights(const rnn_desc_t* d, const void* x, const void* h0, 
   if (fused_dw_shape(&h0d)) {
     rnn::RecPlan plan;
     bool dual;
-    if ((st = bwd_plan(d, di, &plan, &dual))) return st;
-    if (fused_dw(&h0d, plan)) fused_groups = plan.nGroups;
+    if (persistent_plan(d, 1, di, 0, &plan, &dual) && fused_dw(&h0d, plan)) fused_groups = plan.nGroups;
   }
   if (d->direction != 2)
     return bwd_weights_dir(d, x, h0, y, dW_ih, dW_hh, db_ih, db_hh, accumulate, workspace, stream, fused_groups);
@@ -1130,11 +1168,10 @@ RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_p
   const int cell = cell_of(d);
   rnn::RecPlan plan;
   bool dual;
-  auto planner = [&](int cu, int xcds, rnn::RecPlan* p) {
-    return pass == 0 ? rnn::plan_fwd(cell, d->dtype, d->B, d->H, cu, xcds, p)
-                     : rnn::plan_bwd(cell, d->dtype, d->B, d->H, cu, xcds, p);
-  };
-  if (!choose_plan(planner, d->direction == 2, di, &plan, &dual)) return RNN_ERR_UNSUPPORTED;
+  if (!persistent_plan(d, pass, di, wg_per_cu, &plan, &dual)) {
+    out->stepwise = 1;  // no co-resident persistent grid (or asked for): one launch pair per step
+    return RNN_OK;
+  }
   const long long nwg = (long long)plan.nGroups * plan.nSlices;
   out->groups = plan.nGroups;
   out->rows = plan.bg;
@@ -1155,8 +1192,7 @@ RNN_API int rnn_plan_query(const rnn_desc_t* d, int pass, int cu_count, int wg_p
     out->ring = a.xg_bytes ? (a.xpacked ? 2 : 1) : 0;
     out->fused_dw = pass == 1 && fused_dw(&h, plan) ? 1 : 0;
   }
-  const int occ = wg_per_cu > 0 ? wg_per_cu : rnn::max_coresident(plan);
-  return coresidency(plan, dual, occ, di.cu);
+  return RNN_OK;
 }
 
 RNN_API int rnn_handshake_probe(const rnn_desc_t* d, int pass, void* workspace, size_t ws_bytes, void* stream) {
@@ -1164,7 +1200,7 @@ RNN_API int rnn_handshake_probe(const rnn_desc_t* d, int pass, void* workspace, 
   if (st) return st;
   if (pass != 0 && pass != 1) return RNN_ERR_INVALID_ARG;
   const int cell = cell_of(d);
-  if (cell == rnn::CELL_GRU_BASIC) return RNN_ERR_UNSUPPORTED;  // no exchange ring
+  if (cell == rnn::CELL_GRU_BASIC || d->stepwise) return RNN_ERR_UNSUPPORTED;  // no exchange ring
   DevInfo di;
   if ((st = dev_info(&di))) return st;
   g_cu_count = di.cu;

@@ -276,6 +276,15 @@ struct RecArgs {
   float* dwp;          // backward: fused partials, dW_hh [nGroups][K][H] then db_hh [nGroups][K], fp32 (NULL: not fused)
 };
 
+// Per-step recurrence (shapes no persistent plan fits, or on request): one
+// recurrent product and one cell kernel per step (two of each for the basic
+// GRU) on stream s, the same per-step tensors as the persistent kernels
+// save; `scratch` holds stepwise_scratch_floats(cell, B, H) floats. The
+// backward writes AUGRU score-gradient sums to a.datt_part as one slice.
+size_t stepwise_scratch_floats(int cell, int B, int H);
+hipError_t stepwise_fwd(int cell, int dtype, const RecArgs& a, float* scratch, hipStream_t s);
+hipError_t stepwise_bwd(int cell, int dtype, const RecArgs& a, float* scratch, hipStream_t s);
+
 // Kernel argument of the persistent kernels: one direction (dual = 0), or
 // both directions of a bidirectional layer in one cooperative launch
 // (dual = 1: the blocks dispatched to XCDs 0-3 run d[0], those on XCDs 4-7

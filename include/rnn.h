@@ -129,6 +129,13 @@ typedef struct rnn_desc {
                         backward-with-weight-update does; 1 = dW_hh always
                         from the separate product over the saved gate
                         gradients. Same value for both backward calls. */
+  int stepwise;       /* 0 = the persistent kernels where a plan with a co-resident
+                        grid fits the shape and device (rnn_plan_query), else one
+                        recurrent product and one cell kernel per step (the
+                        CUDA fragment page's per-step structure, and popnn's
+                        step loop: the same equations, any H and B the
+                        workspace holds, slower); 1 = the per-step path
+                        always. */
 } rnn_desc_t;
 
 /* Bytes of workspace the three calls need for this descriptor (0 if the
@@ -243,14 +250,16 @@ int rnn_set_handshake_timeout(double seconds);
  * persistent kernel fixes at compile time (its block and batch tiling) and
  * the popnn pages leave to the IPU planner. A persistent grid only runs when
  * all its workgroups are resident at once, since every workgroup waits for
- * the others at every step: the plan is refused (RNN_ERR_UNSUPPORTED) when
- * no instantiated kernel fits `cu_count` compute units with `wg_per_cu`
- * workgroups co-resident per CU. cu_count = 0 queries the current device,
+ * the others at every step: when no instantiated kernel fits `cu_count`
+ * compute units with `wg_per_cu` workgroups co-resident per CU (or the
+ * descriptor sets `stepwise`), the layer takes the per-step path and the
+ * result has stepwise = 1. cu_count = 0 queries the current device,
  * wg_per_cu = 0 asks the HIP runtime for the kernel's occupancy (both need
  * a GPU); with both given the call is pure host computation, the same
- * decision rnn_fwd / rnn_bwd_data take before launching.
+ * decision rnn_fwd / rnn_bwd_data / rnn_bwd_weights take before launching.
  * Returns RNN_OK with *out filled, RNN_ERR_INVALID_ARG (bad descriptor,
- * pass, counts or NULL out), RNN_ERR_UNSUPPORTED, or RNN_ERR_DEVICE. */
+ * pass, counts or NULL out), RNN_ERR_UNSUPPORTED (shape outside the
+ * granularity the kernels need), or RNN_ERR_DEVICE. */
 typedef struct rnn_plan {
   int groups;       /* batch groups (each runs its own recurrence) */
   int rows;         /* batch rows per group */
@@ -267,6 +276,8 @@ typedef struct rnn_plan {
   int fused_dw;     /* pass 1: the BPTT kernel accumulates dW_hh itself (dw_hh_mode 0, a
                        plan with the fused variant, and the planner's model finding that
                        its extra per-step products cost less than the separate product) */
+  int stepwise;     /* 1: no persistent grid (none fits, or the descriptor asks for the
+                       per-step path); the other fields are then zero */
 } rnn_plan_t;
 int rnn_plan_query(const rnn_desc_t* desc, int pass, int cu_count, int wg_per_cu, rnn_plan_t* out);
 

@@ -29,7 +29,7 @@ def host(t):
 
 def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=0, reset_after=True,
               order=None, xpad=0, ypad=0, want_dx=True, acc=False, repeat=1, lengths=None, att=None,
-              recompute=False, dw_hh_mode=0):
+              recompute=False, dw_hh_mode=0, stepwise=False):
     """Forward, backward-data and backward-weights of one layer on the GPU.
     xpad/ypad > 0 store x/dx and y/dy with a larger row stride; lengths is
     an optional host array of B per-row step counts, att optional [T, B]
@@ -42,7 +42,7 @@ def gpu_layer(mode, dtype, params, x, h0, c0, dy, dhT=None, dcT=None, direction=
     attd = None if att is None else dev(att, dtype)
     lay = RnnLayer(mode, T, B, I, H, dtype, direction=direction, reset_after=reset_after,
                    gate_order=order, ldx=ldx, ldy=ldy, lengths=lens, att=attd, recompute=recompute,
-                   dw_hh_mode=dw_hh_mode)
+                   dw_hh_mode=dw_hh_mode, stepwise=stepwise)
     datt = None if att is None else torch.zeros(T, B, dtype=dt, device="cuda")
     xs = torch.zeros(T, B, ldx, dtype=dt, device="cuda")
     xs[:, :, :I] = dev(x, dtype)

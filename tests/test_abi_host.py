@@ -186,13 +186,43 @@ def test_coresidency_refusal_with_injected_cu_count():
     d = g.make_desc(L.RNN_LSTM, 256, 64, 1024, 1024, L.RNN_BF16)
     # half the chip: the planner still finds a grid that fits (16-row groups)
     st, pl = _plan(d, 0, cu=128)
-    assert st == L.RNN_OK and pl.workgroups <= 128
-    # 16 CUs cannot hold W_hh (8 MiB) in the registers of a co-resident grid
+    assert st == L.RNN_OK and pl.workgroups <= 128 and pl.stepwise == 0
+    # 16 CUs cannot hold W_hh (8 MiB) in the registers of a co-resident grid:
+    # no persistent grid, the layer takes the per-step path
     for cu in (16, 31):
-        st, _ = _plan(d, 0, cu=cu)
-        assert st == L.RNN_ERR_UNSUPPORTED, cu
-        st, _ = _plan(d, 1, cu=cu)
-        assert st == L.RNN_ERR_UNSUPPORTED, cu
+        for p in (0, 1):
+            st, pl = _plan(d, p, cu=cu)
+            assert st == L.RNN_OK and pl.stepwise == 1, (cu, p)
+            assert pl.workgroups == 0 and pl.blocks == 0 and pl.fused_dw == 0
+
+
+def test_stepwise_descriptor_field():
+    """`stepwise` = 1 asks for the per-step path on any shape; values other
+    than 0 and 1 are refused; the plan query reports the path taken."""
+    for mode, ra, H, dt in ((L.RNN_LSTM, 1, 1024, L.RNN_BF16), (L.RNN_GRU, 1, 256, L.RNN_F32),
+                            (L.RNN_GRU, 0, 256, L.RNN_F32)):
+        d = g.make_desc(mode, 64, 16, 256, H, dt, reset_after=ra, stepwise=1)
+        assert g.rnn_workspace_bytes(d) > 0
+        for p in (0, 1):
+            st, pl = _plan(d, p)
+            assert st == L.RNN_OK and pl.stepwise == 1 and pl.groups == 0 and pl.fused_dw == 0
+        d0 = g.make_desc(mode, 64, 16, 256, H, dt, reset_after=ra)
+        st, pl = _plan(d0, 1)
+        assert st == L.RNN_OK and pl.stepwise == 0 and pl.groups > 0
+    bad = g.make_desc(L.RNN_LSTM, 8, 2, 16, 32, L.RNN_F32, stepwise=2)
+    assert g.rnn_workspace_bytes(bad) == 0
+
+
+def test_shapes_beyond_the_plan_table_take_the_per_step_path():
+    """fp32 H = 1024 and 2048 (W_hh 16 / 64 MiB), the basic GRU at H = 1024
+    fp32, bf16 H = 4096: no persistent plan, per-step path."""
+    for mode, ra, H, dt in ((L.RNN_LSTM, 1, 1024, L.RNN_F32), (L.RNN_GRU, 1, 2048, L.RNN_F32),
+                            (L.RNN_GRU, 0, 1024, L.RNN_F32), (L.RNN_LSTM, 1, 4096, L.RNN_BF16)):
+        d = g.make_desc(mode, 16, 64, 256, H, dt, reset_after=ra)
+        assert g.rnn_workspace_bytes(d) > 0
+        for p in (0, 1):
+            st, pl = _plan(d, p)
+            assert st == L.RNN_OK and pl.stepwise == 1, (mode, ra, H, dt, p)
 
 
 def test_bidirectional_layer_shares_one_launch():

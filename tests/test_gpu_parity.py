@@ -363,10 +363,12 @@ def test_lstm_recompute_with_final_state_gradients(direction):
 
 # ------------------------------------------------ bidirectional layer ----
 
-@pytest.mark.parametrize("mode,ra,dtype,big", [("lstm", None, "f32", False), ("gru", True, "f32", False),
-                                               ("gru", False, "f32", False), ("lstm", None, "bf16", False),
-                                               ("lstm", None, "bf16", True)])
-def test_bidirectional_layer_runs_both_directions(mode, ra, dtype, big):
+@pytest.mark.parametrize("mode,ra,dtype,big,stepwise", [
+    ("lstm", None, "f32", False, False), ("gru", True, "f32", False, False), ("gru", False, "f32", False, False),
+    ("lstm", None, "bf16", False, False), ("lstm", None, "bf16", True, False),
+    # the per-step path for both directions of a bidirectional layer
+    ("lstm", None, "f32", False, True), ("gru", True, "bf16", False, True), ("gru", False, "f32", False, True)])
+def test_bidirectional_layer_runs_both_directions(mode, ra, dtype, big, stepwise):
     """direction 2: [2, ...] stacked weights and states, y/dy halves in one
     [T, B, 2H] tensor, dx summed over the directions; each direction against
     the oracle with its own weights and initial and final states. `big`:
@@ -393,7 +395,7 @@ def test_bidirectional_layer_runs_both_directions(mode, ra, dtype, big):
     dcT = rnd(rng.standard_normal((2, B, H))) if mode == "lstm" else None
     L = _ragged_lengths(B, T, 83)
     lens = torch.as_tensor(L, dtype=torch.int32).to("cuda")
-    lay = RnnLayer(mode, T, B, I, H, dtype, direction=2, reset_after=bool(ra), lengths=lens)
+    lay = RnnLayer(mode, T, B, I, H, dtype, direction=2, reset_after=bool(ra), lengths=lens, stepwise=stepwise)
     d_ = lambda a: dev(a, dtype)  # noqa: E731
     tdt = lay.torch_dtype
     y = torch.full((T, B, 2 * H), float("nan"), dtype=tdt, device="cuda")
@@ -429,6 +431,54 @@ def test_bidirectional_layer_runs_both_directions(mode, ra, dtype, big):
         assert all(v <= (tol_f if k in ("y", "hT", "cT") else tol_g) for k, v in errs.items()), (dd, errs)
     e = O.rel_err(host(dx), dx_ref)
     assert e <= tol_g, e
+
+
+# ------------------------------------------------------ per-step path ----
+
+@pytest.mark.parametrize("direction", [0, 1])
+@pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stepwise_path(cell, dtype, direction):
+    """The per-step recurrence (forced on a shape the persistent kernels
+    also take) against the oracle: ragged lengths with rows of length 0, 1,
+    T-1 and T, nonzero initial states and final-state gradients; on
+    direction 1 AUGRU scores (GRU) and cell-state recomputation (LSTM)."""
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=11, B=13, I=40, H=48, w_scale=0.15, h0_std=0.5, c0_std=0.5, dtype=dtype)
+    if cell != "lstm":
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    rng = np.random.default_rng(5 + direction)
+    from gru_layer_fwd_amd.synth import round_to
+    dhT = round_to(rng.standard_normal((wl.B, wl.H)), dtype)
+    dcT = round_to(rng.standard_normal((wl.B, wl.H)), dtype) if cell == "lstm" else None
+    L = _ragged_lengths(wl.B, wl.T, 37 + direction)
+    kw = {}
+    if direction == 1 and cell != "lstm":
+        kw["att"] = _scores(wl.T, wl.B, 43, dtype)
+    if direction == 1 and cell == "lstm":
+        kw["recompute"] = True
+    got, ref = _run(wl, inp, P, direction, dhT=dhT, dcT=dcT, lengths=L, stepwise=True, **kw)
+    print(compare(got, ref, dtype, extra=f"stepwise {cell} {dtype} dir{direction}"))
+
+
+@pytest.mark.parametrize("cell,H", [("lstm", 1024), ("gru_ra", 1024), ("gru_basic", 1024), ("lstm", 2048)])
+def test_shapes_beyond_the_plans_run_per_step(cell, H):
+    """fp32 shapes with no persistent plan (W_hh 12-64 MiB): the layer takes
+    the per-step path by itself and matches the oracle."""
+    from gru_layer_fwd_amd import _lib as L
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=5, B=6, I=32, H=H, w_scale=1.0 / np.sqrt(H), h0_std=0.5, c0_std=0.5)
+    if cell != "lstm":
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    d = L.make_desc(L.RNN_LSTM if cell == "lstm" else L.RNN_GRU, wl.T, wl.B, wl.I, H, L.RNN_F32, 0,
+                    int(cell != "gru_basic"))
+    for p in (0, 1):
+        st, plan = L.rnn_plan_query(d, p)
+        assert st == 0 and plan.stepwise == 1
+    got, ref = _run(wl, inp, P, 1, lengths=_ragged_lengths(wl.B, wl.T, 47))
+    print(compare(got, ref, "f32", extra=f"beyond plans {cell} H{H}"))
 
 
 # ------------------------------------------------- failure detection ----
