@@ -167,6 +167,8 @@ def main():
         lines.append(f"| {label} | " + " | ".join(f"{r[k]:.0f}" for k in phases)
                      + f" | {r['step']:.0f} | {r['first_step']:.0f} | {r['startup']:.0f} | "
                      + (f"{ex * 1e3:.0f}" if ex is not None else "-") + " |")
+    lines += ["", "Produced by (from the repository root, library built with `python -m gru_layer_fwd_amd.build`):",
+              "", "```", "python -m gru_layer_fwd_amd.step_timers " + " ".join(sys.argv[1:]), "```"]
     text = "\n".join(lines)
     print(text, flush=True)
     print(json.dumps(res), flush=True)
