@@ -163,6 +163,8 @@ def main():
     ap.add_argument("--separate-dw", action="store_true",
                     help="single-layer workloads: dW_hh from the separate product even where the BPTT kernel "
                          "could accumulate it (dw_hh_mode 1)")
+    ap.add_argument("--stepwise", action="store_true",
+                    help="single-layer workloads: the per-step recurrence instead of the persistent kernels")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the timed region, run one plain device copy of this many MiB (a known-size "
                          "kernel for calibrating rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -199,8 +201,8 @@ def main():
         grads.append([tuple(t[d] for t in gts) for d in range(len(per))])
     order = wl.gate_order()
 
-    if (args.ragged or args.att or args.recompute or args.separate_dw) and (wl.layers != 1 or wl.bidir):
-        raise SystemExit("--ragged / --att / --recompute / --separate-dw apply to single-layer workloads")
+    if (args.ragged or args.att or args.recompute or args.separate_dw or args.stepwise) and (wl.layers != 1 or wl.bidir):
+        raise SystemExit("--ragged / --att / --recompute / --separate-dw / --stepwise apply to single-layer workloads")
     if args.recompute and wl.mode != "lstm":
         raise SystemExit("--recompute applies to LSTM workloads")
     if args.att and wl.mode != "gru":
@@ -215,7 +217,8 @@ def main():
 
     if wl.layers == 1 and not wl.bidir:
         lay = RnnLayer(wl.mode, wl.T, wl.B, wl.I, wl.H, wl.dtype, reset_after=wl.reset_after, gate_order=order,
-                       lengths=lengths, att=att, recompute=args.recompute, dw_hh_mode=int(args.separate_dw))
+                       lengths=lengths, att=att, recompute=args.recompute, dw_hh_mode=int(args.separate_dw),
+                       stepwise=args.stepwise)
         h0, c0 = dev(inp["h0"]), dev(inp["c0"])
         y = torch.empty(wl.T, wl.B, wl.H, dtype=dt, device="cuda")
         hT = torch.empty(wl.B, wl.H, dtype=dt, device="cuda")
@@ -327,7 +330,8 @@ def main():
                    **({"lengths": "uniform [1, T] per row"} if args.ragged else {}),
                    **({"augru_scores": "uniform [0, 1]"} if args.att else {}),
                    **({"cell_states": "recomputed in the backward call"} if args.recompute else {}),
-                   **({"dw_hh": "separate product"} if args.separate_dw else {})},
+                   **({"dw_hh": "separate product"} if args.separate_dw else {}),
+                   **({"recurrence": "per-step kernels"} if args.stepwise else {})},
         "roofline": roof,
         "recurrent_us_per_step": rec,
         "kernels": kern,

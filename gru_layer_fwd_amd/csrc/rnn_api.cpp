@@ -470,8 +470,8 @@ int run_stepwise(const rnn_desc_t* d, int pass, int halves, const rnn::RecArgs (
   const Layout L = layout(&h);
   for (int k = 0; k < halves; ++k) {
     float* scratch = (float*)(ws + k * half_bytes + L.gemm);
-    const hipError_t e = pass == 0 ? rnn::stepwise_fwd(cell_of(d), d->dtype == RNN_BF16, args[k], scratch, s)
-                                   : rnn::stepwise_bwd(cell_of(d), d->dtype == RNN_BF16, args[k], scratch, s);
+    const hipError_t e = pass == 0 ? rnn::stepwise_fwd(cell_of(d), d->dtype == RNN_BF16, args[k], scratch, L.gemm_floats, s)
+                                   : rnn::stepwise_bwd(cell_of(d), d->dtype == RNN_BF16, args[k], scratch, L.gemm_floats, s);
     if (int st = hip_status(e)) return st;
   }
   if (log_on()) fprintf(stderr, "[rnn] %s: per-step path, %d steps\n", pass ? "bwd" : "fwd", d->T);

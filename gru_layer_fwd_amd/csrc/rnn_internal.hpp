@@ -279,11 +279,12 @@ struct RecArgs {
 // Per-step recurrence (shapes no persistent plan fits, or on request): one
 // recurrent product and one cell kernel per step (two of each for the basic
 // GRU) on stream s, the same per-step tensors as the persistent kernels
-// save; `scratch` holds stepwise_scratch_floats(cell, B, H) floats. The
+// save; `scratch` holds `floats` >= stepwise_scratch_floats(cell, B, H)
+// floats (more lets a small batch's products split K over more blocks). The
 // backward writes AUGRU score-gradient sums to a.datt_part as one slice.
 size_t stepwise_scratch_floats(int cell, int B, int H);
-hipError_t stepwise_fwd(int cell, int dtype, const RecArgs& a, float* scratch, hipStream_t s);
-hipError_t stepwise_bwd(int cell, int dtype, const RecArgs& a, float* scratch, hipStream_t s);
+hipError_t stepwise_fwd(int cell, int dtype, const RecArgs& a, float* scratch, size_t floats, hipStream_t s);
+hipError_t stepwise_bwd(int cell, int dtype, const RecArgs& a, float* scratch, size_t floats, hipStream_t s);
 
 // Kernel argument of the persistent kernels: one direction (dual = 0), or
 // both directions of a bidirectional layer in one cooperative launch

@@ -8,6 +8,8 @@
 // paths save the same per-step tensors and the GEMMs around them do not
 // care which one ran. The carried state (h, c forward; the carried
 // gradients backward) lives in fp32 scratch between the launches.
+#include <algorithm>
+
 #include "rnn_internal.hpp"
 
 namespace rnn {
@@ -29,28 +31,32 @@ __device__ __forceinline__ long long wrow(const WPerm& p, int g0, int r, int H) 
 //   forward (BT false):  B(k, n) = W_hh[wrow(n)][k]  (gate rows of the output),
 //   backward (BT true):  B(k, n) = W_hh[wrow(k)][n]  (contraction over gate rows).
 // 32 x 64 output tile per 256 threads, 32-deep k tiles through LDS; each
-// thread accumulates 2 x 4 outputs in a fixed order.
+// thread accumulates 2 x 4 outputs in a fixed order. Split K: block z covers
+// k in [z * kchunk, (z + 1) * kchunk) and writes out + z * M * N (summed by
+// step_reduce in z order).
 template <typename TS, bool BT>
 __global__ __launch_bounds__(256) void step_gemm(const TS* __restrict__ a, long long lda, int kshift, int kskip, int M,
                                                  int K, const TS* __restrict__ W, int H, WPerm perm, int g0, int N,
-                                                 float* __restrict__ out) {
+                                                 int kchunk, float* __restrict__ out) {
   constexpr int TM = 32, TN = 64, TK = 32;
   __shared__ float As[TK][TM + 1];
   __shared__ float Bs[TK][TN + 1];
   const int tid = threadIdx.x;
   const int m0 = blockIdx.y * TM, n0 = blockIdx.x * TN;
+  const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+  out += (long long)blockIdx.z * M * N;
   const int ty = tid >> 4, tx = tid & 15;
   float acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < K; k0 += TK) {
+  for (int k0 = kb; k0 < ke; k0 += TK) {
     for (int i = tid; i < TM * TK; i += 256) {
       const int mm = i / TK, kk = i - mm * TK;
       const int m = m0 + mm, k = k0 + kk;
       float v = 0.f;
-      if (m < M && k < K) v = to_f(a[(long long)m * lda + k + (k >= kshift ? kskip : 0)]);
+      if (m < M && k < ke) v = to_f(a[(long long)m * lda + k + (k >= kshift ? kskip : 0)]);
       As[kk][mm] = v;
     }
     for (int i = tid; i < TK * TN; i += 256) {
@@ -58,12 +64,12 @@ __global__ __launch_bounds__(256) void step_gemm(const TS* __restrict__ a, long 
       if constexpr (!BT) {
         const int nn = i / TK, kk = i - nn * TK;
         const int n = n0 + nn, k = k0 + kk;
-        if (n < N && k < K) v = to_f(W[wrow(perm, g0, n, H) * H + k]);
+        if (n < N && k < ke) v = to_f(W[wrow(perm, g0, n, H) * H + k]);
         Bs[kk][nn] = v;
       } else {
         const int kk = i / TN, nn = i - kk * TN;
         const int n = n0 + nn, k = k0 + kk;
-        if (n < N && k < K) v = to_f(W[wrow(perm, g0, k, H) * H + n]);
+        if (n < N && k < ke) v = to_f(W[wrow(perm, g0, k, H) * H + n]);
         Bs[kk][nn] = v;
       }
     }
@@ -90,6 +96,16 @@ __global__ __launch_bounds__(256) void step_gemm(const TS* __restrict__ a, long 
       if (n < N) out[(long long)m * N + n] = acc[i][j];
     }
   }
+}
+
+// out[i] = sum over z < nz, in order, of part[z * n + i]
+__global__ __launch_bounds__(256) void step_reduce(const float* __restrict__ part, int nz, long long n,
+                                                   float* __restrict__ out) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int z = 0; z < nz; ++z) s += part[(long long)z * n + i];
+  out[i] = s;
 }
 
 __device__ __forceinline__ int row_len(const RecArgs& a, int b) {
@@ -360,19 +376,36 @@ __global__ __launch_bounds__(256) void step_bwd_final(RecArgs a, const float* __
   if (a.dc0 && dcar) ((TS*)a.dc0)[i] = from_f<TS>(dcar[i]);
 }
 
+// One recurrent product into out ([M][N] fp32). Few output tiles (a small
+// batch): K is split over enough blocks to occupy the chip, the partials
+// going to `part` (part_floats available) and summed in a fixed order.
 template <typename TS, bool BT>
 hipError_t gemm_step(const TS* a, long long lda, int kshift, int kskip, int M, int K, const RecArgs& r, int g0, int N,
-                     float* out, hipStream_t s) {
+                     float* out, float* part, long long part_floats, hipStream_t s) {
   WPerm p;
   for (int i = 0; i < 4; ++i) p.p[i] = r.perm[i];
-  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 31) / 32));
+  const long long tiles = (long long)((N + 63) / 64) * ((M + 31) / 32);
+  const long long MN = (long long)M * N;
+  long long ks = (512 + tiles - 1) / tiles;
+  ks = std::min(ks, (long long)((K + 63) / 64));
+  ks = std::min(ks, part_floats / std::max(MN, 1LL));
+  if (ks < 2) ks = 1;
+  const int kchunk = (int)(((K + ks - 1) / ks + 31) / 32 * 32);
+  ks = (K + kchunk - 1) / kchunk;
+  const dim3 grid((unsigned)((N + 63) / 64), (unsigned)((M + 31) / 32), (unsigned)ks);
   hipLaunchKernelGGL((step_gemm<TS, BT>), grid, dim3(256), 0, s, a, lda, kshift, kskip, M, K, (const TS*)r.W_hh,
-                     r.H, p, g0, N, out);
+                     r.H, p, g0, N, kchunk, ks > 1 ? part : out);
+  if (ks > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(step_reduce, dim3((unsigned)((MN + 255) / 256)), dim3(256), 0, s, (const float*)part, (int)ks,
+                       MN, out);
+  }
   return hipGetLastError();
 }
 
 template <typename TS>
-hipError_t fwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
+hipError_t fwd_impl(int cell, const RecArgs& a, float* scratch, size_t floats, hipStream_t s) {
   const int B = a.B, H = a.H, T = a.T;
   const long long BH = (long long)B * H;
   const int GL = cell == CELL_LSTM ? 4 : (cell == CELL_GRU_RA ? 3 : 2);
@@ -381,13 +414,15 @@ hipError_t fwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
   float* cs = hs + BH;
   float* us = cs + BH;
   TS* hsA = (TS*)(us + BH);
+  float* part = us + 2 * BH;  // split-K partials in what remains
+  const long long pf = (long long)floats - (long long)(part - scratch);
   const unsigned nb = (unsigned)((BH + 255) / 256);
   hipLaunchKernelGGL((step_init<TS>), dim3(nb), dim3(256), 0, s, a.h0, cell == CELL_LSTM ? a.c0 : nullptr, BH, hs,
                      cell == CELL_LSTM ? cs : nullptr, hsA);
   hipError_t e = hipGetLastError();
   for (int st = 0; st < T && e == hipSuccess; ++st) {
     const int t = a.dir ? T - 1 - st : st;
-    if ((e = gemm_step<TS, false>(hsA, H, 1 << 30, 0, B, H, a, 0, GL * H, gh, s)) != hipSuccess) break;
+    if ((e = gemm_step<TS, false>(hsA, H, 1 << 30, 0, B, H, a, 0, GL * H, gh, part, pf, s)) != hipSuccess) break;
     if (cell == CELL_LSTM) {
       hipLaunchKernelGGL((step_fwd_cell<TS, CELL_LSTM>), dim3(B), dim3(256), 0, s, a, st, gh, hs, cs, hsA);
     } else if (cell == CELL_GRU_RA) {
@@ -396,7 +431,7 @@ hipError_t fwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
       hipLaunchKernelGGL((step_fwd_grub_a<TS>), dim3(B), dim3(256), 0, s, a, st, gh, hs, us);
       if ((e = hipGetLastError()) != hipSuccess) break;
       const TS* rh = (const TS*)a.rh + (long long)t * BH;
-      if ((e = gemm_step<TS, false>(rh, H, 1 << 30, 0, B, H, a, 2, H, gh, s)) != hipSuccess) break;
+      if ((e = gemm_step<TS, false>(rh, H, 1 << 30, 0, B, H, a, 2, H, gh, part, pf, s)) != hipSuccess) break;
       hipLaunchKernelGGL((step_fwd_grub_b<TS>), dim3(B), dim3(256), 0, s, a, st, gh, hs, us, hsA);
     }
     e = hipGetLastError();
@@ -405,7 +440,7 @@ hipError_t fwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
 }
 
 template <typename TS>
-hipError_t bwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
+hipError_t bwd_impl(int cell, const RecArgs& a, float* scratch, size_t floats, hipStream_t s) {
   const int B = a.B, H = a.H, T = a.T;
   const long long BH = (long long)B * H;
   const long long GDH = (long long)a.GD * H;
@@ -413,6 +448,8 @@ hipError_t bwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
   float* hcar = rec + BH;
   float* dcar = hcar + BH;
   float* dhs = dcar + BH;
+  float* part = dhs + BH;  // split-K partials in what remains
+  const long long pf = (long long)floats - 4 * BH;
   const unsigned nb = (unsigned)((BH + 255) / 256);
   hipLaunchKernelGGL((step_init<TS>), dim3(nb), dim3(256), 0, s, a.dhT, cell == CELL_LSTM ? a.dcT : nullptr, BH,
                      hcar, cell == CELL_LSTM ? dcar : nullptr, (TS*)nullptr);
@@ -422,9 +459,9 @@ hipError_t bwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
       // the previous processing step's gate gradients against W_hh
       const int tn = a.dir ? n - 1 : T - n;
       const TS* dgp = (const TS*)a.dg + (long long)tn * B * GDH;
-      if (cell == CELL_LSTM) e = gemm_step<TS, true>(dgp, GDH, 1 << 30, 0, B, 4 * H, a, 0, H, rec, s);
-      else if (cell == CELL_GRU_RA) e = gemm_step<TS, true>(dgp, GDH, 2 * H, H, B, 3 * H, a, 0, H, rec, s);
-      else e = gemm_step<TS, true>(dgp, GDH, 1 << 30, 0, B, 2 * H, a, 0, H, rec, s);
+      if (cell == CELL_LSTM) e = gemm_step<TS, true>(dgp, GDH, 1 << 30, 0, B, 4 * H, a, 0, H, rec, part, pf, s);
+      else if (cell == CELL_GRU_RA) e = gemm_step<TS, true>(dgp, GDH, 2 * H, H, B, 3 * H, a, 0, H, rec, part, pf, s);
+      else e = gemm_step<TS, true>(dgp, GDH, 1 << 30, 0, B, 2 * H, a, 0, H, rec, part, pf, s);
       if (e != hipSuccess) break;
     }
     if (n == T) {
@@ -442,7 +479,7 @@ hipError_t bwd_impl(int cell, const RecArgs& a, float* scratch, hipStream_t s) {
       if ((e = hipGetLastError()) != hipSuccess) break;
       const int t = a.dir ? n : T - 1 - n;
       const TS* dc = (const TS*)a.dg + (long long)t * B * GDH + 2 * H;
-      if ((e = gemm_step<TS, true>(dc, GDH, 1 << 30, 0, B, H, a, 2, H, rec, s)) != hipSuccess) break;
+      if ((e = gemm_step<TS, true>(dc, GDH, 1 << 30, 0, B, H, a, 2, H, rec, part, pf, s)) != hipSuccess) break;
       hipLaunchKernelGGL((step_bwd_grub_b<TS>), dim3(B), dim3(256), 0, s, a, n, rec, hcar, dhs);
     }
     e = hipGetLastError();
@@ -460,12 +497,14 @@ size_t stepwise_scratch_floats(int cell, int B, int H) {
   return (size_t)(fwd > bwd ? fwd : bwd);
 }
 
-hipError_t stepwise_fwd(int cell, int dtype, const RecArgs& a, float* scratch, hipStream_t s) {
-  return dtype ? fwd_impl<bf16>(cell, a, scratch, s) : fwd_impl<float>(cell, a, scratch, s);
+hipError_t stepwise_fwd(int cell, int dtype, const RecArgs& a, float* scratch, size_t floats, hipStream_t s) {
+  if (floats < stepwise_scratch_floats(cell, a.B, a.H)) return hipErrorInvalidValue;
+  return dtype ? fwd_impl<bf16>(cell, a, scratch, floats, s) : fwd_impl<float>(cell, a, scratch, floats, s);
 }
 
-hipError_t stepwise_bwd(int cell, int dtype, const RecArgs& a, float* scratch, hipStream_t s) {
-  return dtype ? bwd_impl<bf16>(cell, a, scratch, s) : bwd_impl<float>(cell, a, scratch, s);
+hipError_t stepwise_bwd(int cell, int dtype, const RecArgs& a, float* scratch, size_t floats, hipStream_t s) {
+  if (floats < stepwise_scratch_floats(cell, a.B, a.H)) return hipErrorInvalidValue;
+  return dtype ? bwd_impl<bf16>(cell, a, scratch, floats, s) : bwd_impl<float>(cell, a, scratch, floats, s);
 }
 
 }  // namespace rnn
