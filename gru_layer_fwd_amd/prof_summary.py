@@ -53,6 +53,8 @@ def step_labels(names):
             lab = "dx_gemm (W_ih transpose)" if phase == "after_bwd" else "rec_bwd (W_hh transpose)"
         elif "gather_transpose" in n:
             lab = "dw_gemm (transposes)" if phase == "after_bwd" else "aux"
+        elif "dw_partials_finish" in n:
+            lab = "dw_gemm (finish)"
         elif "splitk_finish" in n or "rowsum_finish" in n or "rowsum_rows" in n:
             lab = "dw_gemm (finish)" if phase == "after_bwd" else "proj_gemm (finish)"
         elif "colsum" in n:

@@ -14,6 +14,9 @@ def test_step_labels_follow_dispatch_order():
             "dw_gemm", "dw_gemm (finish)", "dw_gemm (finish)"]
     # two steps in a row: the second starts over at its fill
     assert step_labels(step + step) == want + want
+    # fused recurrent-weight gradient: the partial sums' finishing pass
+    assert step_labels(["rec_bwd<...>", "gemm_kernel<dx>", "gemm_kernel<dW_ih>", "dw_partials_finish<float>"])[-1] \
+        == "dw_gemm (finish)"
 
 
 def test_counter_tables_from_a_multi_counter_pass(tmp_path):
