@@ -542,3 +542,32 @@ def test_fused_recurrent_weight_gradient(cell, B, H, direction):
     # the rest of the backward pass does not depend on where dW_hh is formed
     for k in ("dx", "dh0", "dW_ih", "db_ih"):
         np.testing.assert_array_equal(got[k], sep[k], err_msg=k)
+
+
+@pytest.mark.parametrize("cell,order", [("lstm", (3, 1, 0, 2)), ("gru_ra", (2, 0, 1)), ("gru_basic", (1, 2, 0))])
+@pytest.mark.parametrize("stepwise", [False, True])
+def test_permuted_gate_order_paths(cell, order, stepwise):
+    """A storage order other than the canonical one through the fused dW_hh
+    (the fp32 LSTM and reset-after GRU plans of this shape) and through the
+    per-step path: weights, biases and their gradients addressed through the
+    permutation; then accumulation into the gradients (twice the one-call
+    values)."""
+    from gru_layer_fwd_amd import _lib as L
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=9, B=7, I=24, H=64, w_scale=0.2, h0_std=0.5, c0_std=0.5)
+    if cell != "lstm":
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    if not stepwise and cell != "gru_basic":
+        d = L.make_desc(L.RNN_LSTM if cell == "lstm" else L.RNN_GRU, wl.T, wl.B, wl.I, wl.H, L.RNN_F32, 1, 1,
+                        order)
+        st, plan = L.rnn_plan_query(d, 1)
+        assert st == 0 and plan.fused_dw == 1
+    P = _permute_params(P, order, wl.H)
+    lens = _ragged_lengths(wl.B, wl.T, 53)
+    got, ref = _run(wl, inp, P, 1, order, lengths=lens, stepwise=stepwise)
+    print(compare(got, ref, "f32", extra=f"{cell} order={order} stepwise={stepwise}"))
+    twice = gpu_layer(wl.mode, wl.dtype, P, inp["x"], inp["h0"], inp["c0"], inp["g"], None, None, 1,
+                      wl.reset_after, order, acc=True, repeat=2, lengths=lens, stepwise=stepwise)[1]
+    for k in ("dW_ih", "dW_hh", "db_ih", "db_hh", "dx"):
+        np.testing.assert_allclose(twice[k], 2 * got[k], rtol=1e-5, atol=1e-6, err_msg=k)
