@@ -259,6 +259,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   constexpr int FM = WM / 16, FN = WN / 16;
   auto sA = [&](int b) { return smem + b * (TILE_A + TILE_B); };
   auto sB = [&](int b) { return smem + b * (TILE_A + TILE_B) + TILE_A; };
+  float* const sbias = (float*)(smem + 2 * (TILE_A + TILE_B));  // direct-load kernel: [BN] column biases
 
   const int nM = (int)((g.M + BM - 1) / BM), nN = (int)((g.N + BN - 1) / BN);
   const Tile tl = tile_of(nM, nN, g.ksplit);
@@ -280,6 +281,33 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   const int nk = (ke > kb) ? (int)((ke - kb + BK - 1) / BK) : 0;
   const bool want_rows = AKO && g.rowsum != nullptr && tl.n == 0;
 
+  const bool part_out = g.ksplit > 1;
+  // column biases: the register path keeps column r16 of each 16-column
+  // tile in registers; the direct-load kernel stages the tile's BN column
+  // biases in LDS (one per thread, loaded now and stored after the first
+  // k-tile's wait, which covers the load)
+  float colbias[FN];
+  float bias_v = 0.f;
+  if constexpr (DMA) {
+    const long long n = n0 + threadIdx.x;
+    if (!part_out && g.bias1 && threadIdx.x < BN && n < g.N) {
+      const long long gg = n / g.H;
+      const long long src = pick4(g.perm, gg) * g.H + (n - gg * g.H);
+      bias_v = to_f(((const TS*)g.bias1)[src]);
+      if (g.bias2 && gg != g.bias_skip_gate) bias_v += to_f(((const TS*)g.bias2)[src]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    colbias[j] = 0.f;
+    const long long n = n0 + wn * WN + j * 16 + r16;
+    if (!DMA && !part_out && g.bias1 && n < g.N) {
+      const long long gg = n / g.H;
+      const long long src = pick4(g.perm, gg) * g.H + (n - gg * g.H);
+      colbias[j] = to_f(((const TS*)g.bias1)[src]);
+      if (g.bias2 && gg != g.bias_skip_gate) colbias[j] += to_f(((const TS*)g.bias2)[src]);
+    }
+  }
   f4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -345,7 +373,11 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     // The fragments of the second k-step are read between the products of
     // the first (one A and at most one B fragment per row of products), so
     // their LDS latency hides behind MFMAs; the scheduling barriers keep the
-    // compiler from gathering the reads back into one block.
+    // compiler from gathering the reads back into one block. The MFMA
+    // operands are swapped (B tile rows as the A operand), so that a lane's
+    // accumulator holds 4 consecutive output columns of one row (column
+    // 4q+e of tile j, row r16 of tile i), which the epilogue stages in LDS as
+    // one 8-byte (bf16) or 16-byte (fp32) write instead of four 2-byte ones.
     // row sums: one thread per A row, N tiles below rsp = min(nN, 8) take part
     const int rsp = nN < 8 ? nN : 8;
     const bool rows_kc = g.rowsum != nullptr && tl.n < rsp && threadIdx.x < BM;
@@ -354,6 +386,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     for (int kt = 0; kt < nk; ++kt) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+      if (kt == 0 && threadIdx.x < BN) sbias[threadIdx.x] = bias_v;
       if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
       const char* A = sA(kt & 1);
       const char* Bp = sB(kt & 1);
@@ -365,7 +398,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a0[i], b0[j]);
+        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], b0[j], a0[i]);
         a1[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, 4 + q));
         if (i < FN) b1[i] = *(const uint4*)(Bp + lds_off(wn * WN + i * 16 + r16, 4 + q));
         __builtin_amdgcn_sched_barrier(0);
@@ -373,7 +406,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], a1[i], b1[j]);
+        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], b1[j], a1[i]);
       // A written out transposed: every k-tile, N tile n takes rows
       // [n * rpw, (n+1) * rpw) of the tile in blocks of 8 rows x 2 k (one
       // dword per row from LDS, two output chunks built by byte permutes),
@@ -429,6 +462,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
         }
       }
     }
+    if (nk == 0 && threadIdx.x < BN) sbias[threadIdx.x] = bias_v;
     __syncthreads();
     if (rows_kc && m0 + threadIdx.x < g.M)
       g.rowsum[((long long)tl.kz * g.rs_parts + tl.n) * g.M + m0 + threadIdx.x] = rsum;
@@ -501,26 +535,16 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
   }
 
   // Epilogue. Each wave stages its WM x WN sub-tile in a private 16 KiB
-  // region of LDS (free after the main loop), in row-major order with 32-byte
-  // (bf16) or 64-byte (fp32) blocks XOR-swizzled by row so that the MFMA
-  // layout writes (lane: column r16 of rows 4q+e) spread over the banks, and
-  // writes it back as whole 16-byte chunks, 8 or 16 lanes per output row.
+  // region of LDS (free after the main loop), in row-major order with its
+  // 16-byte pieces XOR-swizzled by row so that the MFMA layout writes spread
+  // over the banks (register path: lane holds column r16 of rows 4q+e, the
+  // pieces permuted in 32- or 64-byte blocks; direct-load kernel: 4 columns
+  // of row r16 per lane, the pieces permuted by (r/2)%8 for bf16 and r%16 for
+  // fp32), and writes it back as whole 16-byte chunks, 8 or 16 lanes per
+  // output row.
   // Split-K slices store their raw fp32 partial tiles; otherwise the column
   // bias is added, rows are mapped (gate-block permutation for c_kind 1) and
   // the storage type is written (added to C when accumulating).
-  const bool part_out = g.ksplit > 1;
-  float colbias[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    colbias[j] = 0.f;
-    const long long n = n0 + wn * WN + j * 16 + r16;
-    if (!part_out && g.bias1 && n < g.N) {
-      const long long gg = n / g.H;
-      const long long src = pick4(g.perm, gg) * g.H + (n - gg * g.H);
-      colbias[j] = to_f(((const TS*)g.bias1)[src]);
-      if (g.bias2 && gg != g.bias_skip_gate) colbias[j] += to_f(((const TS*)g.bias2)[src]);
-    }
-  }
   char* stage = smem + w * 16384;
   auto run = [&](auto zero_ot) {
     using OT = decltype(zero_ot);
@@ -528,20 +552,39 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
     constexpr int CH = 16384 / RB < WM ? 16384 / RB : WM;
     constexpr int CPR = RB / 16;                   // 16-byte chunks per row
     constexpr int EPC = 16 / (int)sizeof(OT);      // elements per chunk
-    auto sw = [](int r) { return (RB == 128) ? (((r >> 2) & 3) << 5) : (((r >> 2) & 1) << 6); };
+    // 16-byte piece c of staged row r sits at piece pc(r, c)
+    auto pc = [](int r, int c) {
+      if constexpr (DMA) return (sizeof(OT) == 2) ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
+      else return c ^ (((RB == 128) ? (((r >> 2) & 3) << 5) : (((r >> 2) & 1) << 6)) >> 4);
+    };
 #pragma unroll
     for (int c0 = 0; c0 < WM; c0 += CH) {
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         if (i * 16 < c0 || i * 16 >= c0 + CH) continue;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          if constexpr (DMA) {
+            const int r = i * 16 + r16 - c0;
+            const int col = j * 16 + 4 * q;
+            if constexpr (sizeof(OT) == 2) {
+              const f4 bv = part_out ? f4{0.f, 0.f, 0.f, 0.f} : *(const f4*)(sbias + wn * WN + col);
+              OT o[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = i * 16 + q * 4 + e - c0;
-            const int byte = (j * 16 + r16) * (int)sizeof(OT);
-            *(OT*)(stage + r * RB + (byte ^ sw(r))) = (OT)(acc[i][j][e] + colbias[j]);
+              for (int e = 0; e < 4; ++e) o[e] = (OT)(acc[i][j][e] + bv[e]);
+              *(uint2*)(stage + r * RB + pc(r, col >> 3) * 16 + (col & 7) * 2) = *(const uint2*)o;
+            } else {
+              *(f4*)(stage + r * RB + pc(r, col >> 2) * 16) = acc[i][j];
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = i * 16 + q * 4 + e - c0;
+              const int byte = (j * 16 + r16) * (int)sizeof(OT);
+              *(OT*)(stage + r * RB + pc(r, byte >> 4) * 16 + (byte & 15)) = (OT)(acc[i][j][e] + colbias[j]);
+            }
           }
+        }
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the wave's own LDS writes
       __builtin_amdgcn_wave_barrier();
@@ -549,7 +592,7 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
       for (int it = 0; it < CH * CPR / 64; ++it) {
         const int idx = it * 64 + lane;
         const int r = idx / CPR, c = idx - r * CPR;
-        const uint4 v = *(const uint4*)(stage + r * RB + ((c * 16) ^ sw(r)));
+        const uint4 v = *(const uint4*)(stage + r * RB + pc(r, c) * 16);
         const long long m = m0 + wm * WM + c0 + r;
         const long long n = n0 + wn * WN + c * EPC;
         const long long nl = nb0 + wn * WN + c * EPC;  // column within the output part
@@ -905,7 +948,7 @@ __global__ void fill_i32(int* p, int v, long long n) {
 template <typename TS, bool AKO, bool BKO, int BM, int BN, bool SPLIT, bool DMA = false>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
   const void* f = (const void*)gemm_kernel<TS, AKO, BKO, BM, BN, SPLIT, DMA>;
-  const int lds = 2 * (BM + BN) * ROWB;
+  const int lds = 2 * (BM + BN) * ROWB + (DMA ? BN * (int)sizeof(float) : 0);
   static bool attr = false;
   if (!attr) {
     hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
