@@ -76,10 +76,13 @@ bool shape_supported(const rnn_desc_t* d) {
   return true;
 }
 
-// bf16 LSTM layers run the weight gradients as one product over k-contiguous
-// (transposed) operands; T*B is then a whole number of 16-byte chunks
+// bf16 LSTM and reset-after GRU layers run the weight gradients as products
+// over k-contiguous (transposed) operands; T*B is then a whole number of
+// 16-byte chunks
 bool nt_weight_grads(const rnn_desc_t* d) {
-  return d->mode == RNN_LSTM && d->dtype == RNN_BF16 && ((long long)d->T * d->B) % 8 == 0;
+  const int cell = cell_of(d);
+  return (cell == rnn::CELL_LSTM || cell == rnn::CELL_GRU_RA) && d->dtype == RNN_BF16 &&
+         ((long long)d->T * d->B) % 8 == 0;
 }
 
 // Step-counter layout of a plan (see FLAG_LINE): adjacent counters for a
@@ -133,6 +136,14 @@ Layout layout(const rnn_desc_t* d) {
     if (f2 > f) f = f2;
     if (f3 > f) f = f3;
     if (cell == rnn::CELL_LSTM && f4 > f) f = f4;
+    if (cell == rnn::CELL_GRU_RA) {
+      // the reset-after GRU's k-contiguous weight gradients: the r and u rows
+      // over [x | h_{t-1}], then the candidate rows of each side
+      const size_t f6 = rnn::gemm_workspace_floats(2LL * d->H, (long long)d->I + d->H, (long long)TB, PLAN_CUS);
+      const size_t f7 = rnn::gemm_workspace_floats(d->H, nmax, (long long)TB, PLAN_CUS);
+      if (f6 > f) f = f6;
+      if (f7 > f) f = f7;
+    }
     // the per-step recurrence keeps its carried state here between launches
     const size_t f5 = rnn::stepwise_scratch_floats(cell, d->B, d->H);
     if (f5 > f) f = f5;
@@ -168,12 +179,13 @@ Layout layout(const rnn_desc_t* d) {
   // W_hh transposed to [H][G*H] in the BPTT kernel's contraction order
   L.wht = off;
   if (cell_of(d) != rnn::CELL_GRU_BASIC) off += up((size_t)H * gates(d) * H * s);
-  // bf16 LSTM: the weight-gradient product as a k-contiguous one: the gate
-  // gradients, x and h_{t-1} transposed to [.][T*B]
+  // bf16 LSTM and reset-after GRU: the weight-gradient products as
+  // k-contiguous ones: the gate gradients (all GD lanes), x and h_{t-1}
+  // transposed to [.][T*B]
   L.dgt = L.xt = L.ht = off;
   if (nt_weight_grads(d)) {
     L.dgt = off;
-    off += up(TB * 4 * H * s);
+    off += up(TB * L.GD * H * s);
     L.xt = off;
     off += up(TB * (size_t)d->I * s);
     L.ht = off;
@@ -794,10 +806,20 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
       g.ld_at = g.M;
     }
     if ((st = hip_status(gemm_dt(d->dtype, g, false, !wt, s)))) return st;
+    if (nt_weight_grads(d) && L.GD > G) {
+      // reset-after GRU: the lane the input gradient does not read (the
+      // candidate gradient times r, for the recurrent side) by a transpose
+      ProfScope ps2(L_AUX, s);
+      const long long TB = (long long)d->T * d->B;
+      const hipError_t e = rnn::launch_gather_transpose<bf16>(
+          rows(ws + L.dg + (size_t)G * d->H * esz(d), (long long)L.GD * d->H), (L.GD - G) * d->H, d->T, d->B,
+          ws + L.dgt + (size_t)G * d->H * TB * esz(d), s);
+      if ((st = hip_status(e))) return st;
+    }
   } else if (nt_weight_grads(d)) {
     ProfScope ps(L_AUX, s);
-    const hipError_t e = rnn::launch_gather_transpose<bf16>(rows(ws + L.dg, (long long)L.GD * d->H), 4 * d->H, d->T,
-                                                            d->B, ws + L.dgt, s);
+    const hipError_t e = rnn::launch_gather_transpose<bf16>(rows(ws + L.dg, (long long)L.GD * d->H), L.GD * d->H,
+                                                            d->T, d->B, ws + L.dgt, s);
     if ((st = hip_status(e))) return st;
   }
   return RNN_OK;
@@ -985,7 +1007,50 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
   // (equal for the two biases) come from its row sums
   const bool fused = fused_groups > 0;
   const bool merged = cell == rnn::CELL_LSTM && dW_ih && dW_hh && d->I % 256 == 0 && !fused;
-  if (merged && nt_weight_grads(d)) {
+  // reset-after GRU (bf16): the r and u rows as one product over
+  // [x | h_{t-1}] like the LSTM's; the candidate rows take different
+  // gradients on the two sides (d_c against x, d_c * r against h_{t-1}), two
+  // products of their own
+  const bool gra_nt = cell == rnn::CELL_GRU_RA && dW_ih && dW_hh && d->I % 256 == 0 && !fused && nt_weight_grads(d);
+  if (gra_nt) {
+    ProfScope ps(L_DW, s);
+    hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
+    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(hprev, H, d->T, d->B, ws + L.ht, s);
+    if ((st = hip_status(e))) return st;
+    // A rows [lane*H, ...) of the transposed gate gradients
+    auto prod = [&](int lane, long long M, rnn::RowMap b, long long N, void* c, long long ldc, long long row0,
+                    void* rs1, void* rs2) {
+      rnn::GemmArgs g{};
+      g.a = rows(ws + L.dgt + (size_t)lane * H * TB * s_el, TB);
+      g.b = b;
+      g.M = M;
+      g.N = N;
+      g.K = TB;
+      g.c = c;
+      g.ldc = ldc;
+      g.c_kind = 1;
+      g.c_row0 = row0;
+      g.H = H;
+      for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+      g.accumulate = acc;
+      g.part = (float*)(ws + L.gemm);
+      g.ws_floats = (long long)L.gemm_floats;
+      g.rowsum_out = rs1;
+      g.rowsum_out2 = rs2;
+      return g;
+    };
+    rnn::GemmArgs g = prod(0, 2LL * H, rows(ws + L.xt, TB), (long long)d->I + H, dW_ih, d->I, 0, db_ih ? db_ih : db_hh,
+                           db_ih ? db_hh : nullptr);
+    g.b2 = rows(ws + L.ht, TB);
+    g.n_split = d->I;
+    g.c2 = dW_hh;
+    g.ldc2 = H;
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+    g = prod(2, H, rows(ws + L.xt, TB), d->I, dW_ih, d->I, 2LL * H, db_ih, nullptr);
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+    g = prod(3, H, rows(ws + L.ht, TB), H, dW_hh, H, 2LL * H, db_hh, nullptr);
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+  } else if (merged && nt_weight_grads(d)) {
     // the same product with k-contiguous operands: dG^T (written by the
     // input-gradient product) against x^T and h_{t-1}^T; the bias gradients
     // from its row sums
@@ -1056,7 +1121,7 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
       return st;
   }
   if (dW_hh && !fused) {
-    if (merged) {
+    if (merged || gra_nt) {
       // done above
     } else if (cell == rnn::CELL_LSTM) {
       if ((st = hip_status(dW(dW_hh, 0, 4LL * H, 0, hprev, H, db_hh)))) return st;

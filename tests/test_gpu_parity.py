@@ -92,15 +92,36 @@ def test_accumulate_and_skip_dx():
         np.testing.assert_array_equal(nodx[k], once[k])
 
 
-def test_bf16_lstm_weight_gradients_without_dx():
-    # bf16 LSTM weight gradients run over transposed gate gradients, written
-    # by the input-gradient product or, when dx is not requested, by a
-    # transpose of their own: both give the same values
-    wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=16, B=32, I=256, H=256, h0_std=0.3, c0_std=0.3)
-    once = gpu_layer("lstm", "bf16", P, inp["x"], inp["h0"], inp["c0"], inp["g"])
-    nodx = gpu_layer("lstm", "bf16", P, inp["x"], inp["h0"], inp["c0"], inp["g"], want_dx=False)
+@pytest.mark.parametrize("cell", ["lstm", "gru_ra"])
+def test_bf16_weight_gradients_without_dx(cell):
+    # bf16 LSTM and reset-after GRU weight gradients run over transposed gate
+    # gradients, written by the input-gradient product (and, for the GRU's
+    # candidate-times-r lane, by a transpose) or, when dx is not requested,
+    # by a transpose of their own: both give the same values
+    if cell == "lstm":
+        wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=16, B=32, I=256, H=256, h0_std=0.3, c0_std=0.3)
+        mode, c0 = "lstm", inp["c0"]
+    else:
+        wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=16, B=24, I=256, H=128, h0_std=0.3)
+        mode, c0 = "gru", None
+    once = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"])
+    nodx = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"], want_dx=False)
     for k in ("dW_ih", "dW_hh", "db_ih", "db_hh", "dh0", "dc0", "y"):
-        np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
+        if k in once:
+            np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
+
+
+@pytest.mark.parametrize("direction,ragged", [(0, False), (1, True)])
+def test_grura_bf16_transposed_weight_gradients(direction, ragged):
+    # reset-after GRU, bf16, I a multiple of 256: the r and u rows of both
+    # weight gradients as one product over [x | h_{t-1}] and the candidate
+    # rows as two products (d_c against x, d_c * r against h_{t-1}), all over
+    # transposed operands; direction 1 with ragged lengths adds the h0 terms
+    # of the rows that start late
+    wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=14, B=24, I=256, H=128, h0_std=0.3)
+    L = _ragged_lengths(wl.B, wl.T, 21 + direction) if ragged else None
+    got, ref = _run(wl, inp, P, direction, lengths=L)
+    print(compare(got, ref, "bf16", extra=f"grura nt dir{direction} ragged={ragged}"))
 
 
 @pytest.mark.parametrize("order,direction", [((1, 0, 2, 3), 0), ((3, 2, 0, 1), 1)])
@@ -133,6 +154,7 @@ def test_deterministic_repeats():
 @pytest.mark.parametrize("name,changes", [
     ("lstm_bf16_t256_b64_i1024_h1024", dict(T=16, B=32, I=256, H=256)),
     ("grura_bf16_t128_b128_i2048_h2048", dict(T=16, B=20, I=128, H=128)),
+    ("grura_bf16_t128_b128_i2048_h2048", dict(T=16, B=16, I=256, H=128)),
     ("grura_bf16_t128_b128_i2048_h2048", dict(T=12, B=16, I=64, H=64, reset_after=False)),
 ])
 def test_bf16_medium(name, changes):
