@@ -34,7 +34,7 @@ long long ldy_of(const rnn_desc_t* d) { return d->ldy ? d->ldy : (d->direction =
 size_t esz(const rnn_desc_t* d) { return d->dtype == RNN_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, wht, dgt, xt, ht, dwp, dwp_bytes,
+  size_t status, flags, partial, gemm, z, c, rh, dg, xb, xb_bytes, gath, attp, wt, wht, dgt, xt, ht, rht, dwp, dwp_bytes,
       total;
   size_t gemm_floats;
   int GZ, GD;
@@ -76,13 +76,12 @@ bool shape_supported(const rnn_desc_t* d) {
   return true;
 }
 
-// bf16 LSTM and reset-after GRU layers run the weight gradients as products
-// over k-contiguous (transposed) operands; T*B is then a whole number of
-// 16-byte chunks
+// bf16 layers run the weight gradients as products over k-contiguous
+// (transposed) operands, the input- and recurrent-side columns of a gate row
+// in one product split at column I (a whole number of 256-wide tiles); T*B is
+// then a whole number of 16-byte chunks
 bool nt_weight_grads(const rnn_desc_t* d) {
-  const int cell = cell_of(d);
-  return (cell == rnn::CELL_LSTM || cell == rnn::CELL_GRU_RA) && d->dtype == RNN_BF16 &&
-         ((long long)d->T * d->B) % 8 == 0;
+  return d->dtype == RNN_BF16 && ((long long)d->T * d->B) % 8 == 0 && d->I % 256 == 0;
 }
 
 // Step-counter layout of a plan (see FLAG_LINE): adjacent counters for a
@@ -136,13 +135,16 @@ Layout layout(const rnn_desc_t* d) {
     if (f2 > f) f = f2;
     if (f3 > f) f = f3;
     if (cell == rnn::CELL_LSTM && f4 > f) f = f4;
-    if (cell == rnn::CELL_GRU_RA) {
-      // the reset-after GRU's k-contiguous weight gradients: the r and u rows
-      // over [x | h_{t-1}], then the candidate rows of each side
+    if (cell != rnn::CELL_LSTM) {
+      // the GRUs' k-contiguous weight gradients: the r and u rows over
+      // [x | h_{t-1}], then the candidate rows (reset-after: each side on its
+      // own; basic: one product over [x | r*h_{t-1}])
       const size_t f6 = rnn::gemm_workspace_floats(2LL * d->H, (long long)d->I + d->H, (long long)TB, PLAN_CUS);
       const size_t f7 = rnn::gemm_workspace_floats(d->H, nmax, (long long)TB, PLAN_CUS);
+      const size_t f8 = rnn::gemm_workspace_floats(d->H, (long long)d->I + d->H, (long long)TB, PLAN_CUS);
       if (f6 > f) f = f6;
       if (f7 > f) f = f7;
+      if (f8 > f) f = f8;
     }
     // the per-step recurrence keeps its carried state here between launches
     const size_t f5 = rnn::stepwise_scratch_floats(cell, d->B, d->H);
@@ -191,6 +193,9 @@ Layout layout(const rnn_desc_t* d) {
     L.ht = off;
     off += up(TB * H * s);
   }
+  // basic GRU: r*h_{t-1} transposed as well (the candidate rows' activation)
+  L.rht = off;
+  if (nt_weight_grads(d) && cell == rnn::CELL_GRU_BASIC) off += up(TB * H * s);
   // fp32 reset-after GRU (H <= 256) and LSTM (H <= 128): per batch group
   // (>= 4 rows) partial recurrent-weight gradients of the fused BPTT kernel
   L.dwp = off;
@@ -1011,7 +1016,10 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
   // [x | h_{t-1}] like the LSTM's; the candidate rows take different
   // gradients on the two sides (d_c against x, d_c * r against h_{t-1}), two
   // products of their own
-  const bool gra_nt = cell == rnn::CELL_GRU_RA && dW_ih && dW_hh && d->I % 256 == 0 && !fused && nt_weight_grads(d);
+  const bool gra_nt = cell == rnn::CELL_GRU_RA && dW_ih && dW_hh && !fused && nt_weight_grads(d);
+  // basic GRU (bf16): the candidate rows see r * h_{t-1} on the recurrent
+  // side and the same gradient d_c on both, so they too are one product
+  const bool grb_nt = cell == rnn::CELL_GRU_BASIC && dW_ih && dW_hh && !fused && nt_weight_grads(d);
   if (gra_nt) {
     ProfScope ps(L_DW, s);
     hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
@@ -1050,6 +1058,40 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
     if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
     g = prod(3, H, rows(ws + L.ht, TB), H, dW_hh, H, 2LL * H, db_hh, nullptr);
     if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
+  } else if (grb_nt) {
+    ProfScope ps(L_DW, s);
+    hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
+    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(hprev, H, d->T, d->B, ws + L.ht, s);
+    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(rows(ws + L.rh, H), H, d->T, d->B, ws + L.rht, s);
+    if ((st = hip_status(e))) return st;
+    // rows [lane*H, lane*H + M) of both weight gradients, one product over
+    // [x | act]; the two bias gradients of those rows are equal
+    auto prod = [&](int lane, long long M, const char* act) {
+      rnn::GemmArgs g{};
+      g.a = rows(ws + L.dgt + (size_t)lane * H * TB * s_el, TB);
+      g.b = rows(ws + L.xt, TB);
+      g.b2 = rows(act, TB);
+      g.n_split = d->I;
+      g.M = M;
+      g.N = (long long)d->I + H;
+      g.K = TB;
+      g.c = dW_ih;
+      g.ldc = d->I;
+      g.c2 = dW_hh;
+      g.ldc2 = H;
+      g.c_kind = 1;
+      g.c_row0 = (long long)lane * H;
+      g.H = H;
+      for (int i = 0; i < 4; ++i) g.perm[i] = perm[i];
+      g.accumulate = acc;
+      g.part = (float*)(ws + L.gemm);
+      g.ws_floats = (long long)L.gemm_floats;
+      g.rowsum_out = db_ih ? db_ih : db_hh;
+      g.rowsum_out2 = db_ih ? db_hh : nullptr;
+      return gemm_dt(d->dtype, g, false, false, s);
+    };
+    if ((st = hip_status(prod(0, 2LL * H, ws + L.ht)))) return st;
+    if ((st = hip_status(prod(2, H, ws + L.rht)))) return st;
   } else if (merged && nt_weight_grads(d)) {
     // the same product with k-contiguous operands: dG^T (written by the
     // input-gradient product) against x^T and h_{t-1}^T; the bias gradients
@@ -1121,7 +1163,7 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
       return st;
   }
   if (dW_hh && !fused) {
-    if (merged || gra_nt) {
+    if (merged || gra_nt || grb_nt) {
       // done above
     } else if (cell == rnn::CELL_LSTM) {
       if ((st = hip_status(dW(dW_hh, 0, 4LL * H, 0, hprev, H, db_hh)))) return st;

@@ -92,36 +92,40 @@ def test_accumulate_and_skip_dx():
         np.testing.assert_array_equal(nodx[k], once[k])
 
 
-@pytest.mark.parametrize("cell", ["lstm", "gru_ra"])
+@pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
 def test_bf16_weight_gradients_without_dx(cell):
-    # bf16 LSTM and reset-after GRU weight gradients run over transposed gate
-    # gradients, written by the input-gradient product (and, for the GRU's
+    # bf16 weight gradients run over transposed gate gradients, written by
+    # the input-gradient product (and, for the reset-after GRU's
     # candidate-times-r lane, by a transpose) or, when dx is not requested,
     # by a transpose of their own: both give the same values
     if cell == "lstm":
         wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=16, B=32, I=256, H=256, h0_std=0.3, c0_std=0.3)
         mode, c0 = "lstm", inp["c0"]
     else:
-        wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=16, B=24, I=256, H=128, h0_std=0.3)
+        wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=16, B=24, I=256, H=128, h0_std=0.3,
+                           reset_after=cell == "gru_ra")
         mode, c0 = "gru", None
-    once = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"])
-    nodx = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"], want_dx=False)
+    ra = cell != "gru_basic"
+    once = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"], reset_after=ra)
+    nodx = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"], want_dx=False, reset_after=ra)
     for k in ("dW_ih", "dW_hh", "db_ih", "db_hh", "dh0", "dc0", "y"):
         if k in once:
             np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
 
 
+@pytest.mark.parametrize("ra", [True, False])
 @pytest.mark.parametrize("direction,ragged", [(0, False), (1, True)])
-def test_grura_bf16_transposed_weight_gradients(direction, ragged):
-    # reset-after GRU, bf16, I a multiple of 256: the r and u rows of both
-    # weight gradients as one product over [x | h_{t-1}] and the candidate
-    # rows as two products (d_c against x, d_c * r against h_{t-1}), all over
-    # transposed operands; direction 1 with ragged lengths adds the h0 terms
-    # of the rows that start late
-    wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=14, B=24, I=256, H=128, h0_std=0.3)
+def test_gru_bf16_transposed_weight_gradients(ra, direction, ragged):
+    # GRU, bf16, I a multiple of 256: the r and u rows of both weight
+    # gradients as one product over [x | h_{t-1}]; the candidate rows as two
+    # products (reset-after: d_c against x, d_c * r against h_{t-1}) or as
+    # one over [x | r * h_{t-1}] (basic), all over transposed operands;
+    # direction 1 with ragged lengths adds the h0 terms of the rows that
+    # start late
+    wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=14, B=24, I=256, H=128, h0_std=0.3, reset_after=ra)
     L = _ragged_lengths(wl.B, wl.T, 21 + direction) if ragged else None
     got, ref = _run(wl, inp, P, direction, lengths=L)
-    print(compare(got, ref, "bf16", extra=f"grura nt dir{direction} ragged={ragged}"))
+    print(compare(got, ref, "bf16", extra=f"gru ra={ra} nt dir{direction} ragged={ragged}"))
 
 
 @pytest.mark.parametrize("order,direction", [((1, 0, 2, 3), 0), ((3, 2, 0, 1), 1)])
