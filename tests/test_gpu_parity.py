@@ -113,6 +113,29 @@ def test_bf16_weight_gradients_without_dx(cell):
             np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
 
 
+@pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
+def test_bf16_transposed_weight_gradients_accumulate(cell):
+    # accumulate = 1 over the transposed weight-gradient products (both
+    # output parts of the merged product, the candidate rows, the bias row
+    # sums): a second call adds its gradients to the first call's stored ones
+    if cell == "lstm":
+        wl, inp, P = _case("lstm_bf16_t256_b64_i1024_h1024", T=8, B=16, I=256, H=128, h0_std=0.3, c0_std=0.3)
+        mode, c0 = "lstm", inp["c0"]
+    else:
+        wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=8, B=16, I=256, H=128, h0_std=0.3,
+                           reset_after=cell == "gru_ra")
+        mode, c0 = "gru", None
+    ra = cell != "gru_basic"
+    once = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"], reset_after=ra)
+    twice = gpu_layer(mode, "bf16", P, inp["x"], inp["h0"], c0, inp["g"], reset_after=ra, acc=True, repeat=2)[1]
+    for k in ("dW_ih", "dW_hh", "db_ih", "db_hh", "dx"):
+        # the stored first gradient is rounded to bf16 before the second is
+        # added in fp32 and the sum rounded again: within two bf16 roundings
+        ref = 2.0 * once[k].astype(np.float64)
+        err = np.max(np.abs(twice[k] - ref)) / max(np.max(np.abs(ref)), 1e-30)
+        assert err < 2 ** -7, (k, err)
+
+
 @pytest.mark.parametrize("ra", [True, False])
 @pytest.mark.parametrize("direction,ragged", [(0, False), (1, True)])
 def test_gru_bf16_transposed_weight_gradients(ra, direction, ragged):
