@@ -76,13 +76,6 @@ bool shape_supported(const rnn_desc_t* d) {
   return true;
 }
 
-// bf16 layers run the weight gradients as products over k-contiguous
-// (transposed) operands, the input- and recurrent-side columns of a gate row
-// in one product split at column I (a whole number of 256-wide tiles); T*B is
-// then a whole number of 16-byte chunks
-bool nt_weight_grads(const rnn_desc_t* d) {
-  return d->dtype == RNN_BF16 && ((long long)d->T * d->B) % 8 == 0 && d->I % 256 == 0;
-}
 
 // Step-counter layout of a plan (see FLAG_LINE): adjacent counters for a
 // batch group on one XCD, one line each otherwise; and the count of ints
@@ -107,6 +100,22 @@ bool fused_dw_shape(const rnn_desc_t* d) {
   if (d->dtype != RNN_F32 || d->dw_hh_mode != 0 || d->stepwise) return false;
   const int cell = cell_of(d);
   return (cell == rnn::CELL_LSTM && d->H <= 128) || (cell == rnn::CELL_GRU_RA && d->H <= 256);
+}
+
+// Weight gradients as products over k-contiguous (transposed) operands, the
+// input- and recurrent-side columns of a gate row in one product split at
+// column I (a whole number of 256-wide tiles); T*B is then a whole number of
+// 16-byte chunks. bf16: always (the direct-load kernel). fp32: for long
+// sequences (T*B >= 8192), where the k-contiguous product's gain outweighs
+// the transposes, and not where the BPTT kernel may accumulate dW_hh itself.
+bool nt_weight_grads(const rnn_desc_t* d) {
+  const long long TB = (long long)d->T * d->B;
+  if (TB % 8 || d->I % 256) return false;
+  return d->dtype == RNN_BF16 || (TB >= 8192 && !fused_dw_shape(d));
+}
+hipError_t transpose_dt(int dtype, const rnn::RowMap& src, int R, int T, int B, void* out, hipStream_t s) {
+  return dtype == RNN_BF16 ? rnn::launch_gather_transpose<bf16>(src, R, T, B, out, s)
+                           : rnn::launch_gather_transpose<float>(src, R, T, B, out, s);
 }
 
 Layout layout(const rnn_desc_t* d) {
@@ -816,14 +825,14 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
       // candidate gradient times r, for the recurrent side) by a transpose
       ProfScope ps2(L_AUX, s);
       const long long TB = (long long)d->T * d->B;
-      const hipError_t e = rnn::launch_gather_transpose<bf16>(
+      const hipError_t e = transpose_dt(d->dtype, 
           rows(ws + L.dg + (size_t)G * d->H * esz(d), (long long)L.GD * d->H), (L.GD - G) * d->H, d->T, d->B,
           ws + L.dgt + (size_t)G * d->H * TB * esz(d), s);
       if ((st = hip_status(e))) return st;
     }
   } else if (nt_weight_grads(d)) {
     ProfScope ps(L_AUX, s);
-    const hipError_t e = rnn::launch_gather_transpose<bf16>(rows(ws + L.dg, (long long)L.GD * d->H), L.GD * d->H,
+    const hipError_t e = transpose_dt(d->dtype, rows(ws + L.dg, (long long)L.GD * d->H), L.GD * d->H,
                                                             d->T, d->B, ws + L.dgt, s);
     if ((st = hip_status(e))) return st;
   }
@@ -1022,8 +1031,8 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
   const bool grb_nt = cell == rnn::CELL_GRU_BASIC && dW_ih && dW_hh && !fused && nt_weight_grads(d);
   if (gra_nt) {
     ProfScope ps(L_DW, s);
-    hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
-    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(hprev, H, d->T, d->B, ws + L.ht, s);
+    hipError_t e = transpose_dt(d->dtype, rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
+    if (e == hipSuccess) e = transpose_dt(d->dtype, hprev, H, d->T, d->B, ws + L.ht, s);
     if ((st = hip_status(e))) return st;
     // A rows [lane*H, ...) of the transposed gate gradients
     auto prod = [&](int lane, long long M, rnn::RowMap b, long long N, void* c, long long ldc, long long row0,
@@ -1060,9 +1069,9 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
     if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
   } else if (grb_nt) {
     ProfScope ps(L_DW, s);
-    hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
-    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(hprev, H, d->T, d->B, ws + L.ht, s);
-    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(rows(ws + L.rh, H), H, d->T, d->B, ws + L.rht, s);
+    hipError_t e = transpose_dt(d->dtype, rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
+    if (e == hipSuccess) e = transpose_dt(d->dtype, hprev, H, d->T, d->B, ws + L.ht, s);
+    if (e == hipSuccess) e = transpose_dt(d->dtype, rows(ws + L.rh, H), H, d->T, d->B, ws + L.rht, s);
     if ((st = hip_status(e))) return st;
     // rows [lane*H, lane*H + M) of both weight gradients, one product over
     // [x | act]; the two bias gradients of those rows are equal
@@ -1098,8 +1107,8 @@ int bwd_weights_dir(const rnn_desc_t* d, const void* x, const void* h0, const vo
     // from its row sums
     ProfScope ps(L_DW, s);
     rnn::GemmArgs g{};
-    hipError_t e = rnn::launch_gather_transpose<bf16>(rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
-    if (e == hipSuccess) e = rnn::launch_gather_transpose<bf16>(hprev, H, d->T, d->B, ws + L.ht, s);
+    hipError_t e = transpose_dt(d->dtype, rows(x, ldx_of(d)), d->I, d->T, d->B, ws + L.xt, s);
+    if (e == hipSuccess) e = transpose_dt(d->dtype, hprev, H, d->T, d->B, ws + L.ht, s);
     if ((st = hip_status(e))) return st;
     g.a = rows(ws + L.dgt, TB);
     g.b = rows(ws + L.xt, TB);

@@ -113,6 +113,22 @@ def test_bf16_weight_gradients_without_dx(cell):
             np.testing.assert_array_equal(nodx[k], once[k], err_msg=k)
 
 
+@pytest.mark.parametrize("cell,H", [("lstm", 192), ("gru_ra", 272), ("gru_basic", 64)])
+def test_f32_transposed_weight_gradients(cell, H):
+    # fp32 layers with T*B >= 8192 and I a multiple of 256 (and no fused
+    # dW_hh in the BPTT kernel) run the weight gradients over transposed
+    # operands as bf16 layers do
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=128, B=64, I=256, H=H, h0_std=0.3)
+    if cell == "lstm":
+        changes["c0_std"] = 0.3
+    else:
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    got, ref = _run(wl, inp, P, direction=1)
+    print(compare(got, ref, "f32", extra=f"{cell} H{H} transposed dW"))
+
+
 @pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
 def test_bf16_transposed_weight_gradients_accumulate(cell):
     # accumulate = 1 over the transposed weight-gradient products (both
