@@ -31,8 +31,10 @@ import json
 import os
 import sys
 
-def step_labels(names):
-    """Step of every dispatch, from the kernel names in dispatch order."""
+def step_labels(names, dx_gemms=1):
+    """Step of every dispatch, from the kernel names in dispatch order.
+    `dx_gemms`: input-gradient products after each backward kernel (2 for
+    bidirectional layers: one per direction, the second accumulating)."""
     out, phase, gemms_after_bwd = [], "start", 0
     for n in names:
         if "rec_fwd" in n:
@@ -45,13 +47,15 @@ def step_labels(names):
                 phase = "start"
         elif "gemm_kernel" in n:
             if phase == "after_bwd":
-                lab = "dx_gemm" if gemms_after_bwd == 0 else "dw_gemm"
+                lab = "dx_gemm" if gemms_after_bwd < dx_gemms else "dw_gemm"
                 gemms_after_bwd += 1
             else:
                 lab = "proj_gemm"
         elif "weight_transpose" in n:
             lab = "dx_gemm (W_ih transpose)" if phase == "after_bwd" else "rec_bwd (W_hh transpose)"
         elif "gather_transpose" in n:
+            # after the backward kernel every transpose serves the weight
+            # gradients (the gate gradients, x, h_{t-1})
             lab = "dw_gemm (transposes)" if phase == "after_bwd" else "aux"
         elif "dw_partials_finish" in n:
             lab = "dw_gemm (finish)"
@@ -71,9 +75,9 @@ def short(name: str) -> str:
     return name if len(name) <= 90 else name[:87] + "..."
 
 
-def read_counters(path):
+def read_counters(path, dx_gemms=1):
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
-    labs = step_labels([r["Kernel_Name"] for r in rows])
+    labs = step_labels([r["Kernel_Name"] for r in rows], dx_gemms)
     per = collections.defaultdict(list)
     copies = []
     for r, lab in zip(rows, labs):
@@ -84,7 +88,7 @@ def read_counters(path):
     return per, (max(copies) if copies else None)
 
 
-def read_counter_set(path):
+def read_counter_set(path, dx_gemms=1):
     """{(kernel, step): {counter: mean per dispatch}} from one --pmc pass with
     several counters (one row per dispatch and counter)."""
     by_disp = collections.OrderedDict()
@@ -92,7 +96,7 @@ def read_counter_set(path):
         d = by_disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "c": {}})
         d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
     names = [d["name"] for d in by_disp.values()]
-    labs = step_labels(names)
+    labs = step_labels(names, dx_gemms)
     acc = collections.defaultdict(lambda: collections.defaultdict(list))
     for d, lab in zip(by_disp.values(), labs):
         for c, v in d["c"].items():
@@ -112,7 +116,7 @@ def algorithmic_flops(workload):
             "rec_fwd": 2.0 * TB * GH * wl.H, "rec_bwd": 2.0 * TB * GH * wl.H}
 
 
-def counter_lines(sets, workload, cus=256, simds=4, xcds=8):
+def counter_lines(sets, workload, cus=256, simds=4, xcds=8, dx_gemms=1):
     """Markdown for the MFMA and LDS counter passes. GRBM_GUI_ACTIVE counts
     the dispatch's cycles once per XCD (its sum over a dispatch is the
     duration times the clock times the XCD count); SQ_VALU_MFMA_BUSY_CYCLES
@@ -120,7 +124,7 @@ def counter_lines(sets, workload, cus=256, simds=4, xcds=8):
     lines = []
     alg = algorithmic_flops(workload)
     for path in sets:
-        cs = read_counter_set(path)
+        cs = read_counter_set(path, dx_gemms)
         counters = sorted({c for v in cs.values() for c in v})
         mops = [c for c in counters if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
         lines += ["", f"Counters per dispatch ({', '.join(counters)}), mean over the dispatches of each kernel and step:", ""]
@@ -162,10 +166,12 @@ def main(argv=None):
     ap.add_argument("--command", required=True, help="the command lines that produced the inputs")
     ap.add_argument("--out", required=True)
     ap.add_argument("--traffic-json", default=None)
+    ap.add_argument("--dx-gemms", type=int, default=1,
+                    help="input-gradient products after each backward kernel (2 for bidirectional layers)")
     a = ap.parse_args(argv)
 
     rows = sorted(csv.DictReader(open(a.trace)), key=lambda r: int(r["Dispatch_Id"]))
-    labs = step_labels([r["Kernel_Name"] for r in rows])
+    labs = step_labels([r["Kernel_Name"] for r in rows], a.dx_gemms)
     dur = collections.defaultdict(list)
     for r, lab in zip(rows, labs):
         dur[(r["Kernel_Name"], lab)].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -177,8 +183,8 @@ def main(argv=None):
         lines.append(f"| `{short(name)}` | {lab} | {len(v)} | {sum(v) / len(v):.1f} | {100 * sum(v) / total:.2f} |")
     traffic = {}
     if a.fetch and a.write and a.copy_bytes:
-        fetch, cf = read_counters(a.fetch)
-        write, cw = read_counters(a.write)
+        fetch, cf = read_counters(a.fetch, a.dx_gemms)
+        write, cw = read_counters(a.write, a.dx_gemms)
         kib = a.copy_bytes / 1024.0
         f_scale, w_scale = kib / cf, kib / cw
         lines += ["", f"HBM traffic per launch (FETCH_SIZE x {f_scale:.3f}, WRITE_SIZE x {w_scale:.3f}; factors make "
@@ -194,7 +200,7 @@ def main(argv=None):
             if lab in ("rec_fwd", "rec_bwd", "proj_gemm", "dx_gemm", "dw_gemm"):
                 traffic[lab] = fr + wr
     if a.counters:
-        lines += counter_lines(a.counters, a.workload)
+        lines += counter_lines(a.counters, a.workload, dx_gemms=a.dx_gemms)
     os.makedirs(os.path.dirname(os.path.abspath(a.out)), exist_ok=True)
     with open(a.out, "w") as fh:
         fh.write("\n".join(lines) + "\n")

@@ -14,6 +14,9 @@ def test_step_labels_follow_dispatch_order():
             "dw_gemm", "dw_gemm (finish)", "dw_gemm (finish)"]
     # two steps in a row: the second starts over at its fill
     assert step_labels(step + step) == want + want
+    # bidirectional layer: one input-gradient product per direction
+    bi = ["rec_bwd<...>", "gemm_kernel<dx dir 0>", "gemm_kernel<dx dir 1>", "gather_transpose<x>", "gemm_kernel<dW>"]
+    assert step_labels(bi, dx_gemms=2)[1:] == ["dx_gemm", "dx_gemm", "dw_gemm (transposes)", "dw_gemm"]
     # fused recurrent-weight gradient: the partial sums' finishing pass
     assert step_labels(["rec_bwd<...>", "gemm_kernel<dx>", "gemm_kernel<dW_ih>", "dw_partials_finish<float>"])[-1] \
         == "dw_gemm (finish)"
