@@ -1011,9 +1011,11 @@ GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long lon
   if (t256 >= cu_count) {
     p.bm = p.bn = 256;
   } else if (K >= 4096 && t256 * 2 <= cu_count && ws_floats > 0) {
-    // few tiles and a long contraction: 256x256 tiles split along K
+    // few tiles and a long contraction: 256x256 tiles split along K, as many
+    // slices as keep every tile's slices within one round of the CUs (a
+    // second, partial round would double the time of the last slices)
     p.bm = p.bn = 256;
-    long long ks = (cu_count + t256 - 1) / t256;
+    long long ks = cu_count / t256;
     if (ks > K / 1024) ks = K / 1024;
     if (ks > 8) ks = 8;
     while (ks > 1 && ks * (M * N + M) > ws_floats) --ks;
@@ -1027,7 +1029,7 @@ GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long lon
     // few 128x128 tiles and a moderate contraction: split it into slices of
     // at least 128 so that more CUs take part
     p.bm = p.bn = 128;
-    long long ks = (cu_count + t128 - 1) / t128;
+    long long ks = cu_count / t128;
     if (ks > K / 128) ks = K / 128;
     if (ks > 16) ks = 16;
     while (ks > 1 && ks * (M * N + M) > ws_floats) --ks;
@@ -1035,7 +1037,7 @@ GemmPlan plan_gemm(long long M, long long N, long long K, int cu_count, long lon
   } else {
     // too few tiles: 256x256 tiles split along K, each slice >= 1024 deep
     p.bm = p.bn = 256;
-    long long ks = (cu_count + t256 - 1) / t256;
+    long long ks = cu_count / t256;
     const long long maxk = K / 1024;
     if (ks > maxk) ks = maxk;
     if (ks > 8) ks = 8;
