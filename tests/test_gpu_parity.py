@@ -129,6 +129,16 @@ def test_f32_transposed_weight_gradients(cell, H):
     print(compare(got, ref, "f32", extra=f"{cell} H{H} transposed dW"))
 
 
+@pytest.mark.parametrize("ra", [True, False])
+def test_augru_bf16_transposed_weight_gradients(ra):
+    # AUGRU scores through the transposed weight-gradient products (the
+    # scaled update gate changes every gate gradient they read)
+    wl, inp, P = _case("grura_bf16_t128_b128_i2048_h2048", T=10, B=16, I=256, H=128, h0_std=0.3, reset_after=ra)
+    att = _scores(wl.T, wl.B, 45, "bf16")
+    got, ref = _run(wl, inp, P, att=att)
+    print(compare(got, ref, "bf16", extra=f"augru ra={ra} transposed dW"))
+
+
 @pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
 def test_bf16_transposed_weight_gradients_accumulate(cell):
     # accumulate = 1 over the transposed weight-gradient products (both
@@ -431,6 +441,7 @@ def test_lstm_recompute_with_final_state_gradients(direction):
 @pytest.mark.parametrize("mode,ra,dtype,big,stepwise", [
     ("lstm", None, "f32", False, False), ("gru", True, "f32", False, False), ("gru", False, "f32", False, False),
     ("lstm", None, "bf16", False, False), ("lstm", None, "bf16", True, False),
+    ("gru", True, "bf16", False, False), ("gru", False, "bf16", False, False),
     # the per-step path for both directions of a bidirectional layer
     ("lstm", None, "f32", False, True), ("gru", True, "bf16", False, True), ("gru", False, "f32", False, True)])
 def test_bidirectional_layer_runs_both_directions(mode, ra, dtype, big, stepwise):
