@@ -361,7 +361,7 @@ struct NoAfter {
   __device__ void operator()(const V&) const {}
 };
 template <typename TS, int MB, int NT, int KI, typename Mid = NoMid, typename After = NoAfter>
-__device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const char* xb, int nbytes,
+__device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][wslots<TS>(KI)], const char* xb, int nbytes,
                                            bool packed, Mid mid = Mid(), After after = After()) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)xb, (short)0, nbytes, BUF_RSRC_W3);
@@ -382,18 +382,28 @@ __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[
 #pragma unroll
       for (int i = 0; i < NL; ++i) {
         const uint4 odd = rot8(v[i]);
+        if constexpr (std::is_same<TS, float>::value) {
+          const VPair<TS> vp = vpair<TS>(v[i], odd);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], Wr[nt][2 * i], v[i]);
+          for (int nt = 0; nt < NT; ++nt) mma_pair(acc[0][nt], &Wr[nt][3 * i], vp);
+        } else {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[0][nt], Wr[nt][2 * i + 1], odd);
+          for (int nt = 0; nt < NT; ++nt) acc[0][nt] = mfma_bf16(Wr[nt][2 * i], v[i], acc[0][nt]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[0][nt] = mfma_bf16(Wr[nt][2 * i + 1], odd, acc[0][nt]);
+        }
       }
       after(v);
       return;
     }
   }
   // loads per batch: at most 16 tiles in flight for one row tile, 8 for more
+  // (fp32: whole pairs of k-steps)
   constexpr int LIM = (MB == 1) ? 4 : 8;
-  constexpr int KB = (LIM / MB) < 1 ? 1 : ((LIM / MB) < KI ? (LIM / MB) : KI);
+  constexpr int KB0 = (LIM / MB) < 1 ? 1 : ((LIM / MB) < KI ? (LIM / MB) : KI);
+  constexpr bool F32 = std::is_same<TS, float>::value;
+  constexpr int KB = (F32 && KB0 % 2) ? KB0 + 1 : KB0;
+  static_assert(KI % 2 == 0 && KB % (F32 ? 2 : 1) == 0, "fp32 k-steps are taken in pairs");
 #pragma unroll
   for (int k0 = 0; k0 < KI; k0 += KB) {
     uint4 v[KB][MB];
@@ -413,13 +423,27 @@ __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    if constexpr (!F32) {
+      // bf16: W slot = k-step
 #pragma unroll
-    for (int i = 0; i < KB; ++i) {
-      if (k0 + i >= KI) break;
+      for (int i = 0; i < KB; ++i) {
+        if (k0 + i >= KI) break;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[mb][nt], Wr[nt][k0 + i], v[i][mb]);
+          for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = mfma_bf16(Wr[nt][k0 + i], v[i][mb], acc[mb][nt]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KB; i += 2) {
+        if (k0 + i >= KI) break;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const VPair<TS> vp = vpair<TS>(v[i][mb], v[i + 1][mb]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma_pair(acc[mb][nt], &Wr[nt][3 * ((k0 + i) / 2)], vp);
+        }
+      }
     }
   }
 }
@@ -429,11 +453,12 @@ __device__ __forceinline__ void contract_x(f4 (&acc)[MB][NT], const uint4 (&Wr)[
 // the end of the batch group, or when src is NULL). The wave owns k-steps
 // [w*KI, w*KI+KI) of the contraction.
 template <typename TS, int MB, int NT, int KI>
-__device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][KI], const TS* src,
+__device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT][wslots<TS>(KI)], const TS* src,
                                          long long ld, int b0, int B, int K, int kshift, int kskip) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   // k-steps per load batch: every load of the step at once where registers allow
   constexpr int KB = (MB >= 4) ? 2 : (KI <= 16 ? KI : 16);
+  static_assert(KI % 2 == 0 && KB % 2 == 0, "fp32 k-steps are taken in pairs");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
   if (src == nullptr) return;
@@ -464,13 +489,27 @@ __device__ __forceinline__ void contract(f4 (&acc)[MB][NT], const uint4 (&Wr)[NT
     }
     // keep the whole batch of loads ahead of its products
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (!std::is_same<TS, float>::value) {
+      // bf16: W slot = k-step
 #pragma unroll
-    for (int kk = 0; kk < KB; ++kk) {
-      if (k0 + kk >= KI) break;
+      for (int kk = 0; kk < KB; ++kk) {
+        if (k0 + kk >= KI) break;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) mma<TS>(acc[mb][nt], Wr[nt][k0 + kk], av[kk][mb]);
+          for (int nt = 0; nt < NT; ++nt) acc[mb][nt] = mfma_bf16(Wr[nt][k0 + kk], av[kk][mb], acc[mb][nt]);
+      }
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < KB; kk += 2) {
+        if (k0 + kk >= KI) break;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const VPair<TS> vp = vpair<TS>(av[kk][mb], av[kk + 1][mb]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) mma_pair(acc[mb][nt], &Wr[nt][3 * ((k0 + kk) / 2)], vp);
+        }
+      }
     }
   }
 }
@@ -530,21 +569,25 @@ __device__ __forceinline__ float red_sum(const float* red, int row, int col) {
 
 // Load the B-operand tiles of W_hh rows (forward: output column col of the
 // tile is W_hh row rowof(col); contraction over the H columns of W_hh).
+// (fp32: split into bf16 pieces, a pair of k-steps at a time)
 template <typename TS, int NT, int KI, typename RowOf>
-__device__ __forceinline__ void load_w_rows(uint4 (&Wr)[NT][KI], const TS* W, int H, RowOf rowof) {
+__device__ __forceinline__ void load_w_rows(uint4 (&Wr)[NT][wslots<TS>(KI)], const TS* W, int H, RowOf rowof) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const long long row = rowof(nt * 16 + r16);
+    uint4 c[KI];
 #pragma unroll
     for (int ks = 0; ks < KI; ++ks) {
       const int k = (w * KI + ks) * KSTEP + q * KQ;
       uint4 v = make_uint4(0, 0, 0, 0);
       if (k < H && row >= 0) v = *(const uint4*)(W + row * H + k);
-      Wr[nt][ks] = v;
+      c[ks] = v;
     }
+#pragma unroll
+    for (int p = 0; p < KI / 2; ++p) wpair(c[2 * p], c[2 * p + 1], &Wr[nt][WPair<TS>::N * p], (TS*)nullptr);
   }
 }
 
@@ -552,14 +595,15 @@ __device__ __forceinline__ void load_w_rows(uint4 (&Wr)[NT][KI], const TS* W, in
 // hidden unit J0+col, contraction index k runs over canonical gate rows
 // kb + [0, K): W_hh[perm[g]*H + k%H][J0+col] with g = k/H).
 template <typename TS, int NT, int KI, typename Perm>
-__device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, int H, const Perm& perm, int J0,
-                                            int gate0, int K, bool unit_major = false) {
+__device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][wslots<TS>(KI)], const TS* W, int H, const Perm& perm,
+                                            int J0, int gate0, int K, bool unit_major = false) {
   constexpr int KQ = Chunk<TS>::KQ, KSTEP = 4 * KQ;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int r16 = lane & 15, q = lane >> 4;
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int col = J0 + nt * 16 + r16;
+    uint4 c[KI];
 #pragma unroll
     for (int ks = 0; ks < KI; ++ks) {
       const int k = (w * KI + ks) * KSTEP + q * KQ;
@@ -578,8 +622,10 @@ __device__ __forceinline__ void load_w_cols(uint4 (&Wr)[NT][KI], const TS* W, in
           for (int i = 0; i < KQ; ++i) e[i] = W[((long long)perm[g] * H + kk + i) * H + col];
         }
       }
-      Wr[nt][ks] = *(const uint4*)e;
+      c[ks] = *(const uint4*)e;
     }
+#pragma unroll
+    for (int p = 0; p < KI / 2; ++p) wpair(c[2 * p], c[2 * p + 1], &Wr[nt][WPair<TS>::N * p], (TS*)nullptr);
   }
 }
 
@@ -662,7 +708,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd(RecLaunch L) {
   }
   const bool local = group_is_local(myflag, gflags, a.nSlices, fstride, place_off, a.status, a.timeout_ticks);
 
-  uint4 Wr[NT][KI];
+  uint4 Wr[NT][wslots<TS>(KI)];
   // LSTM columns are unit-major (column 4u+g: gate g of unit u), so that a
   // unit's four gate sums sit in one 16-byte LDS word per wave; the GRU's
   // three lanes are gate-major (column g*HS+u)
@@ -892,7 +938,7 @@ __global__ __launch_bounds__(NW * 64) void rec_fwd_grub(RecLaunch L) {
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H;
 
-  uint4 WA[NTA][KI], WB[NTB][KI];
+  uint4 WA[NTA][wslots<TS>(KI)], WB[NTB][wslots<TS>(KI)];
   load_w_rows<TS, NTA, KI>(WA, (const TS*)a.W_hh, H, [&](int col) -> long long {
     const int g = col / HS;
     return (long long)a.perm[g] * H + J0 + (col - g * HS);
@@ -1105,7 +1151,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd(RecLaunch L) {
   const int xbytes = K * (packed ? 8 : 16 * MB) * (int)sizeof(TS);
   auto xslot = [&](int step) { return a.xbuf + ((long long)(step & 1) * a.nGroups + grp) * a.xg_bytes; };
 
-  uint4 Wr[NT][KI];
+  uint4 Wr[NT][wslots<TS>(KI)];
   // with W_hh transposed into the contraction order, the operands are rows
   // (one 16-byte load each, as in the forward); reading W_hh columns takes
   // one load per element from eight W rows
@@ -1524,7 +1570,7 @@ __global__ __launch_bounds__(NW * 64) void rec_bwd_grub(RecLaunch L) {
   const int bend = min(B, b0 + a.bg);  // rows of this batch group: [b0, bend)
   const long long GZH = (long long)a.GZ * H, GDH = (long long)a.GD * H;
 
-  uint4 WA[NT][KIA], WB[NT][KIB];
+  uint4 WA[NT][wslots<TS>(KIA)], WB[NT][wslots<TS>(KIB)];
   load_w_cols<TS, NT, KIA>(WA, (const TS*)a.W_hh, H, a.perm, J0, 0, 2 * H);
   load_w_cols<TS, NT, KIB>(WB, (const TS*)a.W_hh, H, a.perm, J0, 2, H);
 
@@ -1836,9 +1882,10 @@ int padded_per_xcd(int groups, int slices, int xcds, int cu_count) {
 // batch group shares one XCD and ~2 us across XCDs (measured); a 16x16x32
 // bf16 MFMA occupies its SIMD for 16 cycles (6.67 ns at 2.4 GHz: the
 // published 2.5 PFLOP/s dense peak over 1024 SIMDs), and a wave alone on its
-// SIMD was measured to issue one every ~10.8 ns; a fp32 k-step is four
-// 16x16x4 fp32 MFMAs of 32 cycles each (the published 157.3 TFLOP/s), 8x the
-// bf16 k-step; every CU reads the whole exchanged vector of its group per
+// SIMD was measured to issue one every ~10.8 ns; a fp32 k-step is three such
+// MFMAs per tile (six per pair of k-steps on the bf16 pieces) plus the split
+// of the wave's 4 vector values into pieces, ~22 VALU instructions of 4
+// cycles, once for all tiles; every CU reads the whole exchanged vector of its group per
 // step, ~150 GB/s from the tiled ring and ~75 GB/s from row layout
 // (measured); the gate epilogue costs ~0.2 us per unit a thread carries.
 //
@@ -1860,8 +1907,9 @@ double contraction_us(int nw, int ki, int ntiles, int K, int kstep) {
       busy_worst = busy;
     }
   }
-  const double t_k = (kstep == 32 ? 16.0 : 8.0 * 16.0) / 2.4e3;  // us per 16x16 k-step on a SIMD
-  return worst * ntiles * t_k * (busy_worst >= 2 ? 1.0 : 10.8 / 6.67);
+  const double lone = busy_worst >= 2 ? 1.0 : 10.8 / 6.67;
+  if (kstep == 32) return worst * ntiles * 16.0 / 2.4e3 * lone;  // us per 16x16 k-step on a SIMD
+  return worst * (ntiles * 3.0 * 16.0 * lone + 88.0) / 2.4e3;
 }
 
 double step_cost(const Entry& e, int bg, int span, int H, int K, int kstep, int esize, bool ring) {

@@ -50,6 +50,94 @@ __device__ __forceinline__ void mma(f4& acc, const uint4& a, const uint4& b) {
   mma_step(acc, a, b, (TS*)nullptr);
 }
 
+// ----------------------------------- fp32 products on the bf16 matrix cores --
+// The recurrent kernels take their products two k-steps at a time. For fp32
+// the 8 values a lane holds for the pair (4 of each chunk) are split exactly
+// into three bf16 pieces, x = hi + mid + lo: hi is x with its low 16 bits
+// cleared (truncation), mid the same of x - hi, lo the rest. x - hi is exact
+// in fp32 and carries at most 16 significant bits, so mid takes 8 of them and
+// lo the remaining <= 8, which bf16 holds exactly. A product of two split
+// operands is then the sum of nine piece products; the six with a combined
+// weight of at least 2^-16 (hi*hi, hi*mid, mid*hi, hi*lo, lo*hi, mid*mid) run
+// as v_mfma_f32_16x16x32_bf16, whose piece products are exact and accumulate
+// in fp32. What is left out (mid*lo, lo*mid, lo*lo) is at most ~3*2^-24 of
+// |a||b| per term, the size of an fp32 rounding. This is the six-product
+// variant of the bf16 splitting of Henry, Tang and Heinecke ("Leveraging the
+// bfloat16 artificial intelligence datatype for higher-precision
+// computations", ARITH 2019). Six 16-cycle bf16 MFMAs replace eight 32-cycle
+// v_mfma_f32_16x16x4_f32 per 32 contraction rows.
+//
+// W tiles are split once, when a kernel loads them: uint4 slots per tile for
+// KI k-steps (bf16: one per k-step; fp32: three per pair, hi, mid, lo).
+template <typename TS> struct WPair;
+template <> struct WPair<bf16> { static constexpr int N = 2; };
+template <> struct WPair<float> { static constexpr int N = 3; };
+template <typename TS>
+constexpr int wslots(int ki) { return WPair<TS>::N * (ki / 2); }
+
+// the vector operand of a pair of k-steps, ready for the products
+template <typename TS> struct VPair;
+template <> struct VPair<bf16> { uint4 p[2]; };
+template <> struct VPair<float> { uint4 p[3]; };
+
+// upper halves of two words (x in the low half of the result)
+__device__ __forceinline__ unsigned hi_halves(unsigned x, unsigned y) { return (x >> 16) | (y & 0xFFFF0000u); }
+// x - (x with its low 16 bits cleared), exact
+__device__ __forceinline__ unsigned rest16(unsigned x) {
+  return __float_as_uint(__uint_as_float(x) - __uint_as_float(x & 0xFFFF0000u));
+}
+// pieces of the 8 values of chunks c0 (bf16 elements 0-3) and c1 (4-7)
+__device__ __forceinline__ void split3(const uint4& c0, const uint4& c1, uint4& h, uint4& m, uint4& l) {
+  const unsigned x[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+  unsigned r1[8], r2[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    r1[i] = rest16(x[i]);
+    r2[i] = rest16(r1[i]);
+  }
+  h = make_uint4(hi_halves(x[0], x[1]), hi_halves(x[2], x[3]), hi_halves(x[4], x[5]), hi_halves(x[6], x[7]));
+  m = make_uint4(hi_halves(r1[0], r1[1]), hi_halves(r1[2], r1[3]), hi_halves(r1[4], r1[5]), hi_halves(r1[6], r1[7]));
+  l = make_uint4(hi_halves(r2[0], r2[1]), hi_halves(r2[2], r2[3]), hi_halves(r2[4], r2[5]), hi_halves(r2[6], r2[7]));
+}
+
+__device__ __forceinline__ VPair<bf16> vpair(const uint4& c0, const uint4& c1, bf16*) { return VPair<bf16>{{c0, c1}}; }
+__device__ __forceinline__ VPair<float> vpair(const uint4& c0, const uint4& c1, float*) {
+  VPair<float> v;
+  split3(c0, c1, v.p[0], v.p[1], v.p[2]);
+  return v;
+}
+template <typename TS>
+__device__ __forceinline__ VPair<TS> vpair(const uint4& c0, const uint4& c1) {
+  return vpair(c0, c1, (TS*)nullptr);
+}
+
+// W slots of one pair (W tile first: the accumulator comes out transposed)
+__device__ __forceinline__ void wpair(const uint4& c0, const uint4& c1, uint4* w, bf16*) {
+  w[0] = c0;
+  w[1] = c1;
+}
+__device__ __forceinline__ void wpair(const uint4& c0, const uint4& c1, uint4* w, float*) {
+  split3(c0, c1, w[0], w[1], w[2]);
+}
+
+__device__ __forceinline__ f4 mfma_bf16(const uint4& a, const uint4& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+__device__ __forceinline__ void mma_pair(f4& acc, const uint4* w, const VPair<bf16>& v) {
+  acc = mfma_bf16(w[0], v.p[0], acc);
+  acc = mfma_bf16(w[1], v.p[1], acc);
+}
+__device__ __forceinline__ void mma_pair(f4& acc, const uint4* w, const VPair<float>& v) {
+  // smallest pieces first
+  acc = mfma_bf16(w[1], v.p[1], acc);
+  acc = mfma_bf16(w[2], v.p[0], acc);
+  acc = mfma_bf16(w[0], v.p[2], acc);
+  acc = mfma_bf16(w[1], v.p[0], acc);
+  acc = mfma_bf16(w[0], v.p[1], acc);
+  acc = mfma_bf16(w[0], v.p[0], acc);
+}
+
 // Logistic sigmoid and tanh from the hardware exponential and reciprocal
 // (v_exp_f32, v_rcp_f32: about 1 ulp each); tanh(z) = 2*sigmoid(2z) - 1,
 // which saturates cleanly for large |z|.
