@@ -322,6 +322,28 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) rs[i][e] = 0.f;
   auto kstep = [&](const char* A, const char* Bp) {
+    if constexpr (std::is_same<TS, float>::value && !(BM == 256 && BN == 256)) {
+      // fp32: the k-tile's two k-steps as one pair on the bf16 matrix cores
+      // (each operand split exactly into hi, mid, lo bf16 pieces, six piece
+      // products per output tile); B pieces once per k-tile, A per row tile.
+      // (The 256x256 register-staged kernel keeps the fp32 MFMA: its staging
+      // registers leave no room for the pieces.)
+      VPair<float> bp[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * WN + j * 16 + r16;
+        bp[j] = vpair<float>(*(const uint4*)(Bp + lds_off(r, q)), *(const uint4*)(Bp + lds_off(r, 4 + q)));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * WM + i * 16 + r16;
+        uint4 ap[3];
+        wpair(*(const uint4*)(A + lds_off(r, q)), *(const uint4*)(A + lds_off(r, 4 + q)), ap, (float*)nullptr);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) mma_pair(acc[i][j], ap, bp[j]);
+      }
+      return;
+    }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       uint4 a[FM], b[FN];
@@ -390,30 +412,51 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
       if (kt + 1 < nk) issue((kt + 1) & 1, kt + 1);
       const char* A = sA(kt & 1);
       const char* Bp = sB(kt & 1);
-      uint4 a0[FM], b0[FN], a1[FM], b1[FN];
+      if constexpr (std::is_same<TS, float>::value) {
+        // fp32: the k-tile's two k-steps as one pair on the bf16 matrix
+        // cores, each operand split exactly into hi, mid, lo bf16 pieces (six
+        // piece products per output tile); the B pieces (first MFMA operand)
+        // once per k-tile, the A pieces per row tile
+        uint4 bw[FN][3];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) a0[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, q));
+        for (int j = 0; j < FN; ++j) {
+          const int r = wn * WN + j * 16 + r16;
+          wpair(*(const uint4*)(Bp + lds_off(r, q)), *(const uint4*)(Bp + lds_off(r, 4 + q)), bw[j], (float*)nullptr);
+        }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b0[j] = *(const uint4*)(Bp + lds_off(wn * WN + j * 16 + r16, q));
+        for (int i = 0; i < FM; ++i) {
+          const int r = wm * WM + i * 16 + r16;
+          const VPair<float> av = vpair<float>(*(const uint4*)(A + lds_off(r, q)), *(const uint4*)(A + lds_off(r, 4 + q)));
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
+          for (int j = 0; j < FN; ++j) mma_pair(acc[i][j], bw[j], av);
+        }
+      } else {
+        uint4 a0[FM], b0[FN], a1[FM], b1[FN];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], b0[j], a0[i]);
-        a1[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, 4 + q));
-        if (i < FN) b1[i] = *(const uint4*)(Bp + lds_off(wn * WN + i * 16 + r16, 4 + q));
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < FM; ++i) a0[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, q));
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b0[j] = *(const uint4*)(Bp + lds_off(wn * WN + j * 16 + r16, q));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], b0[j], a0[i]);
+          a1[i] = *(const uint4*)(A + lds_off(wm * WM + i * 16 + r16, 4 + q));
+          if (i < FN) b1[i] = *(const uint4*)(Bp + lds_off(wn * WN + i * 16 + r16, 4 + q));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], b1[j], a1[i]);
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) mma<TS>(acc[i][j], b1[j], a1[i]);
       // A written out transposed: every k-tile, N tile n takes rows
       // [n * rpw, (n+1) * rpw) of the tile in blocks of 8 rows x 2 k (one
       // dword per row from LDS, two output chunks built by byte permutes),
       // spread over the first waves so that no wave carries it alone; lanes
       // with consecutive row blocks write adjacent 16-byte pieces of one
       // output row
-      if (g.at != nullptr) {
+      // (bf16 only: the host never asks an fp32 product for it)
+      if (sizeof(TS) == 2 && g.at != nullptr) {
         const int rpw = nN >= 32 ? 8 : (BM / nN + 7) / 8 * 8;
         const int nb = rpw / 8;
         for (int it = threadIdx.x; it < nb * (BK / 2); it += NT) {
@@ -457,8 +500,10 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
           const uint4 v = *(const uint4*)(A + lds_off(threadIdx.x, c));
           const unsigned* w4 = (const unsigned*)&v;
 #pragma unroll
-          for (int d = 0; d < 4; ++d)
-            rsum += __uint_as_float(w4[d] << 16) + __uint_as_float(w4[d] & 0xFFFF0000u);
+          for (int d = 0; d < 4; ++d) {
+            if constexpr (sizeof(TS) == 2) rsum += __uint_as_float(w4[d] << 16) + __uint_as_float(w4[d] & 0xFFFF0000u);
+            else rsum += __uint_as_float(w4[d]);
+          }
         }
       }
     }
@@ -574,7 +619,8 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
               for (int e = 0; e < 4; ++e) o[e] = (OT)(acc[i][j][e] + bv[e]);
               *(uint2*)(stage + r * RB + pc(r, col >> 3) * 16 + (col & 7) * 2) = *(const uint2*)o;
             } else {
-              *(f4*)(stage + r * RB + pc(r, col >> 2) * 16) = acc[i][j];
+              const f4 bv = part_out ? f4{0.f, 0.f, 0.f, 0.f} : *(const f4*)(sbias + wn * WN + col);
+              *(f4*)(stage + r * RB + pc(r, col >> 2) * 16) = acc[i][j] + bv;
             }
           } else {
 #pragma unroll
@@ -961,12 +1007,12 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Direct-to-LDS operand loads apply to bf16 products with k-contiguous
-// operands in whole 256x256 tiles without a K split, whose operands each span
-// less than DMA_OOB bytes from their base (32-bit record offsets).
+// Direct-to-LDS operand loads apply to products with k-contiguous operands
+// in 256x256 tiles, whose operands each span less than DMA_OOB bytes from
+// their base (32-bit record offsets).
 template <typename TS>
 bool dma_eligible(const GemmArgs& g, int bm, int bn) {
-  if (!std::is_same<TS, bf16>::value || bm != 256 || bn != 256) return false;
+  if (bm != 256 || bn != 256) return false;
   auto span_ok = [&](const RowMap& m, long long rows) {
     if (m.kind != 0 && m.kind != 1) return false;
     const long long bytes = (rows * m.ld + g.K) * (long long)sizeof(TS);
@@ -981,7 +1027,7 @@ bool dma_eligible(const GemmArgs& g, int bm, int bn) {
 
 template <typename TS, bool AKO, bool BKO>
 hipError_t launch_shape(const GemmArgs& g, int bm, int bn, hipStream_t s) {
-  if constexpr (!AKO && !BKO && std::is_same<TS, bf16>::value) {
+  if constexpr (!AKO && !BKO) {
     if (dma_eligible<TS>(g, bm, bn)) {
       if (g.n_split > 0) return launch_tile<TS, false, false, 256, 256, true, true>(g, s);
       return launch_tile<TS, false, false, 256, 256, false, true>(g, s);
@@ -1069,7 +1115,7 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
   // tiles: from the register-staged k-outer A (one part per slice) or from
   // the k-contiguous A tiles of the direct-load kernel (one part per N tile,
   // at most 8). Other products take no row sums, and only the direct-load
-  // kernel writes A out transposed.
+  // kernel of bf16 products writes A out transposed.
   const bool dma = !a_kouter && !b_kouter && dma_eligible<TS>(g, p.bm, p.bn);
   const long long nN = (g.N + p.bn - 1) / p.bn;
   // k-contiguous A without the direct-load kernel: row sums by a pass of
@@ -1077,7 +1123,9 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
   const bool rows_pass = g.rowsum_out && !a_kouter && !dma;
   void* const at = g.at;
   if (at && a_kouter) return hipErrorInvalidValue;
-  if (!dma) g.at = nullptr;
+  // the direct-load kernel writes the transposed A of bf16 products only
+  const bool at_kernel = dma && std::is_same<TS, bf16>::value;
+  if (!at_kernel) g.at = nullptr;
   g.rs_parts = (g.rowsum_out && dma) ? (int)(nN < 8 ? nN : 8) : 1;
   g.rs_slots = rows_pass ? 1 : g.ksplit * g.rs_parts;
   g.rowsum = (g.rowsum_out && g.part) ? g.part + (long long)g.ksplit * g.M * g.N : nullptr;
@@ -1093,7 +1141,7 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
   else if (a_kouter && b_kouter) e = launch_shape<TS, true, true>(gk, p.bm, p.bn, s);
   else return hipErrorInvalidValue;
   if (e != hipSuccess) return e;
-  if (at && !dma) {
+  if (at && !at_kernel) {
     // A rows are M vectors of K: transposed to at[k * M + m]
     if (g.ld_at != g.M || g.M > 0x7fffffff) return hipErrorInvalidValue;
     if ((e = launch_gather_transpose<TS>(g.a, (int)g.K, 1, (int)g.M, at, s)) != hipSuccess) return e;

@@ -183,10 +183,10 @@ Layout layout(const rnn_desc_t* d) {
   // AUGRU: per hidden slice partial score gradients (slices hold >= 16 units)
   L.attp = off;
   if (d->att) off += up(TB * (H / 16) * sizeof(float));
-  // bf16: W_ih transposed to [I][G*H] for the input gradient (a k-contiguous
+  // W_ih transposed to [I][G*H] for the input gradient (a k-contiguous
   // operand, loaded straight into LDS)
   L.wt = off;
-  if (d->dtype == RNN_BF16) off += up((size_t)d->I * gates(d) * H * s);
+  off += up((size_t)d->I * gates(d) * H * s);
   // W_hh transposed to [H][G*H] in the BPTT kernel's contraction order
   L.wht = off;
   if (cell_of(d) != rnn::CELL_GRU_BASIC) off += up((size_t)H * gates(d) * H * s);
@@ -792,18 +792,19 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
     if ((st = hip_status(e))) return st;
   }
   if (io.dx) {
-    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n]; in bf16
-    // through W_ih transposed to [I][G*H] (both operands k-contiguous)
+    // dx[t,b] = sum over input-side gate rows of dG[t,b][n] W_ih[n], through
+    // W_ih transposed to [I][G*H] (both operands k-contiguous)
     ProfScope ps(L_DX, s);
-    const bool wt = d->dtype == RNN_BF16;
-    if (wt) {
+    {
       const hipError_t e =
-          rnn::launch_weight_transpose<bf16>(io.W_ih, G, d->H, d->I, perm, ws + L.wt, (long long)G * d->H, s);
+          d->dtype == RNN_BF16
+              ? rnn::launch_weight_transpose<bf16>(io.W_ih, G, d->H, d->I, perm, ws + L.wt, (long long)G * d->H, s)
+              : rnn::launch_weight_transpose<float>(io.W_ih, G, d->H, d->I, perm, ws + L.wt, (long long)G * d->H, s);
       if ((st = hip_status(e))) return st;
     }
     rnn::GemmArgs g{};
     g.a = rows(ws + L.dg, (long long)L.GD * d->H);
-    g.b = wt ? rows(ws + L.wt, (long long)G * d->H) : perm_rows(io.W_ih, d->I, d->H, perm);
+    g.b = rows(ws + L.wt, (long long)G * d->H);
     g.M = (long long)d->T * d->B;
     g.N = d->I;
     g.K = (long long)G * d->H;
@@ -819,7 +820,7 @@ int bwd_end(const rnn_desc_t* d, const BwdIO& io, char* ws, const rnn::RecPlan& 
       g.at = ws + L.dgt;
       g.ld_at = g.M;
     }
-    if ((st = hip_status(gemm_dt(d->dtype, g, false, !wt, s)))) return st;
+    if ((st = hip_status(gemm_dt(d->dtype, g, false, false, s)))) return st;
     if (nt_weight_grads(d) && L.GD > G) {
       // reset-after GRU: the lane the input gradient does not read (the
       // candidate gradient times r, for the recurrent side) by a transpose

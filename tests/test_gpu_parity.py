@@ -129,6 +129,34 @@ def test_f32_transposed_weight_gradients(cell, H):
     print(compare(got, ref, "f32", extra=f"{cell} H{H} transposed dW"))
 
 
+@pytest.mark.parametrize("cell", ["lstm", "gru_ra", "gru_basic"])
+def test_f32_products_at_fp32_accuracy(cell):
+    # fp32 recurrent products run on the bf16 matrix cores, each operand split
+    # exactly into three bf16 pieces and the six leading piece products
+    # summed: what they leave out is below 3*2^-24 of |a||b| per term, so two
+    # steps at H = 512 (contractions of 512 to 2048 terms) match the fp64
+    # oracle at fp32 rounding level (measured 1e-7 to 1e-6), far inside the
+    # fp32 tolerance. A split that kept two pieces of one operand (terms left
+    # out of size 2^-16 |a||b|) is off by ~1e-5 in the products and fails
+    # these bounds. dx contracts 2048 terms (LSTM) through the fp32 GEMM.
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=2, B=8, I=64, H=512, h0_std=1.0)
+    if cell == "lstm":
+        changes["c0_std"] = 1.0
+    else:
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    rng = np.random.default_rng(46)
+    dhT = rng.standard_normal((wl.B, wl.H))
+    got, ref = _run(wl, inp, P, dhT=dhT)
+    errs = compare(got, ref, "f32", extra=f"{cell} fp32 accuracy")
+    print(cell, {k: f"{e:.2e}" for k, e in errs.items()})
+    for k, bound in (("y", 1.5e-6), ("hT", 1.5e-6), ("cT", 1.5e-6), ("dh0", 1.5e-6), ("dc0", 1.5e-6),
+                     ("dx", 3e-6), ("dW_ih", 1.5e-6), ("dW_hh", 1.5e-6)):
+        if k in errs:
+            assert errs[k] <= bound, (k, errs[k])
+
+
 @pytest.mark.parametrize("ra", [True, False])
 def test_augru_bf16_transposed_weight_gradients(ra):
     # AUGRU scores through the transposed weight-gradient products (the
