@@ -336,7 +336,8 @@ __device__ __forceinline__ int xoff(int row, int kg, bool packed, int mbt) {
 }
 
 __device__ __forceinline__ unsigned rot8(unsigned v) {
-  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+  // row_ror:8 (every source lane is inside the row, so no old value is kept)
+  return (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, true);
 }
 __device__ __forceinline__ uint4 rot8(const uint4& v) { return make_uint4(rot8(v.x), rot8(v.y), rot8(v.z), rot8(v.w)); }
 

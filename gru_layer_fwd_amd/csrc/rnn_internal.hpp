@@ -53,19 +53,23 @@ __device__ __forceinline__ void mma(f4& acc, const uint4& a, const uint4& b) {
 // ----------------------------------- fp32 products on the bf16 matrix cores --
 // The recurrent kernels take their products two k-steps at a time. For fp32
 // the 8 values a lane holds for the pair (4 of each chunk) are split exactly
-// into three bf16 pieces, x = hi + mid + lo: hi is x with its low 16 bits
-// cleared (truncation), mid the same of x - hi, lo the rest. x - hi is exact
-// in fp32 and carries at most 16 significant bits, so mid takes 8 of them and
-// lo the remaining <= 8, which bf16 holds exactly. A product of two split
-// operands is then the sum of nine piece products; the six with a combined
-// weight of at least 2^-16 (hi*hi, hi*mid, mid*hi, hi*lo, lo*hi, mid*mid) run
-// as v_mfma_f32_16x16x32_bf16, whose piece products are exact and accumulate
-// in fp32. What is left out (mid*lo, lo*mid, lo*lo) is at most ~3*2^-24 of
+// into three bf16 pieces, x = hi + mid + lo: hi is x rounded to bf16 (to
+// nearest even), mid the same of r = x - hi, lo = r - mid. x - hi is exact in
+// fp32 and carries at most 16 significant bits (it is a multiple of x's last
+// unit and at most half a bf16 unit of x), so mid takes 8 of them and lo the
+// remaining <= 8, which bf16 holds exactly. A product of two split operands
+// is then the sum of nine piece products; the six with a combined weight of
+// at least 2^-16 (hi*hi, hi*mid, mid*hi, hi*lo, lo*hi, mid*mid) run as
+// v_mfma_f32_16x16x32_bf16, whose piece products are exact and accumulate in
+// fp32. What is left out (mid*lo, lo*mid, lo*lo) is at most ~3*2^-24 of
 // |a||b| per term, the size of an fp32 rounding. This is the six-product
 // variant of the bf16 splitting of Henry, Tang and Heinecke ("Leveraging the
 // bfloat16 artificial intelligence datatype for higher-precision
 // computations", ARITH 2019). Six 16-cycle bf16 MFMAs replace eight 32-cycle
-// v_mfma_f32_16x16x4_f32 per 32 contraction rows.
+// v_mfma_f32_16x16x4_f32 per 32 contraction rows. Per two values the split
+// is three v_cvt_pk_bf16_f32 and four v_dot2c_f32_bf16 (x - piece as a bf16
+// dot product with (-1, 0) or (0, -1) accumulated onto x: exact, since the
+// difference is representable).
 //
 // W tiles are split once, when a kernel loads them: uint4 slots per tile for
 // KI k-steps (bf16: one per k-step; fp32: three per pair, hi, mid, lo).
@@ -80,24 +84,40 @@ template <typename TS> struct VPair;
 template <> struct VPair<bf16> { uint4 p[2]; };
 template <> struct VPair<float> { uint4 p[3]; };
 
-// upper halves of two words (x in the low half of the result)
-__device__ __forceinline__ unsigned hi_halves(unsigned x, unsigned y) { return (x >> 16) | (y & 0xFFFF0000u); }
-// x - (x with its low 16 bits cleared), exact
-__device__ __forceinline__ unsigned rest16(unsigned x) {
-  return __float_as_uint(__uint_as_float(x) - __uint_as_float(x & 0xFFFF0000u));
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// two values rounded to bf16 (x0 in the low half)
+__device__ __forceinline__ unsigned pk_bf16(float x0, float x1) {
+  const bf16x2 v = {(bf16)x0, (bf16)x1};
+  return __builtin_bit_cast(unsigned, v);
+}
+// x0 - (low half of p), x1 - (high half of p). The (-1, 0) pair goes in a
+// register: left to the compiler it becomes the inline constant -1.0, which
+// the hardware reads as the fp32 bit pattern, i.e. the pair (0, -1) (an
+// in-bounds probe on gfx950: 63 of 64 differences wrong that way, none with
+// the register operand).
+__device__ __forceinline__ float less_lo(unsigned p, float x0) {
+  unsigned n = 0x0000BF80u;
+  asm("" : "+v"(n));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), __builtin_bit_cast(bf16x2, n), x0, false);
+}
+__device__ __forceinline__ float less_hi(unsigned p, float x1) {
+  const bf16x2 n = {(bf16)0.0f, (bf16)-1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p), n, x1, false);
+}
+// pieces of two values: hi, mid, lo words (x0 in the low halves)
+__device__ __forceinline__ void split2(unsigned a, unsigned b, unsigned& h, unsigned& m, unsigned& l) {
+  const float x0 = __uint_as_float(a), x1 = __uint_as_float(b);
+  h = pk_bf16(x0, x1);
+  const float r0 = less_lo(h, x0), r1 = less_hi(h, x1);
+  m = pk_bf16(r0, r1);
+  l = pk_bf16(less_lo(m, r0), less_hi(m, r1));
 }
 // pieces of the 8 values of chunks c0 (bf16 elements 0-3) and c1 (4-7)
 __device__ __forceinline__ void split3(const uint4& c0, const uint4& c1, uint4& h, uint4& m, uint4& l) {
-  const unsigned x[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-  unsigned r1[8], r2[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    r1[i] = rest16(x[i]);
-    r2[i] = rest16(r1[i]);
-  }
-  h = make_uint4(hi_halves(x[0], x[1]), hi_halves(x[2], x[3]), hi_halves(x[4], x[5]), hi_halves(x[6], x[7]));
-  m = make_uint4(hi_halves(r1[0], r1[1]), hi_halves(r1[2], r1[3]), hi_halves(r1[4], r1[5]), hi_halves(r1[6], r1[7]));
-  l = make_uint4(hi_halves(r2[0], r2[1]), hi_halves(r2[2], r2[3]), hi_halves(r2[4], r2[5]), hi_halves(r2[6], r2[7]));
+  split2(c0.x, c0.y, h.x, m.x, l.x);
+  split2(c0.z, c0.w, h.y, m.y, l.y);
+  split2(c1.x, c1.y, h.z, m.z, l.z);
+  split2(c1.z, c1.w, h.w, m.w, l.w);
 }
 
 __device__ __forceinline__ VPair<bf16> vpair(const uint4& c0, const uint4& c1, bf16*) { return VPair<bf16>{{c0, c1}}; }
