@@ -1805,6 +1805,7 @@ const Entry kTable[] = {
     {CELL_LSTM, 1, 1, 8, 1, 8, 4, 0, F_LSTM(bf16, 8, 1, 8, 4)},
     {CELL_LSTM, 1, 1, 4, 8, 2, 16, 0, F_LSTM(bf16, 4, 8, 2, 16)},
     {CELL_LSTM, 1, 1, 8, 8, 2, 8, 0, F_LSTM(bf16, 8, 8, 2, 8)},
+    {CELL_LSTM, 1, 1, 4, 4, 4, 16, 0, F_LSTM(bf16, 4, 4, 4, 16)},
     {CELL_LSTM, 0, 1, 4, 1, 4, 8, 0, F_LSTM(float, 4, 1, 4, 8)},
     {CELL_LSTM, 0, 1, 4, 1, 1, 8, 0, F_LSTM(float, 4, 1, 1, 8)},
     {CELL_LSTM, 0, 1, 8, 1, 4, 4, 0, F_LSTM(float, 8, 1, 4, 4)},
