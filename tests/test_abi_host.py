@@ -182,6 +182,16 @@ def test_headline_plan_one_batch_group_per_xcd():
         assert 0 < pl.model_us_per_step < 10
 
 
+def test_large_lstm_forward_plan_two_64_row_groups():
+    # B = 128, H = 2048 bf16: two groups of 64 rows over 128 slices of 16
+    # units (4 waves), half the per-step vector reads of one 128-row group
+    d = g.make_desc(L.RNN_LSTM, 128, 128, 2048, 2048, L.RNN_BF16)
+    st, pl = _plan(d, 0)
+    assert st == L.RNN_OK
+    assert (pl.groups, pl.rows, pl.slices, pl.units, pl.waves) == (2, 64, 128, 16, 4)
+    assert pl.workgroups == 256 and pl.stepwise == 0
+
+
 def test_coresidency_refusal_with_injected_cu_count():
     d = g.make_desc(L.RNN_LSTM, 256, 64, 1024, 1024, L.RNN_BF16)
     # half the chip: the planner still finds a grid that fits (16-row groups)

@@ -397,6 +397,14 @@ def test_grura_bf16_h1024_augru(rows):
     print(compare(got, ref, "bf16", extra=f"grura h1024 B{rows}"))
 
 
+def test_lstm_bf16_h2048_64_row_groups_ragged():
+    # B = 72 at H = 2048: the forward runs two groups of 64 rows (the second
+    # holding 8) on the 4-wave 64-row kernel, the BPTT 64-row groups as well
+    wl, inp, P = _case("lstm_bf16_t128_b128_i2048_h2048", T=4, B=72, I=64, H=2048, h0_std=0.3, c0_std=0.3)
+    got, ref = _run(wl, inp, P, 1, lengths=_ragged_lengths(wl.B, wl.T, 47))
+    print(compare(got, ref, "bf16", extra="lstm h2048 B72"))
+
+
 # -------------------------------------------- lengths / scores: edges ----
 
 def _edge_case(mode, ra, **sizes):
