@@ -157,6 +157,22 @@ def test_f32_products_at_fp32_accuracy(cell):
             assert errs[k] <= bound, (k, errs[k])
 
 
+def test_f32_direct_load_gemms_ragged():
+    # fp32 products on the direct-to-LDS GEMM kernel (split bf16 pieces) with
+    # ragged sizes: T*B = 8200 rows (the projection's last 256-row tile holds
+    # 8), the transposed weight-gradient products split along K = 8200 into 8
+    # slices of 1088 with a shorter last one, and the bias row sums from the
+    # LDS tiles. The recurrence takes the per-step path at this batch.
+    wl, inp, P = _case("bilstm2_f32_t512_b32_i512_h512", T=41, B=200, I=512, H=512, layers=1, bidir=False,
+                       h0_std=0.3, c0_std=0.3)
+    got, ref = _run(wl, inp, P, 0)
+    errs = compare(got, ref, "f32", extra="f32 direct-load GEMMs, ragged")
+    print(errs)
+    # at fp32 rounding level (measured <= 1.5e-6), as the split products give
+    for k, e in errs.items():
+        assert e <= 5e-6, (k, e)
+
+
 @pytest.mark.parametrize("ra", [True, False])
 def test_augru_bf16_transposed_weight_gradients(ra):
     # AUGRU scores through the transposed weight-gradient products (the
