@@ -23,7 +23,12 @@ import os
 import sys
 import time
 
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, MI355X
+# dense MFMA ceilings on MI355X for the arithmetic each storage type runs on:
+# bf16 products at the published 2.5 PFLOP/s; fp32 products run as six
+# bf16 MFMAs on exact three-piece splits of their operands, so their ceiling
+# is the bf16 peak over six (the published fp32 matrix peak, 157.3 TFLOP/s,
+# is what the fp32 MFMA instructions would give and lies below it)
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 2500.0 / 6}
 PEAK_HBM_GBS = 8000.0
 
 
