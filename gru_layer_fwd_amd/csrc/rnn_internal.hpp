@@ -51,8 +51,10 @@ __device__ __forceinline__ void mma(f4& acc, const uint4& a, const uint4& b) {
 }
 
 // ----------------------------------- fp32 products on the bf16 matrix cores --
-// The recurrent kernels take their products two k-steps at a time. For fp32
-// the 8 values a lane holds for the pair (4 of each chunk) are split exactly
+// The recurrent kernels and the GEMMs take fp32 products two k-steps at a
+// time (mma_step's fp32 form remains for the 256x256 register-staged GEMM,
+// which has no registers left for the pieces). The 8 values a lane holds for
+// the pair (4 of each chunk) are split exactly
 // into three bf16 pieces, x = hi + mid + lo: hi is x rounded to bf16 (to
 // nearest even), mid the same of r = x - hi, lo = r - mid. x - hi is exact in
 // fp32 and carries at most 16 significant bits (it is a multiple of x's last
