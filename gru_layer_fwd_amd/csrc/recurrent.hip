@@ -1886,8 +1886,9 @@ int padded_per_xcd(int groups, int slices, int xcds, int cu_count) {
 // published 2.5 PFLOP/s dense peak over 1024 SIMDs), and a wave alone on its
 // SIMD was measured to issue one every ~10.8 ns; a fp32 k-step is three such
 // MFMAs per tile (six per pair of k-steps on the bf16 pieces) plus the split
-// of the wave's 4 vector values into pieces, ~22 VALU instructions of 4
-// cycles, once for all tiles; every CU reads the whole exchanged vector of its group per
+// of the wave's 4 vector values into pieces, 14 VALU instructions of 4
+// cycles (three conversions and four dot products per two values), once for
+// all tiles; every CU reads the whole exchanged vector of its group per
 // step, ~150 GB/s from the tiled ring and ~75 GB/s from row layout
 // (measured); the gate epilogue costs ~0.2 us per unit a thread carries.
 //
@@ -1911,7 +1912,7 @@ double contraction_us(int nw, int ki, int ntiles, int K, int kstep) {
   }
   const double lone = busy_worst >= 2 ? 1.0 : 10.8 / 6.67;
   if (kstep == 32) return worst * ntiles * 16.0 / 2.4e3 * lone;  // us per 16x16 k-step on a SIMD
-  return worst * (ntiles * 3.0 * 16.0 * lone + 88.0) / 2.4e3;
+  return worst * (ntiles * 3.0 * 16.0 * lone + 56.0) / 2.4e3;
 }
 
 double step_cost(const Entry& e, int bg, int span, int H, int K, int kstep, int esize, bool ring) {
