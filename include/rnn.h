@@ -89,7 +89,11 @@ typedef struct rnn_desc {
   int gate_order[4]; /* gate_order[k] = gate id stored in row block k; a permutation of
                         0..G-1 (LSTM i,f,g,o = 0..3; GRU r,u,c = 0..2). Common orders:
                         LSTM {0,1,2,3} (i,f,g,o) and {1,0,2,3} (f,i,g,o); GRU {0,1,2} */
-  int dtype;         /* RNN_F32 or RNN_BF16 storage; arithmetic accumulates in fp32 */
+  int dtype;         /* RNN_F32 or RNN_BF16 storage; arithmetic accumulates in fp32
+                        (RNN_F32 products run on the bf16 matrix cores, each
+                        operand split exactly into three bf16 pieces and the six
+                        leading piece products summed: results at fp32 rounding
+                        level) */
   int T, B, I, H;    /* T,B >= 1; I % 8 == 0; H % 16 == 0 */
   long long ldx;     /* row stride of x/dx in elements, 0 = I; multiple of 8 */
   long long ldy;     /* row stride of y/dy in elements, 0 = H (direction 2: 2H); multiple of 8 */
