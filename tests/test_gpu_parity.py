@@ -297,6 +297,42 @@ def test_variable_lengths_bf16_medium(cell, H, direction):
     print(compare(got, ref, "bf16", extra=f"{cell} H{H} dir{direction}"))
 
 
+def test_bidir_stack_on_a_side_stream():
+    """A bidirectional stack run on a stream other than torch's current one
+    (default priority): its stacked temporaries and gradient copy-backs are
+    ordered with the library's kernels on that stream, so the results equal
+    those of the current-stream run bit for bit; a raw handle is refused."""
+    from gru_layer_fwd_amd.api import RnnStack
+    from rnn_harness import dev
+    T, B, I, H = 9, 5, 24, 32
+    wl = synth.small(W["bilstm2_f32_t512_b32_i512_h512"], T=T, B=B, I=I, H=H, layers=2, bidir=True, w_scale=0.15)
+    inp = synth.make_inputs(wl)
+    params = [[tuple(dev(a, "f32") for a in (p.W_ih, p.W_hh, p.b_ih, p.b_hh)) for p in per] for per in inp["params"]]
+    x, g = dev(inp["x"], "f32"), dev(inp["g"], "f32")
+
+    def run(stream):
+        st = RnnStack("lstm", T, B, I, H, "f32", 2, True)
+        grads = [[tuple(torch.zeros_like(t) for t in pd) for pd in per] for per in params]
+        dx = torch.empty_like(x)
+        y = st.fwd(x, params, stream=stream)
+        st.bwd(x, params, g, dx, grads, stream=stream)
+        if stream is not None:
+            torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        return y.clone(), dx, grads
+
+    y0, dx0, g0 = run(None)
+    side = torch.cuda.Stream()
+    y1, dx1, g1 = run(side)
+    assert torch.equal(y0, y1) and torch.equal(dx0, dx1)
+    for li in range(2):
+        for d in range(2):
+            for a, b in zip(g0[li][d], g1[li][d]):
+                assert torch.equal(a, b)
+    with pytest.raises(TypeError):
+        RnnStack("lstm", T, B, I, H, "f32", 2, True).fwd(x, params, stream=side.cuda_stream)
+
+
 @pytest.mark.parametrize("mode", ["lstm", "gru"])
 def test_bidir_stack_variable_lengths(mode):
     """Two bidirectional layers sharing one lengths array and nonzero h0/c0:
