@@ -457,6 +457,46 @@ def test_lstm_bf16_h2048_64_row_groups_ragged():
     print(compare(got, ref, "bf16", extra="lstm h2048 B72"))
 
 
+# --------------------------------------------- seeded shape sweep -------
+# Cells, storage types, directions and sizes drawn once from a fixed seed:
+# odd batches, T from 1, I a multiple of 8 and H of 16 that are mostly not
+# multiples of 32 (ragged MFMA tiles and k-steps in the products), ragged
+# lengths on some. Every element against the oracle.
+
+def _sweep_cases(n=18, seed=2026):
+    rng = np.random.default_rng(seed)
+    cells = ["lstm", "gru_ra", "gru_basic"]
+    out = []
+    for i in range(n):
+        cell = cells[i % 3]
+        dtype = "f32" if (i // 3) % 2 == 0 else "bf16"
+        T = int(rng.choice([1, 2, 3, 5, 7]))
+        B = int(rng.choice([1, 3, 5, 9, 17, 20]))
+        I = int(rng.choice([8, 24, 40, 72, 136]))
+        H = int(rng.choice([16, 48, 80, 112, 144, 208]))  # H % 16 == 0 (the boundary's granularity)
+        direction = int(rng.integers(0, 2))
+        ragged = bool(rng.integers(0, 2)) and T > 1
+        out.append((cell, dtype, T, B, I, H, direction, ragged))
+    return out
+
+
+@pytest.mark.parametrize("cell,dtype,T,B,I,H,direction,ragged", _sweep_cases())
+def test_seeded_shape_sweep(cell, dtype, T, B, I, H, direction, ragged):
+    name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
+    changes = dict(T=T, B=B, I=I, H=H, h0_std=0.5, w_scale=0.3, dtype=dtype)
+    if cell == "lstm":
+        changes["c0_std"] = 0.5
+    else:
+        changes["reset_after"] = cell == "gru_ra"
+    wl, inp, P = _case(name, **changes)
+    lengths = _ragged_lengths(B, T, 100 + T * B) if ragged else None
+    rng = np.random.default_rng(H * 7 + I)
+    dhT = rng.standard_normal((B, H))
+    dcT = rng.standard_normal((B, H)) if cell == "lstm" else None
+    got, ref = _run(wl, inp, P, direction, dhT=dhT, dcT=dcT, lengths=lengths)
+    print(compare(got, ref, dtype, extra=f"{cell} {dtype} T{T} B{B} I{I} H{H} dir{direction} ragged={ragged}"))
+
+
 # -------------------------------------------- lengths / scores: edges ----
 
 def _edge_case(mode, ra, **sizes):
