@@ -483,7 +483,10 @@ def _sweep_cases(n=18, seed=2026):
 @pytest.mark.parametrize("cell,dtype,T,B,I,H,direction,ragged", _sweep_cases())
 def test_seeded_shape_sweep(cell, dtype, T, B, I, H, direction, ragged):
     name = "lstm_f32_t8_b2_i16_h32" if cell == "lstm" else "grura_f32_t64_b16_i256_h256"
-    changes = dict(T=T, B=B, I=I, H=H, h0_std=0.5, w_scale=0.3, dtype=dtype)
+    # weights ~ U(+-2/sqrt(H)): pre-activations of order one whatever H (the
+    # workloads' own scale is 1/sqrt(H); far larger weights at large H put
+    # bf16-rounded inputs' error alone near the bf16 tolerance)
+    changes = dict(T=T, B=B, I=I, H=H, h0_std=0.5, w_scale=2.0 / np.sqrt(H), dtype=dtype)
     if cell == "lstm":
         changes["c0_std"] = 0.5
     else:
@@ -495,6 +498,30 @@ def test_seeded_shape_sweep(cell, dtype, T, B, I, H, direction, ragged):
     dcT = rng.standard_normal((B, H)) if cell == "lstm" else None
     got, ref = _run(wl, inp, P, direction, dhT=dhT, dcT=dcT, lengths=lengths)
     print(compare(got, ref, dtype, extra=f"{cell} {dtype} T{T} B{B} I{I} H{H} dir{direction} ragged={ragged}"))
+
+
+def _sweep_cases_large(n=12, seed=2027):
+    # larger hidden sizes and batches, which take the persistent plans' other
+    # instantiations (8-wave kernels, several batch groups, multi-tile rows)
+    rng = np.random.default_rng(seed)
+    cells = ["lstm", "gru_ra", "gru_basic"]
+    out = []
+    for i in range(n):
+        cell = cells[i % 3]
+        dtype = "f32" if (i // 3) % 2 == 0 else "bf16"
+        T = int(rng.choice([2, 3, 4]))
+        B = int(rng.choice([12, 33, 64, 100]))
+        I = int(rng.choice([64, 136, 256]))
+        H = int(rng.choice([256, 384, 512] if dtype == "f32" else [256, 512, 768, 1024]))
+        direction = int(rng.integers(0, 2))
+        ragged = bool(rng.integers(0, 2))
+        out.append((cell, dtype, T, B, I, H, direction, ragged))
+    return out
+
+
+@pytest.mark.parametrize("cell,dtype,T,B,I,H,direction,ragged", _sweep_cases_large())
+def test_seeded_shape_sweep_large(cell, dtype, T, B, I, H, direction, ragged):
+    test_seeded_shape_sweep(cell, dtype, T, B, I, H, direction, ragged)
 
 
 # -------------------------------------------- lengths / scores: edges ----
