@@ -1831,6 +1831,7 @@ const Entry kTable[] = {
     {CELL_GRU_RA, 1, 0, 4, 1, 1, 32, 0, B_GRA(bf16, 4, 1, 1, 32)},
     {CELL_GRU_RA, 1, 0, 8, 1, 2, 16, 0, B_GRA(bf16, 8, 1, 2, 16)},
     {CELL_GRU_RA, 1, 0, 4, 4, 1, 48, 0, B_GRA(bf16, 4, 4, 1, 48)},
+    {CELL_GRU_RA, 1, 0, 8, 4, 1, 24, 0, B_GRA(bf16, 8, 4, 1, 24)},
     {CELL_GRU_RA, 0, 0, 4, 1, 1, 32, 0, B_GRA(float, 4, 1, 1, 32)},
     {CELL_GRU_RA, 0, 0, 4, 1, 1, 12, 0, B_GRA_FDW(float, 4, 1, 1, 12)},
     {CELL_GRU_RA, 0, 0, 8, 1, 1, 6, 0, B_GRA_FDW(float, 8, 1, 1, 6)},

@@ -192,6 +192,15 @@ def test_large_lstm_forward_plan_two_64_row_groups():
     assert pl.workgroups == 256 and pl.stepwise == 0
 
 
+def test_large_gru_bptt_plan_eight_waves():
+    # reset-after GRU B = 128, H = 2048 bf16 BPTT: 64-row groups on the
+    # 8-wave kernel (two waves per SIMD issue its MFMAs at the full rate)
+    d = g.make_desc(L.RNN_GRU, 128, 128, 2048, 2048, L.RNN_BF16, reset_after=1)
+    st, pl = _plan(d, 1)
+    assert st == L.RNN_OK
+    assert (pl.groups, pl.rows, pl.slices, pl.units, pl.waves) == (2, 64, 128, 16, 8)
+
+
 def test_coresidency_refusal_with_injected_cu_count():
     d = g.make_desc(L.RNN_LSTM, 256, 64, 1024, 1024, L.RNN_BF16)
     # half the chip: the planner still finds a grid that fits (16-row groups)
