@@ -681,9 +681,9 @@ __global__ __launch_bounds__((Waves<BM, BN>::NT)) void gemm_kernel(GemmArgs g) {
 // loads, one 16-byte bf16 or two fp32 stores), so the pass runs at stream
 // rate rather than at the latency of single-element accesses.
 template <typename TS>
-__global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
+__device__ __forceinline__ void splitk_finish(const GemmArgs& g, int blk) {
   constexpr int V = 8;
-  const long long idx = ((long long)blockIdx.x * 256 + threadIdx.x) * V;
+  const long long idx = ((long long)blk * 256 + threadIdx.x) * V;
   if (idx >= g.M * g.N) return;
   const long long m = idx / g.N, n = idx - m * g.N;
   float v[V];
@@ -731,8 +731,8 @@ __global__ __launch_bounds__(256) void splitk_finish(GemmArgs g) {
 // Bias gradients from the per-slice row sums: out[perm(row0+m)] (+)= sum_kz rows[kz][m]
 // (and the same into out2 when the two bias gradients coincide).
 template <typename TS>
-__global__ __launch_bounds__(256) void rowsum_finish(GemmArgs g) {
-  const long long m = (long long)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void rowsum_finish(const GemmArgs& g, int blk) {
+  const long long m = (long long)blk * 256 + threadIdx.x;
   if (m >= g.M) return;
   float v = 0.f;
   // slots loaded 8 at a time, then added in order
@@ -756,6 +756,15 @@ __global__ __launch_bounds__(256) void rowsum_finish(GemmArgs g) {
     if (g.accumulate) w2 += to_f(*o2);
     *o2 = from_f<TS>(w2);
   }
+}
+
+// The finishing passes of a product in one launch: blocks [0, nsplit) sum
+// the split-K partial tiles (when K was split), the rest the bias row sums
+// (when asked for). The two read and write disjoint buffers.
+template <typename TS>
+__global__ __launch_bounds__(256) void gemm_finish(GemmArgs g, int nsplit) {
+  if ((int)blockIdx.x < nsplit) splitk_finish<TS>(g, blockIdx.x);
+  else rowsum_finish<TS>(g, blockIdx.x - nsplit);
 }
 
 // Deterministic two-pass column sums (fixed summation order).
@@ -1151,15 +1160,18 @@ hipError_t launch_gemm(const GemmArgs& g0, bool a_kouter, bool b_kouter, int cu_
     hipLaunchKernelGGL((rowsum_rows<TS>), dim3((unsigned)g.M), dim3(256), 0, s, g.a, g.K, g.rowsum);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
+  // the split-K sum and the bias row sums in one launch
+  long long nsplit = 0, nrows = 0;
   if (g.ksplit > 1) {
     const long long n = g.M * g.N;
     if (g.N % 8 != 0 || g.ldc % 8 != 0 || (g.n_split > 0 && (g.ldc2 % 8 != 0 || g.n_split % 8 != 0)))
       return hipErrorInvalidValue;  // whole 8-column groups with 16-byte aligned rows
-    hipLaunchKernelGGL(splitk_finish<TS>, dim3((unsigned)((n / 8 + 255) / 256)), dim3(256), 0, s, g);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    nsplit = (n / 8 + 255) / 256;
   }
-  if (g.rowsum_out) {
-    hipLaunchKernelGGL(rowsum_finish<TS>, dim3((unsigned)((g.M + 255) / 256)), dim3(256), 0, s, g);
+  if (g.rowsum_out) nrows = (g.M + 255) / 256;
+  if (nsplit + nrows > 0) {
+    if (nsplit + nrows > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(gemm_finish<TS>, dim3((unsigned)(nsplit + nrows)), dim3(256), 0, s, g, (int)nsplit);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

@@ -59,7 +59,7 @@ def step_labels(names, dx_gemms=1):
             lab = "dw_gemm (transposes)" if phase == "after_bwd" else "aux"
         elif "dw_partials_finish" in n:
             lab = "dw_gemm (finish)"
-        elif "splitk_finish" in n or "rowsum_finish" in n or "rowsum_rows" in n:
+        elif "gemm_finish" in n or "splitk_finish" in n or "rowsum_finish" in n or "rowsum_rows" in n:
             lab = "dw_gemm (finish)" if phase == "after_bwd" else "proj_gemm (finish)"
         elif "colsum" in n:
             lab = "db_colsum"

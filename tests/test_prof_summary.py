@@ -17,6 +17,9 @@ def test_step_labels_follow_dispatch_order():
     # bidirectional layer: one input-gradient product per direction
     bi = ["rec_bwd<...>", "gemm_kernel<dx dir 0>", "gemm_kernel<dx dir 1>", "gather_transpose<x>", "gemm_kernel<dW>"]
     assert step_labels(bi, dx_gemms=2)[1:] == ["dx_gemm", "dx_gemm", "dw_gemm (transposes)", "dw_gemm"]
+    # the combined split-K / row-sum finishing pass
+    assert step_labels(["rec_bwd<...>", "gemm_kernel<dx>", "gemm_kernel<dW>", "gemm_finish<bf16>"])[-1] \
+        == "dw_gemm (finish)"
     # fused recurrent-weight gradient: the partial sums' finishing pass
     assert step_labels(["rec_bwd<...>", "gemm_kernel<dx>", "gemm_kernel<dW_ih>", "dw_partials_finish<float>"])[-1] \
         == "dw_gemm (finish)"
